@@ -1,0 +1,196 @@
+/* libmoeq8 -- quantized MoE expert FFN (Q8_0 weights x q8_1 activations) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the DS4.1 verify/decode MoE layer described on
+ * lucebox PR #826 "feat(ds41): two-box expert-parallel serving":
+ *   - the commit on fused DS4.1 decode kernels: the router's select and weights
+ *     over the same logits in one launch, one expert grouping per MoE layer for
+ *     gate, up and down, a q8_1 activation memo, and column-range Q8_0 products
+ *     that keep the whole row's lane mapping;
+ *   - the commit adding the RDNA4 Q8_0 gate/up pair: both Q8_0 products read one
+ *     load of each activation fragment, keep the single product's partials and
+ *     reduction, and write SwiGLU-DS4 of the two in the epilogue; batch
+ *     invariant from 1 to 8 columns (the single-token gate/up pair commit);
+ *   - the commit on the fused routed combine: owner route mask, route weighting
+ *     and route sum in one launch, products and sums rounded separately;
+ *     clamped routed SwiGLU;
+ *   - the review finding on moe_combine_masked_kernel: a route masked to -1 is
+ *     skipped and its slot never read.
+ *
+ * Formats (the pages name them and print no layout; this is the layout used):
+ *   Q8_0 block, 34 bytes: fp16 d (little-endian), int8 qs[32]; value = d * q.
+ *   q8_1 block, 36 bytes: fp16 d, fp16 s = d * sum(q), int8 qs[32].
+ *   A row of K values is K/32 consecutive blocks.  Quantisation: fp32
+ *   d = amax/127, q = roundf(x/d) (halves away from zero) on the fp32 quotient,
+ *   d and s stored as fp16 (round to nearest even); an all-zero block is all
+ *   zero bytes.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no mutable global state and never writes an
+ *     input.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns without synchronising.
+ *   - Return value: MOEQ8_OK when the work was enqueued; a negative status when
+ *     the arguments were rejected on the host (nothing enqueued, outputs
+ *     untouched) or the launch failed (MOEQ8_EHIP; the HIP error is cleared).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Non-finite inputs are outside the contract (results unspecified).
+ *   - Columns: 1 <= ncols <= MOEQ8_MAX_COLS.  Column j of an activation
+ *     operand is row j of a row-major [ncols][...] array.
+ *   - K must be a multiple of 64 (whole 2-block lane chunks); weight pointers,
+ *     row strides and expert strides must be multiples of 4 bytes; activation
+ *     and output pointers must be 4-byte aligned.
+ */
+#ifndef MOEQ8_H
+#define MOEQ8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEQ8_ABI_VERSION 1
+#define MOEQ8_QK 32
+#define MOEQ8_Q8_0_BLOCK_BYTES 34
+#define MOEQ8_Q8_1_BLOCK_BYTES 36
+#define MOEQ8_MAX_COLS 8
+#define MOEQ8_MAX_EXPERTS 1024
+#define MOEQ8_MAX_TOPK 16
+
+enum moeq8_status {
+    MOEQ8_OK = 0,
+    MOEQ8_EINVAL = -1,       /* null pointer, bad shape, K % 64, ncols out of range, topk > n_expert */
+    MOEQ8_EALIGN = -2,       /* pointer, stride or k_block_offset alignment */
+    MOEQ8_EUNSUPPORTED = -3, /* valid request the library does not implement (e.g. n_expert > 1024) */
+    MOEQ8_EHIP = -4          /* the HIP launch failed; the error was cleared */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moeq8_status_string(int status);
+
+/* MOEQ8_ABI_VERSION of the built library. */
+int moeq8_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * a1 / a7: q8_1 activation quantisation (the q8_1 rows MMVQ reads; quantise an
+ * activation once and share the rows, the activation memo of the fused decode
+ * kernels commit).
+ *   x     fp32 [n_rows][x_row_stride] (elements); the first k of each row are read
+ *   xq    q8_1 blocks [n_rows][k/32], contiguous (n_rows * k/32 * 36 bytes)
+ * k must be a multiple of 32 here.  n_rows == 0 enqueues nothing and is OK.
+ * ------------------------------------------------------------------------- */
+int q8_1_quantize_rows(const float* x, int64_t n_rows, int64_t k, int64_t x_row_stride,
+                       void* xq, void* stream);
+
+/* Q8_0 weight quantisation with the same block rule (no s field):
+ *   w     fp32 [n_rows][w_row_stride]
+ *   wq    Q8_0 blocks [n_rows][k/32], contiguous (34 bytes each) */
+int q8_0_quantize_rows(const float* w, int64_t n_rows, int64_t k, int64_t w_row_stride,
+                       void* wq, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a3 (+a10): single Q8_0 x q8_1 product, y[c][i] = sum over the k/32 blocks b of
+ * row i of d_w * d_x * sum(qw * qx).
+ *   w                  Q8_0 rows: row i starts at w + i * w_row_stride_bytes.  For a
+ *                      column-range slice this is a view: w points at block
+ *                      k_block_offset of row 0 and w_row_stride_bytes is the full
+ *                      row's stride.
+ *   n, k               rows and (slice) length in values; k % 64 == 0
+ *   k_block_offset     index within the full row of the slice's first block; must
+ *                      be even.  The result is bit-identical to the full-row
+ *                      product with activations zero outside the slice (the
+ *                      whole-row lane mapping of the column-range commit).
+ *   xq                 q8_1 [ncols][k/32]
+ *   y                  fp32 [ncols][n]
+ * Batch invariant: column j's bits do not depend on ncols.
+ * ------------------------------------------------------------------------- */
+int mmvq_q8_0(const void* w, int64_t w_row_stride_bytes, int64_t n, int64_t k,
+              int64_t k_block_offset, const void* xq, int64_t ncols, float* y, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a2 (+a10): Q8_0 gate/up pair on the same q8_1 activations with the SwiGLU-DS4
+ * epilogue h = silu(min(g, 7)) * clamp(u, -7, 7) (the RDNA4 Q8_0 gate/up pair
+ * commit; fp32 epilogue).
+ *   w_gate, w_up       two Q8_0 matrices with the same geometry (as mmvq_q8_0)
+ *   h_out              fp32 [ncols][n]
+ *   g_out, u_out       optional (NULL = not written): the raw products, fp32 [ncols][n]
+ * g_out/u_out are bit-identical to mmvq_q8_0 on each matrix, and h_out is
+ * bit-identical to swiglu_ds4 of them.
+ * ------------------------------------------------------------------------- */
+int mmvq_q8_0_glu_pair(const void* w_gate, const void* w_up, int64_t w_row_stride_bytes,
+                       int64_t n, int64_t k, int64_t k_block_offset, const void* xq,
+                       int64_t ncols, float* h_out, float* g_out, float* u_out, void* stream);
+
+/* Elementwise SwiGLU-DS4 (the GLU kernel of the unfused path):
+ *   h[i] = silu(min(g[i], 7)) * clamp(u[i], -7, 7), fp32, count elements. */
+int swiglu_ds4(const float* g, const float* u, int64_t count, float* h, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a4 + a5: router top-k select and weights over the same logits, owner mask,
+ * and the layer's expert grouping (one launch; the grouping stays on the device).
+ *   logits       fp32 [ncols][n_expert]
+ *   bias         fp32 [n_expert] expert-selection bias, or NULL (zero)
+ *   owner_slot   int32 [n_expert]: local expert index in [0, n_local_expert), or -1
+ *                for an expert owned elsewhere; NULL = every expert local with
+ *                slot = expert index (then n_local_expert must equal n_expert).
+ *                Entries outside [-1, n_local_expert) are treated as -1.
+ *   ids          int32 [ncols][topk] out: local expert of each route, -1 = masked
+ *   weights      fp32 [ncols][topk] out
+ *   grouping     device buffer of moe_grouping_bytes(ncols, topk) bytes, out
+ * Scores: score = sigmoid(logit), the fp64 sigmoid rounded once to fp32;
+ * key = score + bias (fp32).  Slots 0..topk-1 hold the experts with the largest
+ * keys, by (key descending, expert index ascending).  weights = score / (sum of
+ * the topk selected scores, summed in slot order in fp32); the bias selects only;
+ * masked routes keep their weight and count in the sum.
+ * Grouping layout (int32 words): [0] n_active, [1] n_valid routes, [2] ncols,
+ * [3] topk, then expert[R], offset[R+1], route[R] with R = ncols*topk: active
+ * groups a < n_active hold local expert expert[a] (ascending) and the routes
+ * route[offset[a] .. offset[a+1]) (route r = column*topk + slot, ascending).
+ * ------------------------------------------------------------------------- */
+size_t moe_grouping_bytes(int64_t ncols, int32_t topk);
+int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_slot,
+                   int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
+                   int32_t* ids, float* weights, void* grouping, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a6 / a8: grouped per-expert MMVQ over the routed experts, one launch per
+ * projection, using the grouping written by moe_route_topk.
+ *   stage MOEQ8_GATE_UP_SWIGLU: w_a = gate, w_b = up, act_q = xq [ncols][k/32],
+ *         out = h fp32 [ncols][topk][n] = SwiGLU-DS4(gate.x_j, up.x_j) for route (j, s)
+ *   stage MOEQ8_DOWN: w_a = down, w_b = NULL, act_q = hq [ncols*topk][k/32] (one q8_1
+ *         row per route), out = y fp32 [ncols][topk][n]
+ *   Expert e's matrix starts at w + e * expert_stride_bytes; its rows are
+ *   w_row_stride_bytes apart; experts outside [0, n_local_expert) are skipped.
+ * `grouping` must come from moe_route_topk with the same ncols and topk (a
+ * grouping whose header names another column count or top-k is ignored and
+ * nothing is written).
+ * Rows of masked routes (id -1) are NOT written.  Each route's row is
+ * bit-identical to mmvq_q8_0 (DOWN) or mmvq_q8_0_glu_pair's h (GATE_UP) on that
+ * expert and that route's activation row.
+ * ------------------------------------------------------------------------- */
+enum moeq8_stage { MOEQ8_GATE_UP_SWIGLU = 0, MOEQ8_DOWN = 1 };
+int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
+                     int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                     int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
+                     const void* grouping, int64_t ncols, int32_t topk, float* out,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a9: weighted masked combine.
+ *   out[j][i] = sum over slots s ascending with ids[j][s] >= 0 of
+ *               fl(weights[j][s] * y[j][s][i])  (fp32: each product rounded, then
+ *               added in slot order; masked slots are never read)
+ *   y fp32 [ncols][topk][n]; ids int32 [ncols][topk]; weights fp32 [ncols][topk];
+ *   out fp32 [ncols][n] (fully overwritten; all-masked columns give 0).
+ * ------------------------------------------------------------------------- */
+int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
+                int32_t topk, int64_t n, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ8_H */

@@ -1,0 +1,48 @@
+/* libmoeq8 synthetic-input helper: fills device memory with Q8_0 weight blocks
+ * drawn from a counter-based generator, for benchmark-sized weight sets (tens of
+ * GB) that would take minutes to draw and quantise on the host.  Not part of the
+ * FFN path; the same generator is implemented independently on the host so any
+ * filled block can be reproduced there.
+ *
+ * Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom
+ * number generators", OOPSLA 2014).  Output i of the stream with key s is
+ * mix(s + (i + 1) * 0x9E3779B97F4A7C15) with
+ *   mix(z): z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+ *           z *= 0x94D049BB133111EB; z ^= z >> 31    (all modulo 2^64).
+ * Block b of a stream uses outputs 17b .. 17b + 16:
+ *   outputs 17b + t, t < 16: element 2t + h takes bytes 4h .. 4h + 3 of the
+ *     output (little-endian); v = their sum; q = clamp(((v * 43) >> 7) - 171,
+ *     -127, 127);
+ *   output 17b + 16 = o: d = fp16 bits 0x0C00 | (o & 0x3FF); element
+ *     (o >> 10) & 31 becomes -127 if bit 15 of o is set, else +127.
+ * Stream key of (seed, layer, expert, matrix):
+ *   mix(((seed & 0xFFFF) << 48 | (layer & 0xFFFF) << 32 | (expert & 0xFFFF) << 16
+ *        | (matrix & 0xFFFF)) + 0x9E3779B97F4A7C15).
+ */
+#ifndef MOEQ8_SYNTH_H
+#define MOEQ8_SYNTH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Stream key of (seed, layer, expert, matrix) as defined above (host function). */
+uint64_t moeq8_synth_stream_key(uint32_t seed, uint32_t layer, uint32_t expert, uint32_t matrix);
+
+/* Fill `n_mats` consecutive matrices of `blocks_per_mat` Q8_0 blocks each (34 B
+ * per block, contiguous, dst 2-byte aligned, device memory owned by the caller).
+ * Matrix i holds blocks 0 .. blocks_per_mat-1 of the stream with key
+ * moeq8_synth_stream_key(seed, layer0 + i / mats_per_layer,
+ *                        expert0 + i % mats_per_layer, matrix).
+ * Enqueued on `stream` (hipStream_t); returns 0 or a negative moeq8 status. */
+int moeq8_synth_q8_0_fill(void* dst, int64_t n_mats, int64_t blocks_per_mat,
+                          int64_t mats_per_layer, uint32_t seed, uint32_t layer0,
+                          uint32_t expert0, uint32_t matrix, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ8_SYNTH_H */

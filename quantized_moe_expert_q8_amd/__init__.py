@@ -1,0 +1,24 @@
+"""libmoeq8: quantized MoE expert FFN (Q8_0 x q8_1) on AMD MI355X (gfx950).
+
+The compute runs in the HIP library libmoeq8.so (C ABI in include/moeq8.h);
+this package only marshals torch tensors (device memory, streams) into it.
+"""
+
+from ._lib import MoeQ8Error, lib, lib_path  # noqa: F401
+from . import ops  # noqa: F401
+from .ops import (  # noqa: F401
+    GATE_UP_SWIGLU,
+    DOWN,
+    Q8_0_BLOCK_BYTES,
+    Q8_1_BLOCK_BYTES,
+    q8_1_quantize_rows,
+    q8_0_quantize_rows,
+    mmvq_q8_0,
+    mmvq_q8_0_glu_pair,
+    swiglu_ds4,
+    moe_grouping_bytes,
+    moe_route_topk,
+    moe_grouped_mmvq,
+    moe_combine,
+    synth_q8_0_fill,
+)

@@ -1,0 +1,41 @@
+// Weighted masked combine (lucebox PR #826, the routed combine commit: route
+// weighting and route sum in one launch, rounding the products and the sums
+// separately as the unfused ops do; the review of moe_combine_masked_kernel: a
+// route masked to -1 is skipped before anything is read for it).
+#include "moeq8_device.hpp"
+#include "moeq8_host.hpp"
+
+namespace moeq8 {
+
+__global__ void k_combine(const float* __restrict__ y, const int32_t* __restrict__ ids,
+                          const float* __restrict__ w, int topk, int64_t n,
+                          float* __restrict__ out) {
+    const int j = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.0f;  // +0 then the valid products in slot order
+    for (int s = 0; s < topk; ++s) {
+        const int r = j * topk + s;
+        if (ids[r] < 0) continue;
+        const float prod = w[r] * y[(int64_t)r * n + i];
+        acc = acc + prod;
+    }
+    out[(int64_t)j * n + i] = acc;
+}
+
+}  // namespace moeq8
+
+extern "C" int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
+                           int32_t topk, int64_t n, float* out, void* stream) {
+    using namespace moeq8;
+    if (!y || !ids || !weights || !out) return MOEQ8_EINVAL;
+    if (ncols < 1 || ncols > MOEQ8_MAX_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK || n < 0)
+        return MOEQ8_EINVAL;
+    if (((uintptr_t)y | (uintptr_t)ids | (uintptr_t)weights | (uintptr_t)out) & 3u) return MOEQ8_EALIGN;
+    if (n == 0) return MOEQ8_OK;
+    const int64_t bx = (n + 255) / 256;
+    if (bx > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_combine, dim3((uint32_t)bx, (uint32_t)ncols), dim3(256), 0,
+                       (hipStream_t)stream, y, ids, weights, topk, n, out);
+    return check_launch();
+}

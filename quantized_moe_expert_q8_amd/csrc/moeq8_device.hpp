@@ -1,0 +1,138 @@
+// Device-side building blocks shared by every libmoeq8 kernel (gfx950, wave64).
+//
+// Block formats: Q8_0 = {fp16 d; int8 qs[32]} (34 B), q8_1 = {fp16 d; fp16 s;
+// int8 qs[32]} (36 B), rows of K/32 consecutive blocks.
+//
+// Reduction order of every Q8_0 x q8_1 product (single, gate/up pair, grouped):
+//   * A row is cut into 2-block chunks (68 weight bytes, 72 activation bytes).
+//     Absolute chunk c (counted from the first block of the FULL row, so a
+//     column-range slice starting at block k_block_offset has its first chunk at
+//     c = k_block_offset / 2) belongs to logical lane c % 16, round c / 16.
+//   * Chunk value: p(b) = (fp32(d_w) * fp32(d_x)) * float(sumi_b) for its two
+//     blocks b, then p(b0) + p(b1).  fp32(d_w) * fp32(d_x) is exact.
+//   * Logical lane l accumulates its chunks' values in ascending round order,
+//     starting from +0.
+//   * The 16 lane sums are added as a pairwise tree (xor 1, 2, 4, 8).
+// The order never depends on the number of columns, on whether one or two
+// matrices are read, on which rows are launched, or on grouping, so the pair
+// equals the separate products, the grouped launch equals per-route products,
+// results are batch invariant, and a slice equals the zero-padded full row
+// (a zero chunk adds +0, which leaves a lane sum unchanged): the properties the
+// RDNA4 Q8_0 gate/up pair and whole-row-lane slice commits of lucebox PR #826
+// state for their kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moeq8 {
+
+constexpr int QK = 32;
+constexpr int Q80_BYTES = 34;
+constexpr int Q81_BYTES = 36;
+constexpr int LANES_PER_ROW = 16;       // logical lanes of one row
+constexpr int BLOCKS_PER_CHUNK = 2;     // blocks per lane per round
+constexpr int W_CHUNK_BYTES = BLOCKS_PER_CHUNK * Q80_BYTES;  // 68
+constexpr int X_CHUNK_BYTES = BLOCKS_PER_CHUNK * Q81_BYTES;  // 72
+constexpr int W_CHUNK_DWORDS = W_CHUNK_BYTES / 4;            // 17
+constexpr int X_CHUNK_DWORDS = X_CHUNK_BYTES / 4;            // 18
+constexpr float SWIGLU_LIMIT = 7.0f;
+
+// 16-byte vectors that only promise 4-byte alignment: the 34-byte blocks put
+// chunks on 4-byte boundaries, and gfx950 global loads accept that.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits16 & 0xffffu));
+}
+
+// Pins an fp32 value in a register so that instruction selection cannot fold
+// the operation that produced it into its consumer.  Needed where an fp32
+// rounding is part of the definition: without it hipcc turns
+// fp16(a * b) into one v_fma_mixlo_f16, rounding once instead of twice.
+__device__ __forceinline__ float materialize_f32(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t float_to_half_bits(float f) {
+    // round to nearest even (the default rounding mode), subnormals kept
+    return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);
+}
+
+struct WChunk { uint32_t v[W_CHUNK_DWORDS]; };
+struct XChunk { uint32_t v[X_CHUNK_DWORDS]; };
+
+// Raw 68 bytes of a weight chunk (4-byte aligned address).
+__device__ __forceinline__ void load_w_chunk(WChunk& w, const uint8_t* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u32x4 t = q[i];
+        w.v[4 * i + 0] = t.x;
+        w.v[4 * i + 1] = t.y;
+        w.v[4 * i + 2] = t.z;
+        w.v[4 * i + 3] = t.w;
+    }
+    w.v[16] = *reinterpret_cast<const uint32_t*>(p + 64);
+}
+
+// Raw 72 bytes of an activation chunk (8-byte aligned address).
+__device__ __forceinline__ void load_x_chunk(XChunk& x, const uint8_t* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u32x4 t = q[i];
+        x.v[4 * i + 0] = t.x;
+        x.v[4 * i + 1] = t.y;
+        x.v[4 * i + 2] = t.z;
+        x.v[4 * i + 3] = t.w;
+    }
+    u32x2 t = *reinterpret_cast<const u32x2*>(p + 64);
+    x.v[16] = t.x;
+    x.v[17] = t.y;
+}
+
+__device__ __forceinline__ void zero_w_chunk(WChunk& w) {
+#pragma unroll
+    for (int i = 0; i < W_CHUNK_DWORDS; ++i) w.v[i] = 0u;
+}
+
+__device__ __forceinline__ void zero_x_chunk(XChunk& x) {
+#pragma unroll
+    for (int i = 0; i < X_CHUNK_DWORDS; ++i) x.v[i] = 0u;
+}
+
+// Value of one chunk: two blocks, each (d_w * d_x) * sumi, then their sum.
+// Weight block 0 occupies bytes 0..33 (d in the low half of dword 0, quants at
+// byte 2, so each quant dword is funnel-shifted out of two loaded dwords);
+// weight block 1 occupies bytes 34..67 (d in the high half of dword 8, quants in
+// dwords 9..16).  Activation block 0: dword 0 = d | s << 16, quants dwords 1..8;
+// block 1: dword 9, quants dwords 10..17.
+__device__ __forceinline__ float chunk_dot(const WChunk& w, const XChunk& x) {
+    int s0 = 0, s1 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t q0 = (w.v[j] >> 16) | (w.v[j + 1] << 16);
+        s0 = __builtin_amdgcn_sdot4((int)q0, (int)x.v[1 + j], s0, false);
+        s1 = __builtin_amdgcn_sdot4((int)w.v[9 + j], (int)x.v[10 + j], s1, false);
+    }
+    const float dw0 = half_bits_to_float(w.v[0]);
+    const float dw1 = half_bits_to_float(w.v[8] >> 16);
+    const float dx0 = half_bits_to_float(x.v[0]);
+    const float dx1 = half_bits_to_float(x.v[9]);
+    const float p0 = (dw0 * dx0) * (float)s0;
+    const float p1 = (dw1 * dx1) * (float)s1;
+    return p0 + p1;
+}
+
+// SwiGLU-DS4 in fp32: silu(min(g, 7)) * clamp(u, -7, 7).
+__device__ __forceinline__ float swiglu_ds4_f32(float g, float u) {
+    const float gc = fminf(g, SWIGLU_LIMIT);
+    const float uc = fminf(fmaxf(u, -SWIGLU_LIMIT), SWIGLU_LIMIT);
+    const float silu = gc / (1.0f + expf(-gc));
+    return silu * uc;
+}
+
+}  // namespace moeq8

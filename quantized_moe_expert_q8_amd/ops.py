@@ -1,0 +1,270 @@
+"""Thin torch wrappers over the libmoeq8 C ABI (include/moeq8.h).
+
+Each function takes device tensors, checks dtypes, devices and that every
+buffer the kernel will touch lies inside its tensor, then calls the C entry
+point of the same name on the current HIP stream.  All arithmetic runs in the
+library's kernels; torch only provides memory and the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import call, lib
+
+QK = 32
+Q8_0_BLOCK_BYTES = 34
+Q8_1_BLOCK_BYTES = 36
+MAX_COLS = 8
+GATE_UP_SWIGLU = 0
+DOWN = 1
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t, offset: int = 0):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr() + offset)
+
+
+def _cuda(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _nbytes_from_ptr(t: torch.Tensor) -> int:
+    """Bytes from t.data_ptr() to the end of t's storage."""
+    st = t.untyped_storage()
+    return st.data_ptr() + st.nbytes() - t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, nbytes: int, offset: int = 0):
+    if offset < 0 or offset + nbytes > _nbytes_from_ptr(t):
+        raise ValueError(f"{name}: {nbytes} bytes at offset {offset} exceed the tensor's storage")
+
+
+def _contig_rows(t: torch.Tensor, name: str, rows: int, row_elems: int):
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < row_elems or t.stride(1) != 1:
+        raise ValueError(f"{name} must be [>= {rows}, >= {row_elems}] with unit inner stride")
+
+
+# ---------------------------------------------------------------------------
+# quantisers
+# ---------------------------------------------------------------------------
+
+def q8_1_quantize_rows(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x fp32 [rows, k] -> q8_1 blocks uint8 [rows, k/32*36]."""
+    _cuda(x, "x", torch.float32)
+    rows, k = x.shape
+    _contig_rows(x, "x", rows, k)
+    if out is None:
+        out = torch.empty((rows, k // QK * Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", rows * (k // QK) * Q8_1_BLOCK_BYTES)
+    call("q8_1_quantize_rows", _ptr(x), rows, k, x.stride(0), _ptr(out), _stream(x))
+    return out
+
+
+def q8_0_quantize_rows(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """w fp32 [rows, k] -> Q8_0 blocks uint8 [rows, k/32*34]."""
+    _cuda(w, "w", torch.float32)
+    rows, k = w.shape
+    _contig_rows(w, "w", rows, k)
+    if out is None:
+        out = torch.empty((rows, k // QK * Q8_0_BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", rows * (k // QK) * Q8_0_BLOCK_BYTES)
+    call("q8_0_quantize_rows", _ptr(w), rows, k, w.stride(0), _ptr(out), _stream(w))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# products
+# ---------------------------------------------------------------------------
+
+def _weight_extent(n: int, k: int, row_stride: int) -> int:
+    return 0 if n == 0 else (n - 1) * row_stride + (k // QK) * Q8_0_BLOCK_BYTES
+
+
+def _weight_args(w, n, k, w_offset_bytes, w_row_stride_bytes, name="w"):
+    _cuda(w, name, torch.uint8)
+    if w_row_stride_bytes is None:
+        w_row_stride_bytes = w.stride(0) if w.dim() == 2 else (k // QK) * Q8_0_BLOCK_BYTES
+    _need(w, name, _weight_extent(n, k, w_row_stride_bytes), w_offset_bytes)
+    return w_row_stride_bytes
+
+
+def _act_rows(xq, name, rows, k):
+    _cuda(xq, name, torch.uint8)
+    _need(xq, name, rows * (k // QK) * Q8_1_BLOCK_BYTES)
+
+
+def mmvq_q8_0(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, *, ncols: int | None = None,
+              k_block_offset: int = 0, w_offset_bytes: int = 0,
+              w_row_stride_bytes: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [ncols, n] = W . xq.  ``w`` holds Q8_0 rows; the matrix (or the
+    column-range view) starts ``w_offset_bytes`` into it."""
+    ncols = xq.shape[0] if ncols is None else ncols
+    stride = _weight_args(w, n, k, w_offset_bytes, w_row_stride_bytes)
+    _act_rows(xq, "xq", ncols, k)
+    if out is None:
+        out = torch.empty((ncols, n), dtype=torch.float32, device=w.device)
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", ncols * n * 4)
+    call("mmvq_q8_0", _ptr(w, w_offset_bytes), stride, n, k, k_block_offset, _ptr(xq), ncols,
+         _ptr(out), _stream(w))
+    return out
+
+
+def mmvq_q8_0_glu_pair(w_gate: torch.Tensor, w_up: torch.Tensor, xq: torch.Tensor, n: int, k: int,
+                       *, ncols: int | None = None, k_block_offset: int = 0,
+                       w_offset_bytes: int = 0, w_row_stride_bytes: int | None = None,
+                       out: torch.Tensor | None = None, g_out: torch.Tensor | None = None,
+                       u_out: torch.Tensor | None = None) -> torch.Tensor:
+    """h fp32 [ncols, n] = SwiGLU-DS4(Wg . xq, Wu . xq); optional raw products."""
+    ncols = xq.shape[0] if ncols is None else ncols
+    stride = _weight_args(w_gate, n, k, w_offset_bytes, w_row_stride_bytes, "w_gate")
+    stride_u = _weight_args(w_up, n, k, w_offset_bytes, w_row_stride_bytes, "w_up")
+    if stride_u != stride:
+        raise ValueError("w_gate and w_up must share the row stride")
+    _act_rows(xq, "xq", ncols, k)
+    if out is None:
+        out = torch.empty((ncols, n), dtype=torch.float32, device=w_gate.device)
+    for t, nm in ((out, "out"), (g_out, "g_out"), (u_out, "u_out")):
+        if t is not None:
+            _cuda(t, nm, torch.float32)
+            _need(t, nm, ncols * n * 4)
+    call("mmvq_q8_0_glu_pair", _ptr(w_gate, w_offset_bytes), _ptr(w_up, w_offset_bytes), stride, n,
+         k, k_block_offset, _ptr(xq), ncols, _ptr(out), _ptr(g_out), _ptr(u_out), _stream(w_gate))
+    return out
+
+
+def swiglu_ds4(g: torch.Tensor, u: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    _cuda(g, "g", torch.float32)
+    _cuda(u, "u", torch.float32)
+    if g.shape != u.shape or not g.is_contiguous() or not u.is_contiguous():
+        raise ValueError("g and u must be contiguous and of one shape")
+    if out is None:
+        out = torch.empty_like(g)
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", g.numel() * 4)
+    call("swiglu_ds4", _ptr(g), _ptr(u), g.numel(), _ptr(out), _stream(g))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# routing, grouped products, combine
+# ---------------------------------------------------------------------------
+
+def moe_grouping_bytes(ncols: int, topk: int) -> int:
+    return int(lib().moe_grouping_bytes(ncols, topk))
+
+
+def moe_route_topk(logits: torch.Tensor, topk: int, *, bias: torch.Tensor | None = None,
+                   owner_slot: torch.Tensor | None = None, n_local_expert: int | None = None,
+                   ids: torch.Tensor | None = None, weights: torch.Tensor | None = None,
+                   grouping: torch.Tensor | None = None):
+    """Returns (ids int32 [ncols, topk], weights fp32 [ncols, topk], grouping uint8)."""
+    _cuda(logits, "logits", torch.float32)
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be contiguous [ncols, n_expert]")
+    ncols, n_expert = logits.shape
+    if n_local_expert is None:
+        n_local_expert = n_expert if owner_slot is None else int(owner_slot.max().item()) + 1
+    if bias is not None:
+        _cuda(bias, "bias", torch.float32)
+        _need(bias, "bias", n_expert * 4)
+    if owner_slot is not None:
+        _cuda(owner_slot, "owner_slot", torch.int32)
+        _need(owner_slot, "owner_slot", n_expert * 4)
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((ncols, topk), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((ncols, topk), dtype=torch.float32, device=dev)
+    gb = moe_grouping_bytes(ncols, topk)
+    if gb == 0:
+        raise ValueError("ncols or topk out of range")
+    if grouping is None:
+        grouping = torch.empty(gb, dtype=torch.uint8, device=dev)
+    _need(ids, "ids", ncols * topk * 4)
+    _need(weights, "weights", ncols * topk * 4)
+    _need(grouping, "grouping", gb)
+    call("moe_route_topk", _ptr(logits), _ptr(bias), _ptr(owner_slot), ncols, n_expert,
+         n_local_expert, topk, _ptr(ids), _ptr(weights), _ptr(grouping), _stream(logits))
+    return ids, weights, grouping
+
+
+def moe_grouped_mmvq(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, act_q: torch.Tensor,
+                     grouping: torch.Tensor, *, n: int, k: int, n_local_expert: int, ncols: int,
+                     topk: int, expert_stride_bytes: int | None = None,
+                     w_row_stride_bytes: int | None = None,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped per-expert MMVQ.  Experts are stored [n_local][n][k/32] blocks.
+    Returns out fp32 [ncols, topk, n] (masked routes' rows untouched)."""
+    if w_row_stride_bytes is None:
+        w_row_stride_bytes = (k // QK) * Q8_0_BLOCK_BYTES
+    if expert_stride_bytes is None:
+        expert_stride_bytes = n * w_row_stride_bytes
+    extent = (n_local_expert - 1) * expert_stride_bytes + _weight_extent(n, k, w_row_stride_bytes)
+    _cuda(w_a, "w_a", torch.uint8)
+    _need(w_a, "w_a", extent)
+    if stage == GATE_UP_SWIGLU:
+        if w_b is None:
+            raise ValueError("the gate/up stage needs w_b")
+        _cuda(w_b, "w_b", torch.uint8)
+        _need(w_b, "w_b", extent)
+        act_rows = ncols
+    elif stage == DOWN:
+        act_rows = ncols * topk
+    else:
+        raise ValueError("stage must be GATE_UP_SWIGLU or DOWN")
+    _act_rows(act_q, "act_q", act_rows, k)
+    _cuda(grouping, "grouping", torch.uint8)
+    _need(grouping, "grouping", moe_grouping_bytes(ncols, topk))
+    if out is None:
+        out = torch.empty((ncols, topk, n), dtype=torch.float32, device=w_a.device)
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", ncols * topk * n * 4)
+    call("moe_grouped_mmvq", stage, _ptr(w_a), _ptr(w_b), expert_stride_bytes, w_row_stride_bytes,
+         n_local_expert, n, k, _ptr(act_q), _ptr(grouping), ncols, topk, _ptr(out), _stream(w_a))
+    return out
+
+
+def moe_combine(y: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """out fp32 [ncols, n] = sum over unmasked slots of weights * y."""
+    _cuda(y, "y", torch.float32)
+    _cuda(ids, "ids", torch.int32)
+    _cuda(weights, "weights", torch.float32)
+    ncols, topk, n = y.shape
+    if not y.is_contiguous():
+        raise ValueError("y must be contiguous [ncols, topk, n]")
+    _need(ids, "ids", ncols * topk * 4)
+    _need(weights, "weights", ncols * topk * 4)
+    if out is None:
+        out = torch.empty((ncols, n), dtype=torch.float32, device=y.device)
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", ncols * n * 4)
+    call("moe_combine", _ptr(y), _ptr(ids), _ptr(weights), ncols, topk, n, _ptr(out), _stream(y))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# synthetic weights (input generation; not part of the FFN path)
+# ---------------------------------------------------------------------------
+
+def synth_q8_0_fill(dst: torch.Tensor, n_mats: int, blocks_per_mat: int, mats_per_layer: int,
+                    seed: int, layer0: int, expert0: int, matrix: int, offset_bytes: int = 0):
+    _cuda(dst, "dst", torch.uint8)
+    _need(dst, "dst", n_mats * blocks_per_mat * Q8_0_BLOCK_BYTES, offset_bytes)
+    call("moeq8_synth_q8_0_fill", _ptr(dst, offset_bytes), n_mats, blocks_per_mat, mats_per_layer,
+         seed, layer0, expert0, matrix, _stream(dst))
+    return dst

@@ -1,0 +1,127 @@
+"""The C-ABI library loads and exports every symbol include/*.h declares, and
+host-side argument validation rejects bad calls before anything is enqueued
+(CPU only: no compute call is made)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+import quantized_moe_expert_q8_amd as moeq8  # noqa: E402
+from quantized_moe_expert_q8_amd import _lib  # noqa: E402
+
+
+def _declared_functions():
+    names = []
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M):
+            if not m.group(0).lstrip().startswith(("#", "typedef", "enum", "struct")):
+                names.append(m.group(1))
+    return names
+
+
+def test_header_declares_the_hot_path_calls():
+    names = set(_declared_functions())
+    for n in ("q8_1_quantize_rows", "mmvq_q8_0_glu_pair", "moe_route_topk", "moe_grouped_mmvq",
+              "moe_combine", "mmvq_q8_0", "moe_grouping_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    so = ctypes.CDLL(_lib.lib_path())
+    declared = _declared_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(so, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_abi_version_and_status_strings():
+    L = moeq8.lib()
+    assert L.moeq8_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -99):
+        assert L.moeq8_status_string(st)
+
+
+def test_grouping_bytes():
+    L = moeq8.lib()
+    assert L.moe_grouping_bytes(8, 8) == 1024           # 4*(4 + 3*64 + 1) = 788 -> 1024
+    assert L.moe_grouping_bytes(1, 8) == 256
+    assert L.moe_grouping_bytes(0, 8) == 0 and L.moe_grouping_bytes(9, 8) == 0
+    assert L.moe_grouping_bytes(1, 17) == 0
+
+
+try:
+    import torch
+    _HAS_GPU = torch.cuda.is_available()
+except Exception:  # pragma: no cover
+    _HAS_GPU = False
+
+
+# Fake, never-dereferenced addresses: every call below must be rejected on the
+# host before a launch.  Skipped where a GPU is visible, so a validation bug
+# can never turn one of these into a launch on real hardware.
+P = 0x10000
+cpu_only = pytest.mark.skipif(_HAS_GPU, reason="host-validation calls use fake pointers")
+
+
+@cpu_only
+@pytest.mark.parametrize("args,expect", [
+    ((None, 68, 4, 64, 0, P, 1, P, None), -1),           # null weights
+    ((P, 68, 4, 96, 0, P, 1, P, None), -1),              # K % 64
+    ((P, 68, 4, 64, 0, P, 0, P, None), -1),              # ncols 0
+    ((P, 68, 4, 64, 0, P, 9, P, None), -1),              # ncols 9
+    ((P, 68, 4, 64, 1, P, 1, P, None), -2),              # odd block offset
+    ((P + 2, 68, 4, 64, 0, P, 1, P, None), -2),          # misaligned weights
+    ((P, 66, 4, 64, 0, P, 1, P, None), -2),              # row stride % 4
+    ((P, 64, 4, 64, 0, P, 1, P, None), -1),              # row stride shorter than a row
+    ((P, 68, -1, 64, 0, P, 1, P, None), -1),             # negative rows
+    ((P, 68, 4, 64, 0, P + 1, 1, P, None), -2),          # misaligned activations
+])
+def test_mmvq_validation(args, expect):
+    assert moeq8.lib().mmvq_q8_0(*args) == expect
+
+
+@cpu_only
+def test_other_validation():
+    L = moeq8.lib()
+    assert L.mmvq_q8_0(P, 68, 0, 64, 0, P, 1, P, None) == 0                      # n = 0: nothing to do
+    assert L.mmvq_q8_0_glu_pair(P, None, 68, 4, 64, 0, P, 1, P, None, None, None) == -1
+    assert L.q8_1_quantize_rows(P, 2, 48, 48, P, None) == -1                     # k % 32
+    assert L.q8_1_quantize_rows(P, 2, 64, 32, P, None) == -1                     # stride < k
+    assert L.q8_1_quantize_rows(P, 0, 64, 64, P, None) == 0
+    assert L.q8_0_quantize_rows(P, 2, 64, 64, P + 1, None) == -2
+    assert L.swiglu_ds4(None, P, 4, P, None) == -1
+    assert L.moe_route_topk(P, None, None, 2, 8, 8, 9, P, P, P, None) == -1      # topk > n_expert
+    assert L.moe_route_topk(P, None, None, 2, 8, 4, 2, P, P, P, None) == -1      # no owner map, n_local != n
+    assert L.moe_route_topk(P, None, None, 2, 2048, 2048, 8, P, P, P, None) == -3
+    assert L.moe_route_topk(P, None, None, 9, 8, 8, 2, P, P, P, None) == -1
+    assert L.moe_grouped_mmvq(2, P, P, 0, 68, 1, 4, 64, P, P, 1, 1, P, None) == -1  # bad stage
+    assert L.moe_grouped_mmvq(0, P, None, 272, 68, 1, 4, 64, P, P, 1, 1, P, None) == -1  # gate/up without up
+    assert L.moe_grouped_mmvq(1, P, None, 270, 68, 2, 4, 64, P, P, 1, 1, P, None) == -2  # expert stride % 4
+    assert L.moe_grouped_mmvq(1, P, None, 136, 68, 2, 4, 64, P, P, 1, 1, P, None) == -1  # experts overlap
+    assert L.moe_combine(P, P, P, 0, 8, 16, P, None) == -1
+    assert L.moe_combine(P, P, P, 1, 8, 0, P, None) == 0
+    assert L.moeq8_synth_q8_0_fill(P + 1, 1, 1, 1, 0, 0, 0, 0, None) == -2
+
+
+def test_ops_reject_out_of_bounds_views():
+    """The torch layer refuses views that would read past a tensor (CPU tensors
+    are refused first, so this needs no GPU)."""
+    import torch
+    w = torch.zeros(10, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        moeq8.mmvq_q8_0(w, w, 1, 64)
+
+
+def test_synth_stream_key_host_matches_generator():
+    import workloads
+    L = moeq8.lib()
+    for args in [(0, 0, 0, 0), (5, 42, 127, 2), (65535, 3, 9, 5)]:
+        assert L.moeq8_synth_stream_key(*args) == workloads.stream_key(*args)

@@ -1,0 +1,453 @@
+"""GPU parity of each libmoeq8 call against the CPU oracle, plus the GPU-internal
+bit-for-bit invariants (pair == separate + SwiGLU, batch invariance, column-range
+slice == zero-padded full row, row slice == rows of the full product, grouped ==
+per-route products, graph replay == eager, repeat determinism).
+
+Inputs come from the seeded generators only; the oracle never consumes GPU data.
+Bars: bytes/ids/integer dots bit-exact; products <= 1e-5*max(1,|ref|); SwiGLU,
+weights and combine <= 1e-4*max(1,|ref|).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+import quantized_moe_expert_q8_amd as moeq8  # noqa: E402
+from _gpu import DEV, assert_close, bits_equal, host, q80_from_dev, q81_from_dev, say, to_dev  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+PROD_TOL = 1e-5
+EPI_TOL = 1e-4
+
+
+def synth_matrix(seed, n, k, matrix=0, expert=0, layer=0):
+    """Same generator bytes for both sides: (numpy Q8_0 array, device tensor)."""
+    w = workloads.synth_q8_0_matrix(seed, layer, expert, matrix, n, k)
+    return w, to_dev(w)
+
+
+def quantized_pair(x32):
+    """Quantise x on both sides; assert identical bytes; return (oracle, device)."""
+    xo = oracle.quantize_q8_1(x32)
+    xd = moeq8.q8_1_quantize_rows(to_dev(x32))
+    torch.cuda.synchronize()
+    assert host(xd).tobytes() == xo.tobytes()
+    return xo, xd
+
+
+# ---------------------------------------------------------------------------
+# a1 / a7: quantisers
+# ---------------------------------------------------------------------------
+
+def test_quantize_golden_blocks():
+    say("quantize golden")
+    with open(os.path.join(GOLDEN, "q8_blocks_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    x = np.stack([np.array(c["x"], np.float32) for c in cases])
+    q1 = host(moeq8.q8_1_quantize_rows(to_dev(x)))
+    q0 = host(moeq8.q8_0_quantize_rows(to_dev(x)))
+    for i, c in enumerate(cases):
+        assert q1[i].tobytes().hex() == c["q8_1_hex"].replace(" ", ""), c["name"]
+        assert q0[i].tobytes().hex() == c["q8_0_hex"].replace(" ", ""), c["name"]
+
+
+@pytest.mark.parametrize("rows,k", [(1, 32), (3, 256), (37, 4096), (64, 1024), (5, 2048)])
+def test_quantize_bit_exact(rows, k):
+    say(f"quantize rows={rows} k={k}")
+    x = workloads.normal_f32(rows * 31 + k, (rows, k), 1.0)
+    if rows > 2:
+        x[0, :64 if k >= 64 else k] = 0.0                  # all-zero blocks
+        x[1, :] *= np.float32(1e-30)                       # values near the fp32 subnormal range
+        x[2, :32] = np.arange(-16, 16, dtype=np.float32) + np.float32(0.5)  # exact halves
+    xd = to_dev(x)
+    assert host(moeq8.q8_1_quantize_rows(xd)).tobytes() == oracle.quantize_q8_1(x).tobytes()
+    assert host(moeq8.q8_0_quantize_rows(xd)).tobytes() == oracle.quantize_q8_0(x).tobytes()
+
+
+def test_quantize_strided_rows_and_discriminating_blocks():
+    with open(os.path.join(GOLDEN, "q8_rule_discriminating_blocks.json")) as f:
+        blocks = json.load(f)["blocks_hex"]
+    b = np.array([[float.fromhex(h) for h in r] for r in blocks], np.float32)
+    wide = np.zeros((3, 96), np.float32)
+    wide[:, :32] = b
+    wide[:, 32:] = 7.0                                   # beyond k: must not be read
+    xd = to_dev(wide)[:, :64]
+    got = host(moeq8.q8_1_quantize_rows(xd))
+    ref = oracle.quantize_q8_1(wide[:, :64])
+    assert got.tobytes() == ref.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# a3: single product
+# ---------------------------------------------------------------------------
+
+def test_integer_block_dots_unit_scale():
+    """All d = 1: y is the integer dot itself, exactly (|y| < 2^24)."""
+    say("unit-scale integer dots")
+    rng = np.random.default_rng(5)
+    n, k, c = 70, 1024, 3
+    w = np.zeros((n, k // 32), dtype=oracle.Q8_0_DTYPE)
+    w["d"] = 1.0
+    w["qs"] = rng.integers(-127, 128, size=w["qs"].shape)
+    xq = np.zeros((c, k // 32), dtype=oracle.Q8_1_DTYPE)
+    xq["d"] = 1.0
+    xq["qs"] = rng.integers(-127, 128, size=xq["qs"].shape)
+    xq["qs"][2] = 127
+    w["qs"][0] = 127
+    y = host(moeq8.mmvq_q8_0(to_dev(w), to_dev(xq), n, k))
+    exact = xq["qs"].reshape(c, -1).astype(np.int64) @ w["qs"].reshape(n, -1).astype(np.int64).T
+    assert np.array_equal(y.astype(np.int64), exact)
+    assert y[2, 0] == 127 * 127 * 1024
+
+
+@pytest.mark.parametrize("n,k,c", [(1, 64, 1), (5, 256, 3), (63, 1024, 8), (65, 2048, 2),
+                                   (300, 4096, 5), (33, 3072, 4), (17, 8192, 1), (129, 1024, 7)])
+def test_mmvq_vs_oracle(n, k, c):
+    say(f"mmvq n={n} k={k} c={c}")
+    w, wd = synth_matrix(n + k, n, k)
+    xo, xd = quantized_pair(workloads.normal_f32(c * 17 + k, (c, k)))
+    y = host(moeq8.mmvq_q8_0(wd, xd, n, k))
+    assert_close(y, oracle.mmvq(w, xo), PROD_TOL, "mmvq")
+
+
+# ---------------------------------------------------------------------------
+# a2: gate/up pair + SwiGLU-DS4, and the pages' invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k,c", [(512, 256, 1), (100, 4096, 8), (2048, 4096, 5), (64, 1024, 3)])
+def test_pair_vs_oracle_and_separate(n, k, c):
+    say(f"pair n={n} k={k} c={c}")
+    wg, wgd = synth_matrix(1, n, k, matrix=0)
+    wu, wud = synth_matrix(1, n, k, matrix=1)
+    x = workloads.normal_f32(c + 3 * k, (c, k))
+    x[0] *= 40.0                                          # drive g, u past the clamp at 7
+    xo, xd = quantized_pair(x)
+    g = torch.empty((c, n), dtype=torch.float32, device=DEV)
+    u = torch.empty_like(g)
+    h = moeq8.mmvq_q8_0_glu_pair(wgd, wud, xd, n, k, g_out=g, u_out=u)
+    h_ref, g_ref, u_ref = oracle.glu_pair(wg, wu, xo)
+    assert_close(host(g), g_ref, PROD_TOL, "gate")
+    assert_close(host(u), u_ref, PROD_TOL, "up")
+    assert_close(host(h), h_ref, EPI_TOL, "swiglu")
+    assert (np.abs(g_ref) > 7).any() and (np.abs(u_ref) > 7).any()
+    # fused pair == the products kept apart + the GLU kernel, bit for bit
+    g_sep = moeq8.mmvq_q8_0(wgd, xd, n, k)
+    u_sep = moeq8.mmvq_q8_0(wud, xd, n, k)
+    assert bits_equal(g, g_sep) and bits_equal(u, u_sep)
+    assert bits_equal(h, moeq8.swiglu_ds4(g_sep, u_sep))
+    h2 = moeq8.mmvq_q8_0_glu_pair(wgd, wud, xd, n, k)    # without the optional outputs
+    assert bits_equal(h, h2)
+
+
+def test_swiglu_kernel_vs_oracle():
+    g = workloads.normal_f32(91, (4096,), 6.0)
+    u = workloads.normal_f32(92, (4096,), 6.0)
+    g[:4] = [7.0, 100.0, -100.0, 0.0]
+    h = host(moeq8.swiglu_ds4(to_dev(g), to_dev(u)))
+    assert_close(h, oracle.swiglu_ds4(g, u), EPI_TOL, "swiglu_ds4")
+
+
+@pytest.mark.parametrize("k", [256, 1024, 4096])
+def test_batch_invariance(k):
+    say(f"batch invariance k={k}")
+    n = 96
+    wg, wgd = synth_matrix(7, n, k, matrix=0)
+    wu, wud = synth_matrix(7, n, k, matrix=1)
+    _, xd = quantized_pair(workloads.normal_f32(8 + k, (8, k)))
+    h8 = moeq8.mmvq_q8_0_glu_pair(wgd, wud, xd, n, k)
+    y8 = moeq8.mmvq_q8_0(wgd, xd, n, k)
+    for c in range(1, 9):
+        hc = moeq8.mmvq_q8_0_glu_pair(wgd, wud, xd[:c].contiguous(), n, k)
+        yc = moeq8.mmvq_q8_0(wgd, xd[:c].contiguous(), n, k)
+        assert bits_equal(hc, h8[:c]) and bits_equal(yc, y8[:c]), c
+        # a single column alone gives the same bits as inside a batch
+        h1 = moeq8.mmvq_q8_0_glu_pair(wgd, wud, xd[c - 1:c].contiguous(), n, k)
+        assert bits_equal(h1, h8[c - 1:c])
+
+
+@pytest.mark.parametrize("k,kb_off,kslice", [(4096, 0, 2048), (4096, 64, 2048), (2048, 0, 1024),
+                                             (2048, 32, 1024), (1024, 16, 512), (4096, 2, 1024),
+                                             (4096, 38, 2048), (1024, 0, 1024)])
+def test_column_range_slice_equals_zero_padded_full(k, kb_off, kslice):
+    say(f"column range k={k} off={kb_off} k'={kslice}")
+    n = 80
+    nb = k // 32
+    w, wd = synth_matrix(11, n, k, matrix=2)
+    x = workloads.normal_f32(kb_off + kslice, (3, k))
+    x_pad = np.zeros_like(x)
+    lo, hi = kb_off * 32, kb_off * 32 + kslice
+    x_pad[:, lo:hi] = x[:, lo:hi]
+    _, xs = quantized_pair(np.ascontiguousarray(x[:, lo:hi]))
+    _, xpad = quantized_pair(x_pad)
+    row_bytes = nb * 34
+    y_slice = moeq8.mmvq_q8_0(wd, xs, n, kslice, k_block_offset=kb_off, w_offset_bytes=kb_off * 34,
+                              w_row_stride_bytes=row_bytes)
+    y_full = moeq8.mmvq_q8_0(wd, xpad, n, k)
+    assert bits_equal(y_slice, y_full)
+    # the pair keeps the same lanes
+    wu, wud = synth_matrix(11, n, k, matrix=3)
+    h_slice = moeq8.mmvq_q8_0_glu_pair(wd, wud, xs, n, kslice, k_block_offset=kb_off,
+                                       w_offset_bytes=kb_off * 34, w_row_stride_bytes=row_bytes)
+    h_full = moeq8.mmvq_q8_0_glu_pair(wd, wud, xpad, n, k)
+    assert bits_equal(h_slice, h_full)
+    # and the slice matches the oracle's column-range product
+    xo = oracle.quantize_q8_1(np.ascontiguousarray(x[:, lo:hi]))
+    assert_close(host(y_slice), oracle.mmvq_column_range(w, xo, kb_off), PROD_TOL, "slice")
+
+
+def test_row_slice_equals_rows_of_full():
+    n, k = 2048, 4096
+    w, wd = synth_matrix(12, n, k, matrix=0)
+    wu, wud = synth_matrix(12, n, k, matrix=1)
+    _, xd = quantized_pair(workloads.normal_f32(13, (8, k)))
+    h_full = moeq8.mmvq_q8_0_glu_pair(wd, wud, xd, n, k)
+    row_bytes = (k // 32) * 34
+    for r0, nr in [(0, 1024), (1024, 1024), (5, 77)]:
+        h_rows = moeq8.mmvq_q8_0_glu_pair(wd, wud, xd, nr, k, w_offset_bytes=r0 * row_bytes,
+                                          w_row_stride_bytes=row_bytes)
+        assert bits_equal(h_rows, h_full[:, r0:r0 + nr].contiguous())
+
+
+def test_repeat_determinism():
+    n, k = 1024, 4096
+    _, wd = synth_matrix(14, n, k)
+    _, wud = synth_matrix(14, n, k, matrix=1)
+    _, xd = quantized_pair(workloads.normal_f32(15, (5, k)))
+    a = moeq8.mmvq_q8_0_glu_pair(wd, wud, xd, n, k)
+    for _ in range(3):
+        assert bits_equal(a, moeq8.mmvq_q8_0_glu_pair(wd, wud, xd, n, k))
+
+
+# ---------------------------------------------------------------------------
+# a4 / a5: router + grouping
+# ---------------------------------------------------------------------------
+
+def _grouping_words(gt):
+    return host(gt).view(np.int32)
+
+
+def _check_grouping(words, ids_ref):
+    R = ids_ref.size
+    n_active, n_valid, ncols, topk = words[:4]
+    groups = oracle.group_routes(ids_ref)
+    assert n_active == len(groups) and ncols * topk == R
+    assert n_valid == int((ids_ref >= 0).sum())
+    expert = words[4:4 + R]
+    offset = words[4 + R:4 + 2 * R + 1]
+    route = words[4 + 2 * R + 1:4 + 3 * R + 1]
+    for a, (e, routes) in enumerate(groups):
+        assert expert[a] == e
+        assert list(route[offset[a]:offset[a + 1]]) == routes
+
+
+@pytest.mark.parametrize("c,n_exp,topk,local", [(1, 256, 8, 256), (5, 256, 8, 256), (8, 256, 8, 128),
+                                                (8, 64, 6, 64), (3, 1024, 16, 512), (2, 8, 8, 8)])
+def test_route_topk_vs_oracle(c, n_exp, topk, local):
+    say(f"route c={c} E={n_exp} k={topk} local={local}")
+    logits = workloads.router_logits(c + n_exp, c, n_exp)
+    bias = workloads.router_bias(c + n_exp, n_exp)
+    own = None if local == n_exp else workloads.owner_slots(n_exp, local)
+    ids_ref, w_ref, _ = oracle.route_topk(logits, bias, own, topk)
+    ids, w, grouping = moeq8.moe_route_topk(to_dev(logits), topk, bias=to_dev(bias),
+                                            owner_slot=None if own is None else to_dev(own),
+                                            n_local_expert=local)
+    assert np.array_equal(host(ids), ids_ref)
+    assert_close(host(w), w_ref, EPI_TOL, "route weights")
+    assert np.abs(host(w).astype(np.float64) - w_ref).max() < 1e-6
+    _check_grouping(_grouping_words(grouping), ids_ref)
+
+
+def test_route_ties_and_no_bias():
+    logits = np.zeros((2, 256), np.float32)
+    ids, w, _ = moeq8.moe_route_topk(to_dev(logits), 8)
+    assert np.array_equal(host(ids), np.tile(np.arange(8, dtype=np.int32), (2, 1)))
+    assert np.all(host(w) == np.float32(0.125))
+    lg = np.full((1, 16), -5.0, np.float32)
+    top = [3, 9, 1, 12, 7, 0, 14]
+    for r, e in enumerate(top):
+        lg[0, e] = 4.0 - 0.5 * r
+    lg[0, 11] = lg[0, 5] = -1.0
+    ids, _, _ = moeq8.moe_route_topk(to_dev(lg), 8)
+    assert list(host(ids)[0]) == top + [5]
+
+
+def test_route_all_masked():
+    logits = workloads.router_logits(3, 4, 256)
+    own = np.full(256, -1, np.int32)
+    own[200] = 0                                           # one local expert that is never picked
+    logits[:, 200] = -50.0
+    ids, w, grouping = moeq8.moe_route_topk(to_dev(logits), 8, owner_slot=to_dev(own), n_local_expert=1)
+    assert np.all(host(ids) == -1)
+    words = _grouping_words(grouping)
+    assert words[0] == 0 and words[1] == 0
+
+
+# ---------------------------------------------------------------------------
+# a6 / a8 / a9: grouped products and the combine
+# ---------------------------------------------------------------------------
+
+def _tiny_layer(seed, n_local, hidden, inter):
+    wg = np.stack([workloads.synth_q8_0_matrix(seed, 0, e, 0, inter, hidden) for e in range(n_local)])
+    wu = np.stack([workloads.synth_q8_0_matrix(seed, 0, e, 1, inter, hidden) for e in range(n_local)])
+    wdn = np.stack([workloads.synth_q8_0_matrix(seed, 0, e, 2, hidden, inter) for e in range(n_local)])
+    dev = [to_dev(a.reshape(-1)).reshape(-1) for a in (wg, wu, wdn)]
+    return (wg, wu, wdn), dev
+
+
+@pytest.mark.parametrize("c,n_exp,local,hidden,inter", [(1, 32, 32, 1024, 256), (5, 16, 16, 2048, 512),
+                                                        (8, 64, 32, 1024, 1024), (8, 4, 4, 256, 128)])
+def test_grouped_gate_up_down_combine(c, n_exp, local, hidden, inter):
+    say(f"grouped c={c} E={n_exp} local={local} hidden={hidden} inter={inter}")
+    topk = min(8, n_exp)
+    (wg, wu, wdn), (wgd, wud, wdd) = _tiny_layer(c + local, local, hidden, inter)
+    x = workloads.activations(c, c, hidden)
+    logits = workloads.router_logits(c, c, n_exp)
+    bias = workloads.router_bias(c, n_exp)
+    own = workloads.owner_slots(n_exp, local)
+    xo, xd = quantized_pair(x)
+    ids, w, grouping = moeq8.moe_route_topk(to_dev(logits), topk, bias=to_dev(bias),
+                                            owner_slot=to_dev(own), n_local_expert=local)
+    ids_ref, w_ref, _ = oracle.route_topk(logits, bias, own, topk)
+    assert np.array_equal(host(ids), ids_ref)
+
+    # gate/up: each route's h against the oracle and against the pair on that expert
+    h = torch.full((c, topk, inter), float("nan"), device=DEV)
+    moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, wgd, wud, xd, grouping, n=inter, k=hidden,
+                           n_local_expert=local, ncols=c, topk=topk, out=h)
+    hh = host(h)
+    row_b = (hidden // 32) * 34
+    for j in range(c):
+        for s in range(topk):
+            e = ids_ref[j, s]
+            if e < 0:
+                assert np.isnan(hh[j, s]).all()              # masked rows untouched
+                continue
+            h_ref, _, _ = oracle.glu_pair(wg[e], wu[e], xo[j:j + 1])
+            assert_close(hh[j, s], h_ref[0], EPI_TOL, f"grouped h ({j},{s})")
+            hp = moeq8.mmvq_q8_0_glu_pair(wgd, wud, xd[j:j + 1].contiguous(), inter, hidden,
+                                          w_offset_bytes=int(e) * inter * row_b, w_row_stride_bytes=row_b)
+            assert bits_equal(h[j, s:s + 1].contiguous(), hp)
+
+    # a7 on the oracle's h: the GPU quantiser gives the oracle's bytes
+    h_ref32 = np.zeros((c * topk, inter), np.float32)
+    for j in range(c):
+        for s in range(topk):
+            if ids_ref[j, s] >= 0:
+                h_ref32[j * topk + s] = oracle.glu_pair(wg[ids_ref[j, s]], wu[ids_ref[j, s]],
+                                                        xo[j:j + 1])[0][0].astype(np.float32)
+    hq_dev = moeq8.q8_1_quantize_rows(to_dev(h_ref32))
+    hq_ref_all = oracle.quantize_q8_1(h_ref32)
+    assert host(hq_dev).tobytes() == hq_ref_all.tobytes()
+
+    # down on the oracle's hq
+    y = torch.full((c, topk, hidden), float("nan"), device=DEV)
+    moeq8.moe_grouped_mmvq(moeq8.DOWN, wdd, None, hq_dev, grouping, n=hidden, k=inter,
+                           n_local_expert=local, ncols=c, topk=topk, out=y)
+    yy = host(y)
+    y_ref = np.zeros((c, topk, hidden))
+    row_d = (inter // 32) * 34
+    for j in range(c):
+        for s in range(topk):
+            e = ids_ref[j, s]
+            if e < 0:
+                assert np.isnan(yy[j, s]).all()
+                continue
+            y_ref[j, s] = oracle.mmvq(wdn[e], hq_ref_all[j * topk + s:j * topk + s + 1])[0]
+            assert_close(yy[j, s], y_ref[j, s], PROD_TOL, f"grouped y ({j},{s})")
+            ys = moeq8.mmvq_q8_0(wdd, hq_dev[j * topk + s:j * topk + s + 1].contiguous(), hidden, inter,
+                                 w_offset_bytes=int(e) * hidden * row_d, w_row_stride_bytes=row_d)
+            assert bits_equal(y[j, s:s + 1].contiguous(), ys)
+
+    # combine on the oracle's y and weights (masked slots hold NaN and are never read)
+    y32 = np.where(ids_ref[..., None] >= 0, y_ref, np.nan).astype(np.float32)
+    w32 = w_ref.astype(np.float32)
+    out = host(moeq8.moe_combine(to_dev(y32), ids, to_dev(w32)))
+    assert_close(out, oracle.moe_combine(y32.astype(np.float64), ids_ref, w32.astype(np.float64)),
+                 EPI_TOL, "combine")
+    assert np.isfinite(out).all()
+
+
+def test_combine_one_hot_and_all_masked():
+    rng = np.random.default_rng(2)
+    y = rng.normal(size=(3, 8, 4096)).astype(np.float32)
+    ids = np.array([[0, 1, 2, 3, 4, 5, 6, 7], [-1] * 8, [1, -1, 2, -1, 3, -1, 4, -1]], np.int32)
+    w = np.zeros((3, 8), np.float32)
+    w[0, 5] = 1.0
+    w[2] = 0.125
+    y[2, 1] = np.nan
+    out = host(moeq8.moe_combine(to_dev(y), to_dev(ids), to_dev(w)))
+    assert np.array_equal(out[0], y[0, 5])
+    assert np.all(out[1] == 0.0)
+    ref = np.float32(0.125) * y[2, 0]
+    for s in (2, 4, 6):
+        ref = ref + np.float32(0.125) * y[2, s]
+    assert np.array_equal(out[2], ref)                     # fp32: products rounded, sums in slot order
+
+
+def test_graph_replay_matches_eager():
+    """One routed layer captured in a HIP graph and replayed several times, with
+    eager work and synchronisation between replays, equals the eager run."""
+    say("graph replay")
+    c, n_exp, hidden, inter, topk = 5, 32, 1024, 256, 8
+    (_, _, _), (wgd, wud, wdd) = _tiny_layer(21, n_exp, hidden, inter)
+    xd = to_dev(workloads.activations(21, c, hidden))
+    lg = to_dev(workloads.router_logits(21, c, n_exp))
+    bias = to_dev(workloads.router_bias(21, n_exp))
+    xq = torch.empty((c, hidden // 32 * 36), dtype=torch.uint8, device=DEV)
+    ids = torch.empty((c, topk), dtype=torch.int32, device=DEV)
+    w = torch.empty((c, topk), dtype=torch.float32, device=DEV)
+    grouping = torch.empty(moeq8.moe_grouping_bytes(c, topk), dtype=torch.uint8, device=DEV)
+    h = torch.empty((c, topk, inter), dtype=torch.float32, device=DEV)
+    hq = torch.empty((c * topk, inter // 32 * 36), dtype=torch.uint8, device=DEV)
+    y = torch.empty((c, topk, hidden), dtype=torch.float32, device=DEV)
+    out = torch.empty((c, hidden), dtype=torch.float32, device=DEV)
+
+    def layer():
+        moeq8.q8_1_quantize_rows(xd, out=xq)
+        moeq8.moe_route_topk(lg, topk, bias=bias, ids=ids, weights=w, grouping=grouping)
+        moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, wgd, wud, xq, grouping, n=inter, k=hidden,
+                               n_local_expert=n_exp, ncols=c, topk=topk, out=h)
+        moeq8.q8_1_quantize_rows(h.view(c * topk, inter), out=hq)
+        moeq8.moe_grouped_mmvq(moeq8.DOWN, wdd, None, hq, grouping, n=hidden, k=inter,
+                               n_local_expert=n_exp, ncols=c, topk=topk, out=y)
+        moeq8.moe_combine(y, ids, w, out=out)
+
+    layer()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bits_equal(out, ref), i
+        layer()                                            # eager work between replays
+        torch.cuda.synchronize()
+        assert bits_equal(out, ref)
+
+
+def test_synth_fill_matches_host_generator():
+    n_mats, bpm = 3, 4096
+    dst = torch.empty(n_mats * bpm * 34, dtype=torch.uint8, device=DEV)
+    moeq8.synth_q8_0_fill(dst, n_mats, bpm, 2, seed=5, layer0=7, expert0=3, matrix=2)
+    got = host(dst)
+    for i in range(n_mats):
+        ref = workloads.synth_q8_0_blocks(workloads.stream_key(5, 7 + i // 2, 3 + i % 2, 2), 0, bpm)
+        assert got[i * bpm * 34:(i + 1) * bpm * 34].tobytes() == ref.tobytes()
