@@ -1,0 +1,424 @@
+"""Benchmark of the quantized MoE expert FFN on one MI355X.
+
+Step = one pass of the whole hot path over one batch: for each of the 43 MoE
+layers of one GPU's share of the DS4.1 verify step (128 local experts of 256,
+8 columns, half of the shared expert's intermediate axis): quantise x, shared
+gate/up pair + SwiGLU, quantise, shared down (column-range slice), route
+(select + weights + owner mask + grouping), grouped gate/up + SwiGLU,
+quantise h, grouped down, combine.  Inputs are resident in HBM; the step is
+captured once as a HIP graph and replayed.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value     effective HBM GB/s of the step (algorithmic bytes / step time)
+  roofline  the dominant kernel (grouped gate/up + SwiGLU): algorithmic bytes
+            per launch / mean launch time from HIP events, against 8 TB/s
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  sweep     the routed layer (256 experts, top-8) at 1, 2, 4, 5, 8 columns
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate budget of the oracle sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# workload construction
+# ---------------------------------------------------------------------------
+
+class Bank:
+    """Routed experts of L layers x E local experts, plus optional shared
+    expert (full matrices per layer), filled with synthetic Q8_0 blocks."""
+
+    def __init__(self, moeq8, torch, layers, n_local, hidden, inter, seed, shared_inter=0):
+        self.layers, self.n_local, self.hidden, self.inter = layers, n_local, hidden, inter
+        rb_h = hidden // 32 * 34
+        rb_i = inter // 32 * 34
+        self.expert_gu = inter * rb_h
+        self.expert_d = hidden * rb_i
+        dev = "cuda"
+        self.gate = torch.empty((layers, n_local * self.expert_gu), dtype=torch.uint8, device=dev)
+        self.up = torch.empty_like(self.gate)
+        self.down = torch.empty((layers, n_local * self.expert_d), dtype=torch.uint8, device=dev)
+        for t, m, blocks in ((self.gate, 0, inter * hidden // 32), (self.up, 1, inter * hidden // 32),
+                             (self.down, 2, hidden * inter // 32)):
+            moeq8.synth_q8_0_fill(t, layers * n_local, blocks, n_local, seed, 0, 0, m)
+        self.shared_inter = shared_inter
+        if shared_inter:
+            self.sgate = torch.empty((layers, shared_inter * rb_h), dtype=torch.uint8, device=dev)
+            self.sup = torch.empty_like(self.sgate)
+            self.sdown = torch.empty((layers, hidden * (shared_inter // 32 * 34)), dtype=torch.uint8,
+                                     device=dev)
+            for t, m, blocks in ((self.sgate, 3, shared_inter * hidden // 32),
+                                 (self.sup, 4, shared_inter * hidden // 32),
+                                 (self.sdown, 5, hidden * shared_inter // 32)):
+                moeq8.synth_q8_0_fill(t, layers, blocks, 1, seed, 0, 0, m)
+
+    def experts(self, ml, l):
+        return ml.RoutedExperts(self.gate[l], self.up[l], self.down[l], self.n_local, self.hidden,
+                                self.inter)
+
+    def shared(self, ml, l, share_rows, share_index=0):
+        if not self.shared_inter:
+            return None
+        rb_h = self.hidden // 32 * 34
+        return ml.SharedExpertShare(self.sgate[l].view(self.shared_inter, rb_h),
+                                    self.sup[l].view(self.shared_inter, rb_h),
+                                    self.sdown[l].view(self.hidden, self.shared_inter // 32 * 34),
+                                    self.hidden, self.shared_inter, share_index * share_rows, share_rows)
+
+
+def layer_inputs(torch, workloads, seed, layers, cols, hidden, n_expert):
+    xs, lgs, bs = [], [], []
+    for l in range(layers):
+        xs.append(torch.from_numpy(workloads.activations(seed, cols, hidden, layer=l)).cuda())
+        lgs.append(torch.from_numpy(workloads.router_logits(seed, cols, n_expert, layer=l)).cuda())
+        bs.append(torch.from_numpy(workloads.router_bias(seed, n_expert, layer=l)).cuda())
+    return xs, lgs, bs
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes
+# ---------------------------------------------------------------------------
+
+def gate_up_launch_bytes(n_active, n_valid, cols, hidden, inter):
+    """Per grouped gate/up launch: both matrices of every active expert once,
+    the q8_1 x rows once, the h rows written."""
+    return n_active * 2 * inter * (hidden // 32 * 34) + cols * (hidden // 32 * 36) + n_valid * inter * 4
+
+
+def down_launch_bytes(n_active, n_valid, hidden, inter):
+    return n_active * hidden * (inter // 32 * 34) + n_valid * (inter // 32 * 36) + n_valid * hidden * 4
+
+
+def layer_bytes(n_active, n_valid, cols, hidden, inter, topk, shared_rows):
+    """Algorithmic bytes of one layer: every tensor written once by its producer
+    and read once per consumer (weights of the active experts once)."""
+    b = cols * hidden * 4 + cols * (hidden // 32 * 36)               # x read, xq written
+    b += gate_up_launch_bytes(n_active, n_valid, cols, hidden, inter)
+    b += n_valid * inter * 4 + n_valid * (inter // 32 * 36)          # h read, hq written
+    b += down_launch_bytes(n_active, n_valid, hidden, inter)
+    b += n_valid * hidden * 4 + 2 * cols * topk * 8 + cols * hidden * 4  # y read, ids/w, out
+    b += cols * 256 * 4 * 2                                           # logits read (n_expert 256), bias
+    if shared_rows:
+        b += cols * (hidden // 32 * 36)                              # xq read again
+        b += 2 * shared_rows * (hidden // 32 * 34) + cols * shared_rows * 4   # pair weights, hs
+        b += cols * shared_rows * 4 + cols * (shared_rows // 32 * 36)          # hs read, hsq
+        b += hidden * (shared_rows // 32 * 34) + cols * (shared_rows // 32 * 36) + cols * hidden * 4
+    return b
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (oracle, bounded sample)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(workloads, cfg, budget_s, share_rows):
+    import oracle
+    seed, hidden, inter, topk = cfg["seed"], cfg["hidden"], cfg["inter"], cfg["topk"]
+    cols = cfg["cols"][0]
+    n_exp, n_local = cfg["experts"], cfg["local_experts"]
+    own = workloads.owner_slots(n_exp, n_local)
+    total_bytes, total_t, layers_done = 0, 0.0, 0
+    for l in range(cfg["layers"]):
+        x = workloads.activations(seed, cols, hidden, layer=l)
+        lg = workloads.router_logits(seed, cols, n_exp, layer=l)
+        bias = workloads.router_bias(seed, n_exp, layer=l)
+        ids, _, _ = oracle.route_topk(lg, bias, own, topk)
+        used = sorted(set(int(e) for e in ids.reshape(-1) if e >= 0))
+        mats = {e: tuple(workloads.synth_q8_0_matrix(seed, l, e, m, r, k)
+                         for m, r, k in ((0, inter, hidden), (1, inter, hidden), (2, hidden, inter)))
+                for e in used}
+        sg = workloads.synth_q8_0_matrix(seed, l, 0, 3, cfg["shared_inter"], hidden, 0, share_rows)
+        su = workloads.synth_q8_0_matrix(seed, l, 0, 4, cfg["shared_inter"], hidden, 0, share_rows)
+        sd = workloads.synth_q8_0_matrix(seed, l, 0, 5, hidden, cfg["shared_inter"])
+        t0 = time.perf_counter()
+        r = oracle.moe_layer(x, lg, bias, own, lambda e: mats[e], topk)
+        h, _, _ = oracle.glu_pair(sg, su, r["xq"])
+        hq = oracle.quantize_q8_1(h.astype(np.float32))
+        oracle.mmvq(sd[:, :share_rows // 32], hq)
+        total_t += time.perf_counter() - t0
+        n_valid = int((ids >= 0).sum())
+        total_bytes += layer_bytes(len(used), n_valid, cols, hidden, inter, topk, share_rows)
+        layers_done += 1
+        if total_t >= budget_s:
+            break
+    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{layers_done} of {cfg['layers']} layers of {cfg['name']} (numpy oracle, "
+                      f"unfused per-route loop, single thread); {layers_done / total_t:.3f} layers/s"}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU sharding of the "
+                                   "expert FFN is not built (one process per GPU would each run this "
+                                   "step on its own expert share)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import workloads
+    import quantized_moe_expert_q8_amd as moeq8
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+
+    torch.cuda.init()
+    cfg = dict(workloads.CONFIGS["ep_share_l43_e128_c8"], name="ep_share_l43_e128_c8")
+    L, n_local, n_exp = cfg["layers"], cfg["local_experts"], cfg["experts"]
+    hidden, inter, topk, seed, cols = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["seed"], cfg["cols"][0]
+    share_rows = cfg["shared_inter"] // cfg["shared_share"]
+
+    t0 = time.perf_counter()
+    bank = Bank(moeq8, torch, L, n_local, hidden, inter, seed, cfg["shared_inter"])
+    xs, lgs, bs = layer_inputs(torch, workloads, seed, L, cols, hidden, n_exp)
+    owner = torch.from_numpy(workloads.owner_slots(n_exp, n_local)).cuda()
+    ws = ml.Workspace(cols, hidden, inter, topk, share_rows, "cuda")
+    torch.cuda.synchronize()
+    resident = sum(t.numel() for t in (bank.gate, bank.up, bank.down, bank.sgate, bank.sup, bank.sdown))
+    log(f"setup {time.perf_counter() - t0:.1f}s, resident weights {resident / 1e9:.2f} GB")
+
+    experts = [bank.experts(ml, l) for l in range(L)]
+    shared = [bank.shared(ml, l, share_rows) for l in range(L)]
+
+    def step(hook=None):
+        for l in range(L):
+            ml.forward(xs[l], lgs[l], bs[l], owner, n_local, experts[l], shared[l], ws, hook=hook)
+
+    # routing statistics of every layer (measurement input: active experts)
+    n_active, n_valid = [], []
+    for l in range(L):
+        moeq8.moe_route_topk(lgs[l], topk, bias=bs[l], owner_slot=owner, n_local_expert=n_local,
+                             ids=ws.ids, weights=ws.weights, grouping=ws.grouping)
+        words = ws.grouping.cpu().numpy().view(np.int32)
+        n_active.append(int(words[0]))
+        n_valid.append(int(words[1]))
+    step_bytes = sum(layer_bytes(n_active[l], n_valid[l], cols, hidden, inter, topk, share_rows)
+                     for l in range(L))
+    weight_bytes = sum(n_active[l] * ml.expert_bytes(hidden, inter) + ml.shared_share_bytes(hidden, share_rows)
+                       for l in range(L))
+    log(f"active local experts per layer: mean {np.mean(n_active):.1f} (min {min(n_active)}, "
+        f"max {max(n_active)}); step bytes {step_bytes / 1e9:.3f} GB (weights {weight_bytes / 1e9:.3f} GB)")
+
+    # eager warm-up, then capture the step as one graph
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"graph: {ms_per_step:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
+        f"{value:.1f} GB/s, {L / ms_per_step * 1e3:.0f} layers/s")
+
+    # eager step time (launch overhead included) and per-kernel event timing
+    events = {}
+    cur = torch.cuda.current_stream()
+
+    def hook(name, phase):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(cur)
+        events.setdefault(name, []).append((phase, e))
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reps = max(3, args.steps // 5)
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / reps
+    kern_reps = 3
+    for _ in range(kern_reps):
+        step(hook)
+    torch.cuda.synchronize()
+
+    def mean_ms(name):
+        lst = events[name]
+        d = [lst[i][1].elapsed_time(lst[i + 1][1]) for i in range(0, len(lst), 2)]
+        return float(np.mean(d)), d
+
+    gu_ms, gu_all = mean_ms("grouped_gate_up")
+    gu_bytes = [gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter) for l in range(L)] * kern_reps
+    gu_gbps = float(np.sum(gu_bytes) / (np.sum(gu_all) * 1e-3) / 1e9)
+    dn_ms, dn_all = mean_ms("grouped_down")
+    dn_bytes = [down_launch_bytes(n_active[l], n_valid[l], hidden, inter) for l in range(L)] * kern_reps
+    dn_gbps = float(np.sum(dn_bytes) / (np.sum(dn_all) * 1e-3) / 1e9)
+    per_kernel = {}
+    for name in events:
+        m, _ = mean_ms(name)
+        per_kernel[name] = round(m * 1e3, 2)
+    log(f"eager {eager_ms:.3f} ms/step; per-launch mean us: {per_kernel}")
+    log(f"grouped gate/up {gu_gbps:.1f} GB/s, grouped down {dn_gbps:.1f} GB/s")
+
+    result = {
+        "metric": "Q8_0 MoE MMVQ effective HBM GB/s (% of peak) + MoE layers/s at 1-8 cols",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "layers": L, "experts": n_exp, "local_experts": n_local,
+                   "cols": cols, "hidden": hidden, "inter": inter, "topk": topk,
+                   "shared_rows": share_rows, "seed": seed, "graph": True},
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "layers_per_s": round(L / ms_per_step * 1e3, 1),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "step_bytes": step_bytes,
+        "weight_bytes": weight_bytes,
+        "active_experts_mean": round(float(np.mean(n_active)), 2),
+        "per_launch_us": per_kernel,
+        "roofline": {"bound": "hbm", "kernel": "k_mmvq grouped gate/up + SwiGLU",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "mean_launch_us": round(gu_ms * 1e3, 2),
+                     "bytes_per_launch": int(np.mean(gu_bytes))},
+        "grouped_down_gbps": round(dn_gbps, 1),
+    }
+
+    # release the big bank before the sweep
+    del g, bank, experts, shared
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    if not args.no_sweep:
+        result["sweep"] = sweep(torch, workloads, moeq8, ml, args)
+
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        result["cpu_baseline"] = cpu_baseline(workloads, cfg, args.cpu_seconds, share_rows)
+        log(f"cpu baseline {time.perf_counter() - t0:.1f}s: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+def sweep(torch, workloads, moeq8, ml, args):
+    """Routed layer, 256 experts, top-8, at 1..8 columns; 4 weight replicas
+    (13.7 GB) rotate so the 256 MB Infinity Cache cannot serve the reads."""
+    cfg = workloads.CONFIGS["verify_e256_c5"]
+    hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
+    reps = 4
+    bank = Bank(moeq8, torch, reps, n_exp, hidden, inter, 4)
+    out = []
+    for cols in (1, 2, 4, 5, 8):
+        xs, lgs, bs = layer_inputs(torch, workloads, 4, reps, cols, hidden, n_exp)
+        ws = ml.Workspace(cols, hidden, inter, topk, 0, "cuda")
+        experts = [bank.experts(ml, l) for l in range(reps)]
+        n_active, n_valid = [], []
+        for l in range(reps):
+            moeq8.moe_route_topk(lgs[l], topk, bias=bs[l], ids=ws.ids, weights=ws.weights,
+                                 grouping=ws.grouping)
+            words = ws.grouping.cpu().numpy().view(np.int32)
+            n_active.append(int(words[0]))
+            n_valid.append(int(words[1]))
+
+        def step():
+            for l in range(reps):
+                ml.forward(xs[l], lgs[l], bs[l], None, n_exp, experts[l], None, ws)
+
+        step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(20, args.steps)
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n / reps
+        lb = float(np.mean([layer_bytes(n_active[l], n_valid[l], cols, hidden, inter, topk, 0)
+                            for l in range(reps)]))
+        # dominant kernel alone, eager with events
+        evs = []
+        cur = torch.cuda.current_stream()
+        for _ in range(3):
+            for l in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                moeq8.q8_1_quantize_rows(xs[l], out=ws.xq)
+                moeq8.moe_route_topk(lgs[l], topk, bias=bs[l], ids=ws.ids, weights=ws.weights,
+                                     grouping=ws.grouping)
+                a.record(cur)
+                moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, ws.xq,
+                                       ws.grouping, n=inter, k=hidden, n_local_expert=n_exp, ncols=cols,
+                                       topk=topk, out=ws.h)
+                b.record(cur)
+                evs.append((l, a, b))
+        torch.cuda.synchronize()
+        gu_t = sum(a.elapsed_time(b) for _, a, b in evs)
+        gu_b = sum(gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter) for l, _, _ in evs)
+        rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2),
+               "layer_us": round(ms * 1e3, 2), "layers_per_s": round(1e3 / ms, 1),
+               "effective_gbps": round(lb / (ms * 1e-3) / 1e9, 1),
+               "gate_up_gbps": round(gu_b / (gu_t * 1e-3) / 1e9, 1)}
+        log(f"sweep {rec}")
+        out.append(rec)
+        del g
+    del bank
+    torch.cuda.empty_cache()
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,14 +1,20 @@
 // Router top-k select and weights over the same logits, owner mask and the
 // layer's expert grouping, in one launch (lucebox PR #826, the fused DS4.1
-// decode kernels commit: "the router's select and weights over the same logits"
-// and "one expert grouping per MoE layer for gate, up and down"; the routed
-// combine commit: the owner route mask).
+// decode kernels commit: the router's select and weights over the same logits,
+// one expert grouping per MoE layer for gate, up and down; the routed combine
+// commit: the owner route mask).
 //
-// One workgroup; wave j selects column j's top-k by repeated wave-wide argmax
-// under the order (key descending, expert index ascending), which is a strict
-// total order, so the selection is exact and deterministic.  Then the whole
-// workgroup sorts the <= ncols*topk routes by (local expert, route index) and
-// writes the grouping the grouped MMVQ launches read.
+// One workgroup; wave j selects column j's top-k.  Lane l of the wave holds
+// experts [l*PER, (l+1)*PER) (contiguous, so among equal keys the lowest lane
+// holds the lowest index).  Keys are compared as order-preserving u32 images
+// of the fp32 key (the same order as the fp32 comparison for non-NaN keys, -0
+// canonicalised to +0).  Each of the topk rounds takes the lane-local best
+// untaken key, the wave maximum (DPP within rows of 16, then the four rows),
+// and the lowest lane holding it (ballot): exact (key descending, expert
+// ascending) selection.  Rounds run in slot order, so the weight sum is
+// accumulated there in slot order; lane s keeps slot s.  Then waves 0-1 sort
+// the <= 128 routes by (local expert, route index) for the grouping, reading
+// the route ids with unrolled 16-byte LDS loads.
 #include "moeq8_device.hpp"
 #include "moeq8_host.hpp"
 
@@ -17,113 +23,163 @@ namespace moeq8 {
 constexpr int ROUTE_MAX_COLS = 8;
 constexpr int ROUTE_MAX_TOPK = MOEQ8_MAX_TOPK;
 constexpr int ROUTE_MAX_EXPERT = MOEQ8_MAX_EXPERTS;
-constexpr int ROUTE_PER_LANE = ROUTE_MAX_EXPERT / 64;
+constexpr int ROUTE_MAX_R = ROUTE_MAX_COLS * ROUTE_MAX_TOPK;   // 128
 
-__device__ __forceinline__ bool key_before(float ka, int ea, float kb, int eb) {
-    return ka > kb || (ka == kb && ea < eb);
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+    const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+    return v > o ? v : o;
+}
+
+// maximum over the 64 lanes, returned to every lane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max_dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v = max_dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v = max_dpp<0x141>(v);   // row_half_mirror
+    v = max_dpp<0x140>(v);   // row_mirror: every lane holds its row's maximum
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    const uint32_t a = r0 > r1 ? r0 : r1;
+    const uint32_t b = r2 > r3 ? r2 : r3;
+    return a > b ? a : b;
+}
+
+template <int PER>
 __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk(
     const float* __restrict__ logits, const float* __restrict__ bias,
     const int32_t* __restrict__ owner, int ncols, int n_expert, int n_local, int topk,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ grouping) {
-    __shared__ int32_t s_id[ROUTE_MAX_COLS * ROUTE_MAX_TOPK];
-    __shared__ int32_t s_head[ROUTE_MAX_COLS * ROUTE_MAX_TOPK];
-    __shared__ int32_t s_sel_e[ROUTE_MAX_COLS * ROUTE_MAX_TOPK];
-    __shared__ float s_sel_score[ROUTE_MAX_COLS * ROUTE_MAX_TOPK];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) int32_t s_id[ROUTE_MAX_R];
+    __shared__ __attribute__((aligned(16))) int32_t s_headid[ROUTE_MAX_R];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int j = tid >> 6;
+    const int e0 = lane * PER;
+    const int R = ncols * topk;
+    const int Rpad = (R + 7) & ~7;
 
-    if (wave < ncols) {
-        const int j = wave;
-        float key[ROUTE_PER_LANE];
-        float score[ROUTE_PER_LANE];
-        bool taken[ROUTE_PER_LANE];
-#pragma unroll
-        for (int i = 0; i < ROUTE_PER_LANE; ++i) {
-            const int e = lane + 64 * i;
-            taken[i] = true;
-            key[i] = 0.0f;
-            score[i] = 0.0f;
-            if (e < n_expert) {
-                const double z = (double)logits[(int64_t)j * n_expert + e];
-                // sigmoid in fp64, rounded once to fp32
-                score[i] = (float)(1.0 / (1.0 + exp(-z)));
-                key[i] = bias ? score[i] + bias[e] : score[i];
-                taken[i] = false;
-            }
-        }
-        for (int s = 0; s < topk; ++s) {
-            float bk = -INFINITY, bs = 0.0f;
-            int be = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < ROUTE_PER_LANE; ++i) {
-                const int e = lane + 64 * i;
-                if (!taken[i] && key_before(key[i], e, bk, be)) {
-                    bk = key[i];
-                    be = e;
-                    bs = score[i];
-                }
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ok = __shfl_xor(bk, off, 64);
-                const int oe = __shfl_xor(be, off, 64);
-                const float os = __shfl_xor(bs, off, 64);
-                if (key_before(ok, oe, bk, be)) {
-                    bk = ok;
-                    be = oe;
-                    bs = os;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < ROUTE_PER_LANE; ++i)
-                if (lane + 64 * i == be) taken[i] = true;
-            if (lane == 0) {
-                s_sel_e[j * topk + s] = be;
-                s_sel_score[j * topk + s] = bs;
-            }
-        }
-        if (lane == 0) {
-            float sum = 0.0f;
-            for (int s = 0; s < topk; ++s) sum = sum + s_sel_score[j * topk + s];
-            for (int s = 0; s < topk; ++s) {
-                const int e = s_sel_e[j * topk + s];
-                int id = owner ? owner[e] : e;
-                if (id < 0 || id >= n_local) id = -1;
-                ids[j * topk + s] = id;
-                weights[j * topk + s] = s_sel_score[j * topk + s] / sum;
-                s_id[j * topk + s] = id;
-            }
-        }
+    if (tid < ROUTE_MAX_R) {
+        s_id[tid] = -1;
+        s_headid[tid] = -1;
     }
     __syncthreads();
 
-    // grouping: one thread per route sorts the valid routes by (id, route)
-    const int R = ncols * topk;  // <= blockDim.x
-    int32_t* g_expert = grouping + 4;
-    int32_t* g_offset = grouping + 4 + R;
-    int32_t* g_route = grouping + 4 + 2 * R + 1;
-    const int r = threadIdx.x;
+    float sum = 0.0f;
+    float slot_score = 0.0f;
+    int slot_id = -1;
+    if (j < ncols) {
+        float lg[PER], bs[PER], score[PER];
+        int own[PER];
+        uint32_t key[PER];
+        uint32_t valid = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = e0 + i;
+            const bool ok = e < n_expert;
+            valid |= ok ? (1u << i) : 0u;
+            lg[i] = ok ? logits[(int64_t)j * n_expert + e] : 0.0f;
+            bs[i] = (ok && bias) ? bias[e] : 0.0f;
+            own[i] = ok ? (owner ? owner[e] : e) : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            // sigmoid in fp64, rounded once to fp32; key = score + bias in fp32
+            score[i] = (float)(1.0 / (1.0 + exp(-(double)lg[i])));
+            key[i] = ordered_key(bias ? score[i] + bs[i] : score[i]);
+        }
+        uint32_t taken = 0;
+        for (int s = 0; s < topk; ++s) {
+            uint32_t best = 0;
+            int bi = -1;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const bool cand = ((valid & ~taken) >> i) & 1u;
+                if (cand && (bi < 0 || key[i] > best)) {
+                    best = key[i];
+                    bi = i;
+                }
+            }
+            const uint32_t wmax = wave_max_u32(bi >= 0 ? best : 0u);
+            const uint64_t mask = __ballot(bi >= 0 && best == wmax);
+            const int w = (int)__builtin_ctzll(mask);          // lowest lane: lowest expert
+            float my_score = 0.0f;
+            int my_own = -1;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                if (i == bi) {
+                    my_score = score[i];
+                    my_own = own[i];
+                }
+            }
+            if (lane == w) taken |= 1u << bi;
+            const float win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_score), w));
+            const int win_own = __builtin_amdgcn_readlane(my_own, w);
+            sum = sum + win;                                    // slot order
+            if (lane == s) {
+                slot_score = win;
+                slot_id = (win_own < 0 || win_own >= n_local) ? -1 : win_own;
+            }
+        }
+        if (lane < topk) s_id[j * topk + lane] = slot_id;
+    }
+    // only LDS traffic is outstanding at the barriers (every global store is
+    // issued at the end, so no barrier waits for one)
+    __syncthreads();
+
+    // grouping: thread r < R places route r (waves 0 and 1 cover R <= 128)
+    const int r = tid;
     const bool in = r < R;
     const int id = in ? s_id[r] : -1;
     const bool valid = id >= 0;
-    bool head = valid;
-    int pos = 0;
-    if (valid) {
-        for (int q = 0; q < R; ++q) {
-            const int iq = s_id[q];
-            if (iq < 0) continue;
-            if (iq < id || (iq == id && q < r)) ++pos;
-            if (iq == id && q < r) head = false;
+    int pos = 0, before = 0, n_valid = 0;
+    const int4* v4 = reinterpret_cast<const int4*>(s_id);
+#pragma unroll
+    for (int q4 = 0; q4 < ROUTE_MAX_R / 4; ++q4) {
+        if (q4 * 4 < Rpad) {
+            const int4 v = v4[q4];
+            const int vq[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int q = q4 * 4 + t;
+                const int iq = vq[t];
+                n_valid += iq >= 0 ? 1 : 0;
+                pos += (iq >= 0 && (iq < id || (iq == id && q < r))) ? 1 : 0;
+                before += (iq == id && q < r) ? 1 : 0;
+            }
         }
     }
-    if (in) s_head[r] = head ? 1 : 0;
-    const int n_valid = __syncthreads_count(valid);
-    const int n_heads = __syncthreads_count(head);
+    const bool head = valid && before == 0;
+    if (head) s_headid[r] = id;
+    __syncthreads();
+    int act = 0, n_heads = 0;
+    const int4* h4 = reinterpret_cast<const int4*>(s_headid);
+#pragma unroll
+    for (int q4 = 0; q4 < ROUTE_MAX_R / 4; ++q4) {
+        if (q4 * 4 < Rpad) {
+            const int4 v = h4[q4];
+            n_heads += (v.x >= 0) + (v.y >= 0) + (v.z >= 0) + (v.w >= 0);
+            act += (v.x >= 0 && v.x < id) + (v.y >= 0 && v.y < id) + (v.z >= 0 && v.z < id) +
+                   (v.w >= 0 && v.w < id);
+        }
+    }
+
+    // all global stores
+    if (j < ncols && lane < topk) {
+        const int rr = j * topk + lane;
+        ids[rr] = slot_id;
+        weights[rr] = slot_score / sum;
+    }
+    int32_t* g_expert = grouping + 4;
+    int32_t* g_offset = grouping + 4 + R;
+    int32_t* g_route = grouping + 4 + 2 * R + 1;
     if (head) {
-        int act = 0;
-        for (int q = 0; q < R; ++q) act += (s_head[q] && s_id[q] < id) ? 1 : 0;
         g_expert[act] = id;
         g_offset[act] = pos;
     }
@@ -165,8 +221,19 @@ extern "C" int moe_route_topk(const float* logits, const float* bias, const int3
     if (((uintptr_t)logits | (uintptr_t)bias | (uintptr_t)owner_slot | (uintptr_t)ids |
          (uintptr_t)weights | (uintptr_t)grouping) & 3u)
         return MOEQ8_EALIGN;
-    hipLaunchKernelGGL(k_route_topk, dim3(1), dim3(64 * (unsigned)ncols), 0, (hipStream_t)stream,
-                       logits, bias, owner_slot, (int)ncols, (int)n_expert, (int)n_local_expert,
-                       (int)topk, ids, weights, (int32_t*)grouping);
+    // the grouping needs R = ncols * topk <= 128 threads: at least two waves
+    const dim3 block(64 * (unsigned)std::max<int64_t>(ncols, 2));
+    const int per = (int)((n_expert + 63) / 64);
+    const hipStream_t st = (hipStream_t)stream;
+#define MOEQ8_ROUTE_LAUNCH(P)                                                                    \
+    hipLaunchKernelGGL(k_route_topk<P>, dim3(1), block, 0, st, logits, bias, owner_slot,         \
+                       (int)ncols, (int)n_expert, (int)n_local_expert, (int)topk, ids, weights, \
+                       (int32_t*)grouping)
+    if (per <= 1) MOEQ8_ROUTE_LAUNCH(1);
+    else if (per <= 2) MOEQ8_ROUTE_LAUNCH(2);
+    else if (per <= 4) MOEQ8_ROUTE_LAUNCH(4);
+    else if (per <= 8) MOEQ8_ROUTE_LAUNCH(8);
+    else MOEQ8_ROUTE_LAUNCH(16);
+#undef MOEQ8_ROUTE_LAUNCH
     return check_launch();
 }

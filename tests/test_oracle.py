@@ -448,3 +448,21 @@ def test_mutation_swiglu_symmetric_clamp_caught():
     g = np.array([-20.0])
     bad = np.clip(g, -7, 7) / (1 + np.exp(-np.clip(g, -7, 7)))   # mistake: gate clamped both ways
     assert abs(bad[0] - oracle.swiglu_ds4(g, [1.0])[0]) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# input generator: the C and numpy versions of the counter-based block
+# generator agree (the oracle's inputs never depend on which one ran)
+# ---------------------------------------------------------------------------
+
+def test_synthetic_generator_c_matches_numpy():
+    for key_args, first, n in [((5, 1, 2, 0), 0, 4096), ((0, 0, 0, 0), 5, 1000),
+                               ((65535, 42, 127, 5), 123456, 777)]:
+        key = workloads.stream_key(*key_args)
+        a = workloads.synth_q8_0_blocks(key, first, n)
+        b = workloads.synth_q8_0_blocks(key, first, n, use_c=False)
+        assert a.tobytes() == b.tobytes()
+        q = b["qs"].astype(np.int64)
+        assert np.all(np.abs(q).max(axis=1) == 127)
+        d = b["d"].view(np.uint16)
+        assert np.all((d >= 0x0C00) & (d < 0x1000))

@@ -22,6 +22,10 @@ GPU):
 
 from __future__ import annotations
 
+import ctypes
+import os
+import subprocess
+
 import numpy as np
 
 QK = 32
@@ -140,17 +144,55 @@ def stream_key(seed: int, layer: int, expert: int, matrix: int) -> int:
         return int(_mix(np.array([s], dtype=np.uint64) + GAMMA)[0])
 
 
-def synth_q8_0_blocks(key: int, first_block: int, n_blocks: int) -> np.ndarray:
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_C_SRC = os.path.join(_HERE, "synth_q8_0.c")
+_C_LIB = os.path.join(_HERE, "_synth_q8_0.so")
+_C = None
+
+
+def build_c(force: bool = False) -> str:
+    """Compile the C version of the block generator (gcc, host only)."""
+    if force or not os.path.exists(_C_LIB) or os.path.getmtime(_C_LIB) < os.path.getmtime(_C_SRC):
+        tmp = _C_LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-shared", "-fPIC", _C_SRC, "-o", tmp], check=True)
+        os.replace(tmp, _C_LIB)
+    return _C_LIB
+
+
+def _c_lib():
+    global _C
+    if _C is None:
+        try:
+            so = ctypes.CDLL(build_c())
+            so.synth_q8_0_blocks.restype = None
+            so.synth_q8_0_blocks.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_void_p]
+            _C = so
+        except (OSError, subprocess.CalledProcessError):
+            _C = False
+    return _C
+
+
+def synth_q8_0_blocks(key: int, first_block: int, n_blocks: int, use_c: bool = True) -> np.ndarray:
     """Blocks [first_block, first_block + n_blocks) of the stream ``key`` as a
     Q8_0 structured array (34-byte records)."""
+    c = _c_lib() if use_c else False
+    if c:
+        out = np.empty(n_blocks, dtype=Q8_0_DTYPE)
+        c.synth_q8_0_blocks(key, first_block, n_blocks, out.ctypes.data)
+        return out
     b = np.arange(first_block, first_block + n_blocks, dtype=np.uint64)
     i = b[:, None] * np.uint64(WORDS_PER_BLOCK) + np.arange(WORDS_PER_BLOCK, dtype=np.uint64)[None, :]
     with np.errstate(over="ignore"):
         o = _mix(np.uint64(key) + (i + np.uint64(1)) * GAMMA)          # [n, 17]
-    words = np.ascontiguousarray(o[:, :16])
-    by = words.view(np.uint8).reshape(n_blocks, 16, 8).astype(np.int64)  # little-endian bytes
-    v = np.stack([by[:, :, 0:4].sum(-1), by[:, :, 4:8].sum(-1)], axis=-1).reshape(n_blocks, 32)
-    q = np.clip(((v * 43) >> 7) - 171, -127, 127)
+    words = o[:, :16]
+    # byte sums of each 32-bit half of every output (bytes 0..3 and 4..7, little-endian)
+    lo8 = np.uint64(0x00FF00FF00FF00FF)
+    lo16 = np.uint64(0x0000FFFF0000FFFF)
+    t = (words & lo8) + ((words >> np.uint64(8)) & lo8)
+    u = (t & lo16) + ((t >> np.uint64(16)) & lo16)
+    v = np.stack([u & np.uint64(0xFFFFFFFF), u >> np.uint64(32)], axis=-1).reshape(n_blocks, 32)
+    q = np.clip(((v.astype(np.int64) * 43) >> 7) - 171, -127, 127)
     last = o[:, 16]
     p = ((last >> np.uint64(10)) & np.uint64(31)).astype(np.int64)
     neg = ((last >> np.uint64(15)) & np.uint64(1)).astype(bool)
