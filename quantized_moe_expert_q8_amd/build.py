@@ -46,31 +46,33 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link LIB_PATH.  Always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out_path: str = LIB_PATH, extra_flags=()) -> str:
+    """Compile every HIP source and link ``out_path``.  Always rebuilds.
+    ``extra_flags`` (e.g. -D tuning macros) go to every compile."""
+    build_dir = BUILD_DIR if out_path == LIB_PATH else out_path + ".build"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     workers = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, tuple(extra_flags)), srcs))
+    tmp = out_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources", file=sys.stderr)
-    return LIB_PATH
+        print(f"built {out_path} from {len(srcs)} sources", file=sys.stderr)
+    return out_path
 
 
 if __name__ == "__main__":

@@ -21,7 +21,13 @@
 
 namespace moeq8 {
 
-constexpr int WAVES_PER_WG = 4;
+#ifndef MOEQ8_WAVES_PER_WG
+#define MOEQ8_WAVES_PER_WG 4
+#endif
+#ifndef MOEQ8_U_ROWSETS
+#define MOEQ8_U_ROWSETS 2
+#endif
+constexpr int WAVES_PER_WG = MOEQ8_WAVES_PER_WG;
 constexpr int MAX_COLS = 8;
 
 struct MmvqParams {
@@ -223,7 +229,7 @@ __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, floa
 
 namespace {
 
-constexpr int U_ROWSETS = 2;
+constexpr int U_ROWSETS = MOEQ8_U_ROWSETS;
 
 struct Shape {
     int G;

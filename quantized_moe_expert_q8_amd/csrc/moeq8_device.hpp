@@ -64,18 +64,30 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
 struct WChunk { uint32_t v[W_CHUNK_DWORDS]; };
 struct XChunk { uint32_t v[X_CHUNK_DWORDS]; };
 
+#ifndef MOEQ8_NT_WEIGHTS
+#define MOEQ8_NT_WEIGHTS 0
+#endif
+
 // Raw 68 bytes of a weight chunk (4-byte aligned address).
 __device__ __forceinline__ void load_w_chunk(WChunk& w, const uint8_t* p) {
     const u32x4* q = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+#if MOEQ8_NT_WEIGHTS
+        u32x4 t = __builtin_nontemporal_load(q + i);
+#else
         u32x4 t = q[i];
+#endif
         w.v[4 * i + 0] = t.x;
         w.v[4 * i + 1] = t.y;
         w.v[4 * i + 2] = t.z;
         w.v[4 * i + 3] = t.w;
     }
+#if MOEQ8_NT_WEIGHTS
+    w.v[16] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p + 64));
+#else
     w.v[16] = *reinterpret_cast<const uint32_t*>(p + 64);
+#endif
 }
 
 // Raw 72 bytes of an activation chunk (8-byte aligned address).

@@ -12,9 +12,9 @@
 // untaken key, the wave maximum (DPP within rows of 16, then the four rows),
 // and the lowest lane holding it (ballot): exact (key descending, expert
 // ascending) selection.  Rounds run in slot order, so the weight sum is
-// accumulated there in slot order; lane s keeps slot s.  Then waves 0-1 sort
-// the <= 128 routes by (local expert, route index) for the grouping, reading
-// the route ids with unrolled 16-byte LDS loads.
+// accumulated there in slot order; lane s keeps slot s.  Then the routes are
+// sorted by (local expert, route index) for the grouping: with ballots in one
+// wave when there are at most 64 routes, else from the ids in LDS.
 #include "moeq8_device.hpp"
 #include "moeq8_host.hpp"
 
@@ -133,7 +133,62 @@ __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk(
     // issued at the end, so no barrier waits for one)
     __syncthreads();
 
-    // grouping: thread r < R places route r (waves 0 and 1 cover R <= 128)
+    int32_t* g_expert = grouping + 4;
+    int32_t* g_offset = grouping + 4 + R;
+    int32_t* g_route = grouping + 4 + 2 * R + 1;
+    if (j < ncols && lane < topk) {
+        const int rr = j * topk + lane;
+        ids[rr] = slot_id;
+        weights[rr] = slot_score / sum;
+    }
+
+    if (R <= 64) {
+        // one wave: lane r holds route r.  An 11-bit radix pass of ballots over
+        // the local ids (< 1024) gives each lane the masks of valid routes with
+        // a smaller id (lt) and with the same id (eq).
+        if (j != 0) return;
+        const int r = lane;
+        const int id = r < R ? s_id[r] : -1;
+        const bool valid = id >= 0;
+        const uint64_t vmask = __ballot(valid);
+        uint64_t lt = 0, eq = vmask;
+#pragma unroll
+        for (int b = 10; b >= 0; --b) {
+            const uint64_t ones = __ballot(valid && ((id >> b) & 1));
+            const bool mine = valid && ((id >> b) & 1);
+            if (mine) lt |= eq & ~ones;
+            eq &= mine ? ones : ~ones;
+        }
+        const uint64_t below = (r == 0) ? 0ull : (~0ull >> (64 - r));
+        const int before = __popcll(eq & below);
+        const bool head = valid && before == 0;
+        const uint64_t hmask = __ballot(head);
+        const int n_valid = __popcll(vmask);
+        const int n_heads = __popcll(hmask);
+        const int pos = __popcll(lt) + before;
+        if (head) {
+            const int act = __popcll(lt & hmask);
+            g_expert[act] = id;
+            g_offset[act] = pos;
+        }
+        if (valid) g_route[pos] = r;
+        if (r < R) {
+            if (r >= n_valid) g_route[r] = -1;
+            if (r >= n_heads) g_expert[r] = -1;
+            if (r > n_heads) g_offset[r] = n_valid;
+        }
+        if (r == 0) {
+            grouping[0] = n_heads;
+            grouping[1] = n_valid;
+            grouping[2] = ncols;
+            grouping[3] = topk;
+            g_offset[n_heads] = n_valid;
+            g_offset[R] = n_valid;
+        }
+        return;
+    }
+
+    // R in (64, 128]: thread r < R places route r from the ids in LDS
     const int r = tid;
     const bool in = r < R;
     const int id = in ? s_id[r] : -1;
@@ -169,16 +224,6 @@ __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk(
                    (v.w >= 0 && v.w < id);
         }
     }
-
-    // all global stores
-    if (j < ncols && lane < topk) {
-        const int rr = j * topk + lane;
-        ids[rr] = slot_id;
-        weights[rr] = slot_score / sum;
-    }
-    int32_t* g_expert = grouping + 4;
-    int32_t* g_offset = grouping + 4 + R;
-    int32_t* g_route = grouping + 4 + 2 * R + 1;
     if (head) {
         g_expert[act] = id;
         g_offset[act] = pos;

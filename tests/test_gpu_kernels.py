@@ -249,7 +249,8 @@ def _check_grouping(words, ids_ref):
 
 
 @pytest.mark.parametrize("c,n_exp,topk,local", [(1, 256, 8, 256), (5, 256, 8, 256), (8, 256, 8, 128),
-                                                (8, 64, 6, 64), (3, 1024, 16, 512), (2, 8, 8, 8)])
+                                                (8, 64, 6, 64), (3, 1024, 16, 512), (2, 8, 8, 8),
+                                                (8, 256, 16, 256), (5, 64, 16, 20), (7, 100, 10, 100)])
 def test_route_topk_vs_oracle(c, n_exp, topk, local):
     say(f"route c={c} E={n_exp} k={topk} local={local}")
     logits = workloads.router_logits(c + n_exp, c, n_exp)
