@@ -104,6 +104,37 @@ def layer_inputs(torch, workloads, seed, layers, cols, hidden, n_expert):
     return xs, lgs, bs
 
 
+def capture(torch, fn):
+    """Capture fn (already run once eagerly) as a graph on a side stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, fn, reps):
+    """Mean ms of one replay of a graph of fn."""
+    fn()
+    torch.cuda.synchronize()
+    g = capture(torch, fn)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 # ---------------------------------------------------------------------------
 # algorithmic bytes
 # ---------------------------------------------------------------------------
@@ -202,7 +233,8 @@ def main():
     bank = Bank(moeq8, torch, L, n_local, hidden, inter, seed, cfg["shared_inter"])
     xs, lgs, bs = layer_inputs(torch, workloads, seed, L, cols, hidden, n_exp)
     owner = torch.from_numpy(workloads.owner_slots(n_exp, n_local)).cuda()
-    ws = ml.Workspace(cols, hidden, inter, topk, share_rows, "cuda")
+    side = torch.cuda.Stream()
+    wss = [ml.Workspace(cols, hidden, inter, topk, share_rows, "cuda", side_stream=side) for _ in range(L)]
     torch.cuda.synchronize()
     resident = sum(t.numel() for t in (bank.gate, bank.up, bank.down, bank.sgate, bank.sup, bank.sdown))
     log(f"setup {time.perf_counter() - t0:.1f}s, resident weights {resident / 1e9:.2f} GB")
@@ -210,16 +242,17 @@ def main():
     experts = [bank.experts(ml, l) for l in range(L)]
     shared = [bank.shared(ml, l, share_rows) for l in range(L)]
 
-    def step(hook=None):
+    def step():
         for l in range(L):
-            ml.forward(xs[l], lgs[l], bs[l], owner, n_local, experts[l], shared[l], ws, hook=hook)
+            ml.forward(xs[l], lgs[l], bs[l], owner, n_local, experts[l], shared[l], wss[l])
 
+    # eager warm-up, then capture the step as one graph
+    step()
+    torch.cuda.synchronize()
     # routing statistics of every layer (measurement input: active experts)
     n_active, n_valid = [], []
     for l in range(L):
-        moeq8.moe_route_topk(lgs[l], topk, bias=bs[l], owner_slot=owner, n_local_expert=n_local,
-                             ids=ws.ids, weights=ws.weights, grouping=ws.grouping)
-        words = ws.grouping.cpu().numpy().view(np.int32)
+        words = wss[l].grouping.cpu().numpy().view(np.int32)
         n_active.append(int(words[0]))
         n_valid.append(int(words[1]))
     step_bytes = sum(layer_bytes(n_active[l], n_valid[l], cols, hidden, inter, topk, share_rows)
@@ -229,25 +262,11 @@ def main():
     log(f"active local experts per layer: mean {np.mean(n_active):.1f} (min {min(n_active)}, "
         f"max {max(n_active)}); step bytes {step_bytes / 1e9:.3f} GB (weights {weight_bytes / 1e9:.3f} GB)")
 
-    # eager warm-up, then capture the step as one graph
-    step()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        step()
-    torch.cuda.synchronize()
-
+    g = capture(torch, step)
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
@@ -260,47 +279,40 @@ def main():
     log(f"graph: {ms_per_step:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
         f"{value:.1f} GB/s, {L / ms_per_step * 1e3:.0f} layers/s")
 
-    # eager step time (launch overhead included) and per-kernel event timing
-    events = {}
-    cur = torch.cuda.current_stream()
-
-    def hook(name, phase):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(cur)
-        events.setdefault(name, []).append((phase, e))
-
-    step()
-    torch.cuda.synchronize()
+    # eager step (host launch overhead included), for reference
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
     reps = max(3, args.steps // 5)
+    e0.record()
     for _ in range(reps):
         step()
     e1.record()
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / reps
-    kern_reps = 3
-    for _ in range(kern_reps):
-        step(hook)
-    torch.cuda.synchronize()
 
-    def mean_ms(name):
-        lst = events[name]
-        d = [lst[i][1].elapsed_time(lst[i + 1][1]) for i in range(0, len(lst), 2)]
-        return float(np.mean(d)), d
+    # the dominant kernel: a graph of its 43 launches on this step's inputs,
+    # timed with HIP events on the stream it runs on
+    def gate_up_only():
+        for l in range(L):
+            w = wss[l]
+            moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, w.xq,
+                                   w.grouping, n=inter, k=hidden, n_local_expert=n_local,
+                                   ncols=cols, topk=topk, out=w.h)
 
-    gu_ms, gu_all = mean_ms("grouped_gate_up")
-    gu_bytes = [gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter) for l in range(L)] * kern_reps
-    gu_gbps = float(np.sum(gu_bytes) / (np.sum(gu_all) * 1e-3) / 1e9)
-    dn_ms, dn_all = mean_ms("grouped_down")
-    dn_bytes = [down_launch_bytes(n_active[l], n_valid[l], hidden, inter) for l in range(L)] * kern_reps
-    dn_gbps = float(np.sum(dn_bytes) / (np.sum(dn_all) * 1e-3) / 1e9)
-    per_kernel = {}
-    for name in events:
-        m, _ = mean_ms(name)
-        per_kernel[name] = round(m * 1e3, 2)
-    log(f"eager {eager_ms:.3f} ms/step; per-launch mean us: {per_kernel}")
-    log(f"grouped gate/up {gu_gbps:.1f} GB/s, grouped down {dn_gbps:.1f} GB/s")
+    def down_only():
+        for l in range(L):
+            w = wss[l]
+            moeq8.moe_grouped_mmvq(moeq8.DOWN, experts[l].down, None, w.hq, w.grouping, n=hidden,
+                                   k=inter, n_local_expert=n_local, ncols=cols, topk=topk, out=w.y)
+
+    gu_us = time_graph(torch, gate_up_only, args.steps) / L * 1e3
+    dn_us = time_graph(torch, down_only, args.steps) / L * 1e3
+    gu_bytes = float(np.mean([gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter)
+                              for l in range(L)]))
+    dn_bytes = float(np.mean([down_launch_bytes(n_active[l], n_valid[l], hidden, inter) for l in range(L)]))
+    gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
+    dn_gbps = dn_bytes / (dn_us * 1e-6) / 1e9
+    log(f"eager {eager_ms:.3f} ms/step; grouped gate/up {gu_us:.2f} us/launch {gu_gbps:.1f} GB/s; "
+        f"grouped down {dn_us:.2f} us/launch {dn_gbps:.1f} GB/s")
 
     result = {
         "metric": "Q8_0 MoE MMVQ effective HBM GB/s (% of peak) + MoE layers/s at 1-8 cols",
@@ -324,17 +336,16 @@ def main():
         "step_bytes": step_bytes,
         "weight_bytes": weight_bytes,
         "active_experts_mean": round(float(np.mean(n_active)), 2),
-        "per_launch_us": per_kernel,
         "roofline": {"bound": "hbm", "kernel": "k_mmvq grouped gate/up + SwiGLU",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "mean_launch_us": round(gu_ms * 1e3, 2),
-                     "bytes_per_launch": int(np.mean(gu_bytes))},
-        "grouped_down_gbps": round(dn_gbps, 1),
+                     "mean_launch_us": round(gu_us, 2), "bytes_per_launch": int(gu_bytes)},
+        "grouped_down": {"mean_launch_us": round(dn_us, 2), "gbps": round(dn_gbps, 1),
+                         "bytes_per_launch": int(dn_bytes)},
     }
 
     # release the big bank before the sweep
-    del g, bank, experts, shared
+    del g, bank, experts, shared, wss
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 

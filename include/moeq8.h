@@ -171,12 +171,49 @@ int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_
  * bit-identical to mmvq_q8_0 (DOWN) or mmvq_q8_0_glu_pair's h (GATE_UP) on that
  * expert and that route's activation row.
  * ------------------------------------------------------------------------- */
-enum moeq8_stage { MOEQ8_GATE_UP_SWIGLU = 0, MOEQ8_DOWN = 1 };
+enum moeq8_stage { MOEQ8_GATE_UP_SWIGLU = 0, MOEQ8_DOWN = 1, MOEQ8_DOWN_F32_ACT = 2 };
 int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
                      int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
                      int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
                      const void* grouping, int64_t ncols, int32_t topk, float* out,
                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a6 / a8 fused with their neighbours: the grouped launch above, plus
+ *   - stage MOEQ8_DOWN_F32_ACT: act is fp32 h rows [ncols*topk][act_row_stride
+ *     elements] (first k of each row read) and each workgroup quantises the rows
+ *     of its routes to q8_1 in LDS with the block rule of q8_1_quantize_rows (the
+ *     bytes, hence the products, equal q8_1_quantize_rows then MOEQ8_DOWN);
+ *   - an optional dense part (s_a != NULL), run as extra work items of the same
+ *     launch: rows [0, s_n) of the matrix s_a (and s_b for the gate/up stage)
+ *     against all ncols columns, a column-range slice starting at block
+ *     s_k_block_offset of rows s_row_stride_bytes apart (the shared expert's share
+ *     of the pages' expert-parallel split); s_k is the slice length in values and
+ *     must equal k.  q8_1 stages: s_act = q8_1 rows [ncols][k/32] of the dense
+ *     part, or NULL for act rows 0..ncols-1 (the gate/up stage's shared x);
+ *     s_out = SwiGLU-DS4 (gate/up) or the product (down), [ncols][s_n].  Down with
+ *     fp32 activations: s_act = fp32 rows [ncols][s_act_row_stride].
+ *     Each s_out element is bit-identical to mmvq_q8_0_glu_pair / mmvq_q8_0 on
+ *     that slice.  A dense part whose s_k differs from k, or whose slice spans a
+ *     different number of 16-chunk rounds, is MOEQ8_EUNSUPPORTED (call it apart).
+ * act_row_stride is ignored for the q8_1 stages.
+ * ------------------------------------------------------------------------- */
+int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,
+                        int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                        int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                        int64_t act_row_stride, const void* grouping, int64_t ncols, int32_t topk,
+                        float* out, const void* s_a, const void* s_b, int64_t s_row_stride_bytes,
+                        int64_t s_n, int64_t s_k, int64_t s_k_block_offset, const void* s_act,
+                        int64_t s_act_row_stride, float* s_out, void* stream);
+
+/* a1 + a4 + a5 in one launch (the layer prologue): q8_1 quantisation of the
+ * ncols rows of x [ncols][x_row_stride] into xq [ncols][k/32], and
+ * moe_route_topk on the logits.  Outputs are bit-identical to calling
+ * q8_1_quantize_rows and moe_route_topk. */
+int moe_route_topk_quantize(const float* x, int64_t x_row_stride, int64_t k, void* xq,
+                            const float* logits, const float* bias, const int32_t* owner_slot,
+                            int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
+                            int32_t* ids, float* weights, void* grouping, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a9: weighted masked combine.

@@ -9,6 +9,7 @@ from . import ops  # noqa: F401
 from .ops import (  # noqa: F401
     GATE_UP_SWIGLU,
     DOWN,
+    DOWN_F32_ACT,
     Q8_0_BLOCK_BYTES,
     Q8_1_BLOCK_BYTES,
     q8_1_quantize_rows,
@@ -19,6 +20,8 @@ from .ops import (  # noqa: F401
     moe_grouping_bytes,
     moe_route_topk,
     moe_grouped_mmvq,
+    moe_grouped_mmvq_ex,
+    moe_route_topk_quantize,
     moe_combine,
     synth_q8_0_fill,
 )

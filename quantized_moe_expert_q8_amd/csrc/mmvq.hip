@@ -1,10 +1,16 @@
 // Q8_0 x q8_1 matrix-vector products (MMVQ) for gfx950: the single product, the
-// gate/up pair with the SwiGLU-DS4 epilogue, and the grouped per-expert launch.
+// gate/up pair with the SwiGLU-DS4 epilogue, and the grouped per-expert launch
+// (optionally with a dense product over all columns, the shared expert's
+// share, as extra work items of the same launch, and optionally quantising
+// fp32 activation rows to q8_1 inside the launch).
 //
-// One kernel body serves all three (lucebox PR #826, the commit on MMVQ fusion
-// following mul_mat's kernel choice: a fused path must run the arithmetic the
-// unfused path runs).  The reduction order is fixed in moeq8_device.hpp; this
-// file only decides which physical lanes compute which logical chunks.
+// One kernel body serves all of them (lucebox PR #826, the commit on MMVQ
+// fusion following mul_mat's kernel choice: a fused path must run the
+// arithmetic the unfused path runs).  The reduction order is fixed in
+// moeq8_device.hpp; this file only decides which physical lanes compute which
+// logical chunks, and the in-launch quantisation calls the same block
+// quantiser as q8_1_quantize_rows, so fused and unfused launches agree bit for
+// bit.
 //
 // Physical layout.  A wave is 4 lane groups of 16 lanes.  Physical lane l of a
 // group always holds logical lane l.  G lane groups cooperate on one row: group
@@ -28,35 +34,46 @@ namespace moeq8 {
 #define MOEQ8_U_ROWSETS 2
 #endif
 constexpr int WAVES_PER_WG = MOEQ8_WAVES_PER_WG;
+constexpr int U_ROWSETS = MOEQ8_U_ROWSETS;
 constexpr int MAX_COLS = 8;
 
-struct MmvqParams {
-    const uint8_t* w0;          // matrix 0 (single, gate, or grouped w_a) of expert 0 / the matrix
+// One matrix (or gate/up pair) and the column range of its rows that is read.
+struct MatDesc {
+    const uint8_t* w0;          // matrix 0 (single, gate, down)
     const uint8_t* w1;          // matrix 1 (up) or null
-    int64_t w_row_stride;       // bytes
-    int64_t expert_stride;      // bytes (grouped)
-    int64_t n_local;            // grouped: valid expert range
+    int64_t row_stride;         // bytes
     int64_t n;                  // rows
     int32_t nchunks;            // chunks in the slice (k / 64)
     int32_t chunk0;             // absolute index of the slice's first chunk (k_block_offset / 2)
     int32_t r0;                 // first absolute round touched (chunk0 / 16)
-    int32_t nsteps;             // G == 1: rounds to walk
-    const uint8_t* act;         // q8_1 activation rows
-    int64_t act_row_bytes;      // (k / 32) * 36
-    int32_t ncols;              // dense: columns
-    int32_t topk;               // grouped
-    int32_t act_route_div;      // grouped: activation row of route r is r / act_route_div
-    int32_t rows_per_wg;
-    int32_t wg_per_expert;      // grouped
-    const int32_t* grouping;    // grouped
-    float* out0;                // dense: y (single) or h (pair); grouped: out rows per route
-    float* out_g;               // dense pair: optional raw gate products
-    float* out_u;               // dense pair: optional raw up products
+    int32_t wg;                 // row blocks
 };
 
-__device__ __forceinline__ int dpp_row_mirror_i(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);
-}
+struct MmvqParams {
+    MatDesc m;                  // the matrix, or expert 0 of the routed experts
+    int64_t expert_stride;      // grouped: bytes between experts
+    int64_t n_local;            // grouped: valid expert range
+    int32_t nsteps;             // G == 1: rounds to walk (same for m and s)
+    int32_t ncols;
+    int32_t topk;
+    int32_t act_route_div;      // grouped: activation row of route r is r / act_route_div
+    int32_t rows_per_wg;
+    int32_t max_active;         // grouped: bound on the device-side active count
+    const uint8_t* act;         // q8_1 activation rows
+    int64_t act_row_bytes;      // (k / 32) * 36
+    const float* act_f32;       // fp32 activation rows, quantised in the launch
+    int64_t act_f32_stride;     // elements
+    const int32_t* grouping;    // grouped
+    float* out0;                // dense: y (single) or h (pair); grouped: rows per route
+    float* out_g;               // dense pair: optional raw gate products
+    float* out_u;               // dense pair: optional raw up products
+    // dense extra items after the routed ones (grouped launches only)
+    MatDesc s;
+    const uint8_t* s_act_q;     // q8_1 rows [ncols][k/32] of the dense part (q8_1 mode)
+    const float* s_act_f32;     // fp32 rows [ncols][k] of the dense part (fp32 mode)
+    int64_t s_act_f32_stride;
+    float* s_out;               // [ncols][s.n]
+};
 
 // Pairwise tree over the 16 logical lanes of a group using DPP lane moves:
 // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  The
@@ -71,7 +88,7 @@ __device__ __forceinline__ float tree16(float v) {
     iv = __float_as_int(v);
     v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x141, 0xf, 0xf, false));
     iv = __float_as_int(v);
-    v = v + __int_as_float(dpp_row_mirror_i(iv));
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x140, 0xf, 0xf, false));
     return v;
 }
 
@@ -89,8 +106,8 @@ __device__ __forceinline__ float chain_groups(float v, int lane) {
     }
 }
 
-template <int G, int NMAT, int U, bool GROUPED>
-__global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) {
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32>
+__device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
     constexpr int RPW = 4 / G;                         // rows per row set
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -99,31 +116,72 @@ __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) 
     const int gsub = grp % G;                          // round slot within the row
     const int rslot = grp / G;                         // row slot within the row set
 
-    const uint8_t* w0 = p.w0;
-    const uint8_t* w1 = p.w1;
-    int64_t row_block = blockIdx.x;
+    // ---- decode the work item (uniform over the workgroup) ---------------
+    // (fields are copied, never addressed: taking the address of the kernel
+    // argument would move it to scratch memory)
+    const uint8_t* w0 = p.m.w0;
+    const uint8_t* w1 = p.m.w1;
+    int64_t row_stride = p.m.row_stride;
+    int64_t n_rows = p.m.n;
+    int32_t nchunks = p.m.nchunks;
+    int32_t chunk0 = p.m.chunk0;
+    int32_t r0 = p.m.r0;
+    int64_t row_block = item;
     int ncols = p.ncols;
     int route_begin = 0;
+    int R = 0;
+    bool routed = false;
     if constexpr (GROUPED) {
-        const int a = (int)(blockIdx.x / (uint32_t)p.wg_per_expert);
-        row_block = blockIdx.x - (int64_t)a * p.wg_per_expert;
-        const int n_active = p.grouping[0];
-        if (a >= n_active) return;
-        // a grouping written for another column count or top-k is not used
-        if (p.grouping[2] != p.ncols || p.grouping[3] != p.topk) return;
-        const int R = p.grouping[2] * p.grouping[3];
-        const int e = p.grouping[4 + a];
-        if (e < 0 || e >= p.n_local) return;
-        route_begin = p.grouping[4 + R + a];
-        ncols = p.grouping[4 + R + a + 1] - route_begin;
-        if (route_begin < 0 || ncols < 0 || route_begin + ncols > R) return;
-        w0 += (int64_t)e * p.expert_stride;
-        if (NMAT == 2) w1 += (int64_t)e * p.expert_stride;
+        // the dense part's items come first: its blocks carry every column, so
+        // dispatching them early keeps them out of the launch's tail
+        const int64_t n_dense = p.s.wg;
+        if (item >= n_dense) {
+            item -= n_dense;
+            const int a = (int)(item / p.m.wg);
+            row_block = item - (int64_t)a * p.m.wg;
+            const int n_active = p.grouping[0];
+            if (a >= n_active) return;
+            // a grouping written for another column count or top-k is not used
+            if (p.grouping[2] != p.ncols || p.grouping[3] != p.topk) return;
+            R = p.grouping[2] * p.grouping[3];
+            const int e = p.grouping[4 + a];
+            if (e < 0 || e >= p.n_local) return;
+            route_begin = p.grouping[4 + R + a];
+            ncols = p.grouping[4 + R + a + 1] - route_begin;
+            if (route_begin < 0 || ncols < 0 || route_begin + ncols > R) return;
+            w0 += (int64_t)e * p.expert_stride;
+            if (NMAT == 2) w1 += (int64_t)e * p.expert_stride;
+            routed = true;
+        } else {
+            row_block = item;
+            w0 = p.s.w0;
+            w1 = p.s.w1;
+            row_stride = p.s.row_stride;
+            n_rows = p.s.n;
+            nchunks = p.s.nchunks;
+            chunk0 = p.s.chunk0;
+            r0 = p.s.r0;
+        }
     }
     const int64_t row_base = row_block * p.rows_per_wg + (int64_t)wave * (U * RPW) + rslot;
 
     for (int c0 = 0; c0 < ncols; c0 += MAX_COLS) {
         const int nc = min(ncols - c0, MAX_COLS);
+        // output row and activation row of each column of this pass
+        int orow[MAX_COLS];
+        int arow[MAX_COLS];
+#pragma unroll
+        for (int c = 0; c < MAX_COLS; ++c) {
+            orow[c] = c0 + c;
+            arow[c] = c0 + c;
+            if (GROUPED && routed) {
+                int r = (c < nc) ? p.grouping[4 + 2 * R + 1 + route_begin + c0 + c] : 0;
+                if (r < 0 || r >= R) r = -1;
+                orow[c] = r;
+                arow[c] = r < 0 ? 0 : r / p.act_route_div;
+            }
+        }
+
         float acc[MAX_COLS][U][NMAT];
 #pragma unroll
         for (int c = 0; c < MAX_COLS; ++c)
@@ -132,46 +190,71 @@ __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) 
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) acc[c][u][m] = 0.0f;
 
-        const uint8_t* act_row[MAX_COLS];
-#pragma unroll
-        for (int c = 0; c < MAX_COLS; ++c) {
-            int r = c0 + c;
-            if constexpr (GROUPED) {
-                const int R = p.grouping[2] * p.grouping[3];
-                r = (c < nc) ? p.grouping[4 + 2 * R + 1 + route_begin + c0 + c] : 0;
-                r = (r >= 0 && r < R) ? r / p.act_route_div : 0;
-            }
-            act_row[c] = p.act + (int64_t)r * p.act_row_bytes;
-        }
-
-        for (int s = 0; s < p.nsteps; ++s) {
-            const int round = p.r0 + (G == 1 ? s : gsub);
-            const int cabs = round * LANES_PER_ROW + l;            // absolute chunk
-            const int crel = cabs - p.chunk0;                      // chunk within the slice
-            const bool cvalid = (crel >= 0) && (crel < p.nchunks);
-
-            WChunk wc[U][NMAT];
+        WChunk wc[U][NMAT];
+        int crel = 0;
+        bool cvalid = false;
+        auto load_weights = [&](int s) {
+            const int round = r0 + (G == 1 ? s : gsub);
+            crel = round * LANES_PER_ROW + l - chunk0;        // chunk within the slice
+            cvalid = (crel >= 0) && (crel < nchunks);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t row = row_base + (int64_t)u * RPW;
-                const bool ok = cvalid && row < p.n;
+                const bool ok = cvalid && row < n_rows;
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
                     if (ok) {
-                        const uint8_t* base = (m == 0 ? w0 : w1) + row * p.w_row_stride +
-                                              (int64_t)crel * W_CHUNK_BYTES;
-                        load_w_chunk(wc[u][m], base);
+                        load_w_chunk(wc[u][m], (m == 0 ? w0 : w1) + row * row_stride +
+                                                   (int64_t)crel * W_CHUNK_BYTES);
                     } else {
                         zero_w_chunk(wc[u][m]);
                     }
                 }
             }
+        };
+
+        load_weights(0);
+
+        const uint8_t* act_base = (GROUPED && !routed) ? p.s_act_q : p.act;
+        if constexpr (ACT_F32) {
+            // quantise this item's activation rows into LDS while the weight
+            // loads are in flight (same block quantiser as q8_1_quantize_rows)
+            __syncthreads();                               // a previous pass may still read LDS
+            const int nb = nchunks * 2;
+            const float* src = routed ? p.act_f32 : p.s_act_f32;
+            const int64_t stride = routed ? p.act_f32_stride : p.s_act_f32_stride;
+            for (int t = threadIdx.x; t < nc * nb; t += blockDim.x) {
+                const int c = t / nb;
+                const int b = t - c * nb;
+                int ar = c0 + c;
+                if (routed) {
+                    const int r = p.grouping[4 + 2 * R + 1 + route_begin + c0 + c];
+                    ar = (r < 0 || r >= R) ? 0 : r / p.act_route_div;
+                }
+                quantize_block<true>(src + (int64_t)ar * stride + (int64_t)b * QK,
+                                     lds_act + (int64_t)c * p.act_row_bytes + (int64_t)b * Q81_BYTES);
+            }
+            __syncthreads();
+            act_base = lds_act;
+        }
+
+        for (int s = 0; s < p.nsteps; ++s) {
+            if (s > 0) load_weights(s);
 #pragma unroll
             for (int c = 0; c < MAX_COLS; ++c) {
                 if (c < nc) {
                     XChunk xc;
-                    if (cvalid) load_x_chunk(xc, act_row[c] + (int64_t)crel * X_CHUNK_BYTES);
-                    else zero_x_chunk(xc);
+                    if (cvalid) {
+                        if constexpr (ACT_F32) {
+                            load_x_chunk_lds(xc, act_base + (int64_t)c * p.act_row_bytes +
+                                                     (int64_t)crel * X_CHUNK_BYTES);
+                        } else {
+                            load_x_chunk(xc, act_base + (int64_t)arow[c] * p.act_row_bytes +
+                                                 (int64_t)crel * X_CHUNK_BYTES);
+                        }
+                    } else {
+                        zero_x_chunk(xc);
+                    }
 #pragma unroll
                     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -181,6 +264,7 @@ __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) 
         }
 
         // reduce: chain the groups of a row in round order, then the 16-lane tree
+        float* out = (GROUPED && !routed) ? p.s_out : p.out0;
 #pragma unroll
         for (int c = 0; c < MAX_COLS; ++c) {
             if (c < nc) {
@@ -191,22 +275,14 @@ __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) 
                     for (int m = 0; m < NMAT; ++m) v[m] = tree16(chain_groups<G>(acc[c][u][m], lane));
                     const int64_t row = row_base + (int64_t)u * RPW;
                     // one writer lane per (column, row set) among the 16
-                    const bool writer = (gsub == 0) && (l == ((c * U + u) & 15)) && row < p.n;
-                    if (writer) {
-                        int64_t orow;
-                        if constexpr (GROUPED) {
-                            const int R = p.grouping[2] * p.grouping[3];
-                            orow = p.grouping[4 + 2 * R + 1 + route_begin + c0 + c];
-                            if (orow < 0 || orow >= R) continue;
-                        } else {
-                            orow = c0 + c;
-                        }
-                        float* o = p.out0 + orow * p.n + row;
+                    const bool writer = (gsub == 0) && (l == ((c * U + u) & 15)) && row < n_rows;
+                    if (writer && orow[c] >= 0) {
+                        float* o = out + (int64_t)orow[c] * n_rows + row;
                         if constexpr (NMAT == 2) {
                             *o = swiglu_ds4_f32(v[0], v[1]);
                             if constexpr (!GROUPED) {
-                                if (p.out_g) p.out_g[orow * p.n + row] = v[0];
-                                if (p.out_u) p.out_u[orow * p.n + row] = v[1];
+                                if (p.out_g) p.out_g[(int64_t)orow[c] * n_rows + row] = v[0];
+                                if (p.out_u) p.out_u[(int64_t)orow[c] * n_rows + row] = v[1];
                             }
                         } else {
                             *o = v[0];
@@ -216,6 +292,14 @@ __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) 
             }
         }
     }
+}
+
+// One work item = one row block: of one active expert (grouped), of the dense
+// extra matrix (grouped launches with a shared part), or of the one matrix.
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32>
+__global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_act[];
+    mmvq_item<G, NMAT, U, GROUPED, ACT_F32>(p, blockIdx.x, lds_act);
 }
 
 __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, float* h) {
@@ -229,43 +313,47 @@ __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, floa
 
 namespace {
 
-constexpr int U_ROWSETS = MOEQ8_U_ROWSETS;
-
 struct Shape {
     int G;
     int nsteps;
-    int r0;
 };
 
 Shape pick_shape(int64_t chunk0, int64_t nchunks) {
     const int64_t r0 = chunk0 / LANES_PER_ROW;
     const int64_t r1 = (chunk0 + nchunks - 1) / LANES_PER_ROW;
     const int64_t rounds = r1 - r0 + 1;
-    Shape s;
-    s.r0 = (int)r0;
-    if (rounds == 1) { s.G = 1; s.nsteps = 1; }
-    else if (rounds == 2) { s.G = 2; s.nsteps = 1; }
-    else if (rounds <= 4) { s.G = 4; s.nsteps = 1; }
-    else { s.G = 1; s.nsteps = (int)rounds; }
-    return s;
+    if (rounds == 1) return {1, 1};
+    if (rounds == 2) return {2, 1};
+    if (rounds <= 4) return {4, 1};
+    return {1, (int)rounds};
 }
 
-template <int NMAT, bool GROUPED>
-int launch_mmvq(MmvqParams& p, const Shape& s, int64_t n_items_outer, hipStream_t stream) {
-    const int rpw = 4 / s.G;
-    p.rows_per_wg = WAVES_PER_WG * U_ROWSETS * rpw;
-    p.r0 = s.r0;
+MatDesc make_desc(const void* w0, const void* w1, int64_t row_stride, int64_t n, int64_t k,
+                  int64_t k_block_offset, int rows_per_wg) {
+    MatDesc d = {};
+    d.w0 = (const uint8_t*)w0;
+    d.w1 = (const uint8_t*)w1;
+    d.row_stride = row_stride;
+    d.n = n;
+    d.nchunks = (int32_t)(k / 64);
+    d.chunk0 = (int32_t)(k_block_offset / 2);
+    d.r0 = d.chunk0 / LANES_PER_ROW;
+    d.wg = (int32_t)((n + rows_per_wg - 1) / rows_per_wg);
+    return d;
+}
+
+int rows_per_wg_for(const Shape& s) { return WAVES_PER_WG * U_ROWSETS * (4 / s.G); }
+
+template <int NMAT, bool GROUPED, bool ACT_F32>
+int launch_mmvq(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
     p.nsteps = s.nsteps;
-    const int64_t wg_rows = (p.n + p.rows_per_wg - 1) / p.rows_per_wg;
-    p.wg_per_expert = (int32_t)wg_rows;
-    const int64_t grid = GROUPED ? wg_rows * n_items_outer : wg_rows;
     if (grid <= 0) return MOEQ8_OK;
     if (grid > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
     const dim3 block(64 * WAVES_PER_WG);
     switch (s.G) {
-        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U_ROWSETS, GROUPED>), dim3((uint32_t)grid), block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U_ROWSETS, GROUPED>), dim3((uint32_t)grid), block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U_ROWSETS, GROUPED>), dim3((uint32_t)grid), block, 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U_ROWSETS, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U_ROWSETS, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U_ROWSETS, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
     }
     return check_launch();
 }
@@ -278,8 +366,26 @@ int validate_matrix(const void* w, int64_t w_row_stride_bytes, int64_t n, int64_
     if (k_block_offset % 2 != 0) return MOEQ8_EALIGN;
     if (((uintptr_t)w & 3u) != 0 || (w_row_stride_bytes & 3) != 0) return MOEQ8_EALIGN;
     if (n > 1 && w_row_stride_bytes < (k / QK) * Q80_BYTES) return MOEQ8_EINVAL;
-    if (k / 64 > (int64_t)1 << 24 || k_block_offset > ((int64_t)1 << 26)) return MOEQ8_EUNSUPPORTED;
+    if (k / 64 > ((int64_t)1 << 24) || k_block_offset > ((int64_t)1 << 26)) return MOEQ8_EUNSUPPORTED;
+    if (n > ((int64_t)1 << 31)) return MOEQ8_EUNSUPPORTED;
     return MOEQ8_OK;
+}
+
+int dense_call(int nmat, const void* w0, const void* w1, int64_t stride, int64_t n, int64_t k,
+               int64_t kb, const void* xq, int64_t ncols, float* out, float* g, float* u,
+               void* stream) {
+    MmvqParams p = {};
+    const Shape s = pick_shape(kb / 2, k / 64);
+    p.rows_per_wg = rows_per_wg_for(s);
+    p.m = make_desc(w0, w1, stride, n, k, kb, p.rows_per_wg);
+    p.act = (const uint8_t*)xq;
+    p.act_row_bytes = (k / QK) * Q81_BYTES;
+    p.ncols = (int32_t)ncols;
+    p.out0 = out;
+    p.out_g = g;
+    p.out_u = u;
+    if (nmat == 2) return launch_mmvq<2, false, false>(p, s, p.m.wg, 0, (hipStream_t)stream);
+    return launch_mmvq<1, false, false>(p, s, p.m.wg, 0, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -295,17 +401,8 @@ extern "C" int mmvq_q8_0(const void* w, int64_t w_row_stride_bytes, int64_t n, i
     if (!xq || !y || ncols < 1 || ncols > MAX_COLS) return MOEQ8_EINVAL;
     if (((uintptr_t)xq & 3u) || ((uintptr_t)y & 3u)) return MOEQ8_EALIGN;
     if (n == 0) return MOEQ8_OK;
-    MmvqParams p = {};
-    p.w0 = (const uint8_t*)w;
-    p.w_row_stride = w_row_stride_bytes;
-    p.n = n;
-    p.nchunks = (int32_t)(k / 64);
-    p.chunk0 = (int32_t)(k_block_offset / 2);
-    p.act = (const uint8_t*)xq;
-    p.act_row_bytes = (k / QK) * Q81_BYTES;
-    p.ncols = (int32_t)ncols;
-    p.out0 = y;
-    return launch_mmvq<1, false>(p, pick_shape(p.chunk0, p.nchunks), 1, (hipStream_t)stream);
+    return dense_call(1, w, nullptr, w_row_stride_bytes, n, k, k_block_offset, xq, ncols, y, nullptr,
+                      nullptr, stream);
 }
 
 extern "C" int mmvq_q8_0_glu_pair(const void* w_gate, const void* w_up, int64_t w_row_stride_bytes,
@@ -321,20 +418,8 @@ extern "C" int mmvq_q8_0_glu_pair(const void* w_gate, const void* w_up, int64_t 
         ((uintptr_t)u_out & 3u))
         return MOEQ8_EALIGN;
     if (n == 0) return MOEQ8_OK;
-    MmvqParams p = {};
-    p.w0 = (const uint8_t*)w_gate;
-    p.w1 = (const uint8_t*)w_up;
-    p.w_row_stride = w_row_stride_bytes;
-    p.n = n;
-    p.nchunks = (int32_t)(k / 64);
-    p.chunk0 = (int32_t)(k_block_offset / 2);
-    p.act = (const uint8_t*)xq;
-    p.act_row_bytes = (k / QK) * Q81_BYTES;
-    p.ncols = (int32_t)ncols;
-    p.out0 = h_out;
-    p.out_g = g_out;
-    p.out_u = u_out;
-    return launch_mmvq<2, false>(p, pick_shape(p.chunk0, p.nchunks), 1, (hipStream_t)stream);
+    return dense_call(2, w_gate, w_up, w_row_stride_bytes, n, k, k_block_offset, xq, ncols, h_out,
+                      g_out, u_out, stream);
 }
 
 extern "C" int swiglu_ds4(const float* g, const float* u, int64_t count, float* h, void* stream) {
@@ -347,47 +432,100 @@ extern "C" int swiglu_ds4(const float* g, const float* u, int64_t count, float* 
     return check_launch();
 }
 
+extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,
+                                   int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                                   int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                                   int64_t act_row_stride, const void* grouping, int64_t ncols,
+                                   int32_t topk, float* out, const void* s_a, const void* s_b,
+                                   int64_t s_row_stride_bytes, int64_t s_n, int64_t s_k,
+                                   int64_t s_k_block_offset, const void* s_act,
+                                   int64_t s_act_row_stride, float* s_out, void* stream) {
+    if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_DOWN_F32_ACT)
+        return MOEQ8_EINVAL;
+    const bool pair = stage == MOEQ8_GATE_UP_SWIGLU;
+    const bool f32 = stage == MOEQ8_DOWN_F32_ACT;
+    int st = validate_matrix(w_a, w_row_stride_bytes, n, k, 0);
+    if (st) return st;
+    if (pair) {
+        st = validate_matrix(w_b, w_row_stride_bytes, n, k, 0);
+        if (st) return st;
+    }
+    if (!act || !grouping || !out) return MOEQ8_EINVAL;
+    if (ncols < 1 || ncols > MAX_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK) return MOEQ8_EINVAL;
+    if (n_local_expert < 1) return MOEQ8_EINVAL;
+    if (expert_stride_bytes < 0 || (expert_stride_bytes & 3)) return MOEQ8_EALIGN;
+    if (n_local_expert > 1 && expert_stride_bytes < n * w_row_stride_bytes) return MOEQ8_EINVAL;
+    if (((uintptr_t)act & 3u) || ((uintptr_t)grouping & 3u) || ((uintptr_t)out & 3u))
+        return MOEQ8_EALIGN;
+    if (f32 && act_row_stride < k) return MOEQ8_EINVAL;
+    const bool has_s = s_a != nullptr;
+    if (has_s) {
+        // the shared part runs in the same kernel instance: same k and slice shape
+        if (s_k != k) return MOEQ8_EUNSUPPORTED;
+        st = validate_matrix(s_a, s_row_stride_bytes, s_n, k, s_k_block_offset);
+        if (st) return st;
+        if (pair) {
+            st = validate_matrix(s_b, s_row_stride_bytes, s_n, k, s_k_block_offset);
+            if (st) return st;
+        }
+        if (!s_out) return MOEQ8_EINVAL;
+        if ((uintptr_t)s_out & 3u) return MOEQ8_EALIGN;
+        if (f32 && (!s_act || s_act_row_stride < k)) return MOEQ8_EINVAL;
+        if ((uintptr_t)s_act & 3u) return MOEQ8_EALIGN;
+        const Shape a = pick_shape(0, k / 64), b = pick_shape(s_k_block_offset / 2, k / 64);
+        if (a.G != b.G || a.nsteps != b.nsteps) return MOEQ8_EUNSUPPORTED;
+    }
+    if (n == 0 && (!has_s || s_n == 0)) return MOEQ8_OK;
+
+    MmvqParams p = {};
+    const Shape s = pick_shape(0, k / 64);
+    p.rows_per_wg = rows_per_wg_for(s);
+    p.m = make_desc(w_a, w_b, w_row_stride_bytes, n, k, 0, p.rows_per_wg);
+    p.expert_stride = expert_stride_bytes;
+    p.n_local = n_local_expert;
+    p.ncols = (int32_t)ncols;
+    p.topk = topk;
+    p.act_route_div = pair ? topk : 1;
+    p.act = (const uint8_t*)act;
+    p.act_row_bytes = (k / QK) * Q81_BYTES;
+    if (f32) {
+        p.act_f32 = (const float*)act;
+        p.act_f32_stride = act_row_stride;
+    }
+    p.grouping = (const int32_t*)grouping;
+    p.out0 = out;
+    // at most min(ncols * topk, n_local) experts are active; blocks of groups
+    // past the device-side count exit at once
+    const int64_t max_active = std::min<int64_t>(ncols * topk, n_local_expert);
+    p.max_active = (int32_t)max_active;
+    int64_t grid = max_active * p.m.wg;
+    if (has_s) {
+        p.s = make_desc(s_a, s_b, s_row_stride_bytes, s_n, k, s_k_block_offset, p.rows_per_wg);
+        if (f32) {
+            p.s_act_f32 = (const float*)s_act;
+            p.s_act_f32_stride = s_act_row_stride;
+        } else {
+            // q8_1 rows of the dense part: s_act, or act rows 0..ncols-1
+            p.s_act_q = s_act ? (const uint8_t*)s_act : (const uint8_t*)act;
+        }
+        p.s_out = s_out;
+        grid += p.s.wg;
+    }
+    const size_t lds = f32 ? (size_t)MAX_COLS * (size_t)p.act_row_bytes : 0;
+    if (lds > 64 * 1024) return MOEQ8_EUNSUPPORTED;
+    const hipStream_t hs = (hipStream_t)stream;
+    if (pair) return launch_mmvq<2, true, false>(p, s, grid, 0, hs);
+    if (f32) return launch_mmvq<1, true, true>(p, s, grid, lds, hs);
+    return launch_mmvq<1, true, false>(p, s, grid, 0, hs);
+}
+
 extern "C" int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
                                 int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
                                 int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
                                 const void* grouping, int64_t ncols, int32_t topk, float* out,
                                 void* stream) {
     if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN) return MOEQ8_EINVAL;
-    int st = validate_matrix(w_a, w_row_stride_bytes, n, k, 0);
-    if (st) return st;
-    if (stage == MOEQ8_GATE_UP_SWIGLU) {
-        st = validate_matrix(w_b, w_row_stride_bytes, n, k, 0);
-        if (st) return st;
-    }
-    if (!act_q || !grouping || !out) return MOEQ8_EINVAL;
-    if (ncols < 1 || ncols > MAX_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK) return MOEQ8_EINVAL;
-    if (n_local_expert < 1 || expert_stride_bytes < 0 || (expert_stride_bytes & 3)) {
-        return n_local_expert < 1 ? MOEQ8_EINVAL : MOEQ8_EALIGN;
-    }
-    if (n_local_expert > 1 && expert_stride_bytes < n * w_row_stride_bytes) return MOEQ8_EINVAL;
-    if (((uintptr_t)act_q & 3u) || ((uintptr_t)grouping & 3u) || ((uintptr_t)out & 3u))
-        return MOEQ8_EALIGN;
-    if (n == 0) return MOEQ8_OK;
-    MmvqParams p = {};
-    p.w0 = (const uint8_t*)w_a;
-    p.w1 = (const uint8_t*)w_b;
-    p.w_row_stride = w_row_stride_bytes;
-    p.expert_stride = expert_stride_bytes;
-    p.n_local = n_local_expert;
-    p.n = n;
-    p.nchunks = (int32_t)(k / 64);
-    p.chunk0 = 0;
-    p.act = (const uint8_t*)act_q;
-    p.act_row_bytes = (k / QK) * Q81_BYTES;
-    p.topk = topk;
-    p.ncols = (int32_t)ncols;
-    p.act_route_div = (stage == MOEQ8_GATE_UP_SWIGLU) ? topk : 1;
-    p.grouping = (const int32_t*)grouping;
-    p.out0 = out;
-    // at most min(ncols * topk, n_local) experts are active; blocks of groups
-    // past the device-side count exit at once
-    const int64_t max_active = std::min<int64_t>(ncols * topk, n_local_expert);
-    const Shape s = pick_shape(0, p.nchunks);
-    if (stage == MOEQ8_GATE_UP_SWIGLU) return launch_mmvq<2, true>(p, s, max_active, (hipStream_t)stream);
-    return launch_mmvq<1, true>(p, s, max_active, (hipStream_t)stream);
+    return moe_grouped_mmvq_ex(stage, w_a, w_b, expert_stride_bytes, w_row_stride_bytes,
+                               n_local_expert, n, k, act_q, 0, grouping, ncols, topk, out, nullptr,
+                               nullptr, 0, 0, 0, 0, nullptr, 0, nullptr, stream);
 }

@@ -106,6 +106,17 @@ __device__ __forceinline__ void load_x_chunk(XChunk& x, const uint8_t* p) {
     x.v[17] = t.y;
 }
 
+// Activation chunk from LDS (72 bytes at an 8-byte aligned offset).
+__device__ __forceinline__ void load_x_chunk_lds(XChunk& x, const uint8_t* p) {
+    const uint2* q = reinterpret_cast<const uint2*>(p);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        const uint2 t = q[i];
+        x.v[2 * i] = t.x;
+        x.v[2 * i + 1] = t.y;
+    }
+}
+
 __device__ __forceinline__ void zero_w_chunk(WChunk& w) {
 #pragma unroll
     for (int i = 0; i < W_CHUNK_DWORDS; ++i) w.v[i] = 0u;
@@ -137,6 +148,53 @@ __device__ __forceinline__ float chunk_dot(const WChunk& w, const XChunk& x) {
     const float p0 = (dw0 * dx0) * (float)s0;
     const float p1 = (dw1 * dx1) * (float)s1;
     return p0 + p1;
+}
+
+// Quantise one 32-value block (the block rule of both formats): fp32
+// d = amax / 127 (IEEE division), q = roundf(x / d) on the fp32 quotient
+// (halves away from zero), d stored as fp16 (nearest even); q8_1 adds
+// s = fp16(d * sum(q)) with the fp32 product rounded first.  An all-zero block
+// gives all-zero bytes.  dst: 36 bytes (q8_1, 4-byte aligned) or 34 bytes
+// (Q8_0, 2-byte aligned), global or LDS.
+template <bool Q81>
+__device__ __forceinline__ void quantize_block(const float* __restrict__ src, uint8_t* dst) {
+    float v[QK];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK; ++i) {
+        v[i] = src[i];
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const float d = amax / 127.0f;
+    uint32_t packed[QK / 4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < QK / 4; ++i) packed[i] = 0u;
+    if (d != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < QK; ++i) {
+            const int q = (int)roundf(v[i] / d);
+            sum += q;
+            packed[i / 4] |= ((uint32_t)q & 0xffu) << (8 * (i % 4));
+        }
+    }
+    const uint32_t dbits = float_to_half_bits(d);
+    if constexpr (Q81) {
+        uint32_t* o = reinterpret_cast<uint32_t*>(dst);
+        // s = fp16 of the fp32 product (two roundings, as defined)
+        const uint32_t sbits = float_to_half_bits(materialize_f32(d * (float)sum));
+        o[0] = dbits | (sbits << 16);
+#pragma unroll
+        for (int i = 0; i < QK / 4; ++i) o[1 + i] = packed[i];
+    } else {
+        uint16_t* o = reinterpret_cast<uint16_t*>(dst);
+        o[0] = (uint16_t)dbits;
+#pragma unroll
+        for (int i = 0; i < QK / 4; ++i) {
+            o[1 + 2 * i] = (uint16_t)(packed[i] & 0xffffu);
+            o[2 + 2 * i] = (uint16_t)(packed[i] >> 16);
+        }
+    }
 }
 
 // SwiGLU-DS4 in fp32: silu(min(g, 7)) * clamp(u, -7, 7).

@@ -18,44 +18,7 @@ __global__ void k_quantize_rows(const float* __restrict__ x, int64_t n_rows, int
     if (gid >= n_rows * nb) return;
     const int64_t r = gid / nb;
     const int64_t b = gid - r * nb;
-    const float* src = x + r * row_stride + b * QK;
-    float v[QK];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < QK; ++i) {
-        v[i] = src[i];
-        amax = fmaxf(amax, fabsf(v[i]));
-    }
-    const float d = amax / 127.0f;
-    uint32_t packed[QK / 4];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < QK / 4; ++i) packed[i] = 0u;
-    if (d != 0.0f) {
-#pragma unroll
-        for (int i = 0; i < QK; ++i) {
-            const int q = (int)roundf(v[i] / d);
-            sum += q;
-            packed[i / 4] |= ((uint32_t)q & 0xffu) << (8 * (i % 4));
-        }
-    }
-    const uint32_t dbits = float_to_half_bits(d);
-    if constexpr (Q81) {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(out + gid * Q81_BYTES);
-        // s = fp16 of the fp32 product (two roundings, as defined)
-        const uint32_t sbits = float_to_half_bits(materialize_f32(d * (float)sum));
-        dst[0] = dbits | (sbits << 16);
-#pragma unroll
-        for (int i = 0; i < QK / 4; ++i) dst[1 + i] = packed[i];
-    } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(out + gid * Q80_BYTES);
-        dst[0] = (uint16_t)dbits;
-#pragma unroll
-        for (int i = 0; i < QK / 4; ++i) {
-            dst[1 + 2 * i] = (uint16_t)(packed[i] & 0xffffu);
-            dst[2 + 2 * i] = (uint16_t)(packed[i] >> 16);
-        }
-    }
+    quantize_block<Q81>(x + r * row_stride + b * QK, out + gid * (Q81 ? Q81_BYTES : Q80_BYTES));
 }
 
 namespace {

@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 template <int PER>
-__global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk(
+__device__ __forceinline__ void route_body(
     const float* __restrict__ logits, const float* __restrict__ bias,
     const int32_t* __restrict__ owner, int ncols, int n_expert, int n_local, int topk,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ grouping) {
@@ -244,6 +244,34 @@ __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk(
     }
 }
 
+template <int PER>
+__global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk(
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    const int32_t* __restrict__ owner, int ncols, int n_expert, int n_local, int topk,
+    int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ grouping) {
+    route_body<PER>(logits, bias, owner, ncols, n_expert, n_local, topk, ids, weights, grouping);
+}
+
+// The layer prologue: block 0 routes; the other blocks quantise the FFN input
+// to q8_1 (both read only the layer's inputs, so one launch runs them side by
+// side).  Bytes and routing are those of q8_1_quantize_rows and moe_route_topk.
+template <int PER>
+__global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_quantize(
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    const int32_t* __restrict__ owner, int ncols, int n_expert, int n_local, int topk,
+    int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ grouping,
+    const float* __restrict__ x, int64_t x_stride, int64_t nb, uint8_t* __restrict__ xq) {
+    if (blockIdx.x == 0) {
+        route_body<PER>(logits, bias, owner, ncols, n_expert, n_local, topk, ids, weights, grouping);
+        return;
+    }
+    const int64_t gid = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)ncols * nb) return;
+    const int64_t r = gid / nb;
+    const int64_t b = gid - r * nb;
+    quantize_block<true>(x + r * x_stride + b * QK, xq + gid * Q81_BYTES);
+}
+
 }  // namespace moeq8
 
 using namespace moeq8;
@@ -255,23 +283,34 @@ extern "C" size_t moe_grouping_bytes(int64_t ncols, int32_t topk) {
     return (bytes + 255) & ~(size_t)255;
 }
 
-extern "C" int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_slot,
-                              int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
-                              int32_t* ids, float* weights, void* grouping, void* stream) {
+namespace {
+int validate_route(const float* logits, const float* bias, const int32_t* owner_slot, int64_t ncols,
+                   int64_t n_expert, int64_t n_local_expert, int32_t topk, const int32_t* ids,
+                   const float* weights, const void* grouping) {
     if (!logits || !ids || !weights || !grouping) return MOEQ8_EINVAL;
     if (ncols < 1 || ncols > ROUTE_MAX_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return MOEQ8_EINVAL;
     if (n_expert < 1 || topk > n_expert || n_local_expert < 1) return MOEQ8_EINVAL;
     if (!owner_slot && n_local_expert != n_expert) return MOEQ8_EINVAL;
-    if (n_expert > ROUTE_MAX_EXPERT) return MOEQ8_EUNSUPPORTED;
+    if (n_expert > ROUTE_MAX_EXPERT || n_local_expert > ROUTE_MAX_EXPERT) return MOEQ8_EUNSUPPORTED;
     if (((uintptr_t)logits | (uintptr_t)bias | (uintptr_t)owner_slot | (uintptr_t)ids |
          (uintptr_t)weights | (uintptr_t)grouping) & 3u)
         return MOEQ8_EALIGN;
+    return MOEQ8_OK;
+}
+}  // namespace
+
+extern "C" int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_slot,
+                              int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
+                              int32_t* ids, float* weights, void* grouping, void* stream) {
+    const int st = validate_route(logits, bias, owner_slot, ncols, n_expert, n_local_expert, topk,
+                                  ids, weights, grouping);
+    if (st) return st;
     // the grouping needs R = ncols * topk <= 128 threads: at least two waves
     const dim3 block(64 * (unsigned)std::max<int64_t>(ncols, 2));
     const int per = (int)((n_expert + 63) / 64);
-    const hipStream_t st = (hipStream_t)stream;
+    const hipStream_t hs = (hipStream_t)stream;
 #define MOEQ8_ROUTE_LAUNCH(P)                                                                    \
-    hipLaunchKernelGGL(k_route_topk<P>, dim3(1), block, 0, st, logits, bias, owner_slot,         \
+    hipLaunchKernelGGL(k_route_topk<P>, dim3(1), block, 0, hs, logits, bias, owner_slot,         \
                        (int)ncols, (int)n_expert, (int)n_local_expert, (int)topk, ids, weights, \
                        (int32_t*)grouping)
     if (per <= 1) MOEQ8_ROUTE_LAUNCH(1);
@@ -280,5 +319,35 @@ extern "C" int moe_route_topk(const float* logits, const float* bias, const int3
     else if (per <= 8) MOEQ8_ROUTE_LAUNCH(8);
     else MOEQ8_ROUTE_LAUNCH(16);
 #undef MOEQ8_ROUTE_LAUNCH
+    return check_launch();
+}
+
+extern "C" int moe_route_topk_quantize(const float* x, int64_t x_row_stride, int64_t k, void* xq,
+                                       const float* logits, const float* bias,
+                                       const int32_t* owner_slot, int64_t ncols, int64_t n_expert,
+                                       int64_t n_local_expert, int32_t topk, int32_t* ids,
+                                       float* weights, void* grouping, void* stream) {
+    int st = validate_route(logits, bias, owner_slot, ncols, n_expert, n_local_expert, topk, ids,
+                            weights, grouping);
+    if (st) return st;
+    if (!x || !xq || k <= 0 || (k % QK) != 0 || x_row_stride < k) return MOEQ8_EINVAL;
+    if (((uintptr_t)x & 3u) || ((uintptr_t)xq & 3u)) return MOEQ8_EALIGN;
+    const int64_t nb = k / QK;
+    const unsigned threads = 64 * (unsigned)std::max<int64_t>(ncols, 2);
+    const int64_t qblocks = (ncols * nb + threads - 1) / threads;
+    if (qblocks + 1 > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    const dim3 grid((uint32_t)(qblocks + 1)), block(threads);
+    const int per = (int)((n_expert + 63) / 64);
+    const hipStream_t hs = (hipStream_t)stream;
+#define MOEQ8_PRO_LAUNCH(P)                                                                          \
+    hipLaunchKernelGGL(k_route_quantize<P>, grid, block, 0, hs, logits, bias, owner_slot, (int)ncols, \
+                       (int)n_expert, (int)n_local_expert, (int)topk, ids, weights,                   \
+                       (int32_t*)grouping, x, x_row_stride, nb, (uint8_t*)xq)
+    if (per <= 1) MOEQ8_PRO_LAUNCH(1);
+    else if (per <= 2) MOEQ8_PRO_LAUNCH(2);
+    else if (per <= 4) MOEQ8_PRO_LAUNCH(4);
+    else if (per <= 8) MOEQ8_PRO_LAUNCH(8);
+    else MOEQ8_PRO_LAUNCH(16);
+#undef MOEQ8_PRO_LAUNCH
     return check_launch();
 }

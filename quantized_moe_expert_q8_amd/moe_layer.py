@@ -12,7 +12,9 @@ shared-expert commits) on ``ncols`` columns:
     out = sum over unmasked slots of w * y
 
 Buffers live in a workspace allocated once, so ``forward`` allocates nothing
-and can be captured in a HIP graph.  No arithmetic happens here.
+and can be captured in a HIP graph.  The shared expert depends only on xq, so
+it runs on a second stream forked after the quantisation and joined at the
+end of the layer (a parallel branch of the graph).  No arithmetic happens here.
 """
 
 from __future__ import annotations
@@ -61,7 +63,8 @@ class SharedExpertShare:
 
 
 class Workspace:
-    def __init__(self, ncols: int, hidden: int, inter: int, topk: int, shared_rows: int, device):
+    def __init__(self, ncols: int, hidden: int, inter: int, topk: int, shared_rows: int, device,
+                 side_stream=None):
         dev = torch.device(device)
         u8, f32 = torch.uint8, torch.float32
         self.ncols, self.topk = ncols, topk
@@ -69,24 +72,50 @@ class Workspace:
         self.ids = torch.empty((ncols, topk), dtype=torch.int32, device=dev)
         self.weights = torch.empty((ncols, topk), dtype=f32, device=dev)
         self.grouping = torch.empty(ops.moe_grouping_bytes(ncols, topk), dtype=u8, device=dev)
-        self.h = torch.zeros((ncols, topk, inter), dtype=f32, device=dev)
-        self.hq = torch.empty((ncols * topk, inter // QK * Q81), dtype=u8, device=dev)
+        # h and the shared hs live in one buffer when they have the same width
+        # (rows [0, ncols*topk) routed, then ncols shared rows), so one launch
+        # quantises both
+        R = ncols * topk
+        self.joint = bool(shared_rows) and shared_rows == inter
+        rows = R + (ncols if self.joint else 0)
+        self.hh = torch.zeros((rows, inter), dtype=f32, device=dev)
+        self.hhq = torch.zeros((rows, inter // QK * Q81), dtype=u8, device=dev)
+        self.h = self.hh[:R].view(ncols, topk, inter)
+        self.hq = self.hhq[:R]
         self.y = torch.zeros((ncols, topk, hidden), dtype=f32, device=dev)
         self.out = torch.empty((ncols, hidden), dtype=f32, device=dev)
         if shared_rows:
-            self.hs = torch.empty((ncols, shared_rows), dtype=f32, device=dev)
-            self.hsq = torch.empty((ncols, shared_rows // QK * Q81), dtype=u8, device=dev)
+            if self.joint:
+                self.hs = self.hh[R:]
+                self.hsq = self.hhq[R:]
+            else:
+                self.hs = torch.empty((ncols, shared_rows), dtype=f32, device=dev)
+                self.hsq = torch.empty((ncols, shared_rows // QK * Q81), dtype=u8, device=dev)
             self.ys = torch.empty((ncols, hidden), dtype=f32, device=dev)
+            # the shared expert needs only xq, so it runs on a second stream
+            # beside the routed path (a parallel branch when captured)
+            self.side = side_stream if side_stream is not None else torch.cuda.Stream(device=dev)
+            self.fork = torch.cuda.Event()
+            self.join = torch.cuda.Event()
         else:
             self.hs = self.hsq = self.ys = None
+            self.side = None
 
 
 def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
             owner_slot: torch.Tensor | None, n_local_expert: int, experts: RoutedExperts,
-            shared: SharedExpertShare | None, ws: Workspace, hook=None):
-    """Enqueue one layer on the current stream.  ``hook(name, phase)`` (optional)
-    is called before ('begin') and after ('end') each launch, e.g. to record
-    events.  Returns (out, ys) device tensors of the workspace."""
+            shared: SharedExpertShare | None, ws: Workspace, hook=None, fused: bool = True):
+    """Enqueue one layer on the current stream; returns (out, ys) device tensors
+    of the workspace.
+
+    fused=True (five launches): prologue (router + q8_1 of x), grouped gate/up
+    with the shared gate/up rows as extra items, one q8_1 launch over h and hs,
+    grouped down with the shared down slice as extra items, combine.
+    fused=False: the nine separate calls, the shared expert on a second stream.
+    Both give the same bits.  ``hook(name, phase)`` (unfused only) is called
+    around each launch."""
+    if fused:
+        return _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws)
     c, topk = ws.ncols, ws.topk
     hidden, inter = experts.hidden, experts.inter
     mark = hook or (lambda name, phase: None)
@@ -94,20 +123,25 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     mark("q8_1_x", "begin")
     ops.q8_1_quantize_rows(x, out=ws.xq)
     mark("q8_1_x", "end")
+    main = torch.cuda.current_stream(x.device)
     if shared is not None:
-        rb = (hidden // QK) * Q80
-        mark("shared_pair", "begin")
-        ops.mmvq_q8_0_glu_pair(shared.gate, shared.up, ws.xq, shared.rows, hidden, ncols=c,
-                               w_offset_bytes=shared.gate_offset(), w_row_stride_bytes=rb,
-                               out=ws.hs)
-        mark("shared_pair", "end")
-        ops.q8_1_quantize_rows(ws.hs, out=ws.hsq)
-        kb = shared.down_block_offset()
-        mark("shared_down", "begin")
-        ops.mmvq_q8_0(shared.down, ws.hsq, hidden, shared.rows, ncols=c, k_block_offset=kb,
-                      w_offset_bytes=kb * Q80, w_row_stride_bytes=(shared.inter_full // QK) * Q80,
-                      out=ws.ys)
-        mark("shared_down", "end")
+        ws.fork.record(main)
+        ws.side.wait_event(ws.fork)
+        with torch.cuda.stream(ws.side):
+            rb = (hidden // QK) * Q80
+            mark("shared_pair", "begin")
+            ops.mmvq_q8_0_glu_pair(shared.gate, shared.up, ws.xq, shared.rows, hidden, ncols=c,
+                                   w_offset_bytes=shared.gate_offset(), w_row_stride_bytes=rb,
+                                   out=ws.hs)
+            mark("shared_pair", "end")
+            ops.q8_1_quantize_rows(ws.hs, out=ws.hsq)
+            kb = shared.down_block_offset()
+            mark("shared_down", "begin")
+            ops.mmvq_q8_0(shared.down, ws.hsq, hidden, shared.rows, ncols=c, k_block_offset=kb,
+                          w_offset_bytes=kb * Q80,
+                          w_row_stride_bytes=(shared.inter_full // QK) * Q80, out=ws.ys)
+            mark("shared_down", "end")
+            ws.join.record(ws.side)
     mark("route", "begin")
     ops.moe_route_topk(logits, topk, bias=bias, owner_slot=owner_slot, n_local_expert=n_local_expert,
                        ids=ws.ids, weights=ws.weights, grouping=ws.grouping)
@@ -127,6 +161,63 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     mark("combine", "begin")
     ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
     mark("combine", "end")
+    if shared is not None:
+        main.wait_event(ws.join)
+    return ws.out, ws.ys
+
+
+def _rounds(chunk0: int, nchunks: int):
+    r0 = chunk0 // 16
+    r1 = (chunk0 + nchunks - 1) // 16
+    n = r1 - r0 + 1
+    return (1, 1) if n == 1 else (2, 1) if n == 2 else (4, 1) if n <= 4 else (1, n)
+
+
+def _same_round_span(k_block_offset: int, k_slice: int, k: int) -> bool:
+    """Whether a column-range slice can share a launch with full rows of length
+    k: same length and the same lane-group layout."""
+    return k_slice == k and _rounds(k_block_offset // 2, k_slice // 64) == _rounds(0, k // 64)
+
+
+def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws):
+    """Prologue, gate/up (+ shared rows), one quantisation of h and hs, down
+    (+ shared slice), combine: five launches on one stream."""
+    c, topk = ws.ncols, ws.topk
+    hidden, inter = experts.hidden, experts.inter
+    ops.moe_route_topk_quantize(x, logits, topk, bias=bias, owner_slot=owner_slot,
+                                n_local_expert=n_local_expert, xq=ws.xq, ids=ws.ids,
+                                weights=ws.weights, grouping=ws.grouping)
+    R = c * topk
+    sh_gu = sh_dn = None
+    if shared is not None:
+        rb = (hidden // QK) * Q80
+        sh_gu = {"a": shared.gate, "b": shared.up, "row_stride": rb, "n": shared.rows,
+                 "k": hidden, "k_block_offset": 0, "offset_bytes": shared.gate_offset(),
+                 "out": ws.hs}
+        kb = shared.down_block_offset()
+        if ws.joint and _same_round_span(kb, shared.rows, inter):
+            sh_dn = {"a": shared.down, "row_stride": (shared.inter_full // QK) * Q80,
+                     "n": hidden, "k": shared.rows, "k_block_offset": kb,
+                     "offset_bytes": kb * Q80, "out": ws.ys, "act": ws.hsq}
+    ops.moe_grouped_mmvq_ex(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping,
+                            n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
+                            out=ws.h, shared=sh_gu)
+    if ws.joint:
+        # h and hs share one buffer: one launch quantises both
+        ops.q8_1_quantize_rows(ws.hh, out=ws.hhq)
+    else:
+        ops.q8_1_quantize_rows(ws.h.view(R, inter), out=ws.hq)
+        if shared is not None:
+            ops.q8_1_quantize_rows(ws.hs, out=ws.hsq)
+    ops.moe_grouped_mmvq_ex(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
+                            n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y,
+                            shared=sh_dn)
+    if shared is not None and sh_dn is None:
+        kb = shared.down_block_offset()
+        ops.mmvq_q8_0(shared.down, ws.hsq, hidden, shared.rows, ncols=c, k_block_offset=kb,
+                      w_offset_bytes=kb * Q80, w_row_stride_bytes=(shared.inter_full // QK) * Q80,
+                      out=ws.ys)
+    ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
     return ws.out, ws.ys
 
 

@@ -20,6 +20,7 @@ Q8_1_BLOCK_BYTES = 36
 MAX_COLS = 8
 GATE_UP_SWIGLU = 0
 DOWN = 1
+DOWN_F32_ACT = 2
 
 
 def _stream(t: torch.Tensor):
@@ -235,6 +236,118 @@ def moe_grouped_mmvq(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, ac
     _need(out, "out", ncols * topk * n * 4)
     call("moe_grouped_mmvq", stage, _ptr(w_a), _ptr(w_b), expert_stride_bytes, w_row_stride_bytes,
          n_local_expert, n, k, _ptr(act_q), _ptr(grouping), ncols, topk, _ptr(out), _stream(w_a))
+    return out
+
+
+def moe_route_topk_quantize(x: torch.Tensor, logits: torch.Tensor, topk: int, *,
+                            bias: torch.Tensor | None = None,
+                            owner_slot: torch.Tensor | None = None,
+                            n_local_expert: int | None = None, xq: torch.Tensor | None = None,
+                            ids: torch.Tensor | None = None, weights: torch.Tensor | None = None,
+                            grouping: torch.Tensor | None = None):
+    """One launch: xq = q8_1(x) and moe_route_topk(logits).  Returns
+    (xq, ids, weights, grouping)."""
+    _cuda(x, "x", torch.float32)
+    _cuda(logits, "logits", torch.float32)
+    ncols, k = x.shape
+    _contig_rows(x, "x", ncols, k)
+    if logits.dim() != 2 or not logits.is_contiguous() or logits.shape[0] != ncols:
+        raise ValueError("logits must be contiguous [ncols, n_expert]")
+    n_expert = logits.shape[1]
+    if n_local_expert is None:
+        n_local_expert = n_expert if owner_slot is None else int(owner_slot.max().item()) + 1
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((ncols, k // QK * Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=dev)
+    if ids is None:
+        ids = torch.empty((ncols, topk), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((ncols, topk), dtype=torch.float32, device=dev)
+    gb = moe_grouping_bytes(ncols, topk)
+    if gb == 0:
+        raise ValueError("ncols or topk out of range")
+    if grouping is None:
+        grouping = torch.empty(gb, dtype=torch.uint8, device=dev)
+    if bias is not None:
+        _cuda(bias, "bias", torch.float32)
+        _need(bias, "bias", n_expert * 4)
+    if owner_slot is not None:
+        _cuda(owner_slot, "owner_slot", torch.int32)
+        _need(owner_slot, "owner_slot", n_expert * 4)
+    _need(xq, "xq", ncols * (k // QK) * Q8_1_BLOCK_BYTES)
+    _need(ids, "ids", ncols * topk * 4)
+    _need(weights, "weights", ncols * topk * 4)
+    _need(grouping, "grouping", gb)
+    call("moe_route_topk_quantize", _ptr(x), x.stride(0), k, _ptr(xq), _ptr(logits), _ptr(bias),
+         _ptr(owner_slot), ncols, n_expert, n_local_expert, topk, _ptr(ids), _ptr(weights),
+         _ptr(grouping), _stream(x))
+    return xq, ids, weights, grouping
+
+
+def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, act: torch.Tensor,
+                        grouping: torch.Tensor, *, n: int, k: int, n_local_expert: int, ncols: int,
+                        topk: int, out: torch.Tensor, expert_stride_bytes: int | None = None,
+                        w_row_stride_bytes: int | None = None, shared: dict | None = None):
+    """Grouped MMVQ with the fused extras (q8_1 of fp32 activations in the launch
+    for DOWN_F32_ACT; a dense shared-expert part as extra work items).
+
+    shared = {"a", "b" (gate/up only), "row_stride", "n", "k" (slice length, must
+              equal k), "k_block_offset", "offset_bytes", "out",
+              "act" (fp32 [ncols, >= k] for DOWN_F32_ACT; q8_1 rows [ncols, k/32*36]
+              for DOWN; absent for the gate/up stage, which reads act)}."""
+    if w_row_stride_bytes is None:
+        w_row_stride_bytes = (k // QK) * Q8_0_BLOCK_BYTES
+    if expert_stride_bytes is None:
+        expert_stride_bytes = n * w_row_stride_bytes
+    extent = (n_local_expert - 1) * expert_stride_bytes + _weight_extent(n, k, w_row_stride_bytes)
+    _cuda(w_a, "w_a", torch.uint8)
+    _need(w_a, "w_a", extent)
+    act_row_stride = 0
+    if stage == GATE_UP_SWIGLU:
+        _cuda(w_b, "w_b", torch.uint8)
+        _need(w_b, "w_b", extent)
+        _act_rows(act, "act", ncols, k)
+    elif stage == DOWN:
+        _act_rows(act, "act", ncols * topk, k)
+    elif stage == DOWN_F32_ACT:
+        _cuda(act, "act", torch.float32)
+        if act.dim() != 2 or act.stride(1) != 1:
+            raise ValueError("fp32 act must be 2-D with unit inner stride")
+        act_row_stride = act.stride(0)
+        _need(act, "act", ((ncols * topk - 1) * act_row_stride + k) * 4)
+    else:
+        raise ValueError("bad stage")
+    _cuda(grouping, "grouping", torch.uint8)
+    _need(grouping, "grouping", moe_grouping_bytes(ncols, topk))
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", ncols * topk * n * 4)
+    sa = sb = sact = sout = None
+    s_stride = s_n = s_k = s_kb = s_off = s_act_stride = 0
+    if shared is not None:
+        s_stride, s_n, s_kb = shared["row_stride"], shared["n"], shared["k_block_offset"]
+        s_k = shared["k"]
+        s_off = shared.get("offset_bytes", 0)
+        sa, sout = shared["a"], shared["out"]
+        _cuda(sa, "shared a", torch.uint8)
+        _need(sa, "shared a", _weight_extent(s_n, s_k, s_stride), s_off)
+        if stage == GATE_UP_SWIGLU:
+            sb = shared["b"]
+            _cuda(sb, "shared b", torch.uint8)
+            _need(sb, "shared b", _weight_extent(s_n, s_k, s_stride), s_off)
+        _cuda(sout, "shared out", torch.float32)
+        _need(sout, "shared out", ncols * s_n * 4)
+        if stage == DOWN_F32_ACT:
+            sact = shared["act"]
+            _cuda(sact, "shared act", torch.float32)
+            s_act_stride = sact.stride(0)
+            _need(sact, "shared act", ((ncols - 1) * s_act_stride + s_k) * 4)
+        elif stage == DOWN:
+            sact = shared["act"]
+            _act_rows(sact, "shared act", ncols, s_k)
+    call("moe_grouped_mmvq_ex", stage, _ptr(w_a), _ptr(w_b), expert_stride_bytes,
+         w_row_stride_bytes, n_local_expert, n, k, _ptr(act), act_row_stride, _ptr(grouping),
+         ncols, topk, _ptr(out), _ptr(sa, s_off), _ptr(sb, s_off), s_stride, s_n, s_k, s_kb, _ptr(sact),
+         s_act_stride, _ptr(sout), _stream(w_a))
     return out
 
 

@@ -452,3 +452,97 @@ def test_synth_fill_matches_host_generator():
     for i in range(n_mats):
         ref = workloads.synth_q8_0_blocks(workloads.stream_key(5, 7 + i // 2, 3 + i % 2, 2), 0, bpm)
         assert got[i * bpm * 34:(i + 1) * bpm * 34].tobytes() == ref.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# fused launches == the separate calls, bit for bit
+# ---------------------------------------------------------------------------
+
+def test_route_topk_quantize_equals_separate():
+    c, n_exp, hidden, topk = 8, 256, 4096, 8
+    x = to_dev(workloads.activations(31, c, hidden))
+    lg = to_dev(workloads.router_logits(31, c, n_exp))
+    b = to_dev(workloads.router_bias(31, n_exp))
+    own = to_dev(workloads.owner_slots(n_exp, 128))
+    xq, ids, w, g = moeq8.moe_route_topk_quantize(x, lg, topk, bias=b, owner_slot=own, n_local_expert=128)
+    ids2, w2, g2 = moeq8.moe_route_topk(lg, topk, bias=b, owner_slot=own, n_local_expert=128)
+    assert torch.equal(xq, moeq8.q8_1_quantize_rows(x))
+    nw = 4 + 3 * c * topk + 1                               # defined words of the grouping
+    assert torch.equal(ids, ids2) and bits_equal(w, w2)
+    assert torch.equal(g.view(torch.int32)[:nw], g2.view(torch.int32)[:nw])
+
+
+@pytest.mark.parametrize("c,n_exp,hidden,inter,share_rows,half", [(8, 32, 1024, 256, 512, 0),
+                                                                  (8, 32, 1024, 256, 512, 1),
+                                                                  (5, 16, 2048, 1024, 1024, 1),
+                                                                  (1, 8, 4096, 1024, 1024, 0)])
+def test_fused_layer_equals_unfused(c, n_exp, hidden, inter, share_rows, half):
+    """The four-launch layer (prologue, gate/up + shared rows, down with
+    in-launch q8_1 of h and hs + shared slice, combine) against the nine
+    separate calls, every output bit for bit."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    say(f"fused layer c={c} E={n_exp} H={hidden} I={inter} share={share_rows} half={half}")
+    topk = 8 if n_exp >= 8 else n_exp
+    _, (wgd, wud, wdd) = _tiny_layer(c + n_exp, n_exp, hidden, inter)
+    inter_full = 2 * share_rows
+    rb_h, rb_f = hidden // 32 * 34, inter_full // 32 * 34
+    sg = to_dev(workloads.synth_q8_0_matrix(3, 0, 0, 3, inter_full, hidden)).reshape(inter_full, rb_h)
+    su = to_dev(workloads.synth_q8_0_matrix(3, 0, 0, 4, inter_full, hidden)).reshape(inter_full, rb_h)
+    sd = to_dev(workloads.synth_q8_0_matrix(3, 0, 0, 5, hidden, inter_full)).reshape(hidden, rb_f)
+    shared = ml.SharedExpertShare(sg, su, sd, hidden, inter_full, half * share_rows, share_rows)
+    experts = ml.RoutedExperts(wgd, wud, wdd, n_exp, hidden, inter)
+    x = to_dev(workloads.activations(c, c, hidden))
+    lg = to_dev(workloads.router_logits(c, c, n_exp))
+    b = to_dev(workloads.router_bias(c, n_exp))
+    own = to_dev(workloads.owner_slots(n_exp, n_exp // 2))
+    wa = ml.Workspace(c, hidden, inter, topk, share_rows, DEV)
+    wb = ml.Workspace(c, hidden, inter, topk, share_rows, DEV)
+    ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wa, fused=False)
+    ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wb, fused=True)
+    torch.cuda.synchronize()
+    nw = 4 + 3 * c * topk + 1
+    assert torch.equal(wa.xq, wb.xq) and torch.equal(wa.ids, wb.ids)
+    assert torch.equal(wa.grouping.view(torch.int32)[:nw], wb.grouping.view(torch.int32)[:nw])
+    assert bits_equal(wa.weights, wb.weights)
+    assert bits_equal(wa.hs, wb.hs) and bits_equal(wa.ys, wb.ys)
+    valid = (host(wa.ids) >= 0)
+    ha, hb = host(wa.h), host(wb.h)
+    ya, yb = host(wa.y), host(wb.y)
+    for j in range(c):
+        for s in range(topk):
+            if valid[j, s]:
+                assert np.array_equal(ha[j, s].view(np.int32), hb[j, s].view(np.int32))
+                assert np.array_equal(ya[j, s].view(np.int32), yb[j, s].view(np.int32))
+    assert bits_equal(wa.out, wb.out)
+
+
+@pytest.mark.parametrize("c,n_exp,hidden,inter", [(8, 32, 1024, 1024), (3, 16, 2048, 512)])
+def test_down_f32_act_equals_quantize_then_down(c, n_exp, hidden, inter):
+    """MOEQ8_DOWN_F32_ACT (q8_1 of h inside the launch, shared slice as extra
+    items) against q8_1_quantize_rows + MOEQ8_DOWN, bit for bit."""
+    topk = 8
+    _, (_, _, wdd) = _tiny_layer(5 + c, n_exp, hidden, inter)
+    lg = to_dev(workloads.router_logits(c + 1, c, n_exp))
+    ids, w, grouping = moeq8.moe_route_topk(lg, topk)
+    h = to_dev(workloads.normal_f32(77, (c * topk, inter), 2.0))
+    hs = to_dev(workloads.normal_f32(78, (c, inter), 2.0))
+    inter_full = 2 * inter
+    sd = to_dev(workloads.synth_q8_0_matrix(3, 0, 0, 5, hidden, inter_full)).reshape(hidden, -1)
+    rbf = inter_full // 32 * 34
+    for half in (0, 1):
+        kb = half * inter // 32
+        y1 = torch.full((c, topk, hidden), float("nan"), device=DEV)
+        ys1 = torch.empty((c, hidden), device=DEV)
+        moeq8.moe_grouped_mmvq_ex(moeq8.DOWN_F32_ACT, wdd, None, h, grouping, n=hidden, k=inter,
+                                  n_local_expert=n_exp, ncols=c, topk=topk, out=y1,
+                                  shared={"a": sd, "row_stride": rbf, "n": hidden, "k": inter,
+                                          "k_block_offset": kb, "offset_bytes": kb * 34,
+                                          "out": ys1, "act": hs})
+        hq, hsq = moeq8.q8_1_quantize_rows(h), moeq8.q8_1_quantize_rows(hs)
+        y2 = torch.full((c, topk, hidden), float("nan"), device=DEV)
+        moeq8.moe_grouped_mmvq(moeq8.DOWN, wdd, None, hq, grouping, n=hidden, k=inter,
+                               n_local_expert=n_exp, ncols=c, topk=topk, out=y2)
+        ys2 = moeq8.mmvq_q8_0(sd, hsq, hidden, inter, k_block_offset=kb, w_offset_bytes=kb * 34,
+                              w_row_stride_bytes=rbf)
+        assert np.array_equal(host(y1).view(np.int32), host(y2).view(np.int32))
+        assert bits_equal(ys1, ys2)
