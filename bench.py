@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the oracle sample")
+    ap.add_argument("--pmc-copy", action="store_true",
+                    help="after the step, copy 512 MiB device to device once: the known-size "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -104,6 +107,28 @@ def layer_inputs(torch, workloads, seed, layers, cols, hidden, n_expert):
     return xs, lgs, bs
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_grouped_gate_up_ep_share_l43_e128_c8.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs, or None when the kernel's sources changed since
+    the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def capture(torch, fn):
     """Capture fn (already run once eagerly) as a graph on a side stream."""
     s = torch.cuda.Stream()
@@ -147,6 +172,18 @@ def gate_up_launch_bytes(n_active, n_valid, cols, hidden, inter):
 
 def down_launch_bytes(n_active, n_valid, hidden, inter):
     return n_active * hidden * (inter // 32 * 34) + n_valid * (inter // 32 * 36) + n_valid * hidden * 4
+
+
+def shared_gate_up_bytes(cols, hidden, rows):
+    """The shared expert's rows inside the gate/up launch: both matrices' rows,
+    hs written (xq is already counted once for the launch)."""
+    return 2 * rows * (hidden // 32 * 34) + cols * rows * 4
+
+
+def shared_down_bytes(cols, hidden, rows):
+    """The shared down slice inside the down launch: the slice of every row,
+    the hsq rows read, ys written."""
+    return hidden * (rows // 32 * 34) + cols * (rows // 32 * 36) + cols * hidden * 4
 
 
 def layer_bytes(n_active, n_valid, cols, hidden, inter, topk, shared_rows):
@@ -291,24 +328,36 @@ def main():
 
     # the dominant kernel: a graph of its 43 launches on this step's inputs,
     # timed with HIP events on the stream it runs on
+    # the launches exactly as the step issues them (routed experts plus the
+    # shared expert's rows as extra work items)
+    rb_h = hidden // 32 * 34
+
     def gate_up_only():
         for l in range(L):
-            w = wss[l]
-            moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, w.xq,
-                                   w.grouping, n=inter, k=hidden, n_local_expert=n_local,
-                                   ncols=cols, topk=topk, out=w.h)
+            w, sh = wss[l], shared[l]
+            moeq8.moe_grouped_mmvq_ex(
+                moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, w.xq, w.grouping, n=inter,
+                k=hidden, n_local_expert=n_local, ncols=cols, topk=topk, out=w.h,
+                shared={"a": sh.gate, "b": sh.up, "row_stride": rb_h, "n": sh.rows, "k": hidden,
+                        "k_block_offset": 0, "offset_bytes": sh.gate_offset(), "out": w.hs})
 
     def down_only():
         for l in range(L):
-            w = wss[l]
-            moeq8.moe_grouped_mmvq(moeq8.DOWN, experts[l].down, None, w.hq, w.grouping, n=hidden,
-                                   k=inter, n_local_expert=n_local, ncols=cols, topk=topk, out=w.y)
+            w, sh = wss[l], shared[l]
+            kb = sh.down_block_offset()
+            moeq8.moe_grouped_mmvq_ex(
+                moeq8.DOWN, experts[l].down, None, w.hq, w.grouping, n=hidden, k=inter,
+                n_local_expert=n_local, ncols=cols, topk=topk, out=w.y,
+                shared={"a": sh.down, "row_stride": sh.inter_full // 32 * 34, "n": hidden,
+                        "k": sh.rows, "k_block_offset": kb, "offset_bytes": kb * 34,
+                        "out": w.ys, "act": w.hsq})
 
     gu_us = time_graph(torch, gate_up_only, args.steps) / L * 1e3
     dn_us = time_graph(torch, down_only, args.steps) / L * 1e3
     gu_bytes = float(np.mean([gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter)
-                              for l in range(L)]))
-    dn_bytes = float(np.mean([down_launch_bytes(n_active[l], n_valid[l], hidden, inter) for l in range(L)]))
+                              for l in range(L)])) + shared_gate_up_bytes(cols, hidden, share_rows)
+    dn_bytes = float(np.mean([down_launch_bytes(n_active[l], n_valid[l], hidden, inter)
+                              for l in range(L)])) + shared_down_bytes(cols, hidden, share_rows)
     gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
     dn_gbps = dn_bytes / (dn_us * 1e-6) / 1e9
     log(f"eager {eager_ms:.3f} ms/step; grouped gate/up {gu_us:.2f} us/launch {gu_gbps:.1f} GB/s; "
@@ -336,13 +385,26 @@ def main():
         "step_bytes": step_bytes,
         "weight_bytes": weight_bytes,
         "active_experts_mean": round(float(np.mean(n_active)), 2),
-        "roofline": {"bound": "hbm", "kernel": "k_mmvq grouped gate/up + SwiGLU",
+        "roofline": {"bound": "hbm", "kernel": "k_mmvq grouped gate/up + SwiGLU (routed experts "
+                               "and the shared expert's rows in one launch)",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "scaled by a 512 MiB copy)",
                      "mean_launch_us": round(gu_us, 2), "bytes_per_launch": int(gu_bytes)},
         "grouped_down": {"mean_launch_us": round(dn_us, 2), "gbps": round(dn_gbps, 1),
                          "bytes_per_launch": int(dn_bytes)},
     }
+
+    if args.pmc_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("pmc reference: copied 536870912 bytes device to device")
+        del src, dst
 
     # release the big bank before the sweep
     del g, bank, experts, shared, wss
