@@ -546,3 +546,23 @@ def test_down_f32_act_equals_quantize_then_down(c, n_exp, hidden, inter):
                               w_row_stride_bytes=rbf)
         assert np.array_equal(host(y1).view(np.int32), host(y2).view(np.int32))
         assert bits_equal(ys1, ys2)
+
+
+def test_fused_layer_all_routes_masked():
+    """A layer whose routes are all masked writes a zero combine on the fused
+    path, as on the separate calls."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    c, n_exp, hidden, inter, topk = 4, 16, 1024, 256, 8
+    _, (wgd, wud, wdd) = _tiny_layer(44, n_exp, hidden, inter)
+    experts = ml.RoutedExperts(wgd, wud, wdd, n_exp, hidden, inter)
+    x = to_dev(workloads.activations(44, c, hidden))
+    lg = workloads.router_logits(44, c, n_exp)
+    own = np.full(n_exp, -1, np.int32)
+    own[15] = 0
+    lg[:, 15] = -60.0                                     # never selected: every route masked
+    ws = ml.Workspace(c, hidden, inter, topk, 0, DEV)
+    ws.out.fill_(float("nan"))
+    out, _ = ml.forward(x, to_dev(lg), None, to_dev(own), 1, experts, None, ws)
+    torch.cuda.synchronize()
+    assert np.all(host(ws.ids) == -1)
+    assert np.all(host(out) == 0.0)
