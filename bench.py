@@ -171,7 +171,9 @@ def gate_up_launch_bytes(n_active, n_valid, cols, hidden, inter):
 
 
 def down_launch_bytes(n_active, n_valid, hidden, inter):
-    return n_active * hidden * (inter // 32 * 34) + n_valid * (inter // 32 * 36) + n_valid * hidden * 4
+    """Per grouped down launch: every active expert's down matrix once, the fp32
+    h rows once (quantised to q8_1 inside the launch), the y rows written."""
+    return n_active * hidden * (inter // 32 * 34) + n_valid * inter * 4 + n_valid * hidden * 4
 
 
 def shared_gate_up_bytes(cols, hidden, rows):
@@ -182,8 +184,8 @@ def shared_gate_up_bytes(cols, hidden, rows):
 
 def shared_down_bytes(cols, hidden, rows):
     """The shared down slice inside the down launch: the slice of every row,
-    the hsq rows read, ys written."""
-    return hidden * (rows // 32 * 34) + cols * (rows // 32 * 36) + cols * hidden * 4
+    the fp32 hs rows read, ys written."""
+    return hidden * (rows // 32 * 34) + cols * rows * 4 + cols * hidden * 4
 
 
 def layer_bytes(n_active, n_valid, cols, hidden, inter, topk, shared_rows):
@@ -191,15 +193,12 @@ def layer_bytes(n_active, n_valid, cols, hidden, inter, topk, shared_rows):
     and read once per consumer (weights of the active experts once)."""
     b = cols * hidden * 4 + cols * (hidden // 32 * 36)               # x read, xq written
     b += gate_up_launch_bytes(n_active, n_valid, cols, hidden, inter)
-    b += n_valid * inter * 4 + n_valid * (inter // 32 * 36)          # h read, hq written
-    b += down_launch_bytes(n_active, n_valid, hidden, inter)
+    b += down_launch_bytes(n_active, n_valid, hidden, inter)         # h read there (q8_1 in LDS)
     b += n_valid * hidden * 4 + 2 * cols * topk * 8 + cols * hidden * 4  # y read, ids/w, out
     b += cols * 256 * 4 * 2                                           # logits read (n_expert 256), bias
     if shared_rows:
-        b += cols * (hidden // 32 * 36)                              # xq read again
-        b += 2 * shared_rows * (hidden // 32 * 34) + cols * shared_rows * 4   # pair weights, hs
-        b += cols * shared_rows * 4 + cols * (shared_rows // 32 * 36)          # hs read, hsq
-        b += hidden * (shared_rows // 32 * 34) + cols * (shared_rows // 32 * 36) + cols * hidden * 4
+        b += shared_gate_up_bytes(cols, hidden, shared_rows)         # pair weights, hs written
+        b += shared_down_bytes(cols, hidden, shared_rows)            # slice, hs read, ys written
     return b
 
 
@@ -346,11 +345,11 @@ def main():
             w, sh = wss[l], shared[l]
             kb = sh.down_block_offset()
             moeq8.moe_grouped_mmvq_ex(
-                moeq8.DOWN, experts[l].down, None, w.hq, w.grouping, n=hidden, k=inter,
-                n_local_expert=n_local, ncols=cols, topk=topk, out=w.y,
+                moeq8.DOWN_F32_ACT, experts[l].down, None, w.h.view(cols * topk, inter), w.grouping,
+                n=hidden, k=inter, n_local_expert=n_local, ncols=cols, topk=topk, out=w.y,
                 shared={"a": sh.down, "row_stride": sh.inter_full // 32 * 34, "n": hidden,
                         "k": sh.rows, "k_block_offset": kb, "offset_bytes": kb * 34,
-                        "out": w.ys, "act": w.hsq})
+                        "out": w.ys, "act": w.hs})
 
     gu_us = time_graph(torch, gate_up_only, args.steps) / L * 1e3
     dn_us = time_graph(torch, down_only, args.steps) / L * 1e3

@@ -149,6 +149,8 @@ int swiglu_ds4(const float* g, const float* u, int64_t count, float* h, void* st
  * [3] topk, then expert[R], offset[R+1], route[R] with R = ncols*topk: active
  * groups a < n_active hold local expert expert[a] (ascending) and the routes
  * route[offset[a] .. offset[a+1]) (route r = column*topk + slot, ascending).
+ * Eight words of padding follow route[]: the grouped MMVQ reads eight words
+ * from any route entry at once (the padding's contents are never used).
  * ------------------------------------------------------------------------- */
 size_t moe_grouping_bytes(int64_t ncols, int32_t topk);
 int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_slot,

@@ -75,6 +75,57 @@ struct MmvqParams {
     float* s_out;               // [ncols][s.n]
 };
 
+// One int32 word of the grouping.  The grouping is written by an earlier
+// launch and only read in this one, so it may be read through the constant
+// address space: wave-uniform indices then become scalar loads, which do not
+// queue behind the vector loads of weights already in flight.
+__device__ __forceinline__ int32_t grouping_word(const int32_t* g, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)g)[i];
+}
+
+// Eight consecutive grouping words from word i (4-byte alignment; the buffer
+// is padded so that eight words from any route entry stay inside it).
+typedef int32_t int8w __attribute__((ext_vector_type(8), aligned(4)));
+__device__ __forceinline__ int8w grouping_words8(const int32_t* g, int64_t i) {
+    return *(const __attribute__((address_space(4))) int8w*)(g + i);
+}
+
+// The q8_1 block rule on half a block: this lane holds 16 of the block's 32
+// values, the neighbouring lane (lane ^ 1) the other 16.  The block's amax and
+// its integer quant sum are combined across the pair (max and integer sums do
+// not depend on order), so both lanes see the same d and s.  Every lane of the
+// wave must call this; lanes with active == false write nothing.
+__device__ __forceinline__ void quantize_half_q81(const float (&v)[QK / 2], int half, bool active,
+                                                  uint8_t* block) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK / 2; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
+                                                                   0xf, 0xf, false)));
+    const float d = amax / 127.0f;
+    uint32_t packed[QK / 8] = {0u, 0u, 0u, 0u};
+    int sum = 0;
+    if (d != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < QK / 2; ++i) {
+            const int q = (int)roundf(v[i] / d);
+            sum += q;
+            packed[i / 4] |= ((uint32_t)q & 0xffu) << (8 * (i % 4));
+        }
+    }
+    sum += __builtin_amdgcn_update_dpp(0, sum, 0xB1, 0xf, 0xf, false);
+    if (active) {
+        uint32_t* o = reinterpret_cast<uint32_t*>(block);
+        if (half == 0) {
+            // s = fp16 of the fp32 product (two roundings, as defined)
+            const uint32_t sbits = float_to_half_bits(materialize_f32(d * (float)sum));
+            o[0] = float_to_half_bits(d) | (sbits << 16);
+        }
+#pragma unroll
+        for (int j = 0; j < QK / 8; ++j) o[1 + 4 * half + j] = packed[j];
+    }
+}
+
 // Pairwise tree over the 16 logical lanes of a group using DPP lane moves:
 // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  The
 // pairs combined at each level are the same values as an xor 1, 2, 4, 8
@@ -139,15 +190,16 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             item -= n_dense;
             const int a = (int)(item / p.m.wg);
             row_block = item - (int64_t)a * p.m.wg;
-            const int n_active = p.grouping[0];
+            const int n_active = grouping_word(p.grouping, 0);
             if (a >= n_active) return;
             // a grouping written for another column count or top-k is not used
-            if (p.grouping[2] != p.ncols || p.grouping[3] != p.topk) return;
-            R = p.grouping[2] * p.grouping[3];
-            const int e = p.grouping[4 + a];
+            if (grouping_word(p.grouping, 2) != p.ncols || grouping_word(p.grouping, 3) != p.topk)
+                return;
+            R = p.ncols * p.topk;
+            const int e = grouping_word(p.grouping, 4 + a);
             if (e < 0 || e >= p.n_local) return;
-            route_begin = p.grouping[4 + R + a];
-            ncols = p.grouping[4 + R + a + 1] - route_begin;
+            route_begin = grouping_word(p.grouping, 4 + R + a);
+            ncols = grouping_word(p.grouping, 4 + R + a + 1) - route_begin;
             if (route_begin < 0 || ncols < 0 || route_begin + ncols > R) return;
             w0 += (int64_t)e * p.expert_stride;
             if (NMAT == 2) w1 += (int64_t)e * p.expert_stride;
@@ -170,15 +222,27 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
         // output row and activation row of each column of this pass
         int orow[MAX_COLS];
         int arow[MAX_COLS];
+        int8w w8 = {};
+        if constexpr (GROUPED) {
+            // the route entries of this pass as one eight-word read (words
+            // past the pass's nc columns are read but not used; dense items
+            // read words 0..7 and use none)
+            const int64_t base = routed ? 4 + 2 * R + 1 + route_begin + c0 : 0;
+            w8 = grouping_words8(p.grouping, base);
+            int rw[MAX_COLS];
 #pragma unroll
-        for (int c = 0; c < MAX_COLS; ++c) {
-            orow[c] = c0 + c;
-            arow[c] = c0 + c;
-            if (GROUPED && routed) {
-                int r = (c < nc) ? p.grouping[4 + 2 * R + 1 + route_begin + c0 + c] : 0;
-                if (r < 0 || r >= R) r = -1;
-                orow[c] = r;
-                arow[c] = r < 0 ? 0 : r / p.act_route_div;
+            for (int c = 0; c < MAX_COLS; ++c) rw[c] = w8[c];
+#pragma unroll
+            for (int c = 0; c < MAX_COLS; ++c) {
+                const int r = (c >= nc || rw[c] < 0 || rw[c] >= R) ? -1 : rw[c];
+                orow[c] = routed ? r : c0 + c;
+                arow[c] = routed ? (r < 0 ? 0 : r / p.act_route_div) : c0 + c;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < MAX_COLS; ++c) {
+                orow[c] = c0 + c;
+                arow[c] = c0 + c;
             }
         }
 
@@ -190,22 +254,31 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) acc[c][u][m] = 0.0f;
 
+        // A lane whose chunk or row lies outside the matrix contributes +0.
+        // With q8_1 activations it skips the loads and uses zero chunks.  With
+        // fp32 activations every load is issued (such a lane reads chunk 0 of
+        // row 0 and adds +0 in place of its product): a cleared register with
+        // a load in flight would make the activation quantisation wait for the
+        // weight loads as well.
+        constexpr bool UNCOND = ACT_F32;
         WChunk wc[U][NMAT];
-        int crel = 0;
+        int crel = 0;                                      // chunk within the slice (clamped)
         bool cvalid = false;
+        bool ok[U];
         auto load_weights = [&](int s) {
             const int round = r0 + (G == 1 ? s : gsub);
-            crel = round * LANES_PER_ROW + l - chunk0;        // chunk within the slice
-            cvalid = (crel >= 0) && (crel < nchunks);
+            const int cr = round * LANES_PER_ROW + l - chunk0;
+            cvalid = (cr >= 0) && (cr < nchunks);
+            crel = cvalid ? cr : 0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t row = row_base + (int64_t)u * RPW;
-                const bool ok = cvalid && row < n_rows;
+                ok[u] = cvalid && row < n_rows;
+                const int64_t off = ok[u] ? row * row_stride + (int64_t)crel * W_CHUNK_BYTES : 0;
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
-                    if (ok) {
-                        load_w_chunk(wc[u][m], (m == 0 ? w0 : w1) + row * row_stride +
-                                                   (int64_t)crel * W_CHUNK_BYTES);
+                    if (UNCOND || ok[u]) {
+                        load_w_chunk(wc[u][m], (m == 0 ? w0 : w1) + off);
                     } else {
                         zero_w_chunk(wc[u][m]);
                     }
@@ -213,29 +286,53 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             }
         };
 
-        load_weights(0);
-
         const uint8_t* act_base = (GROUPED && !routed) ? p.s_act_q : p.act;
         if constexpr (ACT_F32) {
-            // quantise this item's activation rows into LDS while the weight
-            // loads are in flight (same block quantiser as q8_1_quantize_rows)
+            // Quantise this item's activation rows into LDS with the block rule
+            // of q8_1_quantize_rows.  Two neighbouring lanes share a block, 16
+            // values each, so fewer registers are held across the weight
+            // loads.  The first pass's values are loaded before the weights:
+            // quantising waits for them alone (loads complete in issue order)
+            // while the weight loads are still in flight.
             __syncthreads();                               // a previous pass may still read LDS
             const int nb = nchunks * 2;
+            const int units = nc * nb * 2;                 // half blocks
             const float* src = routed ? p.act_f32 : p.s_act_f32;
             const int64_t stride = routed ? p.act_f32_stride : p.s_act_f32_stride;
-            for (int t = threadIdx.x; t < nc * nb; t += blockDim.x) {
-                const int c = t / nb;
-                const int b = t - c * nb;
-                int ar = c0 + c;
-                if (routed) {
-                    const int r = p.grouping[4 + 2 * R + 1 + route_begin + c0 + c];
-                    ar = (r < 0 || r >= R) ? 0 : r / p.act_route_div;
+            float v[QK / 2];
+            auto load_half = [&](int u) {
+                if (u < units) {
+                    const int blk = u >> 1;
+                    const int c = blk / nb;
+                    const int b = blk - c * nb;
+                    int ar = c0 + c;
+                    if (routed) {
+                        const int r = w8[c];               // c < nc here
+                        ar = (r < 0 || r >= R) ? 0 : r / p.act_route_div;
+                    }
+                    const float* sp = src + (int64_t)ar * stride + (int64_t)b * QK + (u & 1) * (QK / 2);
+#pragma unroll
+                    for (int i = 0; i < QK / 2; ++i) v[i] = sp[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < QK / 2; ++i) v[i] = 0.0f;
                 }
-                quantize_block<true>(src + (int64_t)ar * stride + (int64_t)b * QK,
-                                     lds_act + (int64_t)c * p.act_row_bytes + (int64_t)b * Q81_BYTES);
+            };
+            const int passes = (units + (int)blockDim.x - 1) / (int)blockDim.x;
+            load_half(threadIdx.x);
+            load_weights(0);
+            for (int ps = 0; ps < passes; ++ps) {          // uniform: every lane takes part
+                const int u = ps * (int)blockDim.x + (int)threadIdx.x;
+                if (ps > 0) load_half(u);
+                const int blk = u >> 1;
+                const int c = blk / nb;
+                quantize_half_q81(v, u & 1, u < units,
+                                  lds_act + (int64_t)c * p.act_row_bytes + (int64_t)(blk - c * nb) * Q81_BYTES);
             }
             __syncthreads();
             act_base = lds_act;
+        } else {
+            load_weights(0);
         }
 
         for (int s = 0; s < p.nsteps; ++s) {
@@ -244,21 +341,22 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             for (int c = 0; c < MAX_COLS; ++c) {
                 if (c < nc) {
                     XChunk xc;
-                    if (cvalid) {
-                        if constexpr (ACT_F32) {
-                            load_x_chunk_lds(xc, act_base + (int64_t)c * p.act_row_bytes +
-                                                     (int64_t)crel * X_CHUNK_BYTES);
-                        } else {
-                            load_x_chunk(xc, act_base + (int64_t)arow[c] * p.act_row_bytes +
+                    if constexpr (ACT_F32) {
+                        load_x_chunk_lds(xc, act_base + (int64_t)c * p.act_row_bytes +
                                                  (int64_t)crel * X_CHUNK_BYTES);
-                        }
+                    } else if (cvalid) {
+                        load_x_chunk(xc, act_base + (int64_t)arow[c] * p.act_row_bytes +
+                                             (int64_t)crel * X_CHUNK_BYTES);
                     } else {
                         zero_x_chunk(xc);
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u)
 #pragma unroll
-                        for (int m = 0; m < NMAT; ++m) acc[c][u][m] += chunk_dot(wc[u][m], xc);
+                        for (int m = 0; m < NMAT; ++m) {
+                            const float d = chunk_dot(wc[u][m], xc);
+                            acc[c][u][m] += (UNCOND && !ok[u]) ? 0.0f : d;
+                        }
                 }
             }
         }

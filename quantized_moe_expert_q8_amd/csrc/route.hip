@@ -279,7 +279,9 @@ using namespace moeq8;
 extern "C" size_t moe_grouping_bytes(int64_t ncols, int32_t topk) {
     if (ncols < 1 || ncols > ROUTE_MAX_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return 0;
     const size_t R = (size_t)ncols * (size_t)topk;
-    const size_t bytes = 4 * (4 + 3 * R + 1);
+    // header, expert[R], offset[R+1], route[R], then eight words of padding
+    // so that readers may load eight words from any route entry
+    const size_t bytes = 4 * (4 + 3 * R + 1 + 8);
     return (bytes + 255) & ~(size_t)255;
 }
 

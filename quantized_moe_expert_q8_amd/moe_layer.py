@@ -12,9 +12,10 @@ shared-expert commits) on ``ncols`` columns:
     out = sum over unmasked slots of w * y
 
 Buffers live in a workspace allocated once, so ``forward`` allocates nothing
-and can be captured in a HIP graph.  The shared expert depends only on xq, so
-it runs on a second stream forked after the quantisation and joined at the
-end of the layer (a parallel branch of the graph).  No arithmetic happens here.
+and can be captured in a HIP graph.  The fused form runs the layer as four
+launches on one stream, the shared expert's work riding in the grouped
+launches as extra work items; the unfused form issues the calls above one by
+one, the shared expert on a second stream.  No arithmetic happens here.
 """
 
 from __future__ import annotations
@@ -108,9 +109,10 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     """Enqueue one layer on the current stream; returns (out, ys) device tensors
     of the workspace.
 
-    fused=True (five launches): prologue (router + q8_1 of x), grouped gate/up
-    with the shared gate/up rows as extra items, one q8_1 launch over h and hs,
-    grouped down with the shared down slice as extra items, combine.
+    fused=True (four launches): prologue (router + q8_1 of x), grouped gate/up
+    with the shared gate/up rows as extra items, grouped down that quantises h
+    and hs to q8_1 in the launch with the shared down slice as extra items,
+    combine.
     fused=False: the nine separate calls, the shared expert on a second stream.
     Both give the same bits.  ``hook(name, phase)`` (unfused only) is called
     around each launch."""
@@ -180,8 +182,10 @@ def _same_round_span(k_block_offset: int, k_slice: int, k: int) -> bool:
 
 
 def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws):
-    """Prologue, gate/up (+ shared rows), one quantisation of h and hs, down
-    (+ shared slice), combine: five launches on one stream."""
+    """Prologue, gate/up (+ shared rows), down with the q8_1 quantisation of h
+    and hs inside the launch (+ shared slice), combine: four launches on one
+    stream.  A shared slice whose length or lane layout differs from the
+    routed down product's gets its own quantisation and MMVQ launches."""
     c, topk = ws.ncols, ws.topk
     hidden, inter = experts.hidden, experts.inter
     ops.moe_route_topk_quantize(x, logits, topk, bias=bias, owner_slot=owner_slot,
@@ -195,25 +199,19 @@ def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared,
                  "k": hidden, "k_block_offset": 0, "offset_bytes": shared.gate_offset(),
                  "out": ws.hs}
         kb = shared.down_block_offset()
-        if ws.joint and _same_round_span(kb, shared.rows, inter):
+        if _same_round_span(kb, shared.rows, inter):
             sh_dn = {"a": shared.down, "row_stride": (shared.inter_full // QK) * Q80,
                      "n": hidden, "k": shared.rows, "k_block_offset": kb,
-                     "offset_bytes": kb * Q80, "out": ws.ys, "act": ws.hsq}
+                     "offset_bytes": kb * Q80, "out": ws.ys, "act": ws.hs}
     ops.moe_grouped_mmvq_ex(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping,
                             n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
                             out=ws.h, shared=sh_gu)
-    if ws.joint:
-        # h and hs share one buffer: one launch quantises both
-        ops.q8_1_quantize_rows(ws.hh, out=ws.hhq)
-    else:
-        ops.q8_1_quantize_rows(ws.h.view(R, inter), out=ws.hq)
-        if shared is not None:
-            ops.q8_1_quantize_rows(ws.hs, out=ws.hsq)
-    ops.moe_grouped_mmvq_ex(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
-                            n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y,
-                            shared=sh_dn)
+    ops.moe_grouped_mmvq_ex(ops.DOWN_F32_ACT, experts.down, None, ws.h.view(R, inter), ws.grouping,
+                            n=hidden, k=inter, n_local_expert=experts.n_local, ncols=c, topk=topk,
+                            out=ws.y, shared=sh_dn)
     if shared is not None and sh_dn is None:
         kb = shared.down_block_offset()
+        ops.q8_1_quantize_rows(ws.hs, out=ws.hsq)
         ops.mmvq_q8_0(shared.down, ws.hsq, hidden, shared.rows, ncols=c, k_block_offset=kb,
                       w_offset_bytes=kb * Q80, w_row_stride_bytes=(shared.inter_full // QK) * Q80,
                       out=ws.ys)

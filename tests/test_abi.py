@@ -51,7 +51,7 @@ def test_abi_version_and_status_strings():
 
 def test_grouping_bytes():
     L = moeq8.lib()
-    assert L.moe_grouping_bytes(8, 8) == 1024           # 4*(4 + 3*64 + 1) = 788 -> 1024
+    assert L.moe_grouping_bytes(8, 8) == 1024           # 4*(4 + 3*64 + 1 + 8) = 820 -> 1024
     assert L.moe_grouping_bytes(1, 8) == 256
     assert L.moe_grouping_bytes(0, 8) == 0 and L.moe_grouping_bytes(9, 8) == 0
     assert L.moe_grouping_bytes(1, 17) == 0
