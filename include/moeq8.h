@@ -150,7 +150,10 @@ int swiglu_ds4(const float* g, const float* u, int64_t count, float* h, void* st
  * groups a < n_active hold local expert expert[a] (ascending) and the routes
  * route[offset[a] .. offset[a+1]) (route r = column*topk + slot, ascending).
  * Eight words of padding follow route[]: the grouped MMVQ reads eight words
- * from any route entry at once (the padding's contents are never used).
+ * from any route entry at once (the padding's contents are never used).  Then,
+ * from word T = (4 + 3R + 1 + 8) rounded up to a multiple of 4, a table of 4
+ * words per active group: {expert[a], offset[a], offset[a+1], 0}, which the
+ * grouped MMVQ reads as one 16-byte record per work item.
  * ------------------------------------------------------------------------- */
 size_t moe_grouping_bytes(int64_t ncols, int32_t topk);
 int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_slot,

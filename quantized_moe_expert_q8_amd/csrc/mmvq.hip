@@ -33,8 +33,16 @@ namespace moeq8 {
 #ifndef MOEQ8_U_ROWSETS
 #define MOEQ8_U_ROWSETS 2
 #endif
+#ifndef MOEQ8_U_F32
+#define MOEQ8_U_F32 MOEQ8_U_ROWSETS
+#endif
+#ifndef MOEQ8_U_SINGLE
+#define MOEQ8_U_SINGLE MOEQ8_U_ROWSETS
+#endif
 constexpr int WAVES_PER_WG = MOEQ8_WAVES_PER_WG;
-constexpr int U_ROWSETS = MOEQ8_U_ROWSETS;
+constexpr int U_ROWSETS = MOEQ8_U_ROWSETS;          // row sets per wave: gate/up pair
+constexpr int U_SINGLE = MOEQ8_U_SINGLE;            // one matrix, q8_1 activations
+constexpr int U_F32 = MOEQ8_U_F32;                  // one matrix, fp32 activations
 constexpr int MAX_COLS = 8;
 
 // One matrix (or gate/up pair) and the column range of its rows that is read.
@@ -75,19 +83,19 @@ struct MmvqParams {
     float* s_out;               // [ncols][s.n]
 };
 
-// One int32 word of the grouping.  The grouping is written by an earlier
-// launch and only read in this one, so it may be read through the constant
-// address space: wave-uniform indices then become scalar loads, which do not
-// queue behind the vector loads of weights already in flight.
-__device__ __forceinline__ int32_t grouping_word(const int32_t* g, int64_t i) {
-    return ((const __attribute__((address_space(4))) int32_t*)g)[i];
-}
-
-// Eight consecutive grouping words from word i (4-byte alignment; the buffer
-// is padded so that eight words from any route entry stay inside it).
+// Grouping words are written by an earlier launch and only read in this one,
+// so they may be read through the constant address space: wave-uniform
+// indices then become scalar loads, which do not queue behind the vector loads
+// of weights already in flight.  Eight or four consecutive words from word i
+// (4-byte alignment; the buffer is padded so that eight words from any route
+// entry stay inside it).
 typedef int32_t int8w __attribute__((ext_vector_type(8), aligned(4)));
+typedef int32_t int4w __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ int8w grouping_words8(const int32_t* g, int64_t i) {
     return *(const __attribute__((address_space(4))) int8w*)(g + i);
+}
+__device__ __forceinline__ int4w grouping_words4(const int32_t* g, int64_t i) {
+    return *(const __attribute__((address_space(4))) int4w*)(g + i);
 }
 
 // The q8_1 block rule on half a block: this lane holds 16 of the block's 32
@@ -177,32 +185,62 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
     int32_t nchunks = p.m.nchunks;
     int32_t chunk0 = p.m.chunk0;
     int32_t r0 = p.m.r0;
+    const int32_t m_wg = p.m.wg;
+    const int32_t s_wg = p.s.wg;
+    const int64_t expert_stride = p.expert_stride;
+    const int64_t n_local = p.n_local;
+    const int32_t p_ncols = p.ncols;
+    const int32_t p_topk = p.topk;
+    const int32_t rows_per_wg = p.rows_per_wg;
+    const int32_t* grouping = p.grouping;
+    const uint8_t* act_q = p.act;
+    const uint8_t* s_act_q = p.s_act_q;
+    float* out0 = p.out0;
+    float* s_out = p.s_out;
+    const int64_t act_row_bytes = p.act_row_bytes;
+    const int32_t act_route_div = p.act_route_div;
+    const int32_t nsteps = p.nsteps;
+    // The arguments the decode and the first loads need arrive in one batch
+    // of scalar loads at entry; left alone, the compiler fetches each after
+    // the branch that first uses it, one round trip at a time.
+    asm volatile("" ::"s"(w0), "s"(w1), "s"(row_stride), "s"(n_rows), "s"(nchunks), "s"(chunk0),
+                 "s"(r0), "s"(m_wg), "s"(s_wg), "s"(expert_stride), "s"(n_local), "s"(p_ncols),
+                 "s"(p_topk), "s"(rows_per_wg), "s"(grouping), "s"(act_q), "s"(s_act_q), "s"(out0),
+                 "s"(s_out), "s"(act_row_bytes), "s"(act_route_div), "s"(nsteps));
     int64_t row_block = item;
-    int ncols = p.ncols;
+    int ncols = p_ncols;
     int route_begin = 0;
     int R = 0;
     bool routed = false;
     if constexpr (GROUPED) {
         // the dense part's items come first: its blocks carry every column, so
         // dispatching them early keeps them out of the launch's tail
-        const int64_t n_dense = p.s.wg;
-        if (item >= n_dense) {
-            item -= n_dense;
-            const int a = (int)(item / p.m.wg);
-            row_block = item - (int64_t)a * p.m.wg;
-            const int n_active = grouping_word(p.grouping, 0);
-            if (a >= n_active) return;
-            // a grouping written for another column count or top-k is not used
-            if (grouping_word(p.grouping, 2) != p.ncols || grouping_word(p.grouping, 3) != p.topk)
-                return;
-            R = p.ncols * p.topk;
-            const int e = grouping_word(p.grouping, 4 + a);
-            if (e < 0 || e >= p.n_local) return;
-            route_begin = grouping_word(p.grouping, 4 + R + a);
-            ncols = grouping_word(p.grouping, 4 + R + a + 1) - route_begin;
-            if (route_begin < 0 || ncols < 0 || route_begin + ncols > R) return;
-            w0 += (int64_t)e * p.expert_stride;
-            if (NMAT == 2) w1 += (int64_t)e * p.expert_stride;
+        const uint32_t n_dense = (uint32_t)s_wg;       // grids stay below 2^31 items
+        const uint32_t it = (uint32_t)item;
+        if (it >= n_dense) {
+            const uint32_t wgm = (uint32_t)m_wg;
+            const uint32_t a = (it - n_dense) / wgm;
+            row_block = (int64_t)(it - n_dense - a * wgm);
+            // The header and the group's table entry {expert, first route,
+            // end} in two scalar reads issued together, before any check: the
+            // grid holds at most min(ncols*topk, n_local) groups, so a < R and
+            // both reads are inside the grouping whatever it holds.
+            const int Rk = p_ncols * p_topk;
+            const int4w hdr = grouping_words4(grouping, 0);
+            const int4w grp = grouping_words4(grouping, grouping_table_word(Rk) + 4 * (int64_t)a);
+            const int e = grp[0];
+            // one combined check (no short-circuit): a past the active count, a
+            // grouping written for another column count or top-k, an expert or
+            // route range out of bounds
+            const bool bad = ((int)a >= hdr[0]) | (hdr[2] != p_ncols) | (hdr[3] != p_topk) |
+                             (e < 0) | (e >= n_local) | (grp[1] < 0) | (grp[2] < grp[1]) |
+                             (grp[2] > Rk);
+            if (bad) return;
+            R = Rk;
+            route_begin = grp[1];
+            ncols = grp[2] - grp[1];
+            w0 += (int64_t)e * expert_stride;
+            if (NMAT == 2) w1 += (int64_t)e * expert_stride;
             routed = true;
         } else {
             row_block = item;
@@ -215,37 +253,10 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             r0 = p.s.r0;
         }
     }
-    const int64_t row_base = row_block * p.rows_per_wg + (int64_t)wave * (U * RPW) + rslot;
+    const int64_t row_base = row_block * rows_per_wg + (int64_t)wave * (U * RPW) + rslot;
 
     for (int c0 = 0; c0 < ncols; c0 += MAX_COLS) {
         const int nc = min(ncols - c0, MAX_COLS);
-        // output row and activation row of each column of this pass
-        int orow[MAX_COLS];
-        int arow[MAX_COLS];
-        int8w w8 = {};
-        if constexpr (GROUPED) {
-            // the route entries of this pass as one eight-word read (words
-            // past the pass's nc columns are read but not used; dense items
-            // read words 0..7 and use none)
-            const int64_t base = routed ? 4 + 2 * R + 1 + route_begin + c0 : 0;
-            w8 = grouping_words8(p.grouping, base);
-            int rw[MAX_COLS];
-#pragma unroll
-            for (int c = 0; c < MAX_COLS; ++c) rw[c] = w8[c];
-#pragma unroll
-            for (int c = 0; c < MAX_COLS; ++c) {
-                const int r = (c >= nc || rw[c] < 0 || rw[c] >= R) ? -1 : rw[c];
-                orow[c] = routed ? r : c0 + c;
-                arow[c] = routed ? (r < 0 ? 0 : r / p.act_route_div) : c0 + c;
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < MAX_COLS; ++c) {
-                orow[c] = c0 + c;
-                arow[c] = c0 + c;
-            }
-        }
-
         float acc[MAX_COLS][U][NMAT];
 #pragma unroll
         for (int c = 0; c < MAX_COLS; ++c)
@@ -286,7 +297,33 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             }
         };
 
-        const uint8_t* act_base = (GROUPED && !routed) ? p.s_act_q : p.act;
+        // With q8_1 activations the weight loads go out first: the route read
+        // below is a scalar load, which does not wait for them.
+        if constexpr (!ACT_F32) load_weights(0);
+
+        // output row and activation row of each column of this pass
+        int orow[MAX_COLS];
+        int arow[MAX_COLS];
+        int8w w8 = {};
+        if constexpr (GROUPED) {
+            // the route entries of this pass as one eight-word read (words
+            // past the pass's nc columns are read but not used)
+            if (routed) w8 = grouping_words8(grouping, 4 + 2 * R + 1 + route_begin + c0);
+#pragma unroll
+            for (int c = 0; c < MAX_COLS; ++c) {
+                const int r = (c >= nc || w8[c] < 0 || w8[c] >= R) ? -1 : w8[c];
+                orow[c] = routed ? r : c0 + c;
+                arow[c] = routed ? (r < 0 ? 0 : r / act_route_div) : c0 + c;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < MAX_COLS; ++c) {
+                orow[c] = c0 + c;
+                arow[c] = c0 + c;
+            }
+        }
+
+        const uint8_t* act_base = (GROUPED && !routed) ? s_act_q : act_q;
         if constexpr (ACT_F32) {
             // Quantise this item's activation rows into LDS with the block rule
             // of q8_1_quantize_rows.  Two neighbouring lanes share a block, 16
@@ -308,7 +345,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                     int ar = c0 + c;
                     if (routed) {
                         const int r = w8[c];               // c < nc here
-                        ar = (r < 0 || r >= R) ? 0 : r / p.act_route_div;
+                        ar = (r < 0 || r >= R) ? 0 : r / act_route_div;
                     }
                     const float* sp = src + (int64_t)ar * stride + (int64_t)b * QK + (u & 1) * (QK / 2);
 #pragma unroll
@@ -318,34 +355,33 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                     for (int i = 0; i < QK / 2; ++i) v[i] = 0.0f;
                 }
             };
-            const int passes = (units + (int)blockDim.x - 1) / (int)blockDim.x;
+            constexpr int THREADS = 64 * WAVES_PER_WG;     // the launch's block size
+            const int passes = (units + THREADS - 1) / THREADS;
             load_half(threadIdx.x);
             load_weights(0);
             for (int ps = 0; ps < passes; ++ps) {          // uniform: every lane takes part
-                const int u = ps * (int)blockDim.x + (int)threadIdx.x;
+                const int u = ps * THREADS + (int)threadIdx.x;
                 if (ps > 0) load_half(u);
                 const int blk = u >> 1;
                 const int c = blk / nb;
                 quantize_half_q81(v, u & 1, u < units,
-                                  lds_act + (int64_t)c * p.act_row_bytes + (int64_t)(blk - c * nb) * Q81_BYTES);
+                                  lds_act + (int64_t)c * act_row_bytes + (int64_t)(blk - c * nb) * Q81_BYTES);
             }
             __syncthreads();
             act_base = lds_act;
-        } else {
-            load_weights(0);
         }
 
-        for (int s = 0; s < p.nsteps; ++s) {
+        for (int s = 0; s < nsteps; ++s) {
             if (s > 0) load_weights(s);
 #pragma unroll
             for (int c = 0; c < MAX_COLS; ++c) {
                 if (c < nc) {
                     XChunk xc;
                     if constexpr (ACT_F32) {
-                        load_x_chunk_lds(xc, act_base + (int64_t)c * p.act_row_bytes +
+                        load_x_chunk_lds(xc, act_base + (int64_t)c * act_row_bytes +
                                                  (int64_t)crel * X_CHUNK_BYTES);
                     } else if (cvalid) {
-                        load_x_chunk(xc, act_base + (int64_t)arow[c] * p.act_row_bytes +
+                        load_x_chunk(xc, act_base + (int64_t)arow[c] * act_row_bytes +
                                              (int64_t)crel * X_CHUNK_BYTES);
                     } else {
                         zero_x_chunk(xc);
@@ -362,7 +398,49 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
         }
 
         // reduce: chain the groups of a row in round order, then the 16-lane tree
-        float* out = (GROUPED && !routed) ? p.s_out : p.out0;
+        float* out = (GROUPED && !routed) ? s_out : out0;
+        if constexpr (MAX_COLS * U <= 16) {
+            // Every lane of the 16 ends the tree with every (column, row set)
+            // value, and each such pair has a lane of its own (lane c*U + u):
+            // each lane keeps its pair's values and finishes it alone, so the
+            // epilogue (SwiGLU, the store) runs once per lane instead of once
+            // per pair.
+            float sel[NMAT];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) sel[m] = 0.0f;
+            int sel_orow = -1;
+            int sel_u = 0;
+#pragma unroll
+            for (int c = 0; c < MAX_COLS; ++c) {
+                if (c < nc) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const bool mine = l == c * U + u;
+#pragma unroll
+                        for (int m = 0; m < NMAT; ++m) {
+                            const float v = tree16(chain_groups<G>(acc[c][u][m], lane));
+                            sel[m] = mine ? v : sel[m];
+                        }
+                        sel_orow = mine ? orow[c] : sel_orow;
+                        sel_u = mine ? u : sel_u;
+                    }
+                }
+            }
+            const int64_t row = row_base + (int64_t)sel_u * RPW;
+            if (gsub == 0 && sel_orow >= 0 && row < n_rows) {
+                const int64_t at = (int64_t)sel_orow * n_rows + row;
+                if constexpr (NMAT == 2) {
+                    out[at] = swiglu_ds4_f32(sel[0], sel[1]);
+                    if constexpr (!GROUPED) {
+                        if (p.out_g) p.out_g[at] = sel[0];
+                        if (p.out_u) p.out_u[at] = sel[1];
+                    }
+                } else {
+                    out[at] = sel[0];
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int c = 0; c < MAX_COLS; ++c) {
             if (c < nc) {
@@ -440,18 +518,20 @@ MatDesc make_desc(const void* w0, const void* w1, int64_t row_stride, int64_t n,
     return d;
 }
 
-int rows_per_wg_for(const Shape& s) { return WAVES_PER_WG * U_ROWSETS * (4 / s.G); }
+constexpr int u_for(int nmat, bool act_f32) { return nmat == 2 ? U_ROWSETS : act_f32 ? U_F32 : U_SINGLE; }
 
-template <int NMAT, bool GROUPED, bool ACT_F32>
+int rows_per_wg_for(const Shape& s, int u) { return WAVES_PER_WG * u * (4 / s.G); }
+
+template <int NMAT, bool GROUPED, bool ACT_F32, int U = u_for(NMAT, ACT_F32)>
 int launch_mmvq(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
     p.nsteps = s.nsteps;
     if (grid <= 0) return MOEQ8_OK;
     if (grid > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
     const dim3 block(64 * WAVES_PER_WG);
     switch (s.G) {
-        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U_ROWSETS, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
-        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U_ROWSETS, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
-        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U_ROWSETS, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
     }
     return check_launch();
 }
@@ -474,7 +554,7 @@ int dense_call(int nmat, const void* w0, const void* w1, int64_t stride, int64_t
                void* stream) {
     MmvqParams p = {};
     const Shape s = pick_shape(kb / 2, k / 64);
-    p.rows_per_wg = rows_per_wg_for(s);
+    p.rows_per_wg = rows_per_wg_for(s, u_for(nmat, false));
     p.m = make_desc(w0, w1, stride, n, k, kb, p.rows_per_wg);
     p.act = (const uint8_t*)xq;
     p.act_row_bytes = (k / QK) * Q81_BYTES;
@@ -577,7 +657,7 @@ extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w
 
     MmvqParams p = {};
     const Shape s = pick_shape(0, k / 64);
-    p.rows_per_wg = rows_per_wg_for(s);
+    p.rows_per_wg = rows_per_wg_for(s, u_for(pair ? 2 : 1, f32));
     p.m = make_desc(w_a, w_b, w_row_stride_bytes, n, k, 0, p.rows_per_wg);
     p.expert_stride = expert_stride_bytes;
     p.n_local = n_local_expert;

@@ -38,6 +38,14 @@ constexpr int W_CHUNK_DWORDS = W_CHUNK_BYTES / 4;            // 17
 constexpr int X_CHUNK_DWORDS = X_CHUNK_BYTES / 4;            // 18
 constexpr float SWIGLU_LIMIT = 7.0f;
 
+// Word index of the per-group table of an expert grouping with R routes: it
+// follows the header, expert[R], offset[R+1], route[R] and eight words of
+// padding, rounded up to a 16-byte boundary.  Entry a (4 words) is
+// {expert[a], offset[a], offset[a+1], 0}.
+__host__ __device__ constexpr int64_t grouping_table_word(int64_t R) {
+    return (4 + 3 * R + 1 + 8 + 3) & ~(int64_t)3;
+}
+
 // 16-byte vectors that only promise 4-byte alignment: the 34-byte blocks put
 // chunks on 4-byte boundaries, and gfx950 global loads accept that.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));

@@ -136,6 +136,7 @@ __device__ __forceinline__ void route_body(
     int32_t* g_expert = grouping + 4;
     int32_t* g_offset = grouping + 4 + R;
     int32_t* g_route = grouping + 4 + 2 * R + 1;
+    int4* g_table = reinterpret_cast<int4*>(grouping + grouping_table_word(R));
     if (j < ncols && lane < topk) {
         const int rr = j * topk + lane;
         ids[rr] = slot_id;
@@ -170,6 +171,7 @@ __device__ __forceinline__ void route_body(
             const int act = __popcll(lt & hmask);
             g_expert[act] = id;
             g_offset[act] = pos;
+            g_table[act] = make_int4(id, pos, pos + __popcll(eq), 0);
         }
         if (valid) g_route[pos] = r;
         if (r < R) {
@@ -193,7 +195,7 @@ __device__ __forceinline__ void route_body(
     const bool in = r < R;
     const int id = in ? s_id[r] : -1;
     const bool valid = id >= 0;
-    int pos = 0, before = 0, n_valid = 0;
+    int pos = 0, before = 0, n_valid = 0, same = 0;
     const int4* v4 = reinterpret_cast<const int4*>(s_id);
 #pragma unroll
     for (int q4 = 0; q4 < ROUTE_MAX_R / 4; ++q4) {
@@ -207,6 +209,7 @@ __device__ __forceinline__ void route_body(
                 n_valid += iq >= 0 ? 1 : 0;
                 pos += (iq >= 0 && (iq < id || (iq == id && q < r))) ? 1 : 0;
                 before += (iq == id && q < r) ? 1 : 0;
+                same += (iq == id) ? 1 : 0;
             }
         }
     }
@@ -227,6 +230,7 @@ __device__ __forceinline__ void route_body(
     if (head) {
         g_expert[act] = id;
         g_offset[act] = pos;
+        g_table[act] = make_int4(id, pos, pos + same, 0);
     }
     if (valid) g_route[pos] = r;
     if (in) {
@@ -279,9 +283,9 @@ using namespace moeq8;
 extern "C" size_t moe_grouping_bytes(int64_t ncols, int32_t topk) {
     if (ncols < 1 || ncols > ROUTE_MAX_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return 0;
     const size_t R = (size_t)ncols * (size_t)topk;
-    // header, expert[R], offset[R+1], route[R], then eight words of padding
-    // so that readers may load eight words from any route entry
-    const size_t bytes = 4 * (4 + 3 * R + 1 + 8);
+    // header, expert[R], offset[R+1], route[R], eight words of padding (so
+    // that readers may load eight words from any route entry), the table
+    const size_t bytes = 4 * ((size_t)grouping_table_word((int64_t)R) + 4 * R);
     return (bytes + 255) & ~(size_t)255;
 }
 

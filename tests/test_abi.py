@@ -51,8 +51,10 @@ def test_abi_version_and_status_strings():
 
 def test_grouping_bytes():
     L = moeq8.lib()
-    assert L.moe_grouping_bytes(8, 8) == 1024           # 4*(4 + 3*64 + 1 + 8) = 820 -> 1024
-    assert L.moe_grouping_bytes(1, 8) == 256
+    # header, expert[R], offset[R+1], route[R], 8 words of padding, rounded to
+    # 4 words, then a 4-word table entry per group; whole 256-byte units
+    assert L.moe_grouping_bytes(8, 8) == 2048           # 4*(208 + 4*64) = 1856 -> 2048
+    assert L.moe_grouping_bytes(1, 8) == 512            # 4*(40 + 4*8) = 288 -> 512
     assert L.moe_grouping_bytes(0, 8) == 0 and L.moe_grouping_bytes(9, 8) == 0
     assert L.moe_grouping_bytes(1, 17) == 0
 

@@ -234,6 +234,16 @@ def _grouping_words(gt):
     return host(gt).view(np.int32)
 
 
+def _defined_grouping_words(gt):
+    """The words a grouping defines: header, expert[R], offset[R+1], route[R]
+    and the table entries of the active groups (padding and unused entries
+    hold whatever the buffer held before)."""
+    words = _grouping_words(gt)
+    R = int(words[2]) * int(words[3])
+    t0 = (4 + 3 * R + 1 + 8 + 3) // 4 * 4
+    return (list(words[:4 + 3 * R + 1]), list(words[t0:t0 + 4 * int(words[0])]))
+
+
 def _check_grouping(words, ids_ref):
     R = ids_ref.size
     n_active, n_valid, ncols, topk = words[:4]
@@ -243,9 +253,14 @@ def _check_grouping(words, ids_ref):
     expert = words[4:4 + R]
     offset = words[4 + R:4 + 2 * R + 1]
     route = words[4 + 2 * R + 1:4 + 3 * R + 1]
+    # per-group table {expert, first route, end, 0} at a 16-byte boundary
+    # after route[] and eight words of padding
+    t0 = (4 + 3 * R + 1 + 8 + 3) // 4 * 4
+    table = words[t0:t0 + 4 * R].reshape(R, 4)
     for a, (e, routes) in enumerate(groups):
         assert expert[a] == e
         assert list(route[offset[a]:offset[a + 1]]) == routes
+        assert list(table[a]) == [e, offset[a], offset[a + 1], 0]
 
 
 @pytest.mark.parametrize("c,n_exp,topk,local", [(1, 256, 8, 256), (5, 256, 8, 256), (8, 256, 8, 128),
@@ -467,9 +482,8 @@ def test_route_topk_quantize_equals_separate():
     xq, ids, w, g = moeq8.moe_route_topk_quantize(x, lg, topk, bias=b, owner_slot=own, n_local_expert=128)
     ids2, w2, g2 = moeq8.moe_route_topk(lg, topk, bias=b, owner_slot=own, n_local_expert=128)
     assert torch.equal(xq, moeq8.q8_1_quantize_rows(x))
-    nw = 4 + 3 * c * topk + 1                               # defined words of the grouping
     assert torch.equal(ids, ids2) and bits_equal(w, w2)
-    assert torch.equal(g.view(torch.int32)[:nw], g2.view(torch.int32)[:nw])
+    assert _defined_grouping_words(g) == _defined_grouping_words(g2)
 
 
 @pytest.mark.parametrize("c,n_exp,hidden,inter,share_rows,half", [(8, 32, 1024, 256, 512, 0),
@@ -500,9 +514,8 @@ def test_fused_layer_equals_unfused(c, n_exp, hidden, inter, share_rows, half):
     ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wa, fused=False)
     ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wb, fused=True)
     torch.cuda.synchronize()
-    nw = 4 + 3 * c * topk + 1
     assert torch.equal(wa.xq, wb.xq) and torch.equal(wa.ids, wb.ids)
-    assert torch.equal(wa.grouping.view(torch.int32)[:nw], wb.grouping.view(torch.int32)[:nw])
+    assert _defined_grouping_words(wa.grouping) == _defined_grouping_words(wb.grouping)
     assert bits_equal(wa.weights, wb.weights)
     assert bits_equal(wa.hs, wb.hs) and bits_equal(wa.ys, wb.ys)
     valid = (host(wa.ids) >= 0)
