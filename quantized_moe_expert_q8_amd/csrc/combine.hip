@@ -1,24 +1,37 @@
 // Weighted masked combine (lucebox PR #826, the routed combine commit: route
 // weighting and route sum in one launch, rounding the products and the sums
 // separately as the unfused ops do; the review of moe_combine_masked_kernel: a
-// route masked to -1 is skipped before anything is read for it).
+// route masked to -1 contributes nothing).
 #include "moeq8_device.hpp"
 #include "moeq8_host.hpp"
 
 namespace moeq8 {
 
+// Every slot's id, weight and y value are read up front, so the slots cost one
+// round trip rather than one each; a masked slot's y row (allocated like every
+// other route's) is read but never used: the sum skips it by selection, so
+// nothing it holds, NaN included, reaches the output.
+template <int KMAX>
 __global__ void k_combine(const float* __restrict__ y, const int32_t* __restrict__ ids,
                           const float* __restrict__ w, int topk, int64_t n,
                           float* __restrict__ out) {
     const int j = blockIdx.y;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
+    int id[KMAX];
+    float wt[KMAX], yv[KMAX];
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+        const int r = j * topk + min(s, topk - 1);      // in range for every s
+        id[s] = ids[r];
+        wt[s] = w[r];
+        yv[s] = y[(int64_t)r * n + i];
+    }
     float acc = 0.0f;  // +0 then the valid products in slot order
-    for (int s = 0; s < topk; ++s) {
-        const int r = j * topk + s;
-        if (ids[r] < 0) continue;
-        const float prod = w[r] * y[(int64_t)r * n + i];
-        acc = acc + prod;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+        const float sum = acc + wt[s] * yv[s];
+        acc = (s < topk && id[s] >= 0) ? sum : acc;
     }
     out[(int64_t)j * n + i] = acc;
 }
@@ -35,7 +48,11 @@ extern "C" int moe_combine(const float* y, const int32_t* ids, const float* weig
     if (n == 0) return MOEQ8_OK;
     const int64_t bx = (n + 255) / 256;
     if (bx > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
-    hipLaunchKernelGGL(k_combine, dim3((uint32_t)bx, (uint32_t)ncols), dim3(256), 0,
-                       (hipStream_t)stream, y, ids, weights, topk, n, out);
+    const dim3 grid((uint32_t)bx, (uint32_t)ncols);
+    if (topk <= 8)
+        hipLaunchKernelGGL(k_combine<8>, grid, dim3(256), 0, (hipStream_t)stream, y, ids, weights, topk, n, out);
+    else
+        hipLaunchKernelGGL(k_combine<MOEQ8_MAX_TOPK>, grid, dim3(256), 0, (hipStream_t)stream, y, ids,
+                           weights, topk, n, out);
     return check_launch();
 }
