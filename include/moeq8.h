@@ -14,8 +14,8 @@
  *   - the commit on the fused routed combine: owner route mask, route weighting
  *     and route sum in one launch, products and sums rounded separately;
  *     clamped routed SwiGLU;
- *   - the review finding on moe_combine_masked_kernel: a route masked to -1
- *     contributes nothing, and its id is never used as an index.
+ *   - the review finding on moe_combine_masked_kernel: a route masked to -1 is
+ *     skipped and its slot never read.
  *
  * Formats (the pages name them and print no layout; this is the layout used):
  *   Q8_0 block, 34 bytes: fp16 d (little-endian), int8 qs[32]; value = d * q.
@@ -224,11 +224,8 @@ int moe_route_topk_quantize(const float* x, int64_t x_row_stride, int64_t k, voi
  * a9: weighted masked combine.
  *   out[j][i] = sum over slots s ascending with ids[j][s] >= 0 of
  *               fl(weights[j][s] * y[j][s][i])  (fp32: each product rounded, then
- *               added in slot order; a masked slot's y row is read with the
- *               others but never used, so whatever it holds, NaN included,
- *               does not reach out)
- *   y fp32 [ncols][topk][n] (every row allocated, masked ones included);
- *   ids int32 [ncols][topk]; weights fp32 [ncols][topk];
+ *               added in slot order; masked slots are never read)
+ *   y fp32 [ncols][topk][n]; ids int32 [ncols][topk]; weights fp32 [ncols][topk];
  *   out fp32 [ncols][n] (fully overwritten; all-masked columns give 0).
  * ------------------------------------------------------------------------- */
 int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_t ncols,

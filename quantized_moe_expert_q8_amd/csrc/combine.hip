@@ -1,16 +1,16 @@
 // Weighted masked combine (lucebox PR #826, the routed combine commit: route
 // weighting and route sum in one launch, rounding the products and the sums
 // separately as the unfused ops do; the review of moe_combine_masked_kernel: a
-// route masked to -1 contributes nothing).
+// route masked to -1 is skipped before anything is read for it).
 #include "moeq8_device.hpp"
 #include "moeq8_host.hpp"
 
 namespace moeq8 {
 
-// Every slot's id, weight and y value are read up front, so the slots cost one
-// round trip rather than one each; a masked slot's y row (allocated like every
-// other route's) is read but never used: the sum skips it by selection, so
-// nothing it holds, NaN included, reaches the output.
+// All slots' ids and weights are read first (one round trip of scalar
+// loads), then the y values of the unmasked slots, all issued before any is
+// used (a second round trip, instead of one per slot).  A masked slot's y row
+// is never read, and the sum skips it by selection.
 template <int KMAX>
 __global__ void k_combine(const float* __restrict__ y, const int32_t* __restrict__ ids,
                           const float* __restrict__ w, int topk, int64_t n,
@@ -23,15 +23,19 @@ __global__ void k_combine(const float* __restrict__ y, const int32_t* __restrict
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) {
         const int r = j * topk + min(s, topk - 1);      // in range for every s
-        id[s] = ids[r];
+        id[s] = s < topk ? ids[r] : -1;
         wt[s] = w[r];
-        yv[s] = y[(int64_t)r * n + i];
+    }
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+        yv[s] = 0.0f;
+        if (id[s] >= 0) yv[s] = y[(int64_t)(j * topk + s) * n + i];
     }
     float acc = 0.0f;  // +0 then the valid products in slot order
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) {
         const float sum = acc + wt[s] * yv[s];
-        acc = (s < topk && id[s] >= 0) ? sum : acc;
+        acc = id[s] >= 0 ? sum : acc;
     }
     out[(int64_t)j * n + i] = acc;
 }
