@@ -8,10 +8,11 @@
 // experts [l*PER, (l+1)*PER) (contiguous, so among equal keys the lowest lane
 // holds the lowest index).  Keys are compared as order-preserving u32 images
 // of the fp32 key (the same order as the fp32 comparison for non-NaN keys, -0
-// canonicalised to +0).  Each of the topk rounds takes the lane-local best
-// untaken key, the wave maximum (DPP within rows of 16, then the four rows),
-// and the lowest lane holding it (ballot): exact (key descending, expert
-// ascending) selection.  Rounds run in slot order, so the weight sum is
+// canonicalised to +0).  Each lane sorts its entries once (stable, key
+// descending); each of the topk rounds takes the wave maximum of the lanes'
+// first entries (DPP within rows of 16, then the four rows) and the lowest
+// lane holding it (ballot), whose list then shifts by one: exact (key
+// descending, expert ascending) selection.  Rounds run in slot order, so the weight sum is
 // accumulated there in slot order; lane s keeps slot s.  Then the routes are
 // sorted by (local expert, route index) for the grouping: with ballots in one
 // wave when there are at most 64 routes, else from the ids in LDS.
@@ -90,37 +91,48 @@ __device__ __forceinline__ void route_body(
         }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            // sigmoid in fp64, rounded once to fp32; key = score + bias in fp32
+            // sigmoid in fp64, rounded once to fp32; key = score + bias in fp32.
+            // An expert past n_expert gets key 0, below every real key (the
+            // ordered image of a finite float is positive).
             score[i] = (float)(1.0 / (1.0 + exp(-(double)lg[i])));
-            key[i] = ordered_key(bias ? score[i] + bs[i] : score[i]);
+            key[i] = ((valid >> i) & 1u) ? ordered_key(bias ? score[i] + bs[i] : score[i]) : 0u;
         }
-        uint32_t taken = 0;
+        // Sort the lane's entries once by key, descending: odd-even
+        // transposition swapping only on a strictly larger key, which keeps
+        // equal keys in expert order.  The lane's candidate is then always
+        // entry 0, and the lane that wins a round shifts its list by one.
+#pragma unroll
+        for (int pass = 0; pass < PER; ++pass) {
+#pragma unroll
+            for (int i = pass & 1; i + 1 < PER; i += 2) {
+                const bool sw = key[i + 1] > key[i];
+                const uint32_t k0 = key[i], k1 = key[i + 1];
+                const float s0 = score[i], s1 = score[i + 1];
+                const int o0 = own[i], o1 = own[i + 1];
+                key[i] = sw ? k1 : k0;
+                key[i + 1] = sw ? k0 : k1;
+                score[i] = sw ? s1 : s0;
+                score[i + 1] = sw ? s0 : s1;
+                own[i] = sw ? o1 : o0;
+                own[i + 1] = sw ? o0 : o1;
+            }
+        }
+        // topk <= n_expert (checked on the host), so every round has a
+        // positive maximum and a winner
         for (int s = 0; s < topk; ++s) {
-            uint32_t best = 0;
-            int bi = -1;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const bool cand = ((valid & ~taken) >> i) & 1u;
-                if (cand && (bi < 0 || key[i] > best)) {
-                    best = key[i];
-                    bi = i;
-                }
-            }
-            const uint32_t wmax = wave_max_u32(bi >= 0 ? best : 0u);
-            const uint64_t mask = __ballot(bi >= 0 && best == wmax);
+            const uint32_t wmax = wave_max_u32(key[0]);
+            const uint64_t mask = __ballot(key[0] == wmax);
             const int w = (int)__builtin_ctzll(mask);          // lowest lane: lowest expert
-            float my_score = 0.0f;
-            int my_own = -1;
+            const float win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(score[0]), w));
+            const int win_own = __builtin_amdgcn_readlane(own[0], w);
+            const bool shift = lane == w;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                if (i == bi) {
-                    my_score = score[i];
-                    my_own = own[i];
-                }
+            for (int i = 0; i + 1 < PER; ++i) {
+                key[i] = shift ? key[i + 1] : key[i];
+                score[i] = shift ? score[i + 1] : score[i];
+                own[i] = shift ? own[i + 1] : own[i];
             }
-            if (lane == w) taken |= 1u << bi;
-            const float win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_score), w));
-            const int win_own = __builtin_amdgcn_readlane(my_own, w);
+            key[PER - 1] = shift ? 0u : key[PER - 1];
             sum = sum + win;                                    // slot order
             if (lane == s) {
                 slot_score = win;
