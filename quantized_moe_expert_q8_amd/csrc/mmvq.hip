@@ -165,7 +165,7 @@ __device__ __forceinline__ float chain_groups(float v, int lane) {
     }
 }
 
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32>
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX>
 __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
     constexpr int RPW = 4 / G;                         // rows per row set
     const int lane = threadIdx.x & 63;
@@ -324,6 +324,37 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
         }
 
         const uint8_t* act_base = (GROUPED && !routed) ? s_act_q : act_q;
+        if constexpr (STX && !ACT_F32) {
+            // Copy this pass's q8_1 activation chunks into LDS once for the
+            // workgroup (column c at c * act_row_bytes), with 16-byte
+            // coalesced loads straight into LDS, the waves taking turns by
+            // 1 KB.  Read per lane from global memory instead, every wave
+            // would fetch the same bytes, 72 scattered bytes per lane.  The
+            // host stages only rows of a multiple of 16 bytes, so no piece
+            // straddles two columns.
+            __syncthreads();                               // a previous pass may still read LDS
+            const int total = nc * (int)act_row_bytes;
+            for (int k = wave; k * 1024 < total; k += WAVES_PER_WG) {
+                const int pos = k * 1024 + lane * 16;
+                int c = 0;
+#pragma unroll
+                for (int q = 1; q < MAX_COLS; ++q) c += (pos >= q * (int)act_row_bytes) ? 1 : 0;
+                int ar = c0 + c;
+                if (routed) {
+                    const int r = w8[c];                   // c < nc wherever pos < total
+                    ar = (r < 0 || r >= R) ? 0 : r / act_route_div;
+                }
+                if (pos < total)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(act_base + (int64_t)ar * act_row_bytes + (pos - c * (int)act_row_bytes)),
+                        (void*)(lds_act + k * 1024), 16, 0, 0);
+            }
+            // this wave's copies (and the weight loads issued before them)
+            // have landed; after the barrier so have everyone's
+            __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+            __syncthreads();
+            act_base = lds_act;
+        }
         if constexpr (ACT_F32) {
             // Quantise this item's activation rows into LDS with the block rule
             // of q8_1_quantize_rows.  Two neighbouring lanes share a block, 16
@@ -377,7 +408,9 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             for (int c = 0; c < MAX_COLS; ++c) {
                 if (c < nc) {
                     XChunk xc;
-                    if constexpr (ACT_F32) {
+                    if constexpr (ACT_F32 || STX) {
+                        // staged in LDS (a lane outside the matrix reads
+                        // chunk 0 of the column and adds +0 below)
                         load_x_chunk_lds(xc, act_base + (int64_t)c * act_row_bytes +
                                                  (int64_t)crel * X_CHUNK_BYTES);
                     } else if (cvalid) {
@@ -391,7 +424,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 #pragma unroll
                         for (int m = 0; m < NMAT; ++m) {
                             const float d = chunk_dot(wc[u][m], xc);
-                            acc[c][u][m] += (UNCOND && !ok[u]) ? 0.0f : d;
+                            acc[c][u][m] += ((UNCOND || STX) && !ok[u]) ? 0.0f : d;
                         }
                 }
             }
@@ -472,10 +505,10 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 
 // One work item = one row block: of one active expert (grouped), of the dense
 // extra matrix (grouped launches with a shared part), or of the one matrix.
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32>
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX>
 __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_act[];
-    mmvq_item<G, NMAT, U, GROUPED, ACT_F32>(p, blockIdx.x, lds_act);
+    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX>(p, blockIdx.x, lds_act);
 }
 
 __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, float* h) {
@@ -522,18 +555,46 @@ constexpr int u_for(int nmat, bool act_f32) { return nmat == 2 ? U_ROWSETS : act
 
 int rows_per_wg_for(const Shape& s, int u) { return WAVES_PER_WG * u * (4 / s.G); }
 
-template <int NMAT, bool GROUPED, bool ACT_F32, int U = u_for(NMAT, ACT_F32)>
+template <int NMAT, bool GROUPED, bool ACT_F32, bool STX, int U = u_for(NMAT, ACT_F32)>
+int launch_shape(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
+    const dim3 block(64 * WAVES_PER_WG);
+    switch (s.G) {
+        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U, GROUPED, ACT_F32, STX>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U, GROUPED, ACT_F32, STX>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U, GROUPED, ACT_F32, STX>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+    }
+    return check_launch();
+}
+
+// LDS for q8_1 activations staged per workgroup (ncols rows of the slice),
+// or 0 when staging does not pay or does not fit.  Staging pays when one work
+// item carries many columns (measured on a 1024-row pair at K = 4096 with 8
+// columns: 9.4 -> 8.1 us; with 1 column it costs 6%), so it is used for the
+// dense launches from 4 columns on.  A grouped launch's routed items carry
+// about ncols*topk / active-expert columns (1-2 at 8 columns, top-8), where
+// staging measured slower, so grouped launches never stage.  Rows must be a
+// whole number of 16-byte pieces and all rows must fit in 64 KB.
+size_t staged_act_bytes(bool grouped, int64_t ncols, int64_t act_row_bytes) {
+    const int64_t bytes = ncols * act_row_bytes;
+    const bool stage = !grouped && ncols >= 4 && act_row_bytes % 16 == 0 && bytes <= 64 * 1024;
+    return stage ? (size_t)bytes : 0;
+}
+
+template <int NMAT, bool GROUPED, bool ACT_F32>
 int launch_mmvq(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
     p.nsteps = s.nsteps;
     if (grid <= 0) return MOEQ8_OK;
     if (grid > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
-    const dim3 block(64 * WAVES_PER_WG);
-    switch (s.G) {
-        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
-        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
-        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U, GROUPED, ACT_F32>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+    if constexpr (ACT_F32) {
+        return launch_shape<NMAT, GROUPED, true, false>(p, s, grid, lds_bytes, stream);
+    } else if constexpr (!GROUPED) {
+        // a dense launch has one pass of p.ncols <= MAX_COLS columns
+        const size_t staged = staged_act_bytes(false, p.ncols, p.act_row_bytes);
+        if (staged) return launch_shape<NMAT, false, false, true>(p, s, grid, staged, stream);
+        return launch_shape<NMAT, false, false, false>(p, s, grid, 0, stream);
+    } else {
+        return launch_shape<NMAT, true, false, false>(p, s, grid, 0, stream);
     }
-    return check_launch();
 }
 
 int validate_matrix(const void* w, int64_t w_row_stride_bytes, int64_t n, int64_t k,
