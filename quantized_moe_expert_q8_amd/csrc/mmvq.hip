@@ -64,7 +64,8 @@ struct MmvqParams {
     int32_t nsteps;             // G == 1: rounds to walk (same for m and s)
     int32_t ncols;
     int32_t topk;
-    int32_t act_route_div;      // grouped: activation row of route r is r / act_route_div
+    int32_t act_route_mul;      // grouped: activation row of route r is (r * act_route_mul) >> 16
+                                // = r / d for d = 1 (down) or topk (gate/up)
     int32_t rows_per_wg;
     int32_t max_active;         // grouped: bound on the device-side active count
     const uint8_t* act;         // q8_1 activation rows
@@ -198,7 +199,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
     float* out0 = p.out0;
     float* s_out = p.s_out;
     const int64_t act_row_bytes = p.act_row_bytes;
-    const int32_t act_route_div = p.act_route_div;
+    const int32_t act_route_mul = p.act_route_mul;
     const int32_t nsteps = p.nsteps;
     // The arguments the decode and the first loads need arrive in one batch
     // of scalar loads at entry; left alone, the compiler fetches each after
@@ -206,7 +207,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
     asm volatile("" ::"s"(w0), "s"(w1), "s"(row_stride), "s"(n_rows), "s"(nchunks), "s"(chunk0),
                  "s"(r0), "s"(m_wg), "s"(s_wg), "s"(expert_stride), "s"(n_local), "s"(p_ncols),
                  "s"(p_topk), "s"(rows_per_wg), "s"(grouping), "s"(act_q), "s"(s_act_q), "s"(out0),
-                 "s"(s_out), "s"(act_row_bytes), "s"(act_route_div), "s"(nsteps));
+                 "s"(s_out), "s"(act_row_bytes), "s"(act_route_mul), "s"(nsteps));
     int64_t row_block = item;
     int ncols = p_ncols;
     int route_begin = 0;
@@ -313,7 +314,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             for (int c = 0; c < MAX_COLS; ++c) {
                 const int r = (c >= nc || w8[c] < 0 || w8[c] >= R) ? -1 : w8[c];
                 orow[c] = routed ? r : c0 + c;
-                arow[c] = routed ? (r < 0 ? 0 : r / act_route_div) : c0 + c;
+                arow[c] = routed ? (r < 0 ? 0 : (r * act_route_mul) >> 16) : c0 + c;
             }
         } else {
 #pragma unroll
@@ -342,7 +343,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                 int ar = c0 + c;
                 if (routed) {
                     const int r = w8[c];                   // c < nc wherever pos < total
-                    ar = (r < 0 || r >= R) ? 0 : r / act_route_div;
+                    ar = (r < 0 || r >= R) ? 0 : (r * act_route_mul) >> 16;
                 }
                 if (pos < total)
                     __builtin_amdgcn_global_load_lds(
@@ -376,7 +377,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                     int ar = c0 + c;
                     if (routed) {
                         const int r = w8[c];               // c < nc here
-                        ar = (r < 0 || r >= R) ? 0 : r / act_route_div;
+                        ar = (r < 0 || r >= R) ? 0 : (r * act_route_mul) >> 16;
                     }
                     const float* sp = src + (int64_t)ar * stride + (int64_t)b * QK + (u & 1) * (QK / 2);
 #pragma unroll
@@ -724,7 +725,13 @@ extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w
     p.n_local = n_local_expert;
     p.ncols = (int32_t)ncols;
     p.topk = topk;
-    p.act_route_div = pair ? topk : 1;
+    // route r's activation row is r / d, d = topk for gate/up (a column per
+    // route group) or 1 for down (a row per route); r < ncols*topk <= 128 and
+    // d <= 16, where (r * ceil(65536 / d)) >> 16 is exactly r / d (the
+    // multiplier's excess adds under 128/65536 to r/d, whose fractional part
+    // is at most 15/16)
+    const int32_t route_div = pair ? topk : 1;
+    p.act_route_mul = (65536 + route_div - 1) / route_div;
     p.act = (const uint8_t*)act;
     p.act_row_bytes = (k / QK) * Q81_BYTES;
     if (f32) {
