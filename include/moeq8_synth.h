@@ -1,4 +1,6 @@
-/* libmoeq8 synthetic-input helper: fills device memory with Q8_0 weight blocks
+/* libmoeq8 benchmark helpers (not part of the FFN path).
+ *
+ * 1. Synthetic inputs: fills device memory with Q8_0 weight blocks
  * drawn from a counter-based generator, for benchmark-sized weight sets (tens of
  * GB) that would take minutes to draw and quantise on the host.  Not part of the
  * FFN path; the same generator is implemented independently on the host so any
@@ -40,6 +42,15 @@ uint64_t moeq8_synth_stream_key(uint32_t seed, uint32_t layer, uint32_t expert, 
 int moeq8_synth_q8_0_fill(void* dst, int64_t n_mats, int64_t blocks_per_mat,
                           int64_t mats_per_layer, uint32_t seed, uint32_t layer0,
                           uint32_t expert0, uint32_t matrix, void* stream);
+
+/* 2. Streaming-read ceiling: reads `bytes` of device memory at `buf` once
+ * (`bytes` a multiple of 16, `buf` 16-byte aligned), each workgroup 64 KB with
+ * coalesced 16-byte loads, and folds the words into an xor that is written to
+ * `sink` (one uint32, device memory) only if it equals 0x9E3779B9, so the
+ * loads cannot be dropped.  Measures what a plain read of the same buffers
+ * achieves, the ceiling a bandwidth-bound kernel is compared with.  Enqueued
+ * on `stream`; returns 0 or a negative moeq8 status. */
+int moeq8_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

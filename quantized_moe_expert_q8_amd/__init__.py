@@ -24,4 +24,5 @@ from .ops import (  # noqa: F401
     moe_route_topk_quantize,
     moe_combine,
     synth_q8_0_fill,
+    stream_read,
 )

@@ -72,3 +72,36 @@ extern "C" int moeq8_synth_q8_0_fill(void* dst, int64_t n_mats, int64_t blocks_p
                        matrix);
     return moeq8::check_launch();
 }
+
+namespace {
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+constexpr int64_t STREAM_WG_BYTES = 64 * 1024;
+
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4v* __restrict__ p, int64_t n16,
+                                                     uint32_t* sink) {
+    const int64_t base = (int64_t)blockIdx.x * (STREAM_WG_BYTES / 16);
+    u32x4v v[STREAM_WG_BYTES / 16 / 256];
+#pragma unroll
+    for (int i = 0; i < STREAM_WG_BYTES / 16 / 256; ++i) {
+        const int64_t idx = base + i * 256 + threadIdx.x;
+        v[i] = idx < n16 ? p[idx] : u32x4v{0u, 0u, 0u, 0u};
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < STREAM_WG_BYTES / 16 / 256; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+}  // namespace
+
+extern "C" int moeq8_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes < 0) return MOEQ8_EINVAL;
+    if ((((uintptr_t)buf) & 15u) || (bytes & 15) || (((uintptr_t)sink) & 3u)) return MOEQ8_EALIGN;
+    if (bytes == 0) return MOEQ8_OK;
+    const int64_t blocks = (bytes + STREAM_WG_BYTES - 1) / STREAM_WG_BYTES;
+    if (blocks > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_stream_read, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4v*)buf, bytes / 16, sink);
+    return moeq8::check_launch();
+}

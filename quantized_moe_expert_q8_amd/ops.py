@@ -381,3 +381,14 @@ def synth_q8_0_fill(dst: torch.Tensor, n_mats: int, blocks_per_mat: int, mats_pe
     call("moeq8_synth_q8_0_fill", _ptr(dst, offset_bytes), n_mats, blocks_per_mat, mats_per_layer,
          seed, layer0, expert0, matrix, _stream(dst))
     return dst
+
+
+def stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, offset_bytes: int = 0):
+    """Read nbytes of buf (from offset_bytes) once with a plain coalesced
+    streaming kernel: the read ceiling a bandwidth-bound launch is compared
+    with.  sink: a device tensor of at least 4 bytes."""
+    _cuda(buf, "buf")
+    _cuda(sink, "sink")
+    _need(buf, "buf", nbytes, offset_bytes)
+    _need(sink, "sink", 4)
+    call("moeq8_stream_read", _ptr(buf, offset_bytes), nbytes, _ptr(sink), _stream(buf))

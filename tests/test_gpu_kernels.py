@@ -579,3 +579,29 @@ def test_fused_layer_all_routes_masked():
     torch.cuda.synchronize()
     assert np.all(host(ws.ids) == -1)
     assert np.all(host(out) == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# benchmark helper: the streaming-read ceiling reads every word once
+# ---------------------------------------------------------------------------
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_stream_read_reads_every_word(where):
+    """A buffer of zeros with one marker word: the xor of the 16-byte piece
+    holding it equals the marker, so the sink is written only if that piece
+    was read (the size is not a whole number of 64 KB workgroups)."""
+    say(f"stream read marker {where}")
+    n = 70001 * 16
+    buf = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    at = 0 if where == "first" else n - 4
+    buf[at:at + 4] = torch.tensor([0xB9, 0x79, 0x37, 0x9E], dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(4, dtype=torch.uint8, device=DEV)
+    moeq8.stream_read(buf, n, sink)
+    torch.cuda.synchronize()
+    assert int(host(sink.view(torch.int32))[0]) == 0x9E3779B9 - (1 << 32)
+    clean = torch.zeros(4, dtype=torch.uint8, device=DEV)
+    # the same buffer without the marker's piece: nothing is written
+    moeq8.stream_read(buf, n - 16, clean, offset_bytes=16 if where == "first" else 0)
+    torch.cuda.synchronize()
+    assert int(host(clean.view(torch.int32))[0]) == 0
