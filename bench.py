@@ -455,71 +455,62 @@ def main():
 
 def sweep(torch, workloads, moeq8, ml, args):
     """Routed layer, 256 experts, top-8, at 1..8 columns; 4 weight replicas
-    (13.7 GB) rotate so the 256 MB Infinity Cache cannot serve the reads."""
+    (13.7 GB) rotate so the 256 MB Infinity Cache cannot serve the reads.
+    Per column count: the layer (graph of the four-launch layers), the grouped
+    gate/up launch alone (graph of its launches, HIP events) and the
+    streaming-read ceiling for the same bytes per launch."""
     cfg = workloads.CONFIGS["verify_e256_c5"]
     hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
     reps = 4
     bank = Bank(moeq8, torch, reps, n_exp, hidden, inter, 4)
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
     out = []
     for cols in (1, 2, 4, 5, 8):
         xs, lgs, bs = layer_inputs(torch, workloads, 4, reps, cols, hidden, n_exp)
-        ws = ml.Workspace(cols, hidden, inter, topk, 0, "cuda")
+        wss = [ml.Workspace(cols, hidden, inter, topk, 0, "cuda") for _ in range(reps)]
         experts = [bank.experts(ml, l) for l in range(reps)]
-        n_active, n_valid = [], []
-        for l in range(reps):
-            moeq8.moe_route_topk(lgs[l], topk, bias=bs[l], ids=ws.ids, weights=ws.weights,
-                                 grouping=ws.grouping)
-            words = ws.grouping.cpu().numpy().view(np.int32)
-            n_active.append(int(words[0]))
-            n_valid.append(int(words[1]))
 
         def step():
             for l in range(reps):
-                ml.forward(xs[l], lgs[l], bs[l], None, n_exp, experts[l], None, ws)
+                ml.forward(xs[l], lgs[l], bs[l], None, n_exp, experts[l], None, wss[l])
 
         step()
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        for _ in range(5):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_active, n_valid = [], []
+        for l in range(reps):
+            words = wss[l].grouping.cpu().numpy().view(np.int32)
+            n_active.append(int(words[0]))
+            n_valid.append(int(words[1]))
         n = max(20, args.steps)
-        e0.record()
-        for _ in range(n):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / n / reps
+        ms = time_graph(torch, step, n) / reps
         lb = float(np.mean([layer_bytes(n_active[l], n_valid[l], cols, hidden, inter, topk, 0)
                             for l in range(reps)]))
-        # dominant kernel alone, eager with events
-        evs = []
-        cur = torch.cuda.current_stream()
-        for _ in range(3):
+
+        def gate_up_only():
             for l in range(reps):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                moeq8.q8_1_quantize_rows(xs[l], out=ws.xq)
-                moeq8.moe_route_topk(lgs[l], topk, bias=bs[l], ids=ws.ids, weights=ws.weights,
-                                     grouping=ws.grouping)
-                a.record(cur)
-                moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, ws.xq,
-                                       ws.grouping, n=inter, k=hidden, n_local_expert=n_exp, ncols=cols,
-                                       topk=topk, out=ws.h)
-                b.record(cur)
-                evs.append((l, a, b))
-        torch.cuda.synchronize()
-        gu_t = sum(a.elapsed_time(b) for _, a, b in evs)
-        gu_b = sum(gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter) for l, _, _ in evs)
+                moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, wss[l].xq,
+                                       wss[l].grouping, n=inter, k=hidden, n_local_expert=n_exp,
+                                       ncols=cols, topk=topk, out=wss[l].h)
+
+        gu_b = [gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter) for l in range(reps)]
+        read_b = [int(b) // 16 * 16 for b in gu_b]
+
+        def stream_only():
+            for l in range(reps):
+                moeq8.stream_read(bank.gate[l], read_b[l], sink)
+
+        gu_us = time_graph(torch, gate_up_only, n) / reps * 1e3
+        st_us = time_graph(torch, stream_only, n) / reps * 1e3
+        gu_gbps = float(np.mean(gu_b)) / (gu_us * 1e-6) / 1e9
+        st_gbps = float(np.mean(read_b)) / (st_us * 1e-6) / 1e9
         rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2),
                "layer_us": round(ms * 1e3, 2), "layers_per_s": round(1e3 / ms, 1),
                "effective_gbps": round(lb / (ms * 1e-3) / 1e9, 1),
-               "gate_up_gbps": round(gu_b / (gu_t * 1e-3) / 1e9, 1)}
+               "gate_up_us": round(gu_us, 2), "gate_up_gbps": round(gu_gbps, 1),
+               "gate_up_frac_of_peak": round(gu_gbps / HBM_PEAK_GBPS, 4),
+               "ceiling_gbps": round(st_gbps, 1), "gate_up_frac_of_ceiling": round(gu_gbps / st_gbps, 4)}
         log(f"sweep {rec}")
         out.append(rec)
-        del g
     del bank
     torch.cuda.empty_cache()
     return out
