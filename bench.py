@@ -199,6 +199,7 @@ def layer_bytes(n_active, n_valid, cols, hidden, inter, topk, shared_rows):
     if shared_rows:
         b += shared_gate_up_bytes(cols, hidden, shared_rows)         # pair weights, hs written
         b += shared_down_bytes(cols, hidden, shared_rows)            # slice, hs read, ys written
+        b += cols * hidden * 4                                        # ys read by the combine
     return b
 
 
@@ -280,7 +281,8 @@ def main():
 
     def step():
         for l in range(L):
-            ml.forward(xs[l], lgs[l], bs[l], owner, n_local, experts[l], shared[l], wss[l])
+            ml.forward(xs[l], lgs[l], bs[l], owner, n_local, experts[l], shared[l], wss[l],
+                       add_shared=True)
 
     # eager warm-up, then capture the step as one graph
     step()

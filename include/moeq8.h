@@ -231,6 +231,15 @@ int moe_route_topk_quantize(const float* x, int64_t x_row_stride, int64_t k, voi
 int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
                 int32_t topk, int64_t n, float* out, void* stream);
 
+/* The combine with the shared expert's output added (the MoE block's whole
+ * output; the routed-combine commit joins the shared-expert slice with the
+ * routed partials):
+ *   out[j][i] = moe_combine's out[j][i] + shared_y[j][i]
+ * one fp32 add after the routed slot sum.  shared_y fp32 [ncols][n], not NULL;
+ * it may be the same buffer as out.  Otherwise as moe_combine. */
+int moe_combine_shared(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
+                       int32_t topk, int64_t n, const float* shared_y, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

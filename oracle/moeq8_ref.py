@@ -29,12 +29,16 @@ clamp constant or routing rule.  Readings taken here:
   R4  SwiGLU-DS4: h = silu(min(g, 7)) * clamp(u, -7, 7).
   R5  router: score = sigmoid(logit) rounded to fp32; key = score + bias (fp32
       add); top-k by (key descending, expert index ascending); weights =
-      score / sum of the k selected scores (bias used for selection only);
-      a route whose expert is not local is masked to id -1 but still counts in
-      the normalising sum.
-  R6  combine: out[j] = sum over slots s ascending with id >= 0 of w[j,s]*y[j,s].
-  R7  the activations handed to a quantiser are fp32 tensors, so the SwiGLU
+      score / sum of the k selected scores (bias used for selection only).
+  R6  owner mask: a route whose expert is not local is masked to id -1 but
+      still counts in the normalising sum; masked slots are never read.
+  R7  combine: out[j] = sum over slots s ascending with id >= 0 of w[j,s]*y[j,s].
+  R8  the activations handed to a quantiser are fp32 tensors, so the SwiGLU
       output is rounded to fp32 before it is quantised for the down projection.
+  R15 the MoE block's output is the routed experts' weighted sum plus the
+      shared expert's output: one add after the routed sum.
+  (R9-R14 concern the launch layouts and the synthetic workloads, not what
+  this module computes.)
 
 Floating point here is fp64 unless a step is defined by fp32 rounding (the
 quantisers and the router keys), where it is done in fp32 exactly as defined.
@@ -240,10 +244,14 @@ def group_routes(ids: np.ndarray):
 # a9: weighted masked combine
 # ---------------------------------------------------------------------------
 
-def moe_combine(y, ids, weights):
+def moe_combine(y, ids, weights, shared=None):
     """out[j, n] = sum over slots s (ascending) with ids[j,s] >= 0 of
-    weights[j,s] * y[j,s,n], in fp64 (R6).  Masked slots are never read, as the
-    review of moe_combine_masked_kernel requires."""
+    weights[j,s] * y[j,s,n], in fp64 (R6, R7).  Masked slots are never read, as the
+    review of moe_combine_masked_kernel requires.
+
+    shared [C, n] (optional): the shared expert's output for the same columns,
+    added once after the routed sum (R15; the routed-combine commit queues the
+    shared-expert slice into the same join as the routed partials)."""
     y = np.asarray(y, dtype=np.float64)
     c, k, n = y.shape
     out = np.zeros((c, n), dtype=np.float64)
@@ -251,6 +259,8 @@ def moe_combine(y, ids, weights):
         for s in range(k):
             if ids[j, s] >= 0:
                 out[j] += float(weights[j, s]) * y[j, s]
+    if shared is not None:
+        out = out + np.asarray(shared, dtype=np.float64)
     return out
 
 
@@ -260,7 +270,7 @@ def moe_combine(y, ids, weights):
 
 def expert_ffn(w_gate, w_up, w_down, xq_col):
     """One expert (or the shared expert) on one q8_1 column: gate/up pair with
-    SwiGLU-DS4, h rounded to fp32 and quantised to q8_1 (R7), down product.
+    SwiGLU-DS4, h rounded to fp32 and quantised to q8_1 (R8), down product.
     Returns dict of fp64 g, u, h, the q8_1 hq and fp64 y (all for one column)."""
     h, g, u = glu_pair(w_gate, w_up, xq_col)
     hq = quantize_q8_1(h.astype(np.float32))

@@ -11,10 +11,13 @@ namespace moeq8 {
 // loads), then the y values of the unmasked slots, all issued before any is
 // used (a second round trip, instead of one per slot).  A masked slot's y row
 // is never read, and the sum skips it by selection.
+// add (nullable): the shared expert's output [ncols][n], added once after
+// the routed sum; it may be out itself (each element is read, then written,
+// by the same thread).
 template <int KMAX>
 __global__ void k_combine(const float* __restrict__ y, const int32_t* __restrict__ ids,
-                          const float* __restrict__ w, int topk, int64_t n,
-                          float* __restrict__ out) {
+                          const float* __restrict__ w, int topk, int64_t n, const float* add,
+                          float* out) {
     const int j = blockIdx.y;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -37,26 +40,43 @@ __global__ void k_combine(const float* __restrict__ y, const int32_t* __restrict
         const float sum = acc + wt[s] * yv[s];
         acc = id[s] >= 0 ? sum : acc;
     }
+    if (add) acc = acc + add[(int64_t)j * n + i];
     out[(int64_t)j * n + i] = acc;
 }
 
 }  // namespace moeq8
 
-extern "C" int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
-                           int32_t topk, int64_t n, float* out, void* stream) {
+namespace {
+int combine_call(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
+                 int32_t topk, int64_t n, const float* add, float* out, void* stream) {
     using namespace moeq8;
     if (!y || !ids || !weights || !out) return MOEQ8_EINVAL;
     if (ncols < 1 || ncols > MOEQ8_MAX_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK || n < 0)
         return MOEQ8_EINVAL;
-    if (((uintptr_t)y | (uintptr_t)ids | (uintptr_t)weights | (uintptr_t)out) & 3u) return MOEQ8_EALIGN;
+    if (((uintptr_t)y | (uintptr_t)ids | (uintptr_t)weights | (uintptr_t)out | (uintptr_t)add) & 3u)
+        return MOEQ8_EALIGN;
     if (n == 0) return MOEQ8_OK;
     const int64_t bx = (n + 255) / 256;
     if (bx > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
     const dim3 grid((uint32_t)bx, (uint32_t)ncols);
     if (topk <= 8)
-        hipLaunchKernelGGL(k_combine<8>, grid, dim3(256), 0, (hipStream_t)stream, y, ids, weights, topk, n, out);
+        hipLaunchKernelGGL(k_combine<8>, grid, dim3(256), 0, (hipStream_t)stream, y, ids, weights, topk, n,
+                           add, out);
     else
         hipLaunchKernelGGL(k_combine<MOEQ8_MAX_TOPK>, grid, dim3(256), 0, (hipStream_t)stream, y, ids,
-                           weights, topk, n, out);
+                           weights, topk, n, add, out);
     return check_launch();
+}
+}  // namespace
+
+extern "C" int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
+                           int32_t topk, int64_t n, float* out, void* stream) {
+    return combine_call(y, ids, weights, ncols, topk, n, nullptr, out, stream);
+}
+
+extern "C" int moe_combine_shared(const float* y, const int32_t* ids, const float* weights,
+                                  int64_t ncols, int32_t topk, int64_t n, const float* shared_y,
+                                  float* out, void* stream) {
+    if (!shared_y) return MOEQ8_EINVAL;
+    return combine_call(y, ids, weights, ncols, topk, n, shared_y, out, stream);
 }

@@ -105,9 +105,12 @@ class Workspace:
 
 def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
             owner_slot: torch.Tensor | None, n_local_expert: int, experts: RoutedExperts,
-            shared: SharedExpertShare | None, ws: Workspace, hook=None, fused: bool = True):
+            shared: SharedExpertShare | None, ws: Workspace, hook=None, fused: bool = True,
+            add_shared: bool = False):
     """Enqueue one layer on the current stream; returns (out, ys) device tensors
-    of the workspace.
+    of the workspace.  out is the routed experts' weighted sum, or with
+    add_shared (and a shared share) the MoE block's whole output: that sum plus
+    the shared expert's ys, added inside the combine launch.
 
     fused=True (four launches): prologue (router + q8_1 of x), grouped gate/up
     with the shared gate/up rows as extra items, grouped down that quantises h
@@ -116,8 +119,9 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     fused=False: the nine separate calls, the shared expert on a second stream.
     Both give the same bits.  ``hook(name, phase)`` (unfused only) is called
     around each launch."""
+    add = add_shared and shared is not None
     if fused:
-        return _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws)
+        return _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add)
     c, topk = ws.ncols, ws.topk
     hidden, inter = experts.hidden, experts.inter
     mark = hook or (lambda name, phase: None)
@@ -160,10 +164,12 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     ops.moe_grouped_mmvq(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
                          n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
     mark("grouped_down", "end")
+    if add:
+        main.wait_event(ws.join)                  # the combine reads ys
     mark("combine", "begin")
-    ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
+    ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out, shared=ws.ys if add else None)
     mark("combine", "end")
-    if shared is not None:
+    if shared is not None and not add:
         main.wait_event(ws.join)
     return ws.out, ws.ys
 
@@ -181,7 +187,7 @@ def _same_round_span(k_block_offset: int, k_slice: int, k: int) -> bool:
     return k_slice == k and _rounds(k_block_offset // 2, k_slice // 64) == _rounds(0, k // 64)
 
 
-def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws):
+def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add):
     """Prologue, gate/up (+ shared rows), down with the q8_1 quantisation of h
     and hs inside the launch (+ shared slice), combine: four launches on one
     stream.  A shared slice whose length or lane layout differs from the
@@ -215,7 +221,7 @@ def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared,
         ops.mmvq_q8_0(shared.down, ws.hsq, hidden, shared.rows, ncols=c, k_block_offset=kb,
                       w_offset_bytes=kb * Q80, w_row_stride_bytes=(shared.inter_full // QK) * Q80,
                       out=ws.ys)
-    ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
+    ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out, shared=ws.ys if add else None)
     return ws.out, ws.ys
 
 

@@ -352,8 +352,9 @@ def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
 
 
 def moe_combine(y: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor,
-                out: torch.Tensor | None = None) -> torch.Tensor:
-    """out fp32 [ncols, n] = sum over unmasked slots of weights * y."""
+                out: torch.Tensor | None = None, shared: torch.Tensor | None = None) -> torch.Tensor:
+    """out fp32 [ncols, n] = sum over unmasked slots of weights * y, plus
+    shared [ncols, n] (the shared expert's output) when given; shared may be out."""
     _cuda(y, "y", torch.float32)
     _cuda(ids, "ids", torch.int32)
     _cuda(weights, "weights", torch.float32)
@@ -366,7 +367,15 @@ def moe_combine(y: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor,
         out = torch.empty((ncols, n), dtype=torch.float32, device=y.device)
     _cuda(out, "out", torch.float32)
     _need(out, "out", ncols * n * 4)
-    call("moe_combine", _ptr(y), _ptr(ids), _ptr(weights), ncols, topk, n, _ptr(out), _stream(y))
+    if shared is None:
+        call("moe_combine", _ptr(y), _ptr(ids), _ptr(weights), ncols, topk, n, _ptr(out), _stream(y))
+    else:
+        _cuda(shared, "shared", torch.float32)
+        if not shared.is_contiguous():
+            raise ValueError("shared must be contiguous [ncols, n]")
+        _need(shared, "shared", ncols * n * 4)
+        call("moe_combine_shared", _ptr(y), _ptr(ids), _ptr(weights), ncols, topk, n, _ptr(shared),
+             _ptr(out), _stream(y))
     return out
 
 

@@ -110,7 +110,13 @@ def test_other_validation():
     assert L.moe_grouped_mmvq(1, P, None, 136, 68, 2, 4, 64, P, P, 1, 1, P, None) == -1  # experts overlap
     assert L.moe_combine(P, P, P, 0, 8, 16, P, None) == -1
     assert L.moe_combine(P, P, P, 1, 8, 0, P, None) == 0
+    assert L.moe_combine_shared(P, P, P, 1, 8, 16, None, P, None) == -1         # no shared output
+    assert L.moe_combine_shared(P, P, P, 1, 8, 16, P + 2, P, None) == -2        # misaligned shared
+    assert L.moe_combine_shared(P, P, P, 1, 8, 0, P, P, None) == 0
     assert L.moeq8_synth_q8_0_fill(P + 1, 1, 1, 1, 0, 0, 0, 0, None) == -2
+    assert L.moeq8_stream_read(P + 4, 64, P, None) == -2                         # misaligned buffer
+    assert L.moeq8_stream_read(P, 24, P, None) == -2                             # bytes % 16
+    assert L.moeq8_stream_read(P, 0, P, None) == 0
 
 
 def test_ops_reject_out_of_bounds_views():

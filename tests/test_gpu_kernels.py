@@ -408,6 +408,32 @@ def test_combine_one_hot_and_all_masked():
     assert np.array_equal(out[2], ref)                     # fp32: products rounded, sums in slot order
 
 
+def test_combine_shared_adds_after_the_routed_sum():
+    """moe_combine_shared = the routed combine, then one fp32 add of the shared
+    expert's output (R15): bit for bit against the plain combine plus the
+    shared output on the host, in place (shared is out) too; all masked gives
+    the shared output itself; within tolerance of the oracle."""
+    rng = np.random.default_rng(3)
+    c, topk, n = 5, 8, 4096
+    y = rng.normal(size=(c, topk, n)).astype(np.float32)
+    ids = rng.integers(-1, 20, size=(c, topk)).astype(np.int32)
+    ids[1] = -1
+    w = rng.random((c, topk)).astype(np.float32)
+    shared = rng.normal(size=(c, n)).astype(np.float32)
+    y[ids < 0] = np.nan
+    yd, idd, wd, sd = to_dev(y), to_dev(ids), to_dev(w), to_dev(shared)
+    plain = host(moeq8.moe_combine(yd, idd, wd))
+    got = host(moeq8.moe_combine(yd, idd, wd, shared=sd))
+    assert np.array_equal(got.view(np.int32), (plain + shared).view(np.int32))
+    assert np.array_equal(got[1].view(np.int32), shared[1].view(np.int32))
+    inplace = sd.clone()
+    moeq8.moe_combine(yd, idd, wd, out=inplace, shared=inplace)
+    assert np.array_equal(host(inplace).view(np.int32), got.view(np.int32))
+    ref = oracle.moe_combine(np.nan_to_num(y.astype(np.float64)), ids, w.astype(np.float64),
+                             shared=shared.astype(np.float64))
+    assert_close(got, ref, EPI_TOL, "combine + shared")
+
+
 def test_graph_replay_matches_eager():
     """One routed layer captured in a HIP graph and replayed several times, with
     eager work and synchronisation between replays, equals the eager run."""
@@ -514,6 +540,16 @@ def test_fused_layer_equals_unfused(c, n_exp, hidden, inter, share_rows, half):
     ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wa, fused=False)
     ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wb, fused=True)
     torch.cuda.synchronize()
+    # with the shared expert's output added inside the combine: both forms
+    # agree, and the total is the routed sum plus ys in one fp32 add
+    wc = ml.Workspace(c, hidden, inter, topk, share_rows, DEV)
+    wd = ml.Workspace(c, hidden, inter, topk, share_rows, DEV)
+    ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wc, fused=False, add_shared=True)
+    ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wd, fused=True, add_shared=True)
+    torch.cuda.synchronize()
+    assert bits_equal(wc.out, wd.out)
+    total = host(wb.out) + host(wb.ys)
+    assert np.array_equal(host(wd.out).view(np.int32), total.view(np.int32))
     assert torch.equal(wa.xq, wb.xq) and torch.equal(wa.ids, wb.ids)
     assert _defined_grouping_words(wa.grouping) == _defined_grouping_words(wb.grouping)
     assert bits_equal(wa.weights, wb.weights)

@@ -332,6 +332,16 @@ def test_combine_pins():
     assert np.array_equal(out[0], y[0, 2])                # one-hot weight -> that route's y
     assert np.all(out[1] == 0.0)                          # all masked -> zero
     np.testing.assert_allclose(out[2], 0.5 * y[2, 0] + 0.3 * y[2, 2], rtol=1e-15)
+    # the shared expert's output is added once after the routed sum (R15):
+    # all masked -> exactly the shared output; one-hot on small integers ->
+    # the exact sum; a zero shared output leaves the routed sum unchanged
+    shared = rng.integers(-8, 8, size=(3, 16)).astype(np.float64)
+    yi = np.round(y * 4)
+    yi[2, 1] = np.nan
+    out_s = oracle.moe_combine(yi, ids, w, shared=shared)
+    assert np.array_equal(out_s[1], shared[1])
+    assert np.array_equal(out_s[0], yi[0, 2] + shared[0])
+    assert np.array_equal(oracle.moe_combine(y, ids, w, shared=np.zeros((3, 16))), out)
 
 
 def _tiny_experts(seed, n_exp, hidden, inter):
