@@ -36,8 +36,10 @@
  *     untouched) or the launch failed (MOEQ8_EHIP; the HIP error is cleared).
  *     Faults inside kernels surface at the caller's next synchronisation.
  *   - Non-finite inputs are outside the contract (results unspecified).
- *   - Columns: 1 <= ncols <= MOEQ8_MAX_COLS.  Column j of an activation
- *     operand is row j of a row-major [ncols][...] array.
+ *   - Columns: 1 <= ncols <= MOEQ8_MAX_COLS (MOEQ8_MAX_WIDE_COLS for the wide
+ *     calls and for grouped products and combines that take their
+ *     groupings).  Column j of an activation operand is row j of a row-major
+ *     [ncols][...] array.
  *   - K must be a multiple of 64 (whole 2-block lane chunks); weight pointers,
  *     row strides and expert strides must be multiples of 4 bytes; activation
  *     and output pointers must be 4-byte aligned.
@@ -59,6 +61,7 @@ extern "C" {
 #define MOEQ8_MAX_COLS 8
 #define MOEQ8_MAX_EXPERTS 1024
 #define MOEQ8_MAX_TOPK 16
+#define MOEQ8_MAX_WIDE_COLS 1024   /* columns of the wide-batch calls */
 
 enum moeq8_status {
     MOEQ8_OK = 0,
@@ -219,6 +222,30 @@ int moe_route_topk_quantize(const float* x, int64_t x_row_stride, int64_t k, voi
                             const float* logits, const float* bias, const int32_t* owner_slot,
                             int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
                             int32_t* ids, float* weights, void* grouping, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Wide batches (prefill-like, up to MOEQ8_MAX_WIDE_COLS columns).
+ *
+ * moe_route_topk_wide: the selection and weights of moe_route_topk for each
+ * column (columns are independent; one workgroup per 8 columns), without the
+ * grouping.  Arguments and results as moe_route_topk.
+ *
+ * moe_group_routes: the expert grouping of ids [ncols][topk] in the layout
+ * moe_route_topk writes (header, expert[], offset[], route[], padding, table),
+ * in a buffer of moe_grouping_bytes_wide(ncols, topk) bytes: active local
+ * experts ascending, each with its routes ascending.  ids outside
+ * [0, n_local_expert) count as masked.
+ *
+ * moe_grouped_mmvq / moe_grouped_mmvq_ex and moe_combine accept such wide
+ * groupings (ncols up to MOEQ8_MAX_WIDE_COLS): a work item takes its expert's
+ * routes in passes of MOEQ8_MAX_COLS columns.
+ * ------------------------------------------------------------------------- */
+size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk);
+int moe_route_topk_wide(const float* logits, const float* bias, const int32_t* owner_slot,
+                        int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
+                        int32_t* ids, float* weights, void* stream);
+int moe_group_routes(const int32_t* ids, int64_t ncols, int32_t topk, int64_t n_local_expert,
+                     void* grouping, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a9: weighted masked combine.

@@ -18,6 +18,9 @@ from .ops import (  # noqa: F401
     mmvq_q8_0_glu_pair,
     swiglu_ds4,
     moe_grouping_bytes,
+    moe_grouping_bytes_wide,
+    moe_route_topk_wide,
+    moe_group_routes,
     moe_route_topk,
     moe_grouped_mmvq,
     moe_grouped_mmvq_ex,

@@ -34,6 +34,10 @@ SIGNATURES = {
                                                c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_combine": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]),
     "moe_combine_shared": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_vp, c_vp]),
+    "moe_grouping_bytes_wide": (c_size, [c_i64, c_i32]),
+    "moe_route_topk_wide": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp,
+                                           c_vp]),
+    "moe_group_routes": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]),
     "moeq8_synth_stream_key": (c_u64, [c_u32, c_u32, c_u32, c_u32]),
     "moeq8_synth_q8_0_fill": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_u32, c_u32, c_u32,
                                              c_u32, c_vp]),

@@ -51,7 +51,7 @@ int combine_call(const float* y, const int32_t* ids, const float* weights, int64
                  int32_t topk, int64_t n, const float* add, float* out, void* stream) {
     using namespace moeq8;
     if (!y || !ids || !weights || !out) return MOEQ8_EINVAL;
-    if (ncols < 1 || ncols > MOEQ8_MAX_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK || n < 0)
+    if (ncols < 1 || ncols > MOEQ8_MAX_WIDE_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK || n < 0)
         return MOEQ8_EINVAL;
     if (((uintptr_t)y | (uintptr_t)ids | (uintptr_t)weights | (uintptr_t)out | (uintptr_t)add) & 3u)
         return MOEQ8_EALIGN;

@@ -64,7 +64,8 @@ struct MmvqParams {
     int32_t nsteps;             // G == 1: rounds to walk (same for m and s)
     int32_t ncols;
     int32_t topk;
-    int32_t act_route_mul;      // grouped: activation row of route r is (r * act_route_mul) >> 16
+    int32_t pad0;
+    uint64_t act_route_mul;     // grouped: activation row of route r is (r * act_route_mul) >> 32
                                 // = r / d for d = 1 (down) or topk (gate/up)
     int32_t rows_per_wg;
     int32_t max_active;         // grouped: bound on the device-side active count
@@ -199,7 +200,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
     float* out0 = p.out0;
     float* s_out = p.s_out;
     const int64_t act_row_bytes = p.act_row_bytes;
-    const int32_t act_route_mul = p.act_route_mul;
+    const uint64_t act_route_mul = p.act_route_mul;
     const int32_t nsteps = p.nsteps;
     // The arguments the decode and the first loads need arrive in one batch
     // of scalar loads at entry; left alone, the compiler fetches each after
@@ -314,7 +315,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             for (int c = 0; c < MAX_COLS; ++c) {
                 const int r = (c >= nc || w8[c] < 0 || w8[c] >= R) ? -1 : w8[c];
                 orow[c] = routed ? r : c0 + c;
-                arow[c] = routed ? (r < 0 ? 0 : (r * act_route_mul) >> 16) : c0 + c;
+                arow[c] = routed ? (r < 0 ? 0 : (int)(((uint64_t)r * act_route_mul) >> 32)) : c0 + c;
             }
         } else {
 #pragma unroll
@@ -343,7 +344,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                 int ar = c0 + c;
                 if (routed) {
                     const int r = w8[c];                   // c < nc wherever pos < total
-                    ar = (r < 0 || r >= R) ? 0 : (r * act_route_mul) >> 16;
+                    ar = (r < 0 || r >= R) ? 0 : (int)(((uint64_t)r * act_route_mul) >> 32);
                 }
                 if (pos < total)
                     __builtin_amdgcn_global_load_lds(
@@ -377,7 +378,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                     int ar = c0 + c;
                     if (routed) {
                         const int r = w8[c];               // c < nc here
-                        ar = (r < 0 || r >= R) ? 0 : (r * act_route_mul) >> 16;
+                        ar = (r < 0 || r >= R) ? 0 : (int)(((uint64_t)r * act_route_mul) >> 32);
                     }
                     const float* sp = src + (int64_t)ar * stride + (int64_t)b * QK + (u & 1) * (QK / 2);
 #pragma unroll
@@ -691,7 +692,9 @@ extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w
         if (st) return st;
     }
     if (!act || !grouping || !out) return MOEQ8_EINVAL;
-    if (ncols < 1 || ncols > MAX_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK) return MOEQ8_EINVAL;
+    // wide groupings (moe_group_routes) too: an item takes its routes in
+    // passes of MAX_COLS columns
+    if (ncols < 1 || ncols > MOEQ8_MAX_WIDE_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK) return MOEQ8_EINVAL;
     if (n_local_expert < 1) return MOEQ8_EINVAL;
     if (expert_stride_bytes < 0 || (expert_stride_bytes & 3)) return MOEQ8_EALIGN;
     if (n_local_expert > 1 && expert_stride_bytes < n * w_row_stride_bytes) return MOEQ8_EINVAL;
@@ -726,12 +729,12 @@ extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w
     p.ncols = (int32_t)ncols;
     p.topk = topk;
     // route r's activation row is r / d, d = topk for gate/up (a column per
-    // route group) or 1 for down (a row per route); r < ncols*topk <= 128 and
-    // d <= 16, where (r * ceil(65536 / d)) >> 16 is exactly r / d (the
-    // multiplier's excess adds under 128/65536 to r/d, whose fractional part
+    // route group) or 1 for down (a row per route); r < ncols*topk <= 2^14
+    // and d <= 16, where (r * ceil(2^32 / d)) >> 32 is exactly r / d (the
+    // multiplier's excess adds under 2^14/2^32 to r/d, whose fractional part
     // is at most 15/16)
-    const int32_t route_div = pair ? topk : 1;
-    p.act_route_mul = (65536 + route_div - 1) / route_div;
+    const uint64_t route_div = pair ? (uint64_t)topk : 1u;
+    p.act_route_mul = ((1ull << 32) + route_div - 1) / route_div;
     p.act = (const uint8_t*)act;
     p.act_row_bytes = (k / QK) * Q81_BYTES;
     if (f32) {

@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return a > b ? a : b;
 }
 
-template <int PER>
+template <int PER, bool GROUP = true>
 __device__ __forceinline__ void route_body(
     const float* __restrict__ logits, const float* __restrict__ bias,
     const int32_t* __restrict__ owner, int ncols, int n_expert, int n_local, int topk,
@@ -145,15 +145,16 @@ __device__ __forceinline__ void route_body(
     // issued at the end, so no barrier waits for one)
     __syncthreads();
 
-    int32_t* g_expert = grouping + 4;
-    int32_t* g_offset = grouping + 4 + R;
-    int32_t* g_route = grouping + 4 + 2 * R + 1;
-    int4* g_table = reinterpret_cast<int4*>(grouping + grouping_table_word(R));
     if (j < ncols && lane < topk) {
         const int rr = j * topk + lane;
         ids[rr] = slot_id;
         weights[rr] = slot_score / sum;
     }
+    if constexpr (!GROUP) return;
+    int32_t* g_expert = grouping + 4;
+    int32_t* g_offset = grouping + 4 + R;
+    int32_t* g_route = grouping + 4 + 2 * R + 1;
+    int4* g_table = reinterpret_cast<int4*>(grouping + grouping_table_word(R));
 
     if (R <= 64) {
         // one wave: lane r holds route r.  An 11-bit radix pass of ballots over
@@ -268,6 +269,122 @@ __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk(
     route_body<PER>(logits, bias, owner, ncols, n_expert, n_local, topk, ids, weights, grouping);
 }
 
+// Selection and weights only, for any number of columns: workgroup b takes
+// columns [8b, 8b + 8), each column exactly as in k_route_topk (columns are
+// independent until the grouping, which moe_group_routes builds).
+template <int PER>
+__global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk_wide(
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    const int32_t* __restrict__ owner, int64_t ncols, int n_expert, int n_local, int topk,
+    int32_t* __restrict__ ids, float* __restrict__ weights) {
+    const int64_t c0 = (int64_t)blockIdx.x * ROUTE_MAX_COLS;
+    const int nc = (int)min((int64_t)ROUTE_MAX_COLS, ncols - c0);
+    route_body<PER, false>(logits + c0 * n_expert, bias, owner, nc, n_expert, n_local, topk,
+                           ids + c0 * topk, weights + c0 * topk, nullptr);
+}
+
+// The expert grouping of any number of routes (the same layout as the one
+// moe_route_topk writes), from the route ids, in one workgroup of 1024
+// threads: keys (local expert << 14 | route), invalid routes as 0xFFFFFFFF,
+// sorted ascending in LDS (bitonic), so routes come out by (expert, route
+// index) ascending; a route's position is its rank, an expert's group starts
+// at the first key carrying it.  Deterministic: no atomics.
+constexpr int WIDE_THREADS = 1024;
+constexpr int WIDE_MAX_R = 16384;                      // 1024 columns x top-16
+
+__global__ __launch_bounds__(WIDE_THREADS) void k_group_routes(
+    const int32_t* __restrict__ ids, int64_t ncols, int topk, int n_local,
+    int32_t* __restrict__ grouping) {
+    __shared__ uint32_t key[WIDE_MAX_R];
+    __shared__ int32_t part[WIDE_THREADS];
+    const int tid = threadIdx.x;
+    const int R = (int)ncols * topk;
+    int rp = 1;
+    while (rp < R) rp <<= 1;
+    for (int i = tid; i < rp; i += WIDE_THREADS) {
+        const int id = i < R ? ids[i] : -1;
+        key[i] = (id >= 0 && id < n_local) ? ((uint32_t)id << 14 | (uint32_t)i) : 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    for (int k = 2; k <= rp; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+            for (int i = tid; i < rp; i += WIDE_THREADS) {
+                const int ixj = i ^ jj;
+                if (ixj > i) {
+                    const uint32_t a = key[i], b = key[ixj];
+                    const bool up = (i & k) == 0;
+                    if (up ? (a > b) : (a < b)) {
+                        key[i] = b;
+                        key[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int32_t* g_expert = grouping + 4;
+    int32_t* g_offset = grouping + 4 + R;
+    int32_t* g_route = grouping + 4 + 2 * R + 1;
+    int4* g_table = reinterpret_cast<int4*>(grouping + grouping_table_word(R));
+    // heads (first key of each expert) counted per thread over a contiguous
+    // range of positions, then an exclusive scan of the per-thread counts
+    const int per = (R + WIDE_THREADS - 1) / WIDE_THREADS;
+    const int p0 = tid * per;
+    int heads = 0, valid = 0;
+    for (int p = p0; p < min(p0 + per, R); ++p) {
+        const uint32_t kp = key[p];
+        if (kp == 0xFFFFFFFFu) continue;
+        ++valid;
+        if (p == 0 || (key[p - 1] >> 14) != (kp >> 14)) ++heads;
+    }
+    part[tid] = heads | (valid << 16);                 // both < 2^15 (R <= 16384)
+    __syncthreads();
+    // inclusive scan of part (Hillis-Steele; two fields move together)
+    for (int off = 1; off < WIDE_THREADS; off <<= 1) {
+        const int v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    const int n_heads = part[WIDE_THREADS - 1] & 0xFFFF;
+    const int n_valid = part[WIDE_THREADS - 1] >> 16;
+    int a = (tid > 0 ? part[tid - 1] : 0) & 0xFFFF;    // heads before this thread's range
+    for (int p = p0; p < min(p0 + per, R); ++p) {
+        const uint32_t kp = key[p];
+        if (kp == 0xFFFFFFFFu) {
+            g_route[p] = -1;
+            continue;
+        }
+        g_route[p] = (int32_t)(kp & 0x3FFFu);
+        if (p == 0 || (key[p - 1] >> 14) != (kp >> 14)) {
+            g_expert[a] = (int32_t)(kp >> 14);
+            g_offset[a] = p;
+            ++a;
+        }
+    }
+    for (int q = n_heads + tid; q < R; q += WIDE_THREADS) g_expert[q] = -1;
+    for (int q = n_heads + tid; q <= R; q += WIDE_THREADS) g_offset[q] = n_valid;
+    if (tid == 0) {
+        grouping[0] = n_heads;
+        grouping[1] = n_valid;
+        grouping[2] = (int32_t)ncols;
+        grouping[3] = topk;
+    }
+    // the table: the end of group a is where group a + 1 starts (found again
+    // from the keys, so no wait on other threads' stores is needed)
+    for (int p = p0; p < min(p0 + per, R); ++p) {
+        const uint32_t kp = key[p];
+        if (kp == 0xFFFFFFFFu || !(p == 0 || (key[p - 1] >> 14) != (kp >> 14))) continue;
+        int end = p + 1;
+        while (end < n_valid && (key[end] >> 14) == (kp >> 14)) ++end;
+        // this head's rank: heads before p
+        int rank = (tid > 0 ? part[tid - 1] : 0) & 0xFFFF;
+        for (int q = p0; q < p; ++q)
+            if (key[q] != 0xFFFFFFFFu && (q == 0 || (key[q - 1] >> 14) != (key[q] >> 14))) ++rank;
+        g_table[rank] = make_int4((int)(kp >> 14), p, end, 0);
+    }
+}
+
 // The layer prologue: block 0 routes; the other blocks quantise the FFN input
 // to q8_1 (both read only the layer's inputs, so one launch runs them side by
 // side).  Bytes and routing are those of q8_1_quantize_rows and moe_route_topk.
@@ -292,13 +409,24 @@ __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_quantize(
 
 using namespace moeq8;
 
-extern "C" size_t moe_grouping_bytes(int64_t ncols, int32_t topk) {
-    if (ncols < 1 || ncols > ROUTE_MAX_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return 0;
+namespace {
+size_t grouping_bytes_of(int64_t ncols, int32_t topk) {
     const size_t R = (size_t)ncols * (size_t)topk;
     // header, expert[R], offset[R+1], route[R], eight words of padding (so
     // that readers may load eight words from any route entry), the table
     const size_t bytes = 4 * ((size_t)grouping_table_word((int64_t)R) + 4 * R);
     return (bytes + 255) & ~(size_t)255;
+}
+}  // namespace
+
+extern "C" size_t moe_grouping_bytes(int64_t ncols, int32_t topk) {
+    if (ncols < 1 || ncols > ROUTE_MAX_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return 0;
+    return grouping_bytes_of(ncols, topk);
+}
+
+extern "C" size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk) {
+    if (ncols < 1 || ncols > MOEQ8_MAX_WIDE_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return 0;
+    return grouping_bytes_of(ncols, topk);
 }
 
 namespace {
@@ -367,5 +495,43 @@ extern "C" int moe_route_topk_quantize(const float* x, int64_t x_row_stride, int
     else if (per <= 8) MOEQ8_PRO_LAUNCH(8);
     else MOEQ8_PRO_LAUNCH(16);
 #undef MOEQ8_PRO_LAUNCH
+    return check_launch();
+}
+
+extern "C" int moe_route_topk_wide(const float* logits, const float* bias, const int32_t* owner_slot,
+                                   int64_t ncols, int64_t n_expert, int64_t n_local_expert,
+                                   int32_t topk, int32_t* ids, float* weights, void* stream) {
+    if (!logits || !ids || !weights) return MOEQ8_EINVAL;
+    if (ncols < 1 || ncols > MOEQ8_MAX_WIDE_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return MOEQ8_EINVAL;
+    if (n_expert < 1 || topk > n_expert || n_local_expert < 1) return MOEQ8_EINVAL;
+    if (!owner_slot && n_local_expert != n_expert) return MOEQ8_EINVAL;
+    if (n_expert > ROUTE_MAX_EXPERT || n_local_expert > ROUTE_MAX_EXPERT) return MOEQ8_EUNSUPPORTED;
+    if (((uintptr_t)logits | (uintptr_t)bias | (uintptr_t)owner_slot | (uintptr_t)ids |
+         (uintptr_t)weights) & 3u)
+        return MOEQ8_EALIGN;
+    const dim3 grid((uint32_t)((ncols + ROUTE_MAX_COLS - 1) / ROUTE_MAX_COLS)), block(64 * ROUTE_MAX_COLS);
+    const int per = (int)((n_expert + 63) / 64);
+    const hipStream_t hs = (hipStream_t)stream;
+#define MOEQ8_WIDE_LAUNCH(P)                                                                      \
+    hipLaunchKernelGGL(k_route_topk_wide<P>, grid, block, 0, hs, logits, bias, owner_slot, ncols, \
+                       (int)n_expert, (int)n_local_expert, (int)topk, ids, weights)
+    if (per <= 1) MOEQ8_WIDE_LAUNCH(1);
+    else if (per <= 2) MOEQ8_WIDE_LAUNCH(2);
+    else if (per <= 4) MOEQ8_WIDE_LAUNCH(4);
+    else if (per <= 8) MOEQ8_WIDE_LAUNCH(8);
+    else MOEQ8_WIDE_LAUNCH(16);
+#undef MOEQ8_WIDE_LAUNCH
+    return check_launch();
+}
+
+extern "C" int moe_group_routes(const int32_t* ids, int64_t ncols, int32_t topk,
+                                int64_t n_local_expert, void* grouping, void* stream) {
+    if (!ids || !grouping) return MOEQ8_EINVAL;
+    if (ncols < 1 || ncols > MOEQ8_MAX_WIDE_COLS || topk < 1 || topk > ROUTE_MAX_TOPK) return MOEQ8_EINVAL;
+    if (n_local_expert < 1) return MOEQ8_EINVAL;
+    if (n_local_expert > ROUTE_MAX_EXPERT) return MOEQ8_EUNSUPPORTED;
+    if (((uintptr_t)ids | (uintptr_t)grouping) & 3u) return MOEQ8_EALIGN;
+    hipLaunchKernelGGL(k_group_routes, dim3(1), dim3(WIDE_THREADS), 0, (hipStream_t)stream, ids, ncols,
+                       (int)topk, (int)n_local_expert, (int32_t*)grouping);
     return check_launch();
 }

@@ -168,6 +168,59 @@ def moe_grouping_bytes(ncols: int, topk: int) -> int:
     return int(lib().moe_grouping_bytes(ncols, topk))
 
 
+def moe_grouping_bytes_wide(ncols: int, topk: int) -> int:
+    """Grouping size for up to MOEQ8_MAX_WIDE_COLS columns (the same layout and
+    size formula as moe_grouping_bytes)."""
+    return int(lib().moe_grouping_bytes_wide(ncols, topk))
+
+
+def moe_route_topk_wide(logits: torch.Tensor, topk: int, *, bias: torch.Tensor | None = None,
+                        owner_slot: torch.Tensor | None = None, n_local_expert: int | None = None,
+                        ids: torch.Tensor | None = None, weights: torch.Tensor | None = None):
+    """Selection and weights for up to 1024 columns (no grouping):
+    returns (ids int32 [ncols, topk], weights fp32 [ncols, topk])."""
+    _cuda(logits, "logits", torch.float32)
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be contiguous [ncols, n_expert]")
+    ncols, n_expert = logits.shape
+    if n_local_expert is None:
+        n_local_expert = n_expert if owner_slot is None else int(owner_slot.max().item()) + 1
+    if bias is not None:
+        _cuda(bias, "bias", torch.float32)
+        _need(bias, "bias", n_expert * 4)
+    if owner_slot is not None:
+        _cuda(owner_slot, "owner_slot", torch.int32)
+        _need(owner_slot, "owner_slot", n_expert * 4)
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((ncols, topk), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((ncols, topk), dtype=torch.float32, device=dev)
+    _need(ids, "ids", ncols * topk * 4)
+    _need(weights, "weights", ncols * topk * 4)
+    call("moe_route_topk_wide", _ptr(logits), _ptr(bias), _ptr(owner_slot), ncols, n_expert,
+         n_local_expert, topk, _ptr(ids), _ptr(weights), _stream(logits))
+    return ids, weights
+
+
+def moe_group_routes(ids: torch.Tensor, n_local_expert: int, grouping: torch.Tensor | None = None):
+    """The expert grouping of ids [ncols, topk] (any ncols up to 1024), in the
+    layout moe_route_topk writes; returns the grouping tensor."""
+    _cuda(ids, "ids", torch.int32)
+    if ids.dim() != 2 or not ids.is_contiguous():
+        raise ValueError("ids must be contiguous [ncols, topk]")
+    ncols, topk = ids.shape
+    gb = moe_grouping_bytes_wide(ncols, topk)
+    if gb == 0:
+        raise ValueError("ncols or topk out of range")
+    if grouping is None:
+        grouping = torch.empty(gb, dtype=torch.uint8, device=ids.device)
+    _cuda(grouping, "grouping", torch.uint8)
+    _need(grouping, "grouping", gb)
+    call("moe_group_routes", _ptr(ids), ncols, topk, n_local_expert, _ptr(grouping), _stream(ids))
+    return grouping
+
+
 def moe_route_topk(logits: torch.Tensor, topk: int, *, bias: torch.Tensor | None = None,
                    owner_slot: torch.Tensor | None = None, n_local_expert: int | None = None,
                    ids: torch.Tensor | None = None, weights: torch.Tensor | None = None,
@@ -229,7 +282,7 @@ def moe_grouped_mmvq(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, ac
         raise ValueError("stage must be GATE_UP_SWIGLU or DOWN")
     _act_rows(act_q, "act_q", act_rows, k)
     _cuda(grouping, "grouping", torch.uint8)
-    _need(grouping, "grouping", moe_grouping_bytes(ncols, topk))
+    _need(grouping, "grouping", moe_grouping_bytes_wide(ncols, topk))
     if out is None:
         out = torch.empty((ncols, topk, n), dtype=torch.float32, device=w_a.device)
     _cuda(out, "out", torch.float32)
@@ -318,7 +371,7 @@ def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
     else:
         raise ValueError("bad stage")
     _cuda(grouping, "grouping", torch.uint8)
-    _need(grouping, "grouping", moe_grouping_bytes(ncols, topk))
+    _need(grouping, "grouping", moe_grouping_bytes_wide(ncols, topk))
     _cuda(out, "out", torch.float32)
     _need(out, "out", ncols * topk * n * 4)
     sa = sb = sact = sout = None

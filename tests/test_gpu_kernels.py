@@ -641,3 +641,83 @@ def test_stream_read_reads_every_word(where):
     moeq8.stream_read(buf, n - 16, clean, offset_bytes=16 if where == "first" else 0)
     torch.cuda.synchronize()
     assert int(host(clean.view(torch.int32))[0]) == 0
+
+
+# ---------------------------------------------------------------------------
+# wide batches: selection for many columns, the grouping of many routes, and
+# the grouped products taking an expert's routes in passes of 8 columns
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("c,n_exp,topk,local", [(1, 256, 8, 256), (9, 256, 8, 128), (64, 256, 8, 128),
+                                                (300, 256, 8, 256), (33, 64, 16, 20)])
+def test_route_topk_wide_vs_oracle(c, n_exp, topk, local):
+    say(f"route wide c={c} E={n_exp} k={topk} local={local}")
+    logits = workloads.router_logits(c + 3 * n_exp, c, n_exp)
+    bias = workloads.router_bias(c + 3 * n_exp, n_exp)
+    own = None if local == n_exp else workloads.owner_slots(n_exp, local)
+    ids_ref, w_ref, _ = oracle.route_topk(logits, bias, own, topk)
+    ids, w = moeq8.moe_route_topk_wide(to_dev(logits), topk, bias=to_dev(bias),
+                                       owner_slot=None if own is None else to_dev(own), n_local_expert=local)
+    assert np.array_equal(host(ids), ids_ref)
+    assert np.abs(host(w).astype(np.float64) - w_ref).max() < 1e-6
+    if c <= 8:
+        ids8, w8, g8 = moeq8.moe_route_topk(to_dev(logits), topk, bias=to_dev(bias),
+                                            owner_slot=None if own is None else to_dev(own),
+                                            n_local_expert=local)
+        assert torch.equal(ids, ids8) and bits_equal(w, w8)
+        assert _defined_grouping_words(moeq8.moe_group_routes(ids, local)) == _defined_grouping_words(g8)
+
+
+@pytest.mark.parametrize("c,topk,n_local", [(3, 8, 16), (64, 8, 128), (257, 8, 256), (1024, 8, 1024),
+                                            (511, 16, 37)])
+def test_group_routes_vs_oracle(c, topk, n_local):
+    """The wide grouping against the oracle's grouping (experts ascending,
+    routes ascending within each), with masked routes and ids past n_local."""
+    say(f"group routes c={c} topk={topk} local={n_local}")
+    rng = np.random.default_rng(c + topk)
+    ids = np.stack([rng.choice(n_local + 8, size=topk, replace=False) for _ in range(c)]).astype(np.int32)
+    ids[rng.random((c, topk)) < 0.2] = -1
+    g = moeq8.moe_group_routes(to_dev(ids), n_local)
+    # ids at or past n_local count as masked
+    _check_grouping(_grouping_words(g), np.where(ids < n_local, ids, -1).astype(np.int32))
+
+
+@pytest.mark.parametrize("c,n_exp,hidden,inter", [(40, 32, 1024, 256), (130, 64, 512, 256)])
+def test_wide_grouped_products_vs_oracle(c, n_exp, hidden, inter):
+    """Grouped gate/up and down over a wide grouping (items take their routes
+    in passes of 8 columns) against the oracle, route by route; the down
+    product and the combine read the oracle's h and y."""
+    say(f"wide grouped c={c} E={n_exp} H={hidden} I={inter}")
+    topk = 8
+    (wg, wu, wd), (wgd, wud, wdd) = _tiny_layer(c + n_exp, n_exp, hidden, inter)
+    x = workloads.activations(c, c, hidden)
+    logits = workloads.router_logits(c + 5, c, n_exp)
+    ids_ref, w_ref, _ = oracle.route_topk(logits, None, None, topk)
+    ids, w = moeq8.moe_route_topk_wide(to_dev(logits), topk)
+    assert np.array_equal(host(ids), ids_ref)
+    g = moeq8.moe_group_routes(ids, n_exp)
+    xo, xd = quantized_pair(x)
+    h = torch.full((c, topk, inter), float("nan"), device=DEV)
+    moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, wgd, wud, xd, g, n=inter, k=hidden, n_local_expert=n_exp,
+                           ncols=c, topk=topk, out=h)
+    hh = host(h).reshape(c * topk, inter)
+    h_ref = np.zeros((c * topk, inter))
+    for e, routes in oracle.group_routes(ids_ref):
+        cols = [r // topk for r in routes]
+        h_ref[routes] = oracle.glu_pair(wg[e], wu[e], xo[cols])[0]
+    assert_close(hh, h_ref, EPI_TOL, "wide h")
+    h32 = h_ref.astype(np.float32)
+    hq_ref = oracle.quantize_q8_1(h32)
+    hq = moeq8.q8_1_quantize_rows(to_dev(h32))
+    assert host(hq).tobytes() == hq_ref.tobytes()
+    y = host(moeq8.moe_grouped_mmvq(moeq8.DOWN, wdd, None, hq, g, n=hidden, k=inter, n_local_expert=n_exp,
+                                    ncols=c, topk=topk)).reshape(c * topk, hidden)
+    y_ref = np.zeros((c * topk, hidden))
+    for e, routes in oracle.group_routes(ids_ref):
+        y_ref[routes] = oracle.mmvq(wd[e], hq_ref[routes])
+    assert_close(y, y_ref, PROD_TOL, "wide y")
+    y32 = y_ref.astype(np.float32).reshape(c, topk, hidden)
+    w32 = w_ref.astype(np.float32)
+    out = host(moeq8.moe_combine(to_dev(y32), ids, to_dev(w32)))
+    assert_close(out, oracle.moe_combine(y32.astype(np.float64), ids_ref, w32.astype(np.float64)),
+                 EPI_TOL, "wide combine")
