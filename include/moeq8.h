@@ -238,9 +238,31 @@ int moe_route_topk_quantize(const float* x, int64_t x_row_stride, int64_t k, voi
  *
  * moe_grouped_mmvq / moe_grouped_mmvq_ex and moe_combine accept such wide
  * groupings (ncols up to MOEQ8_MAX_WIDE_COLS): a work item takes its expert's
- * routes in passes of MOEQ8_MAX_COLS columns.
+ * routes in passes of MOEQ8_MAX_COLS columns.  moe_grouped_gemm takes the
+ * same groupings.
  * ------------------------------------------------------------------------- */
 size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk);
+/* moe_grouped_gemm: the grouped products of moe_grouped_mmvq (same stages
+ * MOEQ8_GATE_UP_SWIGLU and MOEQ8_DOWN, same arguments, layouts and results)
+ * computed on the int8 matrix cores, for wide batches where an expert serves
+ * many routes.  The pages run large expert batches on a matrix-core GEMM
+ * (PR #826 description, Results: the WMMA routed-expert GEMM; the fused
+ * DS4.1 decode kernels commit: MMQ for wide Q4_K products); here the formats
+ * and the grouping stay those of the decode path.
+ *   Per output: blocks in ascending order, acc = fma(float(sumi_b),
+ *   d_w,b * d_x,b, acc) from +0 (sumi_b the block's exact integer dot,
+ *   d_w * d_x exact in fp32), then SwiGLU-DS4 for gate/up.  The result equals
+ *   the oracle's product to rounding; it is NOT bit-identical to
+ *   moe_grouped_mmvq, whose reduction order differs.
+ *   Requires n % 32 == 0 and k % 64 == 0 (MOEQ8_EINVAL otherwise); k up to
+ *   about 9000 (LDS; MOEQ8_EUNSUPPORTED beyond).  Rows of masked routes are
+ *   not written. */
+int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
+                     int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                     int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
+                     const void* grouping, int64_t ncols, int32_t topk, float* out,
+                     void* stream);
+
 int moe_route_topk_wide(const float* logits, const float* bias, const int32_t* owner_slot,
                         int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
                         int32_t* ids, float* weights, void* stream);

@@ -23,6 +23,7 @@ from .ops import (  # noqa: F401
     moe_group_routes,
     moe_route_topk,
     moe_grouped_mmvq,
+    moe_grouped_gemm,
     moe_grouped_mmvq_ex,
     moe_route_topk_quantize,
     moe_combine,

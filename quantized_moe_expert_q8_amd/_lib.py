@@ -27,6 +27,8 @@ SIGNATURES = {
                                       c_vp, c_vp]),
     "moe_grouped_mmvq": (ctypes.c_int, [c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                         c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
+    "moe_grouped_gemm": (ctypes.c_int, [c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                        c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
     "moe_grouped_mmvq_ex": (ctypes.c_int, [c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                            c_vp, c_i64, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64,
                                            c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]),

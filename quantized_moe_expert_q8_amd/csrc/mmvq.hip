@@ -85,21 +85,6 @@ struct MmvqParams {
     float* s_out;               // [ncols][s.n]
 };
 
-// Grouping words are written by an earlier launch and only read in this one,
-// so they may be read through the constant address space: wave-uniform
-// indices then become scalar loads, which do not queue behind the vector loads
-// of weights already in flight.  Eight or four consecutive words from word i
-// (4-byte alignment; the buffer is padded so that eight words from any route
-// entry stay inside it).
-typedef int32_t int8w __attribute__((ext_vector_type(8), aligned(4)));
-typedef int32_t int4w __attribute__((ext_vector_type(4), aligned(4)));
-__device__ __forceinline__ int8w grouping_words8(const int32_t* g, int64_t i) {
-    return *(const __attribute__((address_space(4))) int8w*)(g + i);
-}
-__device__ __forceinline__ int4w grouping_words4(const int32_t* g, int64_t i) {
-    return *(const __attribute__((address_space(4))) int4w*)(g + i);
-}
-
 // The q8_1 block rule on half a block: this lane holds 16 of the block's 32
 // values, the neighbouring lane (lane ^ 1) the other 16.  The block's amax and
 // its integer quant sum are combined across the pair (max and integer sums do

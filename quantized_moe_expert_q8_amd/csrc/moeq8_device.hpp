@@ -46,6 +46,21 @@ __host__ __device__ constexpr int64_t grouping_table_word(int64_t R) {
     return (4 + 3 * R + 1 + 8 + 3) & ~(int64_t)3;
 }
 
+// Grouping words are written by an earlier launch and only read in this one,
+// so they may be read through the constant address space: wave-uniform
+// indices then become scalar loads, which do not queue behind the vector loads
+// of weights already in flight.  Eight or four consecutive words from word i
+// (4-byte alignment; the buffer is padded so that eight words from any route
+// entry stay inside it).
+typedef int32_t int8w __attribute__((ext_vector_type(8), aligned(4)));
+typedef int32_t int4w __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ int8w grouping_words8(const int32_t* g, int64_t i) {
+    return *(const __attribute__((address_space(4))) int8w*)(g + i);
+}
+__device__ __forceinline__ int4w grouping_words4(const int32_t* g, int64_t i) {
+    return *(const __attribute__((address_space(4))) int4w*)(g + i);
+}
+
 // 16-byte vectors that only promise 4-byte alignment: the 34-byte blocks put
 // chunks on 4-byte boundaries, and gfx950 global loads accept that.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));

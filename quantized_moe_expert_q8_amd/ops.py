@@ -256,13 +256,8 @@ def moe_route_topk(logits: torch.Tensor, topk: int, *, bias: torch.Tensor | None
     return ids, weights, grouping
 
 
-def moe_grouped_mmvq(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, act_q: torch.Tensor,
-                     grouping: torch.Tensor, *, n: int, k: int, n_local_expert: int, ncols: int,
-                     topk: int, expert_stride_bytes: int | None = None,
-                     w_row_stride_bytes: int | None = None,
-                     out: torch.Tensor | None = None) -> torch.Tensor:
-    """Grouped per-expert MMVQ.  Experts are stored [n_local][n][k/32] blocks.
-    Returns out fp32 [ncols, topk, n] (masked routes' rows untouched)."""
+def _grouped_call(fn: str, stage: int, w_a, w_b, act_q, grouping, n, k, n_local_expert, ncols, topk,
+                  expert_stride_bytes, w_row_stride_bytes, out):
     if w_row_stride_bytes is None:
         w_row_stride_bytes = (k // QK) * Q8_0_BLOCK_BYTES
     if expert_stride_bytes is None:
@@ -287,9 +282,31 @@ def moe_grouped_mmvq(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, ac
         out = torch.empty((ncols, topk, n), dtype=torch.float32, device=w_a.device)
     _cuda(out, "out", torch.float32)
     _need(out, "out", ncols * topk * n * 4)
-    call("moe_grouped_mmvq", stage, _ptr(w_a), _ptr(w_b), expert_stride_bytes, w_row_stride_bytes,
+    call(fn, stage, _ptr(w_a), _ptr(w_b), expert_stride_bytes, w_row_stride_bytes,
          n_local_expert, n, k, _ptr(act_q), _ptr(grouping), ncols, topk, _ptr(out), _stream(w_a))
     return out
+
+
+def moe_grouped_mmvq(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, act_q: torch.Tensor,
+                     grouping: torch.Tensor, *, n: int, k: int, n_local_expert: int, ncols: int,
+                     topk: int, expert_stride_bytes: int | None = None,
+                     w_row_stride_bytes: int | None = None,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped per-expert MMVQ.  Experts are stored [n_local][n][k/32] blocks.
+    Returns out fp32 [ncols, topk, n] (masked routes' rows untouched)."""
+    return _grouped_call("moe_grouped_mmvq", stage, w_a, w_b, act_q, grouping, n, k, n_local_expert,
+                         ncols, topk, expert_stride_bytes, w_row_stride_bytes, out)
+
+
+def moe_grouped_gemm(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, act_q: torch.Tensor,
+                     grouping: torch.Tensor, *, n: int, k: int, n_local_expert: int, ncols: int,
+                     topk: int, expert_stride_bytes: int | None = None,
+                     w_row_stride_bytes: int | None = None,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """The grouped products on the int8 matrix cores (wide batches): same
+    arguments and results as moe_grouped_mmvq, equal to rounding (n % 32 == 0)."""
+    return _grouped_call("moe_grouped_gemm", stage, w_a, w_b, act_q, grouping, n, k, n_local_expert,
+                         ncols, topk, expert_stride_bytes, w_row_stride_bytes, out)
 
 
 def moe_route_topk_quantize(x: torch.Tensor, logits: torch.Tensor, topk: int, *,

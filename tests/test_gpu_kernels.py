@@ -721,3 +721,94 @@ def test_wide_grouped_products_vs_oracle(c, n_exp, hidden, inter):
     out = host(moeq8.moe_combine(to_dev(y32), ids, to_dev(w32)))
     assert_close(out, oracle.moe_combine(y32.astype(np.float64), ids_ref, w32.astype(np.float64)),
                  EPI_TOL, "wide combine")
+
+
+# ---------------------------------------------------------------------------
+# wide batches on the int8 matrix cores (moe_grouped_gemm)
+# ---------------------------------------------------------------------------
+
+def _gemm_case(c, n_exp, local, topk, hidden, inter, seed):
+    (wg, wu, wd), (wgd, wud, wdd) = _tiny_layer(seed, local, hidden, inter)
+    x = workloads.activations(seed, c, hidden)
+    logits = workloads.router_logits(seed + 1, c, n_exp)
+    own = None if local == n_exp else workloads.owner_slots(n_exp, local)
+    ids_ref, w_ref, _ = oracle.route_topk(logits, None, own, topk)
+    ids, _ = moeq8.moe_route_topk_wide(to_dev(logits), topk, owner_slot=None if own is None else to_dev(own),
+                                       n_local_expert=local)
+    assert np.array_equal(host(ids), ids_ref)
+    g = moeq8.moe_group_routes(ids, local)
+    return (wg, wu, wd), (wgd, wud, wdd), x, ids_ref, ids, g
+
+
+@pytest.mark.parametrize("c,n_exp,local,topk,hidden,inter", [
+    (40, 32, 32, 8, 1024, 256),      # gate/up K=1024: 4 route tiles per pass
+    (40, 8, 8, 4, 4096, 256),        # gate/up K=4096: one tile per pass, ~20 routes per expert (2 passes)
+    (130, 64, 40, 8, 320, 128),      # owner mask (masked routes); down n = 320: a half-empty row tile
+    (3, 16, 16, 8, 128, 64),         # K = 128 and 64: fewer block pairs than are prefetched
+    (1, 4, 4, 4, 64, 64),
+])
+def test_grouped_gemm_vs_oracle(c, n_exp, local, topk, hidden, inter):
+    """moe_grouped_gemm gate/up (h) and down (y) against the oracle route by
+    route; the down stage reads the oracle's h (quantised on both sides, bytes
+    equal); rows of masked routes stay untouched."""
+    say(f"grouped gemm c={c} E={n_exp} local={local} k={topk} H={hidden} I={inter}")
+    (wg, wu, wd), (wgd, wud, wdd), x, ids_ref, ids, g = _gemm_case(c, n_exp, local, topk, hidden, inter,
+                                                                   c + hidden + inter)
+    xo, xd = quantized_pair(x)
+    h = torch.full((c, topk, inter), float("nan"), device=DEV)
+    moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU, wgd, wud, xd, g, n=inter, k=hidden, n_local_expert=local,
+                           ncols=c, topk=topk, out=h)
+    hh = host(h).reshape(c * topk, inter)
+    masked = ids_ref.reshape(-1) < 0
+    assert np.isnan(hh[masked]).all()
+    h_ref = np.zeros((c * topk, inter))
+    for e, routes in oracle.group_routes(ids_ref):
+        h_ref[routes] = oracle.glu_pair(wg[e], wu[e], xo[[r // topk for r in routes]])[0]
+    assert_close(hh[~masked], h_ref[~masked], EPI_TOL, "gemm h")
+
+    h32 = h_ref.astype(np.float32)
+    hq_ref = oracle.quantize_q8_1(h32)
+    hq = moeq8.q8_1_quantize_rows(to_dev(h32))
+    assert host(hq).tobytes() == hq_ref.tobytes()
+    y = torch.full((c, topk, hidden), float("nan"), device=DEV)
+    moeq8.moe_grouped_gemm(moeq8.DOWN, wdd, None, hq, g, n=hidden, k=inter, n_local_expert=local,
+                           ncols=c, topk=topk, out=y)
+    yy = host(y).reshape(c * topk, hidden)
+    assert np.isnan(yy[masked]).all()
+    y_ref = np.zeros((c * topk, hidden))
+    for e, routes in oracle.group_routes(ids_ref):
+        y_ref[routes] = oracle.mmvq(wd[e], hq_ref[routes])
+    assert_close(yy[~masked], y_ref[~masked], PROD_TOL, "gemm y")
+
+
+def test_grouped_gemm_integer_dots_unit_scale():
+    """With every block scale 1.0 (fp16 0x3C00) each output is the exact
+    integer sum of the block dots, which fp32 holds exactly here: the matrix
+    core path must give it bit for bit (a wrong fragment layout, block order or
+    scale pairing changes it)."""
+    c, topk, n_exp, hidden, inter = 24, 4, 4, 256, 64
+    rng = np.random.default_rng(7)
+    nb = hidden // 32
+
+    def q8_0(rows):
+        w = np.zeros((n_exp, rows, nb), workloads.Q8_0_DTYPE)
+        w["d"] = np.float16(1.0)
+        w["qs"] = rng.integers(-127, 128, size=(n_exp, rows, nb, 32))
+        return w
+
+    wg, wu = q8_0(inter), q8_0(inter)
+    xq = np.zeros((c, nb), np.dtype([("d", "<f2"), ("s", "<f2"), ("qs", "i1", (32,))]))
+    xq["d"] = np.float16(1.0)
+    xq["qs"] = rng.integers(-127, 128, size=(c, nb, 32))
+    ids_np = np.stack([rng.choice(n_exp, size=topk, replace=False) for _ in range(c)]).astype(np.int32)
+    g = moeq8.moe_group_routes(to_dev(ids_np), n_exp)
+    h = moeq8.moe_grouped_gemm(moeq8.DOWN, to_dev(wg.reshape(-1)).reshape(-1), None,
+                               to_dev(np.repeat(xq, topk, axis=0).reshape(-1)).reshape(-1), g, n=inter,
+                               k=hidden, n_local_expert=n_exp, ncols=c, topk=topk)
+    hh = host(h).reshape(c * topk, inter)
+    qs_w = wg["qs"].astype(np.int64)                  # [E, rows, nb, 32]
+    qs_x = np.repeat(xq, topk, axis=0)["qs"].astype(np.int64)   # [R, nb, 32]
+    for r in range(c * topk):
+        e = ids_np.reshape(-1)[r]
+        exact = np.einsum("nbk,bk->n", qs_w[e], qs_x[r])
+        assert np.array_equal(hh[r], exact.astype(np.float32)), r
