@@ -14,6 +14,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
             per launch / mean launch time from HIP events, against 8 TB/s
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
   sweep     the routed layer (256 experts, top-8) at 1, 2, 4, 5, 8 columns
+  wide      the same layer at 32..1024 columns: grouped products on the int8
+            matrix cores against the grouped MMVQ in passes of 8 columns
 """
 
 from __future__ import annotations
@@ -44,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-wide", action="store_true",
+                    help="skip the wide-batch (32..1024 columns) measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the oracle sample")
     ap.add_argument("--pmc-copy", action="store_true",
@@ -447,6 +451,8 @@ def main():
 
     if not args.no_sweep:
         result["sweep"] = sweep(torch, workloads, moeq8, ml, args)
+    if not args.no_wide:
+        result["wide"] = wide_sweep(torch, workloads, moeq8, ml, args)
 
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -514,6 +520,79 @@ def sweep(torch, workloads, moeq8, ml, args):
         log(f"sweep {rec}")
         out.append(rec)
     del bank
+    torch.cuda.empty_cache()
+    return out
+
+
+def wide_gate_up_bytes(n_active, n_valid, cols, hidden, inter):
+    return gate_up_launch_bytes(n_active, n_valid, cols, hidden, inter)
+
+
+def wide_down_bytes(n_active, n_valid, hidden, inter):
+    """Per grouped down launch on q8_1 h: every active expert's down matrix
+    once, the q8_1 h rows once, the y rows written."""
+    return n_active * hidden * (inter // 32 * 34) + n_valid * (inter // 32 * 36) + n_valid * hidden * 4
+
+
+def wide_sweep(torch, workloads, moeq8, ml, args):
+    """The 256-expert layer at 32..1024 columns (one weight copy, 3.4 GB: a
+    launch over all experts reads far more than the 256 MB Infinity Cache).
+    Per column count: the seven-launch layer with the grouped products on the
+    matrix cores and with the grouped MMVQ, and each grouped product alone
+    (graphs, HIP events), against a plain streaming read of as many bytes."""
+    cfg = workloads.CONFIGS["wide_e256"]
+    hidden, inter, topk, n_exp, seed = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"], cfg["seed"]
+    bank = Bank(moeq8, torch, 1, n_exp, hidden, inter, seed)
+    experts = bank.experts(ml, 0)
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    out = []
+    for cols in cfg["cols"]:
+        x = torch.from_numpy(workloads.activations(seed, cols, hidden)).cuda()
+        lg = torch.from_numpy(workloads.router_logits(seed, cols, n_exp)).cuda()
+        bs = torch.from_numpy(workloads.router_bias(seed, n_exp)).cuda()
+        ws = ml.WideWorkspace(cols, hidden, inter, topk, "cuda")
+        ml.forward_wide(x, lg, bs, None, n_exp, experts, ws)
+        torch.cuda.synchronize()
+        words = ws.grouping.cpu().numpy().view(np.int32)
+        n_active, n_valid = int(words[0]), int(words[1])
+        reps = 10 if cols >= 512 else 20
+        rec = {"cols": cols, "active_experts": n_active,
+               "routes_per_expert_mean": round(n_valid / max(1, n_active), 2)}
+        gu_b = gate_up_launch_bytes(n_active, n_valid, cols, hidden, inter)
+        dn_b = wide_down_bytes(n_active, n_valid, hidden, inter)
+        for name, fn in (("gemm", moeq8.moe_grouped_gemm), ("mmvq", moeq8.moe_grouped_mmvq)):
+            layer_ms = time_graph(torch, lambda: ml.forward_wide(x, lg, bs, None, n_exp, experts, ws,
+                                                                 products=name), reps)
+            gu_us = time_graph(torch, lambda: fn(moeq8.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq,
+                                                 ws.grouping, n=inter, k=hidden, n_local_expert=n_exp,
+                                                 ncols=cols, topk=topk, out=ws.h), reps) * 1e3
+            dn_us = time_graph(torch, lambda: fn(moeq8.DOWN, experts.down, None, ws.hq, ws.grouping,
+                                                 n=hidden, k=inter, n_local_expert=n_exp, ncols=cols,
+                                                 topk=topk, out=ws.y), reps) * 1e3
+            rec[name] = {"layer_us": round(layer_ms * 1e3, 1),
+                         "cols_per_s": round(cols / (layer_ms * 1e-3), 1),
+                         "gate_up_us": round(gu_us, 1),
+                         "gate_up_gbps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
+                         "down_us": round(dn_us, 1),
+                         "down_gbps": round(dn_b / (dn_us * 1e-6) / 1e9, 1)}
+        # the ceiling: as many bytes read from the gate and up banks
+        half = min(int(gu_b) // 2, bank.gate[0].numel()) // 16 * 16
+
+        def stream_only():
+            moeq8.stream_read(bank.gate[0], half, sink)
+            moeq8.stream_read(bank.up[0], half, sink)
+
+        st_us = time_graph(torch, stream_only, reps) * 1e3
+        st_bytes = 2 * half
+        rec["gate_up_bytes"] = int(gu_b)
+        rec["down_bytes"] = int(dn_b)
+        rec["ceiling_gbps"] = round(st_bytes / (st_us * 1e-6) / 1e9, 1)
+        rec["gemm"]["gate_up_frac_of_peak"] = round(rec["gemm"]["gate_up_gbps"] / HBM_PEAK_GBPS, 4)
+        rec["gemm"]["gate_up_frac_of_ceiling"] = round(rec["gemm"]["gate_up_gbps"] / rec["ceiling_gbps"], 4)
+        log(f"wide {rec}")
+        out.append(rec)
+        del ws, x, lg, bs
+    del bank, experts
     torch.cuda.empty_cache()
     return out
 

@@ -254,9 +254,10 @@ size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk);
  *   d_w * d_x exact in fp32), then SwiGLU-DS4 for gate/up.  The result equals
  *   the oracle's product to rounding; it is NOT bit-identical to
  *   moe_grouped_mmvq, whose reduction order differs.
- *   Requires n % 32 == 0 and k % 64 == 0 (MOEQ8_EINVAL otherwise); k up to
- *   about 9000 (LDS; MOEQ8_EUNSUPPORTED beyond).  Rows of masked routes are
- *   not written. */
+ *   Requires n % 32 == 0 and k % 64 == 0 (MOEQ8_EINVAL otherwise).  Rows of
+ *   masked routes are not written.  Work is split into (expert, 16-route
+ *   chunk, row tile) units, so an expert with many routes spreads over many
+ *   workgroups. */
 int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
                      int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
                      int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,

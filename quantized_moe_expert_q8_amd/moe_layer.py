@@ -225,6 +225,51 @@ def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared,
     return ws.out, ws.ys
 
 
+class WideWorkspace:
+    """Buffers of one wide-batch layer (up to 1024 columns, no shared expert)."""
+
+    def __init__(self, ncols: int, hidden: int, inter: int, topk: int, device):
+        dev = torch.device(device)
+        u8, f32 = torch.uint8, torch.float32
+        R = ncols * topk
+        self.ncols, self.topk = ncols, topk
+        self.xq = torch.empty((ncols, hidden // QK * Q81), dtype=u8, device=dev)
+        self.ids = torch.empty((ncols, topk), dtype=torch.int32, device=dev)
+        self.weights = torch.empty((ncols, topk), dtype=f32, device=dev)
+        self.grouping = torch.empty(ops.moe_grouping_bytes_wide(ncols, topk), dtype=u8, device=dev)
+        self.h = torch.zeros((ncols, topk, inter), dtype=f32, device=dev)
+        self.hq = torch.zeros((R, inter // QK * Q81), dtype=u8, device=dev)
+        self.y = torch.zeros((ncols, topk, hidden), dtype=f32, device=dev)
+        self.out = torch.empty((ncols, hidden), dtype=f32, device=dev)
+
+
+def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
+                 owner_slot: torch.Tensor | None, n_local_expert: int, experts: RoutedExperts,
+                 ws: WideWorkspace, products: str = "gemm"):
+    """A routed layer over many columns (prefill-like): q8_1 of x, per-column
+    selection, one expert grouping, grouped gate/up + SwiGLU, q8_1 of h,
+    grouped down, combine; seven launches on the current stream, nothing
+    allocated.  products="gemm" runs the grouped products on the int8 matrix
+    cores (moe_grouped_gemm), "mmvq" runs the grouped MMVQ in passes of 8
+    columns.  Returns ws.out."""
+    if products not in ("gemm", "mmvq"):
+        raise ValueError("products must be 'gemm' or 'mmvq'")
+    grouped = ops.moe_grouped_gemm if products == "gemm" else ops.moe_grouped_mmvq
+    c, topk = ws.ncols, ws.topk
+    hidden, inter = experts.hidden, experts.inter
+    ops.q8_1_quantize_rows(x, out=ws.xq)
+    ops.moe_route_topk_wide(logits, topk, bias=bias, owner_slot=owner_slot,
+                            n_local_expert=n_local_expert, ids=ws.ids, weights=ws.weights)
+    ops.moe_group_routes(ws.ids, experts.n_local, grouping=ws.grouping)
+    grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
+            n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
+    ops.q8_1_quantize_rows(ws.h.view(c * topk, inter), out=ws.hq)
+    grouped(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
+            n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
+    ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
+    return ws.out
+
+
 def expert_bytes(hidden: int, inter: int) -> int:
     """Q8_0 bytes of one routed expert (gate + up + down)."""
     return 3 * inter * (hidden // QK) * Q80

@@ -348,3 +348,77 @@ def test_ep_share_l43_e128_c8():
         assert bits_equal(hs_full[:, :share].contiguous(), w.hs)
     del g, bank
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# wide batches: the 256-expert layer at 512 columns on the matrix-core GEMM
+# ---------------------------------------------------------------------------
+
+def test_wide_e256_c512():
+    """The wide layer (forward_wide, products on the int8 matrix cores) at 512
+    columns, 256 experts resident (synthetic blocks, the same generator on both
+    sides): q8_1(x) bytes, ids and the grouping exact, weights, and for three
+    sampled experts every route's h (against the oracle) and y (the down GEMM
+    run on q8_1 of the oracle's h, zero rows elsewhere, which must give exact
+    zeros); the combine on synthetic y at full size."""
+    cfg = workloads.CONFIGS["wide_e256"]
+    H, I, E, topk, seed = cfg["hidden"], cfg["inter"], cfg["experts"], cfg["topk"], cfg["seed"]
+    c = 512
+    say(f"config wide_e256 at {c} columns")
+    rb_h, rb_i = H // 32 * 34, I // 32 * 34
+    gate = torch.empty(E * I * rb_h, dtype=torch.uint8, device=DEV)
+    up = torch.empty_like(gate)
+    down = torch.empty(E * H * rb_i, dtype=torch.uint8, device=DEV)
+    moeq8.synth_q8_0_fill(gate, E, I * H // 32, E, seed, 0, 0, workloads.MATRIX_GATE)
+    moeq8.synth_q8_0_fill(up, E, I * H // 32, E, seed, 0, 0, workloads.MATRIX_UP)
+    moeq8.synth_q8_0_fill(down, E, H * I // 32, E, seed, 0, 0, workloads.MATRIX_DOWN)
+    experts = ml.RoutedExperts(gate, up, down, E, H, I)
+    x = workloads.activations(seed, c, H)
+    logits = workloads.router_logits(seed, c, E)
+    bias = workloads.router_bias(seed, E)
+    ws = ml.WideWorkspace(c, H, I, topk, DEV)
+    ml.forward_wide(to_dev(x), to_dev(logits), to_dev(bias), None, E, experts, ws)
+    torch.cuda.synchronize()
+
+    xq_ref = oracle.quantize_q8_1(x)
+    assert host(ws.xq).tobytes() == xq_ref.tobytes()
+    ids_ref, w_ref, _ = oracle.route_topk(logits, bias, None, topk)
+    assert np.array_equal(host(ws.ids), ids_ref)
+    assert_close(host(ws.weights), w_ref, EPI_TOL, "weights")
+    groups = oracle.group_routes(ids_ref)
+    words = host(ws.grouping).view(np.int32)
+    R = c * topk
+    assert words[0] == len(groups) and words[1] == R
+    offset = words[4 + R:4 + 2 * R + 1]
+    route = words[4 + 2 * R + 1:4 + 3 * R + 1]
+    for a, (e, routes) in enumerate(groups):
+        assert words[4 + a] == e and list(route[offset[a]:offset[a + 1]]) == routes
+
+    by_load = sorted(groups, key=lambda g: len(g[1]))
+    sample = [by_load[0], by_load[len(by_load) // 2], by_load[-1]]
+    say(f"  {len(groups)} active experts; sampled loads {[len(r) for _, r in sample]}")
+    hh = host(ws.h).reshape(R, I)
+    h_in = np.zeros((R, I), np.float32)
+    y_ref = {}
+    for e, routes in sample:
+        wg = workloads.synth_q8_0_matrix(seed, 0, e, workloads.MATRIX_GATE, I, H)
+        wu = workloads.synth_q8_0_matrix(seed, 0, e, workloads.MATRIX_UP, I, H)
+        wd = workloads.synth_q8_0_matrix(seed, 0, e, workloads.MATRIX_DOWN, H, I)
+        h_ref = oracle.glu_pair(wg, wu, xq_ref[[r // topk for r in routes]])[0]
+        assert_close(hh[routes], h_ref, EPI_TOL, f"h of expert {e}")
+        h_in[routes] = h_ref.astype(np.float32)
+        y_ref[e] = (routes, oracle.mmvq(wd, oracle.quantize_q8_1(h_ref.astype(np.float32))))
+    hq_in = moeq8.q8_1_quantize_rows(to_dev(h_in))
+    assert host(hq_in).tobytes() == oracle.quantize_q8_1(h_in).tobytes()
+    y = host(moeq8.moe_grouped_gemm(moeq8.DOWN, down, None, hq_in, ws.grouping, n=H, k=I,
+                                    n_local_expert=E, ncols=c, topk=topk)).reshape(R, H)
+    sampled = np.zeros(R, bool)
+    for e, (routes, yr) in y_ref.items():
+        assert_close(y[routes], yr, PROD_TOL, f"y of expert {e}")
+        sampled[routes] = True
+    assert np.all(y[~sampled] == 0.0)
+
+    y32 = workloads.normal_f32(seed + 100, (c, topk, H))
+    comb = host(moeq8.moe_combine(to_dev(y32), ws.ids, to_dev(w_ref.astype(np.float32))))
+    assert_close(comb, oracle.moe_combine(y32.astype(np.float64), ids_ref, w_ref.astype(np.float32)
+                                          .astype(np.float64)), EPI_TOL, "combine")

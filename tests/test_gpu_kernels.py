@@ -741,10 +741,12 @@ def _gemm_case(c, n_exp, local, topk, hidden, inter, seed):
 
 
 @pytest.mark.parametrize("c,n_exp,local,topk,hidden,inter", [
-    (40, 32, 32, 8, 1024, 256),      # gate/up K=1024: 4 route tiles per pass
-    (40, 8, 8, 4, 4096, 256),        # gate/up K=4096: one tile per pass, ~20 routes per expert (2 passes)
+    (40, 32, 32, 8, 1024, 256),      # gate/up K = 1024
+    (40, 8, 8, 4, 4096, 256),        # K = 4096, ~20 routes per expert: two 16-route chunks
+    (300, 4, 4, 4, 256, 64),         # every column routes to all 4 experts: 19 chunks each
+    (48, 256, 256, 8, 256, 64),      # ~150 active experts: the unit search spans several waves of groups
     (130, 64, 40, 8, 320, 128),      # owner mask (masked routes); down n = 320: a half-empty row tile
-    (3, 16, 16, 8, 128, 64),         # K = 128 and 64: fewer block pairs than are prefetched
+    (3, 16, 16, 8, 128, 64),         # K = 128 and 64: fewer block pairs than a step holds
     (1, 4, 4, 4, 64, 64),
 ])
 def test_grouped_gemm_vs_oracle(c, n_exp, local, topk, hidden, inter):

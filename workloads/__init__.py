@@ -18,6 +18,8 @@ GPU):
   ep_share_l43_e128_c8    one GPU's share of a two-way split: 43 layers x 128
                           local experts, routing over 256 with the other 128
                           masked, 8 columns, half of the shared expert, seed 5
+  wide_e256               the routed layer at 32, 128, 512 and 1024 columns
+                          (prefill-like batches), seed 6
 """
 
 from __future__ import annotations
@@ -46,6 +48,10 @@ CONFIGS = {
     "ep_share_l43_e128_c8": dict(kind="routed", experts=256, local_experts=128, layers=43,
                                  hidden=4096, inter=1024, cols=(8,), topk=8, seed=5,
                                  shared_inter=2048, shared_share=2),
+    # wide batches (prefill-like, many columns) on the same 256-expert layer:
+    # the grouped products at 32..1024 columns, every expert typically active
+    "wide_e256": dict(kind="wide", experts=256, local_experts=256, layers=1, hidden=4096,
+                      inter=1024, cols=(32, 128, 512, 1024), topk=8, seed=6),
 }
 
 
