@@ -27,10 +27,13 @@
 // fragments through a private LDS area (no workgroup barrier anywhere), while
 // the next step's loads are in flight.
 //
-// Work.  A work unit is (group, row tile, chunk of up to 16 of the group's
-// routes): the routing is very uneven at wide batches (one expert may get
-// hundreds of routes), so a heavily routed expert is spread over many units
-// instead of one unit looping over its routes.  Units are numbered with the
+// Work.  A work unit is (group, row tile, chunk of up to 16 * NT of the
+// group's routes); a wave runs its chunk as NT 16-route tiles against each
+// weight load (the rearranged weights stay in LDS while the tiles' activations
+// pass through one shared area in turn), so weight rows are read once per
+// chunk.  The routing is very uneven at wide batches (one expert may get
+// hundreds of routes), so a heavily routed expert is spread over several
+// chunks instead of one unit looping over its routes.  Units are numbered with the
 // chunk fastest, and unit u runs on XCD u / ceil(units / 8) (workgroups are
 // dispatched to the 8 XCDs round-robin), so the chunks that read the same
 // weight rows run on one XCD at about the same time and share its L2.
@@ -50,7 +53,12 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int GEMM_WAVES = MOEQ8_GEMM_WAVES;
 constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
-constexpr int CHUNK = 16;                // routes per unit = MFMA M
+constexpr int TILE = 16;                 // routes per matrix-core tile = MFMA M
+#ifndef MOEQ8_GEMM_NT
+#define MOEQ8_GEMM_NT 2
+#endif
+constexpr int NT = MOEQ8_GEMM_NT;        // tiles per wave (one weight load each step)
+constexpr int CHUNK = TILE * NT;         // routes per work unit
 constexpr int SP = 4;                    // block pairs per step (one per lane quarter)
 constexpr int SB = 2 * SP;               // blocks per step
 constexpr int XCDS = 8;
@@ -123,7 +131,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 }
 
 template <bool PAIR>
-__global__ __launch_bounds__(GEMM_THREADS) void k_grouped_gemm(const GemmParams p) {
+__global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void k_grouped_gemm(
+    const GemmParams p) {
     constexpr int WAVE_ROWS = PAIR ? 16 : 32;
     constexpr int WG_ROWS = WAVE_ROWS * GEMM_WAVES;
     __shared__ __align__(16) uint8_t lds_all[GEMM_WAVES * L_WAVE];
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_grouped_gemm(const GemmParams 
     const uint32_t tiles = (uint32_t)p.tiles;
     const uint32_t xcd = blockIdx.x % XCDS;
     const uint32_t slot = blockIdx.x / XCDS;
-    // chunks <= n_active + n_valid / 16, so slots past this bound have nothing
+    // chunks <= n_active + n_valid / CHUNK, so slots past this bound have nothing
     const uint32_t bound = ((uint32_t)n_active + (uint32_t)hdr[1] / CHUNK) * tiles;
     if (slot >= (bound + XCDS - 1) / XCDS) return;
 
@@ -190,47 +199,64 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_grouped_gemm(const GemmParams 
     const uint32_t rem = u - ubase;
     const uint32_t t = rem / nchunk;                   // row tile
     const int rbegin = gbegin + (int)(rem - t * nchunk) * CHUNK;
-    const int nr = min(gend - rbegin, CHUNK);          // routes of this unit, 1..16
+    const int nr = min(gend - rbegin, CHUNK);          // routes of this unit, 1..CHUNK
 
     const int64_t r0 = (int64_t)t * WG_ROWS + (int64_t)wave * WAVE_ROWS;
     if (r0 >= p.n) return;                             // n % 32 == 0: whole waves in or out
 
     // ---- operands ---------------------------------------------------------
     const int32_t* route = p.grouping + 4 + 2 * (int64_t)Rk + 1;
-    // lane (c, q) loads route slot c (clamped to the unit's last route: its
-    // results are computed but not stored) and weight row c of each fragment
-    const int myroute = route[rbegin + min(c, nr - 1)];
-    const int rr = (myroute >= 0 && myroute < Rk) ? myroute : 0;
-    const int64_t arow = (int64_t)(((uint64_t)(uint32_t)rr * p.act_route_mul) >> 32);
-    const uint8_t* abase = p.act + arow * p.act_row_bytes + (int64_t)q * (2 * Q81_BYTES);
+    // lane (c, q) loads route slot 16t + c of each tile t (clamped to the
+    // unit's last route: its results are computed but not stored) and weight
+    // row c of each fragment
+    const uint8_t* abase[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        const int myroute = route[rbegin + min(TILE * tt + c, nr - 1)];
+        const int rr = (myroute >= 0 && myroute < Rk) ? myroute : 0;
+        const int64_t arow = (int64_t)(((uint64_t)(uint32_t)rr * p.act_route_mul) >> 32);
+        abase[tt] = p.act + arow * p.act_row_bytes + (int64_t)q * (2 * Q81_BYTES);
+    }
+    const int ntiles = (nr + TILE - 1) / TILE;         // tiles holding routes, 1..NT
     const int64_t ew = (int64_t)e * p.expert_stride + (r0 + c) * p.row_stride + (int64_t)q * (2 * Q80_BYTES);
     const uint8_t* wbase0 = p.w0 + ew;
     const uint8_t* wbase1 = PAIR ? p.w1 + ew : wbase0 + 16 * p.row_stride;
     const int npairs = p.nb >> 1;
     const int nsteps = (npairs + SP - 1) / SP;
 
-    struct Step { W68 w[2]; A72 a; };
-    auto load_step = [&](Step& st, int s) {
-        // pair SP*s + q of each row (clamped to the last pair: re-read, unused)
-        const int j = min(SP * min(s, nsteps - 1) + q, npairs - 1) - q;
-        const int64_t wo = (int64_t)j * (2 * Q80_BYTES);
-        load68(st.w[0], wbase0 + wo);
-        load68(st.w[1], wbase1 + wo);
-        load72(st.a, abase + (int64_t)j * (2 * Q81_BYTES));
+    // Weights of a step are double-buffered; the activations of each tile
+    // are single-buffered: tile t's loads for step s + 1 go out as soon as its
+    // step-s values are in LDS, which is after step s + 1's weight loads and
+    // before step s + 2's, so every wait is for the oldest loads in flight.
+    auto pair_of = [&](int s) {
+        // pair SP*s + q of each row (clamped to the last pair: re-read, unused),
+        // as an offset from the lane's own pair q
+        return min(SP * min(s, nsteps - 1) + q, npairs - 1) - q;
+    };
+    auto load_w = [&](W68 (&w)[2], int s) {
+        const int64_t wo = (int64_t)pair_of(s) * (2 * Q80_BYTES);
+        load68(w[0], wbase0 + wo);
+        load68(w[1], wbase1 + wo);
+    };
+    A72 areg[NT];
+    auto load_a = [&](int tt, int s) {
+        load72(areg[tt], abase[tt] + (int64_t)pair_of(s) * (2 * Q81_BYTES));
     };
 
-    float acc[2][4];
+    float acc[NT][2][4];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[f][i] = 0.0f;
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tt][f][i] = 0.0f;
 
     // Rearrange a step into fragment order in LDS, then run its blocks.
-    auto run_step = [&](const Step& st, int s) {
+    auto run_step = [&](const W68 (&wst)[2], int s) {
         // this lane's two blocks are k = 2q and 2q + 1 of the step
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-            const W68& w = st.w[f];
+            const W68& w = wst[f];
             uint32_t q0[8];                                // block 2q's quants, dword aligned
 #pragma unroll
             for (int i = 0; i < 8; ++i) q0[i] = __builtin_amdgcn_alignbit(w.v[i + 1], w.v[i], 16);
@@ -244,19 +270,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_grouped_gemm(const GemmParams 
             *reinterpret_cast<float2*>(lds + L_DW + ((f * 16 + c) * SB + 2 * q) * 4) =
                 make_float2(half_bits_to_float(w.v[0]), half_bits_to_float(w.v[8] >> 16));
         }
-        {
-            const A72& a = st.a;
-            uint8_t* aq = lds + L_AQ;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                *reinterpret_cast<uint2*>(aq + frag_off(2 * q, qq, c)) = make_uint2(a.v[1 + 2 * qq], a.v[2 + 2 * qq]);
-                *reinterpret_cast<uint2*>(aq + frag_off(2 * q + 1, qq, c)) =
-                    make_uint2(a.v[10 + 2 * qq], a.v[11 + 2 * qq]);
-            }
-            float* dx = reinterpret_cast<float*>(lds + L_DX);
-            dx[(2 * q) * 16 + c] = half_bits_to_float(a.v[0]);
-            dx[(2 * q + 1) * 16 + c] = half_bits_to_float(a.v[9]);
-        }
         // the row scales of this lane's weight row for all blocks of the step
         float dw[2][SB];
 #pragma unroll
@@ -268,46 +281,71 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_grouped_gemm(const GemmParams 
         }
         const int kvalid = min(SB, p.nb - SB * s);         // blocks of this step inside the row
 #pragma unroll
-        for (int k = 0; k < SB; ++k) {
-            if (k >= kvalid) break;
-            const long xa = *reinterpret_cast<const long*>(lds + L_AQ + frag_off(k, q, c));
-            const float4 dx4 = *reinterpret_cast<const float4*>(lds + L_DX + (k * 16 + 4 * q) * 4);
-            const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
+        for (int tt = 0; tt < NT; ++tt) {
+            if (tt >= ntiles) break;
+            {
+                const A72& a = areg[tt];
+                uint8_t* aq = lds + L_AQ;
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                const long wb = *reinterpret_cast<const long*>(lds + L_WQ + f * (SB * 512) + frag_off(k, q, c));
-                const i32x4 z = {0, 0, 0, 0};
-                const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa, wb, z, 0, 0, 0);
+                for (int qq = 0; qq < 4; ++qq) {
+                    *reinterpret_cast<uint2*>(aq + frag_off(2 * q, qq, c)) = make_uint2(a.v[1 + 2 * qq], a.v[2 + 2 * qq]);
+                    *reinterpret_cast<uint2*>(aq + frag_off(2 * q + 1, qq, c)) =
+                        make_uint2(a.v[10 + 2 * qq], a.v[11 + 2 * qq]);
+                }
+                float* dx = reinterpret_cast<float*>(lds + L_DX);
+                dx[(2 * q) * 16 + c] = half_bits_to_float(a.v[0]);
+                dx[(2 * q + 1) * 16 + c] = half_bits_to_float(a.v[9]);
+            }
+            load_a(tt, s + 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[f][i] = fmaf((float)d[i], dw[f][k] * dxv[i], acc[f][i]);
+            for (int k = 0; k < SB; ++k) {
+                if (k >= kvalid) break;
+                const long xa = *reinterpret_cast<const long*>(lds + L_AQ + frag_off(k, q, c));
+                const float4 dx4 = *reinterpret_cast<const float4*>(lds + L_DX + (k * 16 + 4 * q) * 4);
+                const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const long wb = *reinterpret_cast<const long*>(lds + L_WQ + f * (SB * 512) + frag_off(k, q, c));
+                    const i32x4 z = {0, 0, 0, 0};
+                    const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa, wb, z, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[tt][f][i] = fmaf((float)d[i], dw[f][k] * dxv[i], acc[tt][f][i]);
+                }
             }
         }
     };
 
-    Step sa, sb;
-    load_step(sa, 0);
+    W68 wa[2], wb[2];
+    load_w(wa, 0);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+        if (tt < ntiles) load_a(tt, 0);
     for (int s = 0; s < nsteps; s += 2) {
-        load_step(sb, s + 1);
-        run_step(sa, s);
+        load_w(wb, s + 1);
+        run_step(wa, s);
         if (s + 1 >= nsteps) break;
-        load_step(sa, s + 2);
-        run_step(sb, s + 1);
+        load_w(wa, s + 2);
+        run_step(wb, s + 1);
     }
 
     // ---- epilogue: lane (c, q) holds row r0 + c (+16 for the second down
-    // fragment) of route slots 4q + i --------------------------------------
+    // fragment) of route slots 16t + 4q + i ---------------------------------
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int slotr = 4 * q + i;
-        if (slotr >= nr) continue;
-        const int r = route[rbegin + slotr];
-        if (r < 0 || r >= Rk) continue;
-        float* o = p.out + (int64_t)r * p.n + r0 + c;
-        if constexpr (PAIR) {
-            o[0] = swiglu_ds4_f32(acc[0][i], acc[1][i]);
-        } else {
-            o[0] = acc[0][i];
-            o[16] = acc[1][i];
+    for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slotr = TILE * tt + 4 * q + i;
+            if (slotr >= nr) continue;
+            const int r = route[rbegin + slotr];
+            if (r < 0 || r >= Rk) continue;
+            float* o = p.out + (int64_t)r * p.n + r0 + c;
+            if constexpr (PAIR) {
+                o[0] = swiglu_ds4_f32(acc[tt][0][i], acc[tt][1][i]);
+            } else {
+                o[0] = acc[tt][0][i];
+                o[16] = acc[tt][1][i];
+            }
         }
     }
 }
