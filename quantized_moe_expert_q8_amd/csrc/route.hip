@@ -285,103 +285,136 @@ __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_topk_wide(
 
 // The expert grouping of any number of routes (the same layout as the one
 // moe_route_topk writes), from the route ids, in one workgroup of 1024
-// threads: keys (local expert << 14 | route), invalid routes as 0xFFFFFFFF,
-// sorted ascending in LDS (bitonic), so routes come out by (expert, route
-// index) ascending; a route's position is its rank, an expert's group starts
-// at the first key carrying it.  Deterministic: no atomics.
+// threads, as a counting sort that needs no ordering from atomics:
+//   1. wave w counts the local experts of its contiguous share of the routes
+//      (LDS atomic adds: the counts do not depend on their order);
+//   2. per expert, the waves' counts become a prefix over waves, and one
+//      block scan over experts gives each expert's first position and each
+//      active expert's group index;
+//   3. wave w places its share in ascending route order, 64 routes at a time:
+//      a route's rank among the earlier lanes holding the same expert comes
+//      from ballots over the expert's bits.
+// So routes come out by (expert, route index) ascending, as a stable sort by
+// expert gives; ids outside [0, n_local) are masked.
 constexpr int WIDE_THREADS = 1024;
+constexpr int WIDE_WAVES = WIDE_THREADS / 64;
 constexpr int WIDE_MAX_R = 16384;                      // 1024 columns x top-16
+
+// exclusive prefix sum over the 1024 threads; *total gets the sum
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint32_t incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t t = (uint32_t)__builtin_amdgcn_ds_bpermute((lane - d) << 2, (int)incl);
+        if (lane >= d) incl += t;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int i = 0; i < WIDE_WAVES; ++i) {
+        const uint32_t x = wsum[i];
+        before += i < w ? x : 0u;
+        all += x;
+    }
+    *total = all;
+    return before + incl - v;
+}
 
 __global__ __launch_bounds__(WIDE_THREADS) void k_group_routes(
     const int32_t* __restrict__ ids, int64_t ncols, int topk, int n_local,
     int32_t* __restrict__ grouping) {
-    __shared__ uint32_t key[WIDE_MAX_R];
-    __shared__ int32_t part[WIDE_THREADS];
-    const int tid = threadIdx.x;
+    // per-wave counts, two 16-bit counters per word (a wave holds at most
+    // 1024 routes, so a counter never carries into its neighbour)
+    __shared__ uint32_t cnt[WIDE_WAVES][MOEQ8_MAX_EXPERTS / 2];
+    __shared__ int32_t first[MOEQ8_MAX_EXPERTS];
+    __shared__ uint32_t wsum[WIDE_WAVES];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int R = (int)ncols * topk;
-    int rp = 1;
-    while (rp < R) rp <<= 1;
-    for (int i = tid; i < rp; i += WIDE_THREADS) {
-        const int id = i < R ? ids[i] : -1;
-        key[i] = (id >= 0 && id < n_local) ? ((uint32_t)id << 14 | (uint32_t)i) : 0xFFFFFFFFu;
+    const int share = ((R + WIDE_WAVES - 1) / WIDE_WAVES + 63) / 64 * 64;   // routes per wave
+    const int rb = w * share, re = min(R, rb + share);
+    auto key_of = [&](int r) -> int {                  // local expert, or n_local when masked
+        if (r >= re) return MOEQ8_MAX_EXPERTS;
+        const int id = ids[r];
+        return (id >= 0 && id < n_local) ? id : MOEQ8_MAX_EXPERTS;
+    };
+
+    for (int i = tid; i < WIDE_WAVES * (MOEQ8_MAX_EXPERTS / 2); i += WIDE_THREADS) (&cnt[0][0])[i] = 0u;
+    __syncthreads();
+    for (int r = rb + lane; r < re; r += 64) {
+        const int e = key_of(r);
+        if (e < MOEQ8_MAX_EXPERTS) atomicAdd(&cnt[w][e >> 1], 1u << (16 * (e & 1)));
     }
     __syncthreads();
-    for (int k = 2; k <= rp; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < rp; i += WIDE_THREADS) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const uint32_t a = key[i], b = key[ixj];
-                    const bool up = (i & k) == 0;
-                    if (up ? (a > b) : (a < b)) {
-                        key[i] = b;
-                        key[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
+
+    // thread e: expert e's count per wave -> prefix over waves, total
+    const int e = tid;
+    uint32_t tot = 0;
+    if (e < n_local) {
+        for (int v = 0; v < WIDE_WAVES; ++v) {
+            const uint32_t word = cnt[v][e >> 1];
+            const uint32_t c = (word >> (16 * (e & 1))) & 0xffffu;
+            tot += c;
         }
     }
+    __syncthreads();                                   // every thread has read its counts
+    if (e < n_local) {
+        uint32_t run = 0;
+        for (int v = 0; v < WIDE_WAVES; ++v) {
+            const uint32_t c = (cnt[v][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            // only this thread changes expert e's half of the word; xor
+            // replaces it without touching the neighbour's half
+            atomicXor(&cnt[v][e >> 1], ((c ^ run) & 0xffffu) << (16 * (e & 1)));
+            run += c;
+        }
+    }
+    // one scan of (active << 16 | count): positions and group indices
+    uint32_t all = 0;
+    const uint32_t packed = (tot > 0 ? (1u << 16) : 0u) | tot;   // tot <= 16384 < 2^16
+    const uint32_t ex = block_excl_scan(packed, wsum, &all);
+    const int pos0 = (int)(ex & 0xffffu), grp = (int)(ex >> 16);
+    const int n_valid = (int)(all & 0xffffu), n_heads = (int)(all >> 16);
+    if (e < MOEQ8_MAX_EXPERTS) first[e] = pos0;
     int32_t* g_expert = grouping + 4;
     int32_t* g_offset = grouping + 4 + R;
     int32_t* g_route = grouping + 4 + 2 * R + 1;
     int4* g_table = reinterpret_cast<int4*>(grouping + grouping_table_word(R));
-    // heads (first key of each expert) counted per thread over a contiguous
-    // range of positions, then an exclusive scan of the per-thread counts
-    const int per = (R + WIDE_THREADS - 1) / WIDE_THREADS;
-    const int p0 = tid * per;
-    int heads = 0, valid = 0;
-    for (int p = p0; p < min(p0 + per, R); ++p) {
-        const uint32_t kp = key[p];
-        if (kp == 0xFFFFFFFFu) continue;
-        ++valid;
-        if (p == 0 || (key[p - 1] >> 14) != (kp >> 14)) ++heads;
-    }
-    part[tid] = heads | (valid << 16);                 // both < 2^15 (R <= 16384)
-    __syncthreads();
-    // inclusive scan of part (Hillis-Steele; two fields move together)
-    for (int off = 1; off < WIDE_THREADS; off <<= 1) {
-        const int v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    const int n_heads = part[WIDE_THREADS - 1] & 0xFFFF;
-    const int n_valid = part[WIDE_THREADS - 1] >> 16;
-    int a = (tid > 0 ? part[tid - 1] : 0) & 0xFFFF;    // heads before this thread's range
-    for (int p = p0; p < min(p0 + per, R); ++p) {
-        const uint32_t kp = key[p];
-        if (kp == 0xFFFFFFFFu) {
-            g_route[p] = -1;
-            continue;
-        }
-        g_route[p] = (int32_t)(kp & 0x3FFFu);
-        if (p == 0 || (key[p - 1] >> 14) != (kp >> 14)) {
-            g_expert[a] = (int32_t)(kp >> 14);
-            g_offset[a] = p;
-            ++a;
-        }
+    if (tot > 0) {
+        g_expert[grp] = e;
+        g_offset[grp] = pos0;
+        g_table[grp] = make_int4(e, pos0, pos0 + (int)tot, 0);
     }
     for (int q = n_heads + tid; q < R; q += WIDE_THREADS) g_expert[q] = -1;
     for (int q = n_heads + tid; q <= R; q += WIDE_THREADS) g_offset[q] = n_valid;
+    for (int q = n_valid + tid; q < R; q += WIDE_THREADS) g_route[q] = -1;
     if (tid == 0) {
         grouping[0] = n_heads;
         grouping[1] = n_valid;
         grouping[2] = (int32_t)ncols;
         grouping[3] = topk;
     }
-    // the table: the end of group a is where group a + 1 starts (found again
-    // from the keys, so no wait on other threads' stores is needed)
-    for (int p = p0; p < min(p0 + per, R); ++p) {
-        const uint32_t kp = key[p];
-        if (kp == 0xFFFFFFFFu || !(p == 0 || (key[p - 1] >> 14) != (kp >> 14))) continue;
-        int end = p + 1;
-        while (end < n_valid && (key[end] >> 14) == (kp >> 14)) ++end;
-        // this head's rank: heads before p
-        int rank = (tid > 0 ? part[tid - 1] : 0) & 0xFFFF;
-        for (int q = p0; q < p; ++q)
-            if (key[q] != 0xFFFFFFFFu && (q == 0 || (key[q - 1] >> 14) != (key[q] >> 14))) ++rank;
-        g_table[rank] = make_int4((int)(kp >> 14), p, end, 0);
+    __syncthreads();                                   // first[] and the wave prefixes are in place
+
+    // placement, 64 routes of the wave's share at a time, in route order
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int r0 = rb; r0 < re; r0 += 64) {
+        const int r = r0 + lane;
+        const int k = key_of(r);                        // < 2^11
+        uint64_t same = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 11; ++b) {
+            const uint64_t ones = __ballot((k >> b) & 1);
+            same &= ((k >> b) & 1) ? ones : ~ones;
+        }
+        if (k < MOEQ8_MAX_EXPERTS) {
+            const uint32_t word = cnt[w][k >> 1];
+            const int before_w = (int)((word >> (16 * (k & 1))) & 0xffffu);
+            g_route[first[k] + before_w + __popcll(same & below)] = r;
+        }
+        // the wave's reads of cnt come before its updates (in-order LDS):
+        // the highest lane of each expert adds the expert's routes here
+        if (k < MOEQ8_MAX_EXPERTS && (same >> lane) == 1ull)
+            atomicAdd(&cnt[w][k >> 1], (uint32_t)__popcll(same) << (16 * (k & 1)));
     }
 }
 
