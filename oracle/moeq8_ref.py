@@ -37,11 +37,20 @@ clamp constant or routing rule.  Readings taken here:
       output is rounded to fp32 before it is quantised for the down projection.
   R15 the MoE block's output is the routed experts' weighted sum plus the
       shared expert's output: one add after the routed sum.
+  R17 8-bit exchange block (the prefill partials' wire format of PR #826's
+      8-bit prefill exchange commit: 32 int8 values and one f32 scale) =
+      {f32 d; int8 qs[32]} (36 B, 1.125 B a value), little-endian, array of
+      structures; d and the codes follow R2's rule, but d is kept as the fp32
+      quotient (the scale is f32 on the wire, so no fp16 rounding).
+  R18 the exchange sum: each rank's value is the fp32 product d * q (one
+      rounding); the ranks' values are added in fp32 in ascending rank order
+      from +0, which makes the result the same on every rank.
   (R9-R14 concern the launch layouts and the synthetic workloads, not what
   this module computes.)
 
 Floating point here is fp64 unless a step is defined by fp32 rounding (the
-quantisers and the router keys), where it is done in fp32 exactly as defined.
+quantisers, the router keys and the exchange codec's f32 scale and rank-order
+sum), where it is done in fp32 exactly as defined.
 """
 
 from __future__ import annotations
@@ -51,7 +60,8 @@ import numpy as np
 QK = 32  # values per block
 Q8_0_DTYPE = np.dtype([("d", "<f2"), ("qs", "i1", (QK,))])  # 34 bytes
 Q8_1_DTYPE = np.dtype([("d", "<f2"), ("s", "<f2"), ("qs", "i1", (QK,))])  # 36 bytes
-assert Q8_0_DTYPE.itemsize == 34 and Q8_1_DTYPE.itemsize == 36
+Q8X_DTYPE = np.dtype([("d", "<f4"), ("qs", "i1", (QK,))])  # 36 bytes: exchange block (R17)
+assert Q8_0_DTYPE.itemsize == 34 and Q8_1_DTYPE.itemsize == 36 and Q8X_DTYPE.itemsize == 36
 
 SWIGLU_LIMIT = 7.0
 
@@ -262,6 +272,43 @@ def moe_combine(y, ids, weights, shared=None):
     if shared is not None:
         out = out + np.asarray(shared, dtype=np.float64)
     return out
+
+
+# ---------------------------------------------------------------------------
+# 8-bit block exchange codec (readings R17, R18)
+# ---------------------------------------------------------------------------
+
+def q8x_encode(x: np.ndarray) -> np.ndarray:
+    """Prefill partials fp32 [rows, n] -> exchange blocks [rows, n/32] (R17):
+    the block rule of R2 with the scale kept in fp32.  The 8-bit prefill
+    exchange commit of PR #826 sends partials in this form."""
+    x = np.asarray(x, dtype=np.float32)
+    rows, n = x.shape
+    assert n % QK == 0
+    d, q = _quantize_blocks(x.reshape(rows, n // QK, QK))
+    out = np.zeros((rows, n // QK), dtype=Q8X_DTYPE)
+    out["d"] = d
+    out["qs"] = q.astype(np.int8)
+    return out
+
+
+def q8x_dequantize(blocks: np.ndarray) -> np.ndarray:
+    """Exchange blocks [rows, nb] -> fp32 values [rows, nb*32]: the fp32
+    product d * q, rounded once (R18)."""
+    d = blocks["d"].astype(np.float32)
+    q = blocks["qs"].astype(np.float32)                   # exact
+    return (d[..., None] * q).astype(np.float32).reshape(blocks.shape[0], -1)
+
+
+def q8x_decode_sum(parts) -> np.ndarray:
+    """The exchange's sum (R18): every rank's dequantized values added in fp32
+    in ascending rank order from +0.  parts: the ranks' block arrays in rank
+    order, each [rows, nb].  Returns fp32 [rows, nb*32]."""
+    parts = list(parts)
+    acc = np.zeros((parts[0].shape[0], parts[0].shape[1] * QK), dtype=np.float32)
+    for blocks in parts:
+        acc = (acc + q8x_dequantize(blocks)).astype(np.float32)
+    return acc
 
 
 # ---------------------------------------------------------------------------

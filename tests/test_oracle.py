@@ -476,3 +476,121 @@ def test_synthetic_generator_c_matches_numpy():
         assert np.all(np.abs(q).max(axis=1) == 127)
         d = b["d"].view(np.uint16)
         assert np.all((d >= 0x0C00) & (d < 0x1000))
+
+
+# ---------------------------------------------------------------------------
+# 8-bit block exchange codec pins (R17, R18)
+# ---------------------------------------------------------------------------
+
+def exact_block_q8x(xs):
+    """R17 in exact rationals: (d as the fp32 quotient amax/127, codes)."""
+    fx = [Fraction(float(v)) for v in np.asarray(xs, dtype=np.float32)]
+    amax = max(abs(v) for v in fx)
+    d = rn32(amax / 127)
+    if d == 0:
+        return Fraction(0), [0] * 32
+    q = []
+    for v in fx:
+        quot = rn32(v / d)
+        m = abs(quot) + Fraction(1, 2)
+        n = m.numerator // m.denominator
+        q.append(n if quot >= 0 else -n)
+    return d, q
+
+
+def test_q8x_block_is_1_125_bytes_per_value():
+    # 32 int8 values and one f32 scale: 1.125 bytes a value, as the pages state
+    assert oracle.Q8X_DTYPE.itemsize == 36
+    assert oracle.Q8X_DTYPE.itemsize / 32 == 1.125
+    b = oracle.q8x_encode(np.zeros((3, 64), np.float32))
+    assert b.shape == (3, 2) and b.tobytes() == bytes(3 * 2 * 36)   # all-zero blocks: all-zero bytes
+
+
+def test_q8x_power_of_two_scale_closed_form():
+    # amax = 127 * 2^-2: d = 2^-2 exactly, and values on the grid are their own codes
+    q = np.array([127, -127] + list(range(-15, 15)), np.int32)
+    x = (q.astype(np.float32) * np.float32(0.25))[None]
+    b = oracle.q8x_encode(x)
+    assert float(b["d"][0, 0]) == 0.25
+    assert list(b["qs"][0, 0]) == list(q)
+    assert np.array_equal(oracle.q8x_dequantize(b), x)
+    raw = b.tobytes()
+    assert raw[:4] == np.float32(0.25).tobytes() and raw[4] == 127 and raw[5] == 256 - 127
+
+
+def test_q8x_codes_match_exact_rational_rule():
+    rng = np.random.default_rng(12)
+    xs = [rng.normal(0, 1, 32).astype(np.float32) for _ in range(40)]
+    xs.append(np.array([127.0] + [k + 0.5 for k in range(-15, 16)], dtype=np.float32))   # exact halves
+    xs.append(np.array([1.0] + [0.3 * (k - 15) / 15 for k in range(31)], np.float32))       # d = 1/127
+    xs.append(np.array([1e-30] * 31 + [-3e-30], dtype=np.float32))
+    xs.extend(list(_discriminating_blocks()))
+    x = np.stack(xs)
+    b = oracle.q8x_encode(x)
+    for i in range(x.shape[0]):
+        d, q = exact_block_q8x(x[i])
+        assert Fraction(float(b["d"][i, 0])) == d
+        assert [int(v) for v in b["qs"][i, 0]] == q
+
+
+def test_q8x_round_trip_within_half_a_code():
+    x = workloads.normal_f32(21, (64, 4096), 3.0)
+    b = oracle.q8x_encode(x)
+    back = oracle.q8x_dequantize(b).astype(np.float64)
+    d = np.repeat(b["d"].astype(np.float64), 32, axis=1)
+    # |x/d - q| <= 1/2 up to the fp32 quotient's and product's roundings
+    assert np.all(np.abs(x - back) <= 0.5 * d * (1 + 2.0 ** -20) + np.abs(x) * 2.0 ** -22)
+
+
+def _blocks_from(dq_rows):
+    """Exchange blocks from explicit (d, codes) per row: one block per row."""
+    out = np.zeros((len(dq_rows), 1), dtype=oracle.Q8X_DTYPE)
+    for i, (d, q) in enumerate(dq_rows):
+        out["d"][i, 0] = np.float32(d)
+        out["qs"][i, 0] = np.asarray(q, np.int8)
+    return out
+
+
+def test_q8x_decode_sum_in_rank_order():
+    # rank 0 holds 127 * 2^20 (fp32 spacing 8 there), ranks 1 and 2 hold 3:
+    # ((127*2^20 + 3) + 3) = 127*2^20 in fp32, while the exact sum 127*2^20 + 6
+    # rounds to 127*2^20 + 8; so the rank order is visible in the result
+    big = _blocks_from([(2.0 ** 20, [127] + [0] * 31)])
+    three = _blocks_from([(1.0, [3] + [0] * 31)])
+    s = oracle.q8x_decode_sum([big, three, three])
+    assert s[0, 0] == np.float32(127 * 2 ** 20)
+    assert oracle.q8x_decode_sum([three, three, big])[0, 0] == np.float32(127 * 2 ** 20 + 8)
+    assert np.all(s[0, 1:] == 0)
+
+
+def test_q8x_decode_sum_single_rank_and_fp64_bound():
+    rng = np.random.default_rng(9)
+    parts = [oracle.q8x_encode(workloads.normal_f32(100 + r, (8, 256), 1.0 + r)) for r in range(5)]
+    assert np.array_equal(oracle.q8x_decode_sum(parts[:1]), oracle.q8x_dequantize(parts[0]))
+    vals = np.stack([oracle.q8x_dequantize(p).astype(np.float64) for p in parts])
+    s = oracle.q8x_decode_sum(parts).astype(np.float64)
+    exact = vals.sum(axis=0)
+    # fp32 left-to-right sum of 5 terms: |error| <= 4 * 2^-24 * sum |terms| (first order)
+    assert np.all(np.abs(s - exact) <= 4 * 2.0 ** -24 * np.abs(vals).sum(axis=0) * (1 + 1e-6))
+    # a product d*q that is not exact in fp32 is rounded once
+    b = _blocks_from([(np.float32(1) / np.float32(3), [127] + [0] * 31)])
+    assert oracle.q8x_dequantize(b)[0, 0] == np.float32(np.float32(1 / 3) * np.float32(127))
+    _ = rng
+
+
+def test_mutation_q8x_mistakes_caught():
+    # an fp16-rounded scale fails the exact rule on a block whose d is not an fp16 value
+    xs = np.array([1.0] + [0.3 * (k - 15) / 15 for k in range(31)], np.float32)
+    d_exact, _ = exact_block_q8x(xs)
+    assert Fraction(float(np.float16(float(d_exact)))) != d_exact
+    # summing in reverse rank order fails the planted-order pin
+    big = _blocks_from([(2.0 ** 20, [127] + [0] * 31)])
+    three = _blocks_from([(1.0, [3] + [0] * 31)])
+    rev = np.zeros((1, 32), np.float32)
+    for blocks in reversed([big, three, three]):
+        rev = (rev + oracle.q8x_dequantize(blocks)).astype(np.float32)
+    assert rev[0, 0] != oracle.q8x_decode_sum([big, three, three])[0, 0]
+    # ties to even on the exact-halves block changes codes
+    xh = np.array([127.0] + [k + 0.5 for k in range(-15, 16)], dtype=np.float32)
+    _, q = exact_block_q8x(xh)
+    assert list(np.round(xh / np.float32(1.0)).astype(int)) != q
