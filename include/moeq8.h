@@ -62,6 +62,8 @@ extern "C" {
 #define MOEQ8_MAX_EXPERTS 1024
 #define MOEQ8_MAX_TOPK 16
 #define MOEQ8_MAX_WIDE_COLS 1024   /* columns of the wide-batch calls */
+#define MOEQ8_MAX_EXCHANGE_RANKS 64  /* ranks one exchange sum takes */
+#define MOEQ8_EXCHANGE_BLOCK_BYTES 36
 
 enum moeq8_status {
     MOEQ8_OK = 0,
@@ -289,6 +291,36 @@ int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_
  * it may be the same buffer as out.  Otherwise as moe_combine. */
 int moe_combine_shared(const float* y, const int32_t* ids, const float* weights, int64_t ncols,
                        int32_t topk, int64_t n, const float* shared_y, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 8-bit block exchange codec for prefill-sized partials (PR #826, the 8-bit
+ * prefill exchange commit: partials travel as blocks of 32 int8 values with
+ * one f32 scale, 1.125 bytes a value, are gathered from every rank, and every
+ * rank sums the ranks' dequantized values in rank order so all ranks get the
+ * same result).  The gather crosses devices and is not part of this library.
+ *
+ * Block: {f32 d; int8 qs[32]}, MOEQ8_EXCHANGE_BLOCK_BYTES = 36 bytes.
+ *
+ * q8_block_encode: x fp32 [rows][n] (row stride x_stride elements >= n,
+ *   n % 32 == 0) -> blocks [rows][n/32], contiguous, written in full.
+ *   d = amax / 127 in fp32 (IEEE division, kept in fp32), q = roundf(x / d) on
+ *   the fp32 quotient (halves away from zero); an all-zero block gives d = 0
+ *   and q = 0.  x and blocks 4-byte aligned (16-byte aligned x with
+ *   x_stride % 4 == 0 takes the vector path; results are the same).
+ *
+ * q8_block_decode_sum: gathered holds nranks block arrays [rows][n/32], rank r
+ *   at gathered + r * rank_stride_bytes (>= rows * n/32 * 36, multiple of 4;
+ *   ignored when nranks == 1); 1 <= nranks <= MOEQ8_MAX_EXCHANGE_RANKS.
+ *   out fp32 [rows][n] (row stride out_stride >= n) is overwritten with
+ *     out = (((+0 + v_0) + v_1) + ... + v_{nranks-1}),  v_r = fl(d_r * q_r)
+ *   in fp32: each product rounded once, sums in ascending rank order.
+ *
+ * Both: rows == 0 enqueues nothing; errors are returned before any launch.
+ * ------------------------------------------------------------------------- */
+int q8_block_encode(const float* x, int64_t rows, int64_t n, int64_t x_stride, void* blocks,
+                    void* stream);
+int q8_block_decode_sum(const void* gathered, int32_t nranks, int64_t rank_stride_bytes,
+                        int64_t rows, int64_t n, float* out, int64_t out_stride, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,9 @@ from .ops import (  # noqa: F401
     moe_grouped_mmvq_ex,
     moe_route_topk_quantize,
     moe_combine,
+    EXCHANGE_BLOCK_BYTES,
+    q8_block_encode,
+    q8_block_decode_sum,
     synth_q8_0_fill,
     stream_read,
 )

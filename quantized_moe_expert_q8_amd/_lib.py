@@ -36,6 +36,8 @@ SIGNATURES = {
                                                c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_combine": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]),
     "moe_combine_shared": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_vp, c_vp]),
+    "q8_block_encode": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
+    "q8_block_decode_sum": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "moe_grouping_bytes_wide": (c_size, [c_i64, c_i32]),
     "moe_route_topk_wide": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp,
                                            c_vp]),

@@ -17,6 +17,7 @@ from ._lib import call, lib
 QK = 32
 Q8_0_BLOCK_BYTES = 34
 Q8_1_BLOCK_BYTES = 36
+EXCHANGE_BLOCK_BYTES = 36
 MAX_COLS = 8
 GATE_UP_SWIGLU = 0
 DOWN = 1
@@ -83,6 +84,44 @@ def q8_0_quantize_rows(w: torch.Tensor, out: torch.Tensor | None = None) -> torc
     _cuda(out, "out", torch.uint8)
     _need(out, "out", rows * (k // QK) * Q8_0_BLOCK_BYTES)
     call("q8_0_quantize_rows", _ptr(w), rows, k, w.stride(0), _ptr(out), _stream(w))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 8-bit block exchange codec
+# ---------------------------------------------------------------------------
+
+def q8_block_encode(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Partials fp32 [rows, n] -> exchange blocks uint8 [rows, n/32*36]."""
+    _cuda(x, "x", torch.float32)
+    rows, n = x.shape
+    _contig_rows(x, "x", rows, n)
+    if out is None:
+        out = torch.empty((rows, n // QK * EXCHANGE_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", rows * (n // QK) * EXCHANGE_BLOCK_BYTES)
+    call("q8_block_encode", _ptr(x), rows, n, x.stride(0), _ptr(out), _stream(x))
+    return out
+
+
+def q8_block_decode_sum(gathered: torch.Tensor, rows: int, n: int,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """gathered uint8 [nranks, >= rows*n/32*36] (rank r's blocks in row r) ->
+    out fp32 [rows, n]: the ranks' dequantized values summed in rank order."""
+    _cuda(gathered, "gathered", torch.uint8)
+    if gathered.dim() != 2 or gathered.stride(1) != 1:
+        raise ValueError("gathered must be [nranks, bytes] with unit inner stride")
+    nranks = gathered.shape[0]
+    need = rows * (n // QK) * EXCHANGE_BLOCK_BYTES
+    if gathered.shape[1] < need:
+        raise ValueError(f"gathered rows must hold {need} bytes")
+    _need(gathered, "gathered", (nranks - 1) * gathered.stride(0) * gathered.element_size() + need)
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.float32, device=gathered.device)
+    _cuda(out, "out", torch.float32)
+    _contig_rows(out, "out", rows, n)
+    call("q8_block_decode_sum", _ptr(gathered), nranks, gathered.stride(0), rows, n, _ptr(out),
+         out.stride(0), _stream(gathered))
     return out
 
 

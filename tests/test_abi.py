@@ -29,7 +29,8 @@ def _declared_functions():
 def test_header_declares_the_hot_path_calls():
     names = set(_declared_functions())
     for n in ("q8_1_quantize_rows", "mmvq_q8_0_glu_pair", "moe_route_topk", "moe_grouped_mmvq",
-              "moe_combine", "mmvq_q8_0", "moe_grouping_bytes"):
+              "moe_combine", "mmvq_q8_0", "moe_grouping_bytes", "moe_grouped_gemm", "q8_block_encode",
+              "q8_block_decode_sum"):
         assert n in names
 
 
@@ -114,6 +115,15 @@ def test_other_validation():
     assert L.moe_grouped_gemm(1, P, None, 272, 68, 1, 64, 64, P, P, 1025, 1, P, None) == -1  # ncols
     assert L.moe_grouped_gemm(1, P, None, 270, 68, 2, 64, 64, P, P, 1, 1, P, None) == -2  # expert stride % 4
     assert L.moe_grouped_gemm(1, P, None, 272, 68, 1, 0, 64, P, P, 1, 1, P, None) == 0
+    assert L.q8_block_encode(P, 2, 48, 48, P, None) == -1                        # n % 32
+    assert L.q8_block_encode(P, 2, 64, 32, P, None) == -1                        # stride < n
+    assert L.q8_block_encode(P + 2, 2, 64, 64, P, None) == -2
+    assert L.q8_block_encode(P, 0, 64, 64, P, None) == 0
+    assert L.q8_block_decode_sum(P, 0, 0, 2, 64, P, 64, None) == -1              # no ranks
+    assert L.q8_block_decode_sum(P, 65, 1 << 20, 2, 64, P, 64, None) == -1       # too many ranks
+    assert L.q8_block_decode_sum(P, 2, 100, 2, 64, P, 64, None) == -1            # ranks overlap
+    assert L.q8_block_decode_sum(P, 2, 146, 2, 64, P, 64, None) == -2            # rank stride % 4
+    assert L.q8_block_decode_sum(P, 2, 144, 0, 64, P, 64, None) == 0
     assert L.moe_combine(P, P, P, 0, 8, 16, P, None) == -1
     assert L.moe_combine(P, P, P, 1, 8, 0, P, None) == 0
     assert L.moe_combine_shared(P, P, P, 1, 8, 16, None, P, None) == -1         # no shared output

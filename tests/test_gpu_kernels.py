@@ -814,3 +814,56 @@ def test_grouped_gemm_integer_dots_unit_scale():
         e = ids_np.reshape(-1)[r]
         exact = np.einsum("nbk,bk->n", qs_w[e], qs_x[r])
         assert np.array_equal(hh[r], exact.astype(np.float32)), r
+
+
+# ---------------------------------------------------------------------------
+# 8-bit block exchange codec: bytes and sums bit for bit against the oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,n,stride", [(1, 32, 32), (7, 96, 96), (33, 4096, 4096), (5, 64, 67),
+                                           (1024, 4096, 4096)])
+def test_q8_block_encode_bytes(rows, n, stride):
+    """Encode against the oracle, byte for byte: contiguous and strided rows (a
+    stride that is not a multiple of 4 takes the scalar path), zero blocks,
+    a block of exact halves and a block whose scale is not an fp16 value."""
+    say(f"q8x encode rows={rows} n={n} stride={stride}")
+    x = workloads.normal_f32(rows * 7 + n, (rows, stride), 2.0)
+    x[0, :32] = 0.0
+    if n >= 64:
+        x[0, 32:64] = np.array([127.0] + [k + 0.5 for k in range(-15, 16)], np.float32)
+    if rows > 1:
+        x[1, :32] = np.array([1.0] + [0.3 * (k - 15) / 15 for k in range(31)], np.float32)
+    xd = to_dev(x)
+    blocks = moeq8.q8_block_encode(xd[:, :n])
+    ref = oracle.q8x_encode(np.ascontiguousarray(x[:, :n]))
+    assert host(blocks).tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("nranks,rows,n", [(1, 3, 64), (2, 1024, 4096), (3, 17, 160), (8, 64, 1024)])
+def test_q8_block_decode_sum_bits(nranks, rows, n):
+    """The rank-order sum of the oracle-encoded blocks of every rank, bit for
+    bit (fp32 products and sums in the defined order), including the planted
+    case where only ascending rank order gives the result."""
+    say(f"q8x decode_sum nranks={nranks} rows={rows} n={n}")
+    parts = [oracle.q8x_encode(workloads.normal_f32(50 + r, (rows, n), 1.0 + 3 * r)) for r in range(nranks)]
+    if nranks == 3:
+        parts[0]["d"][0, 0] = np.float32(2.0 ** 20)
+        parts[0]["qs"][0, 0, 0] = 127
+        for r in (1, 2):
+            parts[r]["d"][0, 0] = np.float32(1.0)
+            parts[r]["qs"][0, 0, 0] = 3
+    gathered = np.stack([p.reshape(-1).view(np.uint8) for p in parts])
+    out = moeq8.q8_block_decode_sum(to_dev(gathered), rows, n)
+    ref = oracle.q8x_decode_sum(parts)
+    got = host(out)
+    assert got.tobytes() == ref.tobytes()
+    if nranks == 3:
+        assert got[0, 0] == np.float32(127 * 2 ** 20)
+
+
+def test_q8_block_round_trip_on_gpu():
+    """encode -> decode of one rank gives the oracle's dequantized values."""
+    x = workloads.normal_f32(3, (64, 512), 1.0)
+    blocks = moeq8.q8_block_encode(to_dev(x))
+    back = host(moeq8.q8_block_decode_sum(blocks.view(1, -1), 64, 512))
+    assert back.tobytes() == oracle.q8x_dequantize(oracle.q8x_encode(x)).tobytes()
