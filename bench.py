@@ -16,6 +16,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   sweep     the routed layer (256 experts, top-8) at 1, 2, 4, 5, 8 columns
   wide      the same layer at 32..1024 columns: grouped products on the int8
             matrix cores against the grouped MMVQ in passes of 8 columns
+  codec     the 8-bit block exchange codec on prefill partials of 4096 values
+            a row (a 1K-row band and an 8K-row one): encode, and the
+            rank-order decode-sum of 2 and 8 ranks' blocks
 """
 
 from __future__ import annotations
@@ -48,6 +51,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-wide", action="store_true",
                     help="skip the wide-batch (32..1024 columns) measurement")
+    ap.add_argument("--no-codec", action="store_true",
+                    help="skip the 8-bit exchange codec measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the oracle sample")
     ap.add_argument("--pmc-copy", action="store_true",
@@ -146,6 +151,15 @@ def capture(torch, fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def time_graph_each(torch, fn, per_graph, reps):
+    """Mean ms of one call of fn, from a graph of per_graph calls replayed reps
+    times (short launches: one graph replay per call would time the replay)."""
+    def many():
+        for _ in range(per_graph):
+            fn()
+    return time_graph(torch, many, reps) / per_graph
 
 
 def time_graph(torch, fn, reps):
@@ -453,6 +467,8 @@ def main():
         result["sweep"] = sweep(torch, workloads, moeq8, ml, args)
     if not args.no_wide:
         result["wide"] = wide_sweep(torch, workloads, moeq8, ml, args)
+    if not args.no_codec:
+        result["codec"] = codec_bench(torch, workloads, moeq8, args)
 
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -593,6 +609,36 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
         out.append(rec)
         del ws, x, lg, bs
     del bank, experts
+    torch.cuda.empty_cache()
+    return out
+
+
+def codec_bench(torch, workloads, moeq8, args):
+    """The exchange codec on [rows, 4096] fp32 partials: encode (reads 4 B,
+    writes 1.125 B a value) and decode-sum of R ranks (reads R * 1.125 B,
+    writes 4 B a value), timed with HIP events over graphs of 20 launches."""
+    n = 4096
+    out = []
+    for rows in (1024, 8192):
+        x = torch.from_numpy(workloads.normal_f32(7, (rows, n), 1.0)).cuda()
+        blocks = moeq8.q8_block_encode(x)
+        per = blocks.numel()
+        gathered = torch.empty((8, per), dtype=torch.uint8, device="cuda")
+        for r in range(8):
+            gathered[r].copy_(blocks.view(-1))
+        res = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+        reps, per = 10, 20
+        enc_us = time_graph_each(torch, lambda: moeq8.q8_block_encode(x, out=blocks), per, reps) * 1e3
+        rec = {"rows": rows, "n": n, "encode_us": round(enc_us, 2),
+               "encode_gbps": round(rows * n * 5.125 / (enc_us * 1e-6) / 1e9, 1)}
+        for nr in (2, 8):
+            g = gathered[:nr]
+            us = time_graph_each(torch, lambda: moeq8.q8_block_decode_sum(g, rows, n, out=res), per, reps) * 1e3
+            rec[f"decode_sum_{nr}_us"] = round(us, 2)
+            rec[f"decode_sum_{nr}_gbps"] = round(rows * n * (nr * 1.125 + 4) / (us * 1e-6) / 1e9, 1)
+        log(f"codec {rec}")
+        out.append(rec)
+        del x, blocks, gathered, res
     torch.cuda.empty_cache()
     return out
 
