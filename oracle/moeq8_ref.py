@@ -45,6 +45,14 @@ clamp constant or routing rule.  Readings taken here:
   R18 the exchange sum: each rank's value is the fp32 product d * q (one
       rounding); the ranks' values are added in fp32 in ascending rank order
       from +0, which makes the result the same on every rank.
+  R19 a bandwidth-only low-bit weight format (the pages' cold experts use a
+      2-bit format they do not define): Q4 block = {fp16 d; uint8 qs[16]}
+      (18 B, 4.5 bits a weight); value i < 16 is the low nibble of qs[i],
+      value i + 16 its high nibble; w = d * (code - 8).  Quantiser: fp32
+      d = amax / 7 (IEEE division), code = clamp(roundf(x / d), -8, 7) + 8 on
+      the fp32 quotient, d stored fp16 (nearest even); an all-zero block has
+      d = 0 and every code 8.  Products with q8_1 activations are the exact
+      sums over blocks of d_w * d_x * sum((code - 8) * q).
   (R9-R14 concern the launch layouts and the synthetic workloads, not what
   this module computes.)
 
@@ -61,7 +69,9 @@ QK = 32  # values per block
 Q8_0_DTYPE = np.dtype([("d", "<f2"), ("qs", "i1", (QK,))])  # 34 bytes
 Q8_1_DTYPE = np.dtype([("d", "<f2"), ("s", "<f2"), ("qs", "i1", (QK,))])  # 36 bytes
 Q8X_DTYPE = np.dtype([("d", "<f4"), ("qs", "i1", (QK,))])  # 36 bytes: exchange block (R17)
+Q4_DTYPE = np.dtype([("d", "<f2"), ("qs", "u1", (QK // 2,))])  # 18 bytes: 4-bit weights (R19)
 assert Q8_0_DTYPE.itemsize == 34 and Q8_1_DTYPE.itemsize == 36 and Q8X_DTYPE.itemsize == 36
+assert Q4_DTYPE.itemsize == 18
 
 SWIGLU_LIMIT = 7.0
 
@@ -272,6 +282,60 @@ def moe_combine(y, ids, weights, shared=None):
     if shared is not None:
         out = out + np.asarray(shared, dtype=np.float64)
     return out
+
+
+# ---------------------------------------------------------------------------
+# 4-bit weight blocks (reading R19)
+# ---------------------------------------------------------------------------
+
+def quantize_q4(w: np.ndarray) -> np.ndarray:
+    """Weights fp32 [rows, K] -> Q4 blocks [rows, K/32] (R19)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, k = w.shape
+    assert k % QK == 0
+    x = w.reshape(rows, k // QK, QK)
+    amax = np.max(np.abs(x), axis=-1)
+    d = (amax / np.float32(7.0)).astype(np.float32)
+    safe_d = np.where(d == 0, np.float32(1.0), d).astype(np.float32)
+    quot = (x / safe_d[..., None]).astype(np.float32)
+    q = np.clip(_round_half_away(quot), -8, 7).astype(np.int32)
+    q = np.where(d[..., None] == 0, 0, q)
+    code = (q + 8).astype(np.uint8)                       # 0..15
+    out = np.zeros((rows, k // QK), dtype=Q4_DTYPE)
+    out["d"] = d.astype(np.float16)
+    out["qs"] = code[..., :QK // 2] | (code[..., QK // 2:] << 4)
+    return out
+
+
+def q4_values(blocks: np.ndarray) -> np.ndarray:
+    """Q4 blocks [..., nb] -> signed codes (code - 8) int32 [..., nb, 32]."""
+    qs = blocks["qs"].astype(np.int32)
+    return np.concatenate([qs & 0xF, qs >> 4], axis=-1) - 8
+
+
+def dequantize_q4(blocks: np.ndarray) -> np.ndarray:
+    """Q4 blocks [rows, nb] -> fp64 weights [rows, nb*32]."""
+    d = blocks["d"].astype(np.float64)
+    return (d[..., None] * q4_values(blocks)).reshape(blocks.shape[0], -1)
+
+
+def mmvq_q4(w: np.ndarray, xq: np.ndarray) -> np.ndarray:
+    """y[c, n] = sum_b d_w[n,b] * d_x[c,b] * sum_i (code - 8) * q_x, in fp64
+    (every term exact).  w: Q4 [N, nb]; xq: q8_1 [C, nb].  Returns fp64 [C, N]."""
+    assert w.shape[1] == xq.shape[1]
+    wv = q4_values(w).astype(np.int64)                    # [N, nb, 32]
+    xv = xq["qs"].astype(np.int64)                        # [C, nb, 32]
+    sumi = np.einsum("nbk,cbk->cnb", wv, xv).astype(np.float64)
+    dw = w["d"].astype(np.float64)
+    dx = xq["d"].astype(np.float64)
+    return np.einsum("nb,cb,cnb->cn", dw, dx, sumi)
+
+
+def glu_pair_q4(w_gate, w_up, xq):
+    """Gate/up pair of Q4 matrices with the SwiGLU-DS4 epilogue: (h, g, u) fp64."""
+    g = mmvq_q4(w_gate, xq)
+    u = mmvq_q4(w_up, xq)
+    return swiglu_ds4(g, u), g, u
 
 
 # ---------------------------------------------------------------------------

@@ -594,3 +594,96 @@ def test_mutation_q8x_mistakes_caught():
     xh = np.array([127.0] + [k + 0.5 for k in range(-15, 16)], dtype=np.float32)
     _, q = exact_block_q8x(xh)
     assert list(np.round(xh / np.float32(1.0)).astype(int)) != q
+
+
+# ---------------------------------------------------------------------------
+# 4-bit weight blocks (R19)
+# ---------------------------------------------------------------------------
+
+def exact_block_q4(xs):
+    """R19 in exact rationals: (fp16 d, codes 0..15)."""
+    fx = [Fraction(float(v)) for v in np.asarray(xs, dtype=np.float32)]
+    amax = max(abs(v) for v in fx)
+    d = rn32(amax / 7)
+    if d == 0:
+        return Fraction(0), [8] * 32
+    codes = []
+    for v in fx:
+        quot = rn32(v / d)
+        m = abs(quot) + Fraction(1, 2)
+        n = m.numerator // m.denominator
+        n = n if quot >= 0 else -n
+        codes.append(min(7, max(-8, n)) + 8)
+    return rn16(d), codes
+
+
+def test_q4_block_layout_closed_form():
+    # amax = 7 * 2^-3: d = 2^-3; values on the grid are their codes; nibble order
+    q = np.array([7, -7, 0, 1, -1] + [k % 15 - 7 for k in range(27)], np.int32)
+    x = (q.astype(np.float32) * np.float32(0.125))[None]
+    b = oracle.quantize_q4(x)
+    assert oracle.Q4_DTYPE.itemsize == 18 and b.shape == (1, 1)
+    assert float(b["d"][0, 0]) == 0.125
+    codes = q + 8
+    raw = b.tobytes()
+    assert raw[:2] == np.float16(0.125).tobytes()
+    for i in range(16):
+        assert raw[2 + i] == (codes[i] | (codes[16 + i] << 4))
+    assert np.array_equal(oracle.q4_values(b)[0, 0], q)
+    assert np.array_equal(oracle.dequantize_q4(b)[0], x[0].astype(np.float64))
+    z = oracle.quantize_q4(np.zeros((1, 32), np.float32))
+    assert z.tobytes() == bytes(2) + bytes([0x88] * 16)
+
+
+def test_q4_quantize_matches_exact_rational_rule():
+    rng = np.random.default_rng(13)
+    xs = [rng.normal(0, 0.02, 32).astype(np.float32) for _ in range(40)]
+    xs.append(np.array([7.0] + [k + 0.5 for k in range(-8, 7)] + [0.25 * k for k in range(16)], np.float32))
+    xs.append(np.array([1.0] + [0.9 * (k - 15) / 15 for k in range(31)], np.float32))
+    for x in xs:
+        b = oracle.quantize_q4(x[None])[0, 0]
+        d16, codes = exact_block_q4(x)
+        assert Fraction(float(b["d"])) == d16
+        got = [int(v) for v in np.concatenate([b["qs"] & 0xF, b["qs"] >> 4])]
+        assert got == codes
+
+
+def test_q4_products_match_dequantized_fp64():
+    rng = np.random.default_rng(14)
+    w = oracle.quantize_q4(rng.normal(0, 0.02, (24, 256)).astype(np.float32))
+    xq = oracle.quantize_q8_1(rng.normal(0, 1, (3, 256)).astype(np.float32))
+    y = oracle.mmvq_q4(w, xq)
+    brute = oracle.dequantize(xq) @ oracle.dequantize_q4(w).T
+    np.testing.assert_allclose(y, brute, rtol=1e-12, atol=1e-12)
+
+
+def test_q4_unit_scale_closed_form():
+    # all scales 1: the product is the integer dot of (code - 8) with the quants
+    rng = np.random.default_rng(15)
+    w = np.zeros((5, 4), oracle.Q4_DTYPE)
+    w["d"] = 1.0
+    w["qs"] = rng.integers(0, 256, size=(5, 4, 16))
+    xq = np.zeros((2, 4), oracle.Q8_1_DTYPE)
+    xq["d"] = 1.0
+    xq["qs"] = rng.integers(-127, 128, size=(2, 4, 32))
+    y = oracle.mmvq_q4(w, xq)
+    for c in range(2):
+        for n in range(5):
+            tot = 0
+            for b in range(4):
+                for i in range(16):
+                    byte = int(w["qs"][n, b, i])
+                    tot += ((byte & 15) - 8) * int(xq["qs"][c, b, i]) + ((byte >> 4) - 8) * int(xq["qs"][c, b, 16 + i])
+            assert y[c, n] == tot
+
+
+def test_mutation_q4_mistakes_caught():
+    # swapping the nibble halves, or dropping the -8 offset, breaks the closed forms
+    q = np.array([7, -7, 0, 1, -1] + [k % 15 - 7 for k in range(27)], np.int32)
+    x = (q.astype(np.float32) * np.float32(0.125))[None]
+    b = oracle.quantize_q4(x)
+    qs = b["qs"][0, 0].astype(np.int32)
+    swapped = np.concatenate([qs >> 4, qs & 0xF]) - 8
+    assert not np.array_equal(swapped, q)
+    no_offset = np.concatenate([qs & 0xF, qs >> 4])
+    assert not np.array_equal(no_offset, q)
