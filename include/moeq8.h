@@ -64,6 +64,7 @@ extern "C" {
 #define MOEQ8_MAX_WIDE_COLS 1024   /* columns of the wide-batch calls */
 #define MOEQ8_MAX_EXCHANGE_RANKS 64  /* ranks one exchange sum takes */
 #define MOEQ8_EXCHANGE_BLOCK_BYTES 36
+#define MOEQ8_Q4_BLOCK_BYTES 18
 
 enum moeq8_status {
     MOEQ8_OK = 0,
@@ -321,6 +322,40 @@ int q8_block_encode(const float* x, int64_t rows, int64_t n, int64_t x_stride, v
                     void* stream);
 int q8_block_decode_sum(const void* gathered, int32_t nranks, int64_t rank_stride_bytes,
                         int64_t rows, int64_t n, float* out, int64_t out_stride, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Bandwidth-only 4-bit expert weights.  The pages stream cold experts in a
+ * 2-bit format they do not define, through the prefetching loop of the grouped
+ * MoE MMVQ commit; a plainly defined 4-bit block stands in here:
+ *   Q4 block = {fp16 d; uint8 qs[16]}, MOEQ8_Q4_BLOCK_BYTES = 18 (4.5 bits a
+ *   weight); value i < 16 is the low nibble of qs[i], value i + 16 the high
+ *   nibble; w = d * (code - 8).
+ * q4_quantize_rows: w fp32 [n_rows][k] -> Q4 blocks [n_rows][k/32]: fp32
+ *   d = amax / 7 (IEEE division), code = clamp(roundf(w / d), -8, 7) + 8 on the
+ *   fp32 quotient, d stored fp16 (nearest even); an all-zero block gives d = 0
+ *   and codes 8.  w 4-byte aligned, wq 2-byte aligned.
+ * mmvq_q4, mmvq_q4_glu_pair, moe_grouped_mmvq_q4: the products of mmvq_q8_0,
+ *   mmvq_q8_0_glu_pair and moe_grouped_mmvq_ex (no shared part; stages
+ *   MOEQ8_GATE_UP_SWIGLU, MOEQ8_DOWN, MOEQ8_DOWN_F32_ACT) with Q4 weights, on
+ *   q8_1 activations; the same arguments, with row strides of at least
+ *   k/32 * 18 bytes (a multiple of 4).  A block contributes
+ *   (d_w * d_x) * sum((code - 8) * q), with the same reduction order as the
+ *   Q8_0 products, so the same invariants hold (batch invariance at 1..8
+ *   columns, pair == separate products + SwiGLU, grouped == per-route
+ *   products, column-range slices == zero-padded full rows).
+ * ------------------------------------------------------------------------- */
+int q4_quantize_rows(const float* w, int64_t n_rows, int64_t k, int64_t w_row_stride, void* wq,
+                     void* stream);
+int mmvq_q4(const void* w, int64_t w_row_stride_bytes, int64_t n, int64_t k, int64_t k_block_offset,
+            const void* xq, int64_t ncols, float* y, void* stream);
+int mmvq_q4_glu_pair(const void* w_gate, const void* w_up, int64_t w_row_stride_bytes, int64_t n,
+                     int64_t k, int64_t k_block_offset, const void* xq, int64_t ncols, float* h_out,
+                     float* g_out, float* u_out, void* stream);
+int moe_grouped_mmvq_q4(int32_t stage, const void* w_a, const void* w_b,
+                        int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                        int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                        int64_t act_row_stride, const void* grouping, int64_t ncols, int32_t topk,
+                        float* out, void* stream);
 
 #ifdef __cplusplus
 }

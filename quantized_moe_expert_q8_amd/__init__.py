@@ -30,6 +30,11 @@ from .ops import (  # noqa: F401
     EXCHANGE_BLOCK_BYTES,
     q8_block_encode,
     q8_block_decode_sum,
+    Q4_BLOCK_BYTES,
+    q4_quantize_rows,
+    mmvq_q4,
+    mmvq_q4_glu_pair,
+    moe_grouped_mmvq_q4,
     synth_q8_0_fill,
     stream_read,
 )

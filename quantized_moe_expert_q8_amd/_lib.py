@@ -38,6 +38,12 @@ SIGNATURES = {
     "moe_combine_shared": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "q8_block_encode": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "q8_block_decode_sum": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "q4_quantize_rows": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
+    "mmvq_q4": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]),
+    "mmvq_q4_glu_pair": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_i64,
+                                        c_vp, c_vp, c_vp, c_vp]),
+    "moe_grouped_mmvq_q4": (ctypes.c_int, [c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                           c_vp, c_i64, c_vp, c_i64, c_i32, c_vp, c_vp]),
     "moe_grouping_bytes_wide": (c_size, [c_i64, c_i32]),
     "moe_route_topk_wide": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp,
                                            c_vp]),

@@ -25,6 +25,8 @@
 #include "moeq8_device.hpp"
 #include "moeq8_host.hpp"
 
+#include <type_traits>
+
 namespace moeq8 {
 
 #ifndef MOEQ8_WAVES_PER_WG
@@ -152,8 +154,13 @@ __device__ __forceinline__ float chain_groups(float v, int lane) {
     }
 }
 
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX>
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4>
 __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
+    // weight chunk: two Q8_0 blocks (68 B) or two 4-bit blocks (36 B); the
+    // chunk's value has the same form either way, so the reduction order and
+    // every launch shape are shared
+    using WC = std::conditional_t<Q4, W4Chunk, WChunk>;
+    constexpr int64_t WCB = Q4 ? W4_CHUNK_BYTES : W_CHUNK_BYTES;
     constexpr int RPW = 4 / G;                         // rows per row set
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -259,7 +266,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
         // a load in flight would make the activation quantisation wait for the
         // weight loads as well.
         constexpr bool UNCOND = ACT_F32;
-        WChunk wc[U][NMAT];
+        WC wc[U][NMAT];
         int crel = 0;                                      // chunk within the slice (clamped)
         bool cvalid = false;
         bool ok[U];
@@ -272,7 +279,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             for (int u = 0; u < U; ++u) {
                 const int64_t row = row_base + (int64_t)u * RPW;
                 ok[u] = cvalid && row < n_rows;
-                const int64_t off = ok[u] ? row * row_stride + (int64_t)crel * W_CHUNK_BYTES : 0;
+                const int64_t off = ok[u] ? row * row_stride + (int64_t)crel * WCB : 0;
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
                     if (UNCOND || ok[u]) {
@@ -492,10 +499,10 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 
 // One work item = one row block: of one active expert (grouped), of the dense
 // extra matrix (grouped launches with a shared part), or of the one matrix.
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX>
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4>
 __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_act[];
-    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX>(p, blockIdx.x, lds_act);
+    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX, Q4>(p, blockIdx.x, lds_act);
 }
 
 __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, float* h) {
@@ -542,13 +549,13 @@ constexpr int u_for(int nmat, bool act_f32) { return nmat == 2 ? U_ROWSETS : act
 
 int rows_per_wg_for(const Shape& s, int u) { return WAVES_PER_WG * u * (4 / s.G); }
 
-template <int NMAT, bool GROUPED, bool ACT_F32, bool STX, int U = u_for(NMAT, ACT_F32)>
+template <int NMAT, bool GROUPED, bool ACT_F32, bool STX, bool Q4, int U = u_for(NMAT, ACT_F32)>
 int launch_shape(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
     const dim3 block(64 * WAVES_PER_WG);
     switch (s.G) {
-        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U, GROUPED, ACT_F32, STX>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
-        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U, GROUPED, ACT_F32, STX>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
-        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U, GROUPED, ACT_F32, STX>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        case 1: hipLaunchKernelGGL((k_mmvq<1, NMAT, U, GROUPED, ACT_F32, STX, Q4>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U, GROUPED, ACT_F32, STX, Q4>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
+        default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U, GROUPED, ACT_F32, STX, Q4>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
     }
     return check_launch();
 }
@@ -567,31 +574,31 @@ size_t staged_act_bytes(bool grouped, int64_t ncols, int64_t act_row_bytes) {
     return stage ? (size_t)bytes : 0;
 }
 
-template <int NMAT, bool GROUPED, bool ACT_F32>
+template <int NMAT, bool GROUPED, bool ACT_F32, bool Q4>
 int launch_mmvq(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
     p.nsteps = s.nsteps;
     if (grid <= 0) return MOEQ8_OK;
     if (grid > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
     if constexpr (ACT_F32) {
-        return launch_shape<NMAT, GROUPED, true, false>(p, s, grid, lds_bytes, stream);
+        return launch_shape<NMAT, GROUPED, true, false, Q4>(p, s, grid, lds_bytes, stream);
     } else if constexpr (!GROUPED) {
         // a dense launch has one pass of p.ncols <= MAX_COLS columns
         const size_t staged = staged_act_bytes(false, p.ncols, p.act_row_bytes);
-        if (staged) return launch_shape<NMAT, false, false, true>(p, s, grid, staged, stream);
-        return launch_shape<NMAT, false, false, false>(p, s, grid, 0, stream);
+        if (staged) return launch_shape<NMAT, false, false, true, Q4>(p, s, grid, staged, stream);
+        return launch_shape<NMAT, false, false, false, Q4>(p, s, grid, 0, stream);
     } else {
-        return launch_shape<NMAT, true, false, false>(p, s, grid, 0, stream);
+        return launch_shape<NMAT, true, false, false, Q4>(p, s, grid, 0, stream);
     }
 }
 
 int validate_matrix(const void* w, int64_t w_row_stride_bytes, int64_t n, int64_t k,
-                    int64_t k_block_offset) {
+                    int64_t k_block_offset, int64_t block_bytes = Q80_BYTES) {
     if (!w || n < 0 || k <= 0) return MOEQ8_EINVAL;
     if (k % 64 != 0) return MOEQ8_EINVAL;
     if (k_block_offset < 0) return MOEQ8_EINVAL;
     if (k_block_offset % 2 != 0) return MOEQ8_EALIGN;
     if (((uintptr_t)w & 3u) != 0 || (w_row_stride_bytes & 3) != 0) return MOEQ8_EALIGN;
-    if (n > 1 && w_row_stride_bytes < (k / QK) * Q80_BYTES) return MOEQ8_EINVAL;
+    if (n > 1 && w_row_stride_bytes < (k / QK) * block_bytes) return MOEQ8_EINVAL;
     if (k / 64 > ((int64_t)1 << 24) || k_block_offset > ((int64_t)1 << 26)) return MOEQ8_EUNSUPPORTED;
     if (n > ((int64_t)1 << 31)) return MOEQ8_EUNSUPPORTED;
     return MOEQ8_OK;
@@ -599,7 +606,7 @@ int validate_matrix(const void* w, int64_t w_row_stride_bytes, int64_t n, int64_
 
 int dense_call(int nmat, const void* w0, const void* w1, int64_t stride, int64_t n, int64_t k,
                int64_t kb, const void* xq, int64_t ncols, float* out, float* g, float* u,
-               void* stream) {
+               void* stream, bool q4 = false) {
     MmvqParams p = {};
     const Shape s = pick_shape(kb / 2, k / 64);
     p.rows_per_wg = rows_per_wg_for(s, u_for(nmat, false));
@@ -610,8 +617,13 @@ int dense_call(int nmat, const void* w0, const void* w1, int64_t stride, int64_t
     p.out0 = out;
     p.out_g = g;
     p.out_u = u;
-    if (nmat == 2) return launch_mmvq<2, false, false>(p, s, p.m.wg, 0, (hipStream_t)stream);
-    return launch_mmvq<1, false, false>(p, s, p.m.wg, 0, (hipStream_t)stream);
+    const hipStream_t hs = (hipStream_t)stream;
+    if (q4) {
+        if (nmat == 2) return launch_mmvq<2, false, false, true>(p, s, p.m.wg, 0, hs);
+        return launch_mmvq<1, false, false, true>(p, s, p.m.wg, 0, hs);
+    }
+    if (nmat == 2) return launch_mmvq<2, false, false, false>(p, s, p.m.wg, 0, hs);
+    return launch_mmvq<1, false, false, false>(p, s, p.m.wg, 0, hs);
 }
 
 }  // namespace
@@ -658,22 +670,25 @@ extern "C" int swiglu_ds4(const float* g, const float* u, int64_t count, float* 
     return check_launch();
 }
 
-extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,
-                                   int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
-                                   int64_t n_local_expert, int64_t n, int64_t k, const void* act,
-                                   int64_t act_row_stride, const void* grouping, int64_t ncols,
-                                   int32_t topk, float* out, const void* s_a, const void* s_b,
-                                   int64_t s_row_stride_bytes, int64_t s_n, int64_t s_k,
-                                   int64_t s_k_block_offset, const void* s_act,
-                                   int64_t s_act_row_stride, float* s_out, void* stream) {
+namespace moeq8 {
+namespace {
+int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
+                 int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                 int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                 int64_t act_row_stride, const void* grouping, int64_t ncols,
+                 int32_t topk, float* out, const void* s_a, const void* s_b,
+                 int64_t s_row_stride_bytes, int64_t s_n, int64_t s_k,
+                 int64_t s_k_block_offset, const void* s_act,
+                 int64_t s_act_row_stride, float* s_out, void* stream) {
+    const int64_t bb = q4 ? Q4_BYTES : Q80_BYTES;
     if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_DOWN_F32_ACT)
         return MOEQ8_EINVAL;
     const bool pair = stage == MOEQ8_GATE_UP_SWIGLU;
     const bool f32 = stage == MOEQ8_DOWN_F32_ACT;
-    int st = validate_matrix(w_a, w_row_stride_bytes, n, k, 0);
+    int st = validate_matrix(w_a, w_row_stride_bytes, n, k, 0, bb);
     if (st) return st;
     if (pair) {
-        st = validate_matrix(w_b, w_row_stride_bytes, n, k, 0);
+        st = validate_matrix(w_b, w_row_stride_bytes, n, k, 0, bb);
         if (st) return st;
     }
     if (!act || !grouping || !out) return MOEQ8_EINVAL;
@@ -690,10 +705,10 @@ extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w
     if (has_s) {
         // the shared part runs in the same kernel instance: same k and slice shape
         if (s_k != k) return MOEQ8_EUNSUPPORTED;
-        st = validate_matrix(s_a, s_row_stride_bytes, s_n, k, s_k_block_offset);
+        st = validate_matrix(s_a, s_row_stride_bytes, s_n, k, s_k_block_offset, bb);
         if (st) return st;
         if (pair) {
-            st = validate_matrix(s_b, s_row_stride_bytes, s_n, k, s_k_block_offset);
+            st = validate_matrix(s_b, s_row_stride_bytes, s_n, k, s_k_block_offset, bb);
             if (st) return st;
         }
         if (!s_out) return MOEQ8_EINVAL;
@@ -748,10 +763,31 @@ extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w
     const size_t lds = f32 ? (size_t)MAX_COLS * (size_t)p.act_row_bytes : 0;
     if (lds > 64 * 1024) return MOEQ8_EUNSUPPORTED;
     const hipStream_t hs = (hipStream_t)stream;
-    if (pair) return launch_mmvq<2, true, false>(p, s, grid, 0, hs);
-    if (f32) return launch_mmvq<1, true, true>(p, s, grid, lds, hs);
-    return launch_mmvq<1, true, false>(p, s, grid, 0, hs);
+    if (q4) {
+        if (pair) return launch_mmvq<2, true, false, true>(p, s, grid, 0, hs);
+        if (f32) return launch_mmvq<1, true, true, true>(p, s, grid, lds, hs);
+        return launch_mmvq<1, true, false, true>(p, s, grid, 0, hs);
+    }
+    if (pair) return launch_mmvq<2, true, false, false>(p, s, grid, 0, hs);
+    if (f32) return launch_mmvq<1, true, true, false>(p, s, grid, lds, hs);
+    return launch_mmvq<1, true, false, false>(p, s, grid, 0, hs);
 }
+}  // namespace
+}  // namespace moeq8
+
+extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,
+                                   int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                                   int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                                   int64_t act_row_stride, const void* grouping, int64_t ncols,
+                                   int32_t topk, float* out, const void* s_a, const void* s_b,
+                                   int64_t s_row_stride_bytes, int64_t s_n, int64_t s_k,
+                                   int64_t s_k_block_offset, const void* s_act,
+                                   int64_t s_act_row_stride, float* s_out, void* stream) {
+    return grouped_impl(false, stage, w_a, w_b, expert_stride_bytes, w_row_stride_bytes, n_local_expert, n,
+                        k, act, act_row_stride, grouping, ncols, topk, out, s_a, s_b, s_row_stride_bytes,
+                        s_n, s_k, s_k_block_offset, s_act, s_act_row_stride, s_out, stream);
+}
+
 
 extern "C" int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
                                 int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
@@ -762,4 +798,44 @@ extern "C" int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
     return moe_grouped_mmvq_ex(stage, w_a, w_b, expert_stride_bytes, w_row_stride_bytes,
                                n_local_expert, n, k, act_q, 0, grouping, ncols, topk, out, nullptr,
                                nullptr, 0, 0, 0, 0, nullptr, 0, nullptr, stream);
+}
+
+// ---- 4-bit weights (Q4 blocks of 18 bytes; the same kernels and reduction
+// order, a 36-byte chunk per lane) ------------------------------------------
+
+extern "C" int mmvq_q4(const void* w, int64_t w_row_stride_bytes, int64_t n, int64_t k,
+                       int64_t k_block_offset, const void* xq, int64_t ncols, float* y, void* stream) {
+    int st = validate_matrix(w, w_row_stride_bytes, n, k, k_block_offset, Q4_BYTES);
+    if (st) return st;
+    if (!xq || !y || ncols < 1 || ncols > MAX_COLS) return MOEQ8_EINVAL;
+    if (((uintptr_t)xq & 3u) || ((uintptr_t)y & 3u)) return MOEQ8_EALIGN;
+    if (n == 0) return MOEQ8_OK;
+    return dense_call(1, w, nullptr, w_row_stride_bytes, n, k, k_block_offset, xq, ncols, y, nullptr,
+                      nullptr, stream, true);
+}
+
+extern "C" int mmvq_q4_glu_pair(const void* w_gate, const void* w_up, int64_t w_row_stride_bytes,
+                                int64_t n, int64_t k, int64_t k_block_offset, const void* xq,
+                                int64_t ncols, float* h_out, float* g_out, float* u_out, void* stream) {
+    int st = validate_matrix(w_gate, w_row_stride_bytes, n, k, k_block_offset, Q4_BYTES);
+    if (st) return st;
+    st = validate_matrix(w_up, w_row_stride_bytes, n, k, k_block_offset, Q4_BYTES);
+    if (st) return st;
+    if (!xq || !h_out || ncols < 1 || ncols > MAX_COLS) return MOEQ8_EINVAL;
+    if (((uintptr_t)xq & 3u) || ((uintptr_t)h_out & 3u) || ((uintptr_t)g_out & 3u) ||
+        ((uintptr_t)u_out & 3u))
+        return MOEQ8_EALIGN;
+    if (n == 0) return MOEQ8_OK;
+    return dense_call(2, w_gate, w_up, w_row_stride_bytes, n, k, k_block_offset, xq, ncols, h_out,
+                      g_out, u_out, stream, true);
+}
+
+extern "C" int moe_grouped_mmvq_q4(int32_t stage, const void* w_a, const void* w_b,
+                                   int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                                   int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                                   int64_t act_row_stride, const void* grouping, int64_t ncols,
+                                   int32_t topk, float* out, void* stream) {
+    return grouped_impl(true, stage, w_a, w_b, expert_stride_bytes, w_row_stride_bytes, n_local_expert, n,
+                        k, act, act_row_stride, grouping, ncols, topk, out, nullptr, nullptr, 0, 0, 0, 0,
+                        nullptr, 0, nullptr, stream);
 }

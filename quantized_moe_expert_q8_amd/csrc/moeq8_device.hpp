@@ -220,6 +220,99 @@ __device__ __forceinline__ void quantize_block(const float* __restrict__ src, ui
     }
 }
 
+// ---- 4-bit weight blocks -------------------------------------------------
+// Q4 block = {fp16 d; uint8 qs[16]} (18 B): value i < 16 in the low nibble of
+// qs[i], value i + 16 in the high nibble, w = d * (code - 8).  A chunk is two
+// blocks (36 B, dword aligned in any row of an even number of blocks): block
+// 0's d in the low half of dword 0 and its codes at bytes 2..17 (so each code
+// dword is funnel-shifted out of two loaded dwords), block 1's d in the high
+// half of dword 4 and its codes in dwords 5..8.
+constexpr int Q4_BYTES = 18;
+constexpr int W4_CHUNK_BYTES = BLOCKS_PER_CHUNK * Q4_BYTES;   // 36
+constexpr int W4_CHUNK_DWORDS = W4_CHUNK_BYTES / 4;           // 9
+
+struct W4Chunk { uint32_t v[W4_CHUNK_DWORDS]; };
+
+__device__ __forceinline__ void load_w_chunk(W4Chunk& w, const uint8_t* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#if MOEQ8_NT_WEIGHTS
+        u32x4 t = __builtin_nontemporal_load(q + i);
+#else
+        u32x4 t = q[i];
+#endif
+        w.v[4 * i + 0] = t.x;
+        w.v[4 * i + 1] = t.y;
+        w.v[4 * i + 2] = t.z;
+        w.v[4 * i + 3] = t.w;
+    }
+    w.v[8] = *reinterpret_cast<const uint32_t*>(p + 32);
+}
+
+__device__ __forceinline__ void zero_w_chunk(W4Chunk& w) {
+#pragma unroll
+    for (int i = 0; i < W4_CHUNK_DWORDS; ++i) w.v[i] = 0u;
+}
+
+// Four codes (one per byte, 0..15) -> four signed bytes code - 8, with no
+// borrow between bytes: (c | 0x80) - 8 stays in 120..135, and flipping bit 7
+// back gives c - 8 modulo 256.
+__device__ __forceinline__ int signed_nibbles(uint32_t c4) {
+    return (int)(((c4 | 0x80808080u) - 0x08080808u) ^ 0x80808080u);
+}
+
+// Value of a 4-bit chunk against a q8_1 chunk, in the same form as the Q8_0
+// chunk: (d_w * d_x) * sumi per block, then the sum of the two blocks.  sumi
+// is the exact integer sum of (code - 8) * q.
+__device__ __forceinline__ float chunk_dot(const W4Chunk& w, const XChunk& x) {
+    int s0 = 0, s1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t c0 = (w.v[i] >> 16) | (w.v[i + 1] << 16);   // block 0, bytes 4i .. 4i+3
+        s0 = __builtin_amdgcn_sdot4(signed_nibbles(c0 & 0x0f0f0f0fu), (int)x.v[1 + i], s0, false);
+        s0 = __builtin_amdgcn_sdot4(signed_nibbles((c0 >> 4) & 0x0f0f0f0fu), (int)x.v[5 + i], s0, false);
+        const uint32_t c1 = w.v[5 + i];                             // block 1
+        s1 = __builtin_amdgcn_sdot4(signed_nibbles(c1 & 0x0f0f0f0fu), (int)x.v[10 + i], s1, false);
+        s1 = __builtin_amdgcn_sdot4(signed_nibbles((c1 >> 4) & 0x0f0f0f0fu), (int)x.v[14 + i], s1, false);
+    }
+    const float dw0 = half_bits_to_float(w.v[0]);
+    const float dw1 = half_bits_to_float(w.v[4] >> 16);
+    const float dx0 = half_bits_to_float(x.v[0]);
+    const float dx1 = half_bits_to_float(x.v[9]);
+    const float p0 = (dw0 * dx0) * (float)s0;
+    const float p1 = (dw1 * dx1) * (float)s1;
+    return p0 + p1;
+}
+
+// The 4-bit block rule: fp32 d = amax / 7 (IEEE division), code =
+// clamp(roundf(x / d), -8, 7) + 8 on the fp32 quotient, d stored fp16 (nearest
+// even); an all-zero block has d = 0 and every code 8.  dst: 18 bytes, 2-byte
+// aligned.
+__device__ __forceinline__ void quantize_block_q4(const float* __restrict__ src, uint8_t* dst) {
+    float v[QK];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK; ++i) {
+        v[i] = src[i];
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const float d = amax / 7.0f;
+    uint32_t code[QK];
+#pragma unroll
+    for (int i = 0; i < QK; ++i) {
+        int q = 0;
+        if (d != 0.0f) q = min(7, max(-8, (int)roundf(v[i] / d)));
+        code[i] = (uint32_t)(q + 8);
+    }
+    uint16_t* o = reinterpret_cast<uint16_t*>(dst);
+    o[0] = (uint16_t)float_to_half_bits(d);
+#pragma unroll
+    for (int i = 0; i < QK / 4; ++i)                   // bytes 2i, 2i+1 of qs
+        o[1 + i] = (uint16_t)(code[2 * i] | (code[16 + 2 * i] << 4) |
+                              ((code[2 * i + 1] | (code[16 + 2 * i + 1] << 4)) << 8));
+}
+
 // SwiGLU-DS4 in fp32: silu(min(g, 7)) * clamp(u, -7, 7).
 __device__ __forceinline__ float swiglu_ds4_f32(float g, float u) {
     const float gc = fminf(g, SWIGLU_LIMIT);

@@ -21,6 +21,15 @@ __global__ void k_quantize_rows(const float* __restrict__ x, int64_t n_rows, int
     quantize_block<Q81>(x + r * row_stride + b * QK, out + gid * (Q81 ? Q81_BYTES : Q80_BYTES));
 }
 
+__global__ void k_quantize_rows_q4(const float* __restrict__ x, int64_t n_rows, int64_t nb,
+                                   int64_t row_stride, uint8_t* __restrict__ out) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= n_rows * nb) return;
+    const int64_t r = gid / nb;
+    const int64_t b = gid - r * nb;
+    quantize_block_q4(x + r * row_stride + b * QK, out + gid * Q4_BYTES);
+}
+
 namespace {
 template <bool Q81>
 int launch_quantize(const float* x, int64_t n_rows, int64_t k, int64_t stride, void* out,
@@ -46,4 +55,20 @@ extern "C" int q8_1_quantize_rows(const float* x, int64_t n_rows, int64_t k, int
 extern "C" int q8_0_quantize_rows(const float* w, int64_t n_rows, int64_t k, int64_t w_row_stride,
                                   void* wq, void* stream) {
     return moeq8::launch_quantize<false>(w, n_rows, k, w_row_stride, wq, stream);
+}
+
+// 4-bit weight blocks (Q4: fp16 d = amax / 7, 32 codes of 4 bits), for
+// bandwidth-only expert weights.
+extern "C" int q4_quantize_rows(const float* w, int64_t n_rows, int64_t k, int64_t w_row_stride,
+                                void* wq, void* stream) {
+    using namespace moeq8;
+    if (!w || !wq || n_rows < 0 || k <= 0 || (k % QK) != 0 || w_row_stride < k) return MOEQ8_EINVAL;
+    if (((uintptr_t)w & 3u) || ((uintptr_t)wq & 1u)) return MOEQ8_EALIGN;
+    const int64_t total = n_rows * (k / QK);
+    if (total == 0) return MOEQ8_OK;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_quantize_rows_q4, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream, w,
+                       n_rows, k / QK, w_row_stride, (uint8_t*)wq);
+    return check_launch();
 }

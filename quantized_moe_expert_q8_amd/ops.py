@@ -18,6 +18,7 @@ QK = 32
 Q8_0_BLOCK_BYTES = 34
 Q8_1_BLOCK_BYTES = 36
 EXCHANGE_BLOCK_BYTES = 36
+Q4_BLOCK_BYTES = 18
 MAX_COLS = 8
 GATE_UP_SWIGLU = 0
 DOWN = 1
@@ -129,15 +130,15 @@ def q8_block_decode_sum(gathered: torch.Tensor, rows: int, n: int,
 # products
 # ---------------------------------------------------------------------------
 
-def _weight_extent(n: int, k: int, row_stride: int) -> int:
-    return 0 if n == 0 else (n - 1) * row_stride + (k // QK) * Q8_0_BLOCK_BYTES
+def _weight_extent(n: int, k: int, row_stride: int, block_bytes: int = Q8_0_BLOCK_BYTES) -> int:
+    return 0 if n == 0 else (n - 1) * row_stride + (k // QK) * block_bytes
 
 
-def _weight_args(w, n, k, w_offset_bytes, w_row_stride_bytes, name="w"):
+def _weight_args(w, n, k, w_offset_bytes, w_row_stride_bytes, name="w", block_bytes=Q8_0_BLOCK_BYTES):
     _cuda(w, name, torch.uint8)
     if w_row_stride_bytes is None:
-        w_row_stride_bytes = w.stride(0) if w.dim() == 2 else (k // QK) * Q8_0_BLOCK_BYTES
-    _need(w, name, _weight_extent(n, k, w_row_stride_bytes), w_offset_bytes)
+        w_row_stride_bytes = w.stride(0) if w.dim() == 2 else (k // QK) * block_bytes
+    _need(w, name, _weight_extent(n, k, w_row_stride_bytes, block_bytes), w_offset_bytes)
     return w_row_stride_bytes
 
 
@@ -183,6 +184,101 @@ def mmvq_q8_0_glu_pair(w_gate: torch.Tensor, w_up: torch.Tensor, xq: torch.Tenso
             _need(t, nm, ncols * n * 4)
     call("mmvq_q8_0_glu_pair", _ptr(w_gate, w_offset_bytes), _ptr(w_up, w_offset_bytes), stride, n,
          k, k_block_offset, _ptr(xq), ncols, _ptr(out), _ptr(g_out), _ptr(u_out), _stream(w_gate))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 4-bit weights (Q4 blocks: fp16 d, 32 codes of 4 bits, 18 bytes)
+# ---------------------------------------------------------------------------
+
+def q4_quantize_rows(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """w fp32 [rows, k] -> Q4 blocks uint8 [rows, k/32*18]."""
+    _cuda(w, "w", torch.float32)
+    rows, k = w.shape
+    _contig_rows(w, "w", rows, k)
+    if out is None:
+        out = torch.empty((rows, k // QK * Q4_BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", rows * (k // QK) * Q4_BLOCK_BYTES)
+    call("q4_quantize_rows", _ptr(w), rows, k, w.stride(0), _ptr(out), _stream(w))
+    return out
+
+
+def mmvq_q4(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, *, ncols: int | None = None,
+            k_block_offset: int = 0, w_offset_bytes: int = 0,
+            w_row_stride_bytes: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [ncols, n] = W . xq with Q4 weight rows."""
+    ncols = xq.shape[0] if ncols is None else ncols
+    stride = _weight_args(w, n, k, w_offset_bytes, w_row_stride_bytes, block_bytes=Q4_BLOCK_BYTES)
+    _act_rows(xq, "xq", ncols, k)
+    if out is None:
+        out = torch.empty((ncols, n), dtype=torch.float32, device=w.device)
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", ncols * n * 4)
+    call("mmvq_q4", _ptr(w, w_offset_bytes), stride, n, k, k_block_offset, _ptr(xq), ncols,
+         _ptr(out), _stream(w))
+    return out
+
+
+def mmvq_q4_glu_pair(w_gate: torch.Tensor, w_up: torch.Tensor, xq: torch.Tensor, n: int, k: int,
+                     *, ncols: int | None = None, k_block_offset: int = 0, w_offset_bytes: int = 0,
+                     w_row_stride_bytes: int | None = None, out: torch.Tensor | None = None,
+                     g_out: torch.Tensor | None = None, u_out: torch.Tensor | None = None) -> torch.Tensor:
+    """h fp32 [ncols, n] = SwiGLU-DS4(Wg . xq, Wu . xq) with Q4 weights."""
+    ncols = xq.shape[0] if ncols is None else ncols
+    stride = _weight_args(w_gate, n, k, w_offset_bytes, w_row_stride_bytes, "w_gate", Q4_BLOCK_BYTES)
+    stride_u = _weight_args(w_up, n, k, w_offset_bytes, w_row_stride_bytes, "w_up", Q4_BLOCK_BYTES)
+    if stride_u != stride:
+        raise ValueError("w_gate and w_up must share the row stride")
+    _act_rows(xq, "xq", ncols, k)
+    if out is None:
+        out = torch.empty((ncols, n), dtype=torch.float32, device=w_gate.device)
+    for t, nm in ((out, "out"), (g_out, "g_out"), (u_out, "u_out")):
+        if t is not None:
+            _cuda(t, nm, torch.float32)
+            _need(t, nm, ncols * n * 4)
+    call("mmvq_q4_glu_pair", _ptr(w_gate, w_offset_bytes), _ptr(w_up, w_offset_bytes), stride, n,
+         k, k_block_offset, _ptr(xq), ncols, _ptr(out), _ptr(g_out), _ptr(u_out), _stream(w_gate))
+    return out
+
+
+def moe_grouped_mmvq_q4(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, act: torch.Tensor,
+                        grouping: torch.Tensor, *, n: int, k: int, n_local_expert: int, ncols: int,
+                        topk: int, out: torch.Tensor | None = None,
+                        expert_stride_bytes: int | None = None) -> torch.Tensor:
+    """Grouped per-expert products with Q4 expert weights [n_local][n][k/32]:
+    stages GATE_UP_SWIGLU and DOWN on q8_1 rows, DOWN_F32_ACT on fp32 h rows
+    [ncols*topk, k].  Returns out fp32 [ncols, topk, n]."""
+    row_stride = (k // QK) * Q4_BLOCK_BYTES
+    if expert_stride_bytes is None:
+        expert_stride_bytes = n * row_stride
+    extent = (n_local_expert - 1) * expert_stride_bytes + _weight_extent(n, k, row_stride, Q4_BLOCK_BYTES)
+    _cuda(w_a, "w_a", torch.uint8)
+    _need(w_a, "w_a", extent)
+    act_stride = 0
+    if stage == GATE_UP_SWIGLU:
+        if w_b is None:
+            raise ValueError("the gate/up stage needs w_b")
+        _cuda(w_b, "w_b", torch.uint8)
+        _need(w_b, "w_b", extent)
+        _act_rows(act, "act", ncols, k)
+    elif stage == DOWN:
+        _act_rows(act, "act", ncols * topk, k)
+    elif stage == DOWN_F32_ACT:
+        _cuda(act, "act", torch.float32)
+        _contig_rows(act, "act", ncols * topk, k)
+        act_stride = act.stride(0)
+    else:
+        raise ValueError("stage must be GATE_UP_SWIGLU, DOWN or DOWN_F32_ACT")
+    _cuda(grouping, "grouping", torch.uint8)
+    _need(grouping, "grouping", moe_grouping_bytes_wide(ncols, topk))
+    if out is None:
+        out = torch.empty((ncols, topk, n), dtype=torch.float32, device=w_a.device)
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", ncols * topk * n * 4)
+    call("moe_grouped_mmvq_q4", stage, _ptr(w_a), _ptr(w_b), expert_stride_bytes, row_stride,
+         n_local_expert, n, k, _ptr(act), act_stride, _ptr(grouping), ncols, topk, _ptr(out),
+         _stream(w_a))
     return out
 
 

@@ -124,6 +124,14 @@ def test_other_validation():
     assert L.q8_block_decode_sum(P, 2, 100, 2, 64, P, 64, None) == -1            # ranks overlap
     assert L.q8_block_decode_sum(P, 2, 146, 2, 64, P, 64, None) == -2            # rank stride % 4
     assert L.q8_block_decode_sum(P, 2, 144, 0, 64, P, 64, None) == 0
+    assert L.q4_quantize_rows(P, 2, 48, 48, P, None) == -1                       # k % 32
+    assert L.q4_quantize_rows(P, 2, 64, 64, P + 1, None) == -2
+    assert L.mmvq_q4(P, 34, 4, 64, 0, P, 1, P, None) == -2                       # row stride % 4
+    assert L.mmvq_q4(P, 32, 4, 64, 0, P, 1, P, None) == -1                       # row shorter than a row
+    assert L.mmvq_q4(P, 36, 4, 96, 0, P, 1, P, None) == -1                       # k % 64
+    assert L.mmvq_q4_glu_pair(P, None, 36, 4, 64, 0, P, 1, P, None, None, None) == -1
+    assert L.moe_grouped_mmvq_q4(3, P, P, 144, 36, 1, 4, 64, P, 0, P, 1, 1, P, None) == -1   # bad stage
+    assert L.moe_grouped_mmvq_q4(0, P, None, 144, 36, 1, 4, 64, P, 0, P, 1, 1, P, None) == -1  # no up
     assert L.moe_combine(P, P, P, 0, 8, 16, P, None) == -1
     assert L.moe_combine(P, P, P, 1, 8, 0, P, None) == 0
     assert L.moe_combine_shared(P, P, P, 1, 8, 16, None, P, None) == -1         # no shared output

@@ -867,3 +867,112 @@ def test_q8_block_round_trip_on_gpu():
     blocks = moeq8.q8_block_encode(to_dev(x))
     back = host(moeq8.q8_block_decode_sum(blocks.view(1, -1), 64, 512))
     assert back.tobytes() == oracle.q8x_dequantize(oracle.q8x_encode(x)).tobytes()
+
+
+# ---------------------------------------------------------------------------
+# 4-bit weights (Q4): quantiser bytes, products against the oracle, and the
+# invariants the shared reduction order gives
+# ---------------------------------------------------------------------------
+
+def _q4_both(w32):
+    """Quantise on both sides; assert identical bytes; return (oracle, device)."""
+    wo = oracle.quantize_q4(w32)
+    wd = moeq8.q4_quantize_rows(to_dev(w32))
+    assert host(wd).tobytes() == wo.tobytes()
+    return wo, wd
+
+
+@pytest.mark.parametrize("n,k", [(5, 32), (64, 4096), (300, 1024)])
+def test_q4_quantize_bytes(n, k):
+    w = workloads.normal_f32(n + k, (n, k), 0.02)
+    w[0, :32] = 0.0
+    if k >= 64:
+        w[0, 32:64] = np.array([7.0] + [0.5 * (i - 15) for i in range(31)], np.float32)
+    _q4_both(w)
+
+
+@pytest.mark.parametrize("n,k,c", [(64, 256, 1), (256, 1024, 3), (512, 4096, 8), (96, 2048, 5)])
+def test_q4_mmvq_and_pair_vs_oracle(n, k, c):
+    say(f"q4 mmvq n={n} k={k} c={c}")
+    wg, wgd = _q4_both(workloads.normal_f32(n * 3 + k, (n, k), 0.02))
+    wu, wud = _q4_both(workloads.normal_f32(n * 5 + k, (n, k), 0.02))
+    xo, xd = quantized_pair(workloads.activations(c + k, c, k))
+    y = host(moeq8.mmvq_q4(wgd, xd, n, k))
+    assert_close(y, oracle.mmvq_q4(wg, xo), PROD_TOL, "q4 product")
+    g = torch.empty((c, n), device=DEV)
+    u = torch.empty((c, n), device=DEV)
+    h = moeq8.mmvq_q4_glu_pair(wgd, wud, xd, n, k, g_out=g, u_out=u)
+    h_ref, _, _ = oracle.glu_pair_q4(wg, wu, xo)
+    assert_close(host(h), h_ref, EPI_TOL, "q4 pair")
+    # the pair's raw products are the separate products, and h is their SwiGLU
+    assert bits_equal(g, moeq8.mmvq_q4(wgd, xd, n, k))
+    assert bits_equal(u, moeq8.mmvq_q4(wud, xd, n, k))
+    assert bits_equal(h, moeq8.swiglu_ds4(g, u))
+
+
+def test_q4_batch_invariance_and_slices():
+    n, k = 128, 4096
+    w, wd = _q4_both(workloads.normal_f32(3, (n, k), 0.02))
+    xo, xd = quantized_pair(workloads.activations(9, 8, k))
+    full = moeq8.mmvq_q4(wd, xd, n, k)
+    for c in (1, 2, 5):
+        assert bits_equal(moeq8.mmvq_q4(wd, xd[:c].contiguous(), n, k), full[:c].contiguous())
+    # a column-range slice (blocks 32..64 of each row) equals the full product on
+    # activations that are zero outside the slice
+    kb, ks = 32, 1024
+    xs = workloads.activations(10, 2, k)
+    xz = np.zeros_like(xs)
+    xz[:, kb * 32:kb * 32 + ks] = xs[:, kb * 32:kb * 32 + ks]
+    _, xzd = quantized_pair(xz)
+    _, xsd = quantized_pair(np.ascontiguousarray(xs[:, kb * 32:kb * 32 + ks]))
+    sl = moeq8.mmvq_q4(wd, xsd, n, ks, k_block_offset=kb, w_offset_bytes=kb * 18,
+                       w_row_stride_bytes=(k // 32) * 18)
+    assert bits_equal(sl, moeq8.mmvq_q4(wd, xzd, n, k))
+
+
+@pytest.mark.parametrize("c,n_exp,hidden,inter", [(1, 16, 1024, 256), (8, 32, 2048, 512), (40, 16, 1024, 256)])
+def test_q4_grouped_vs_oracle_and_dense(c, n_exp, hidden, inter):
+    """Grouped gate/up and down (q8_1 and fp32 h) with Q4 experts: against the
+    oracle per route, and bit-equal to the dense product on each route."""
+    say(f"q4 grouped c={c} E={n_exp} H={hidden} I={inter}")
+    topk = 8
+    gate = [workloads.normal_f32(100 + e, (inter, hidden), 0.02) for e in range(n_exp)]
+    up = [workloads.normal_f32(300 + e, (inter, hidden), 0.02) for e in range(n_exp)]
+    down = [workloads.normal_f32(500 + e, (hidden, inter), 0.02) for e in range(n_exp)]
+    wg, wgd = _q4_both(np.concatenate(gate))
+    wu, wud = _q4_both(np.concatenate(up))
+    wdn, wdd = _q4_both(np.concatenate(down))
+    wg = wg.reshape(n_exp, inter, -1)
+    wu = wu.reshape(n_exp, inter, -1)
+    wdn = wdn.reshape(n_exp, hidden, -1)
+    x = workloads.activations(c + 1, c, hidden)
+    logits = workloads.router_logits(c + 2, c, n_exp)
+    ids_ref, _, _ = oracle.route_topk(logits, None, None, topk)
+    ids, _ = moeq8.moe_route_topk_wide(to_dev(logits), topk)
+    g = moeq8.moe_group_routes(ids, n_exp)
+    xo, xd = quantized_pair(x)
+    h = moeq8.moe_grouped_mmvq_q4(moeq8.GATE_UP_SWIGLU, wgd.view(-1), wud.view(-1), xd, g, n=inter,
+                                  k=hidden, n_local_expert=n_exp, ncols=c, topk=topk)
+    hh = host(h).reshape(c * topk, inter)
+    h_ref = np.zeros((c * topk, inter))
+    for e, routes in oracle.group_routes(ids_ref):
+        h_ref[routes] = oracle.glu_pair_q4(wg[e], wu[e], xo[[r // topk for r in routes]])[0]
+    assert_close(hh, h_ref, EPI_TOL, "q4 grouped h")
+    rb = (hidden // 32) * 18
+    for j in range(0, c, max(1, c // 4)):
+        e = int(ids_ref[j, 0])
+        hp = moeq8.mmvq_q4_glu_pair(wgd.view(-1), wud.view(-1), xd[j:j + 1].contiguous(), inter, hidden,
+                                    w_offset_bytes=e * inter * rb, w_row_stride_bytes=rb)
+        assert bits_equal(h[j, 0:1].contiguous(), hp)
+    # down on the oracle's h: q8_1 rows and, in one launch, fp32 rows
+    h32 = h_ref.astype(np.float32)
+    hq_ref, hq = quantized_pair(h32)
+    y = host(moeq8.moe_grouped_mmvq_q4(moeq8.DOWN, wdd.view(-1), None, hq, g, n=hidden, k=inter,
+                                       n_local_expert=n_exp, ncols=c, topk=topk)).reshape(c * topk, hidden)
+    y_ref = np.zeros((c * topk, hidden))
+    for e, routes in oracle.group_routes(ids_ref):
+        y_ref[routes] = oracle.mmvq_q4(wdn[e], hq_ref[routes])
+    assert_close(y, y_ref, PROD_TOL, "q4 grouped y")
+    yf = host(moeq8.moe_grouped_mmvq_q4(moeq8.DOWN_F32_ACT, wdd.view(-1), None, to_dev(h32), g, n=hidden,
+                                        k=inter, n_local_expert=n_exp, ncols=c, topk=topk)).reshape(c * topk, hidden)
+    assert yf.tobytes() == y.tobytes()
