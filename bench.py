@@ -16,6 +16,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   sweep     the routed layer (256 experts, top-8) at 1, 2, 4, 5, 8 columns
   wide      the same layer at 32..1024 columns: grouped products on the int8
             matrix cores against the grouped MMVQ in passes of 8 columns
+  q4_sweep  the routed layer of the sweep with 4-bit expert weights (18-byte
+            blocks) at 1, 2, 4, 5, 8 columns
   codec     the 8-bit block exchange codec on prefill partials of 4096 values
             a row (a 1K-row band and an 8K-row one): encode, and the
             rank-order decode-sum of 2 and 8 ranks' blocks
@@ -53,6 +55,8 @@ def parse():
                     help="skip the wide-batch (32..1024 columns) measurement")
     ap.add_argument("--no-codec", action="store_true",
                     help="skip the 8-bit exchange codec measurement")
+    ap.add_argument("--no-q4", action="store_true",
+                    help="skip the 4-bit expert-weight sweep")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the oracle sample")
     ap.add_argument("--pmc-copy", action="store_true",
@@ -469,6 +473,8 @@ def main():
         result["wide"] = wide_sweep(torch, workloads, moeq8, ml, args)
     if not args.no_codec:
         result["codec"] = codec_bench(torch, workloads, moeq8, args)
+    if not args.no_q4:
+        result["q4_sweep"] = q4_sweep(torch, workloads, moeq8, ml, args)
 
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -639,6 +645,87 @@ def codec_bench(torch, workloads, moeq8, args):
         log(f"codec {rec}")
         out.append(rec)
         del x, blocks, gathered, res
+    torch.cuda.empty_cache()
+    return out
+
+
+def q4_sweep(torch, workloads, moeq8, ml, args):
+    """The sweep's routed layer (256 experts, top-8, no shared expert) with
+    4-bit expert weights: N(0, 0.02^2) weights drawn on the GPU (torch, seeded)
+    and quantised by q4_quantize_rows, 4 rotating replicas (5.4 GB).  Per
+    column count: the four-launch layer, the grouped gate/up alone, and the
+    streaming ceiling for the same bytes."""
+    cfg = workloads.CONFIGS["verify_e256_c5"]
+    hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
+    reps = 4
+    q4b = 18
+    gen = torch.Generator(device="cuda").manual_seed(44)
+    per_gu = inter * (hidden // 32) * q4b
+    per_d = hidden * (inter // 32) * q4b
+    banks = []
+    for _ in range(reps):
+        t = {}
+        for name, rows, k, per in (("gate", inter, hidden, per_gu), ("up", inter, hidden, per_gu),
+                                   ("down", hidden, inter, per_d)):
+            buf = torch.empty(n_exp * per, dtype=torch.uint8, device="cuda")
+            for e in range(n_exp):
+                w = torch.randn((rows, k), generator=gen, device="cuda") * 0.02
+                moeq8.q4_quantize_rows(w, out=buf[e * per:(e + 1) * per].view(rows, -1))
+            t[name] = buf
+        banks.append(t)
+    torch.cuda.synchronize()
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    row_gu = (hidden // 32) * q4b
+    out = []
+    for cols in (1, 2, 4, 5, 8):
+        xs, lgs, bs = layer_inputs(torch, workloads, 4, reps, cols, hidden, n_exp)
+        wss = [ml.Workspace(cols, hidden, inter, topk, 0, "cuda") for _ in range(reps)]
+        experts = [ml.RoutedExperts(b["gate"], b["up"], b["down"], n_exp, hidden, inter, fmt="q4")
+                   for b in banks]
+
+        def step():
+            for l in range(reps):
+                ml.forward(xs[l], lgs[l], bs[l], None, n_exp, experts[l], None, wss[l])
+
+        step()
+        torch.cuda.synchronize()
+        n_active, n_valid = [], []
+        for l in range(reps):
+            words = wss[l].grouping.cpu().numpy().view(np.int32)
+            n_active.append(int(words[0]))
+            n_valid.append(int(words[1]))
+        n = max(20, args.steps)
+        ms = time_graph(torch, step, n) / reps
+
+        def gate_up_only():
+            for l in range(reps):
+                moeq8.moe_grouped_mmvq_q4(moeq8.GATE_UP_SWIGLU, banks[l]["gate"], banks[l]["up"], wss[l].xq,
+                                          wss[l].grouping, n=inter, k=hidden, n_local_expert=n_exp,
+                                          ncols=cols, topk=topk, out=wss[l].h)
+
+        gu_b = [n_active[l] * 2 * inter * row_gu + cols * (hidden // 32 * 36) + n_valid[l] * inter * 4
+                for l in range(reps)]
+        read_b = [int(b) // 16 * 16 for b in gu_b]
+
+        def stream_only():
+            for l in range(reps):
+                moeq8.stream_read(banks[l]["gate"], min(read_b[l], banks[l]["gate"].numel() // 16 * 16), sink)
+
+        gu_us = time_graph(torch, gate_up_only, n) / reps * 1e3
+        st_us = time_graph(torch, stream_only, n) / reps * 1e3
+        gu_gbps = float(np.mean(gu_b)) / (gu_us * 1e-6) / 1e9
+        st_bytes = float(np.mean([min(b, banks[0]["gate"].numel() // 16 * 16) for b in read_b]))
+        st_gbps = st_bytes / (st_us * 1e-6) / 1e9
+        weights = float(np.mean([n_active[l] * ml.expert_bytes_q4(hidden, inter) for l in range(reps)]))
+        rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2),
+               "layer_us": round(ms * 1e3, 2), "layers_per_s": round(1e3 / ms, 1),
+               "expert_weight_gbps": round(weights / (ms * 1e-3) / 1e9, 1),
+               "gate_up_us": round(gu_us, 2), "gate_up_gbps": round(gu_gbps, 1),
+               "gate_up_frac_of_peak": round(gu_gbps / HBM_PEAK_GBPS, 4),
+               "ceiling_gbps": round(st_gbps, 1), "gate_up_frac_of_ceiling": round(gu_gbps / st_gbps, 4)}
+        log(f"q4 {rec}")
+        out.append(rec)
+    del banks
     torch.cuda.empty_cache()
     return out
 

@@ -545,11 +545,16 @@ MatDesc make_desc(const void* w0, const void* w1, int64_t row_stride, int64_t n,
     return d;
 }
 
-constexpr int u_for(int nmat, bool act_f32) { return nmat == 2 ? U_ROWSETS : act_f32 ? U_F32 : U_SINGLE; }
+#ifndef MOEQ8_U_Q4_SCALE
+#define MOEQ8_U_Q4_SCALE 1
+#endif
+constexpr int u_for(int nmat, bool act_f32, bool q4 = false) {
+    return (nmat == 2 ? U_ROWSETS : act_f32 ? U_F32 : U_SINGLE) * (q4 ? MOEQ8_U_Q4_SCALE : 1);
+}
 
 int rows_per_wg_for(const Shape& s, int u) { return WAVES_PER_WG * u * (4 / s.G); }
 
-template <int NMAT, bool GROUPED, bool ACT_F32, bool STX, bool Q4, int U = u_for(NMAT, ACT_F32)>
+template <int NMAT, bool GROUPED, bool ACT_F32, bool STX, bool Q4, int U = u_for(NMAT, ACT_F32, Q4)>
 int launch_shape(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
     const dim3 block(64 * WAVES_PER_WG);
     switch (s.G) {
@@ -609,7 +614,7 @@ int dense_call(int nmat, const void* w0, const void* w1, int64_t stride, int64_t
                void* stream, bool q4 = false) {
     MmvqParams p = {};
     const Shape s = pick_shape(kb / 2, k / 64);
-    p.rows_per_wg = rows_per_wg_for(s, u_for(nmat, false));
+    p.rows_per_wg = rows_per_wg_for(s, u_for(nmat, false, q4));
     p.m = make_desc(w0, w1, stride, n, k, kb, p.rows_per_wg);
     p.act = (const uint8_t*)xq;
     p.act_row_bytes = (k / QK) * Q81_BYTES;
@@ -722,7 +727,7 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
 
     MmvqParams p = {};
     const Shape s = pick_shape(0, k / 64);
-    p.rows_per_wg = rows_per_wg_for(s, u_for(pair ? 2 : 1, f32));
+    p.rows_per_wg = rows_per_wg_for(s, u_for(pair ? 2 : 1, f32, q4));
     p.m = make_desc(w_a, w_b, w_row_stride_bytes, n, k, 0, p.rows_per_wg);
     p.expert_stride = expert_stride_bytes;
     p.n_local = n_local_expert;

@@ -33,14 +33,17 @@ Q81 = ops.Q8_1_BLOCK_BYTES
 
 @dataclass
 class RoutedExperts:
-    """Local experts of one layer, Q8_0, each [rows][k/32] blocks, experts
-    ``expert_stride`` bytes apart (views into larger tensors are fine)."""
+    """Local experts of one layer, each [rows][k/32] blocks, experts
+    ``expert_stride`` bytes apart (views into larger tensors are fine).
+    fmt: "q8_0" (34-byte blocks) or "q4" (18-byte 4-bit blocks, for
+    bandwidth-only expert weights)."""
     gate: torch.Tensor       # uint8, n_local x inter x hidden/32 blocks
     up: torch.Tensor
     down: torch.Tensor       # uint8, n_local x hidden x inter/32 blocks
     n_local: int
     hidden: int
     inter: int
+    fmt: str = "q8_0"
 
 
 @dataclass
@@ -120,6 +123,10 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     Both give the same bits.  ``hook(name, phase)`` (unfused only) is called
     around each launch."""
     add = add_shared and shared is not None
+    if experts.fmt == "q4":
+        return _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add)
+    if experts.fmt != "q8_0":
+        raise ValueError("experts.fmt must be 'q8_0' or 'q4'")
     if fused:
         return _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add)
     c, topk = ws.ncols, ws.topk
@@ -268,6 +275,40 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
             n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
     ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
     return ws.out
+
+
+def _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add):
+    """The layer with 4-bit routed experts: prologue, grouped gate/up,
+    grouped down quantising h in the launch, combine (four launches); a shared
+    expert (Q8_0) runs as its own pair, quantisation and down calls."""
+    c, topk = ws.ncols, ws.topk
+    hidden, inter = experts.hidden, experts.inter
+    ops.moe_route_topk_quantize(x, logits, topk, bias=bias, owner_slot=owner_slot,
+                                n_local_expert=n_local_expert, xq=ws.xq, ids=ws.ids,
+                                weights=ws.weights, grouping=ws.grouping)
+    R = c * topk
+    ops.moe_grouped_mmvq_q4(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping,
+                            n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
+                            out=ws.h)
+    ops.moe_grouped_mmvq_q4(ops.DOWN_F32_ACT, experts.down, None, ws.h.view(R, inter), ws.grouping,
+                            n=hidden, k=inter, n_local_expert=experts.n_local, ncols=c, topk=topk,
+                            out=ws.y)
+    if shared is not None:
+        rb = (hidden // QK) * Q80
+        ops.mmvq_q8_0_glu_pair(shared.gate, shared.up, ws.xq, shared.rows, hidden, ncols=c,
+                               w_offset_bytes=shared.gate_offset(), w_row_stride_bytes=rb, out=ws.hs)
+        ops.q8_1_quantize_rows(ws.hs, out=ws.hsq)
+        kb = shared.down_block_offset()
+        ops.mmvq_q8_0(shared.down, ws.hsq, hidden, shared.rows, ncols=c, k_block_offset=kb,
+                      w_offset_bytes=kb * Q80, w_row_stride_bytes=(shared.inter_full // QK) * Q80,
+                      out=ws.ys)
+    ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out, shared=ws.ys if add else None)
+    return ws.out, ws.ys
+
+
+def expert_bytes_q4(hidden: int, inter: int) -> int:
+    """Bytes of one routed expert in 4-bit blocks (gate + up + down)."""
+    return 3 * inter * (hidden // QK) * ops.Q4_BLOCK_BYTES
 
 
 def expert_bytes(hidden: int, inter: int) -> int:

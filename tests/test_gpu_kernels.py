@@ -976,3 +976,28 @@ def test_q4_grouped_vs_oracle_and_dense(c, n_exp, hidden, inter):
     yf = host(moeq8.moe_grouped_mmvq_q4(moeq8.DOWN_F32_ACT, wdd.view(-1), None, to_dev(h32), g, n=hidden,
                                         k=inter, n_local_expert=n_exp, ncols=c, topk=topk)).reshape(c * topk, hidden)
     assert yf.tobytes() == y.tobytes()
+
+
+def test_q4_layer_equals_its_calls():
+    """moe_layer.forward with 4-bit experts (four launches) gives the bits of
+    the separate calls: route, grouped gate/up, q8_1 of h, grouped down,
+    combine."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    c, n_exp, hidden, inter, topk = 5, 16, 1024, 256, 8
+    wg = moeq8.q4_quantize_rows(to_dev(workloads.normal_f32(1, (n_exp * inter, hidden), 0.02))).view(-1)
+    wu = moeq8.q4_quantize_rows(to_dev(workloads.normal_f32(2, (n_exp * inter, hidden), 0.02))).view(-1)
+    wd = moeq8.q4_quantize_rows(to_dev(workloads.normal_f32(3, (n_exp * hidden, inter), 0.02))).view(-1)
+    experts = ml.RoutedExperts(wg, wu, wd, n_exp, hidden, inter, fmt="q4")
+    x = to_dev(workloads.activations(4, c, hidden))
+    lg = to_dev(workloads.router_logits(5, c, n_exp))
+    ws = ml.Workspace(c, hidden, inter, topk, 0, DEV)
+    out, _ = ml.forward(x, lg, None, None, n_exp, experts, None, ws)
+    out = out.clone()
+    ids, w, g = moeq8.moe_route_topk(lg, topk)
+    xq = moeq8.q8_1_quantize_rows(x)
+    h = moeq8.moe_grouped_mmvq_q4(moeq8.GATE_UP_SWIGLU, wg, wu, xq, g, n=inter, k=hidden, n_local_expert=n_exp,
+                                  ncols=c, topk=topk)
+    hq = moeq8.q8_1_quantize_rows(h.view(c * topk, inter))
+    y = moeq8.moe_grouped_mmvq_q4(moeq8.DOWN, wd, None, hq, g, n=hidden, k=inter, n_local_expert=n_exp,
+                                  ncols=c, topk=topk)
+    assert bits_equal(out, moeq8.moe_combine(y, ids, w))
