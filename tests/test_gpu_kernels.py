@@ -1001,3 +1001,26 @@ def test_q4_layer_equals_its_calls():
     y = moeq8.moe_grouped_mmvq_q4(moeq8.DOWN, wd, None, hq, g, n=hidden, k=inter, n_local_expert=n_exp,
                                   ncols=c, topk=topk)
     assert bits_equal(out, moeq8.moe_combine(y, ids, w))
+
+
+def test_grouped_gemm_takes_the_decode_grouping():
+    """moe_grouped_gemm on the grouping moe_route_topk writes (8 columns, owner
+    mask) gives the oracle's products, like the grouped MMVQ on it."""
+    c, n_exp, local, hidden, inter, topk = 8, 64, 32, 1024, 256, 8
+    (wg, wu, wdn), (wgd, wud, wdd) = _tiny_layer(77, local, hidden, inter)
+    x = workloads.activations(78, c, hidden)
+    logits = workloads.router_logits(79, c, n_exp)
+    own = workloads.owner_slots(n_exp, local)
+    xo, xd = quantized_pair(x)
+    ids, _, grouping = moeq8.moe_route_topk(to_dev(logits), topk, owner_slot=to_dev(own), n_local_expert=local)
+    ids_ref, _, _ = oracle.route_topk(logits, None, own, topk)
+    assert np.array_equal(host(ids), ids_ref)
+    h = torch.full((c, topk, inter), float("nan"), device=DEV)
+    moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU, wgd, wud, xd, grouping, n=inter, k=hidden, n_local_expert=local,
+                           ncols=c, topk=topk, out=h)
+    hh = host(h).reshape(c * topk, inter)
+    masked = ids_ref.reshape(-1) < 0
+    assert np.isnan(hh[masked]).all()
+    for e, routes in oracle.group_routes(ids_ref):
+        ref = oracle.glu_pair(wg[e], wu[e], xo[[r // topk for r in routes]])[0]
+        assert_close(hh[routes], ref, EPI_TOL, f"gemm on decode grouping, expert {e}")
