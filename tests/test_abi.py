@@ -157,3 +157,11 @@ def test_synth_stream_key_host_matches_generator():
     L = moeq8.lib()
     for args in [(0, 0, 0, 0), (5, 42, 127, 2), (65535, 3, 9, 5)]:
         assert L.moeq8_synth_stream_key(*args) == workloads.stream_key(*args)
+
+
+def test_wide_products_choice():
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    assert ml.wide_products_for(32, 8, 256) == "mmvq"       # one route per expert
+    assert ml.wide_products_for(128, 8, 256) == "gemm"      # four routes per expert
+    assert ml.wide_products_for(1024, 8, 256) == "gemm"
+    assert ml.wide_products_for(8, 8, 16) == "gemm"

@@ -377,7 +377,7 @@ def test_wide_e256_c512():
     logits = workloads.router_logits(seed, c, E)
     bias = workloads.router_bias(seed, E)
     ws = ml.WideWorkspace(c, H, I, topk, DEV)
-    ml.forward_wide(to_dev(x), to_dev(logits), to_dev(bias), None, E, experts, ws)
+    ml.forward_wide(to_dev(x), to_dev(logits), to_dev(bias), None, E, experts, ws, products="gemm")
     torch.cuda.synchronize()
 
     xq_ref = oracle.quantize_q8_1(x)
