@@ -29,14 +29,14 @@
 //
 // Work.  A work unit is (group, row tile, chunk of up to 16 * NT of the
 // group's routes); a wave runs its chunk as NT 16-route tiles against each
-// weight load (the rearranged weights stay in LDS while the tiles' activations
-// pass through one shared area in turn), so weight rows are read once per
-// chunk.  The routing is very uneven at wide batches (one expert may get
-// hundreds of routes), so a heavily routed expert is spread over several
-// chunks instead of one unit looping over its routes.  Units are numbered with the
-// chunk fastest, and unit u runs on XCD u / ceil(units / 8) (workgroups are
-// dispatched to the 8 XCDs round-robin), so the chunks that read the same
-// weight rows run on one XCD at about the same time and share its L2.
+// weight load (the rearranged weights stay in LDS while the tiles'
+// activations pass through one LDS area of the wave in turn), so weight rows
+// are read once per chunk.  The routing is very uneven at wide batches (one
+// expert may get hundreds of routes), so a heavily routed expert is spread
+// over several chunks instead of one unit looping over its routes.  Units are
+// numbered with the chunk fastest, and unit u runs on XCD u / ceil(units / 8)
+// (workgroups are dispatched to the 8 XCDs round-robin), so the chunks that
+// read the same weight rows run on one XCD close together in time.
 //   gate/up: a wave owns 16 rows of the gate and the same 16 rows of the up
 //            matrix; both share every activation fragment; SwiGLU-DS4 epilogue.
 //   down:    a wave owns 32 consecutive rows (two 16-row fragments).
