@@ -87,59 +87,6 @@ struct MmvqParams {
     float* s_out;               // [ncols][s.n]
 };
 
-// The q8_1 block rule on half a block: this lane holds 16 of the block's 32
-// values, the neighbouring lane (lane ^ 1) the other 16.  The block's amax and
-// its integer quant sum are combined across the pair (max and integer sums do
-// not depend on order), so both lanes see the same d and s.  Every lane of the
-// wave must call this; lanes with active == false write nothing.
-__device__ __forceinline__ void quantize_half_q81(const float (&v)[QK / 2], int half, bool active,
-                                                  uint8_t* block) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < QK / 2; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
-                                                                   0xf, 0xf, false)));
-    const float d = amax / 127.0f;
-    uint32_t packed[QK / 8] = {0u, 0u, 0u, 0u};
-    int sum = 0;
-    if (d != 0.0f) {
-#pragma unroll
-        for (int i = 0; i < QK / 2; ++i) {
-            const int q = (int)roundf(v[i] / d);
-            sum += q;
-            packed[i / 4] |= ((uint32_t)q & 0xffu) << (8 * (i % 4));
-        }
-    }
-    sum += __builtin_amdgcn_update_dpp(0, sum, 0xB1, 0xf, 0xf, false);
-    if (active) {
-        uint32_t* o = reinterpret_cast<uint32_t*>(block);
-        if (half == 0) {
-            // s = fp16 of the fp32 product (two roundings, as defined)
-            const uint32_t sbits = float_to_half_bits(materialize_f32(d * (float)sum));
-            o[0] = float_to_half_bits(d) | (sbits << 16);
-        }
-#pragma unroll
-        for (int j = 0; j < QK / 8; ++j) o[1 + 4 * half + j] = packed[j];
-    }
-}
-
-// Pairwise tree over the 16 logical lanes of a group using DPP lane moves:
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  The
-// pairs combined at each level are the same values as an xor 1, 2, 4, 8
-// butterfly (quads, then the two quads of each half, then the two halves), and
-// a + b == b + a, so every lane ends with the same tree sum.
-__device__ __forceinline__ float tree16(float v) {
-    int iv = __float_as_int(v);
-    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xf, 0xf, false));
-    iv = __float_as_int(v);
-    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xf, 0xf, false));
-    iv = __float_as_int(v);
-    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x141, 0xf, 0xf, false));
-    iv = __float_as_int(v);
-    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x140, 0xf, 0xf, false));
-    return v;
-}
-
 // Chain the G per-round values of one logical lane in round order (group 0
 // holds the earliest round), result valid in group 0.
 template <int G>

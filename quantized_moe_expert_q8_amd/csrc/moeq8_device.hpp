@@ -173,6 +173,31 @@ __device__ __forceinline__ float chunk_dot(const WChunk& w, const XChunk& x) {
     return p0 + p1;
 }
 
+// Reciprocal of a block scale for q8_code: NaN for a scale below the normal
+// range, which sends every value of the block to the IEEE division.
+__device__ __forceinline__ float q8_code_rcp(float d) {
+    return d >= 0x1p-126f ? __builtin_amdgcn_rcpf(d) : __builtin_nanf("");
+}
+
+// Code of x in a block of scale d (|x| <= 127 d): roundf of the correctly
+// rounded fp32 quotient x / d, as the block rule defines it, without a
+// division for almost every value.  t = x * rcp(d) is within 3.1e-5 of the
+// correctly rounded quotient (v_rcp_f32 within an ulp, one rounded multiply,
+// |x / d| <= 127), so where t lies more than 2^-12 from every half-integer
+// both round to the same integer and rint(t) is it; the other values (and a
+// NaN t from q8_code_rcp) take the IEEE division.  The division is the rule;
+// this only decides when it can be skipped.
+__device__ __forceinline__ int q8_code(float x, float d, float rd) {
+    const float t = x * rd;
+    const float r = __builtin_rintf(t);
+    const bool near = !(fabsf(t - r) < 0.5f - 0x1p-12f);
+    int q = (int)r;
+    if (__builtin_expect(__ballot(near) != 0, 0)) {
+        if (near) q = (int)roundf(x / d);
+    }
+    return q;
+}
+
 // Quantise one 32-value block (the block rule of both formats): fp32
 // d = amax / 127 (IEEE division), q = roundf(x / d) on the fp32 quotient
 // (halves away from zero), d stored as fp16 (nearest even); q8_1 adds
@@ -189,6 +214,7 @@ __device__ __forceinline__ void quantize_block(const float* __restrict__ src, ui
         amax = fmaxf(amax, fabsf(v[i]));
     }
     const float d = amax / 127.0f;
+    const float rd = q8_code_rcp(d);
     uint32_t packed[QK / 4];
     int sum = 0;
 #pragma unroll
@@ -196,7 +222,7 @@ __device__ __forceinline__ void quantize_block(const float* __restrict__ src, ui
     if (d != 0.0f) {
 #pragma unroll
         for (int i = 0; i < QK; ++i) {
-            const int q = (int)roundf(v[i] / d);
+            const int q = q8_code(v[i], d, rd);
             sum += q;
             packed[i / 4] |= ((uint32_t)q & 0xffu) << (8 * (i % 4));
         }
@@ -311,6 +337,60 @@ __device__ __forceinline__ void quantize_block_q4(const float* __restrict__ src,
     for (int i = 0; i < QK / 4; ++i)                   // bytes 2i, 2i+1 of qs
         o[1 + i] = (uint16_t)(code[2 * i] | (code[16 + 2 * i] << 4) |
                               ((code[2 * i + 1] | (code[16 + 2 * i + 1] << 4)) << 8));
+}
+
+// The q8_1 block rule on half a block: this lane holds 16 of the block's 32
+// values, the neighbouring lane (lane ^ 1) the other 16.  The block's amax and
+// its integer quant sum are combined across the pair (max and integer sums do
+// not depend on order), so both lanes see the same d and s.  Every lane of the
+// wave must call this; lanes with active == false write nothing.
+__device__ __forceinline__ void quantize_half_q81(const float (&v)[QK / 2], int half, bool active,
+                                                  uint8_t* block) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK / 2; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
+                                                                   0xf, 0xf, false)));
+    const float d = amax / 127.0f;
+    const float rd = q8_code_rcp(d);
+    uint32_t packed[QK / 8] = {0u, 0u, 0u, 0u};
+    int sum = 0;
+    if (d != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < QK / 2; ++i) {
+            const int q = q8_code(v[i], d, rd);
+            sum += q;
+            packed[i / 4] |= ((uint32_t)q & 0xffu) << (8 * (i % 4));
+        }
+    }
+    sum += __builtin_amdgcn_update_dpp(0, sum, 0xB1, 0xf, 0xf, false);
+    if (active) {
+        uint32_t* o = reinterpret_cast<uint32_t*>(block);
+        if (half == 0) {
+            // s = fp16 of the fp32 product (two roundings, as defined)
+            const uint32_t sbits = float_to_half_bits(materialize_f32(d * (float)sum));
+            o[0] = float_to_half_bits(d) | (sbits << 16);
+        }
+#pragma unroll
+        for (int j = 0; j < QK / 8; ++j) o[1 + 4 * half + j] = packed[j];
+    }
+}
+
+// Pairwise tree over the 16 logical lanes of a group using DPP lane moves:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  The
+// pairs combined at each level are the same values as an xor 1, 2, 4, 8
+// butterfly (quads, then the two quads of each half, then the two halves), and
+// a + b == b + a, so every lane ends with the same tree sum.
+__device__ __forceinline__ float tree16(float v) {
+    int iv = __float_as_int(v);
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xf, 0xf, false));
+    iv = __float_as_int(v);
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xf, 0xf, false));
+    iv = __float_as_int(v);
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x141, 0xf, 0xf, false));
+    iv = __float_as_int(v);
+    v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x140, 0xf, 0xf, false));
+    return v;
 }
 
 // SwiGLU-DS4 in fp32: silu(min(g, 7)) * clamp(u, -7, 7).
