@@ -441,8 +441,9 @@ def main():
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "scaled by a 512 MiB copy)",
                      "mean_launch_us": round(gu_us, 2), "bytes_per_launch": int(gu_bytes),
-                     "ceiling": {"what": "plain coalesced streaming read of the same bytes per "
-                                         "launch from the same weight bank, 43 launches in a graph",
+                     "ceiling": {"what": "plain coalesced nontemporal streaming read of the same "
+                                         "bytes per launch from the same weight bank, 43 launches "
+                                         "in a graph",
                                  "gbps": round(st_gbps, 1), "mean_launch_us": round(st_us, 2),
                                  "frac_of_ceiling": round(gu_gbps / st_gbps, 4)}},
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, 10)), 4),

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_stream_read(const u32x4v* __restrict__ 
 #pragma unroll
     for (int i = 0; i < STREAM_WG_BYTES / 16 / 256; ++i) {
         const int64_t idx = base + i * 256 + threadIdx.x;
-        v[i] = idx < n16 ? p[idx] : u32x4v{0u, 0u, 0u, 0u};
+        v[i] = idx < n16 ? __builtin_nontemporal_load(p + idx) : u32x4v{0u, 0u, 0u, 0u};
     }
     uint32_t acc = 0;
 #pragma unroll
