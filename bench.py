@@ -97,9 +97,27 @@ class Bank:
                                  (self.sdown, 5, hidden * shared_inter // 32)):
                 moeq8.synth_q8_0_fill(t, layers, blocks, 1, seed, 0, 0, m)
 
+    packed = False
+
+    def pack_gate_up(self, moeq8, torch):
+        """Repack every layer's routed (and shared) gate and up matrices into the
+        64-chunk packed layout the fused gate/up launch reads, in place through
+        one layer-sized buffer."""
+        for banks, rows in (((self.gate, self.up), self.n_local * self.inter),
+                            ((getattr(self, "sgate", None), getattr(self, "sup", None)), self.shared_inter)):
+            if not rows or banks[0] is None:
+                continue
+            tmp = torch.empty_like(banks[0][0])
+            for bank in banks:
+                for l in range(self.layers):
+                    moeq8.q8_0_pack64_rows(bank[l], rows, self.hidden, out=tmp)
+                    bank[l].copy_(tmp)
+            del tmp
+        self.packed = True
+
     def experts(self, ml, l):
         return ml.RoutedExperts(self.gate[l], self.up[l], self.down[l], self.n_local, self.hidden,
-                                self.inter)
+                                self.inter, packed=self.packed)
 
     def shared(self, ml, l, share_rows, share_index=0):
         if not self.shared_inter:
@@ -108,7 +126,8 @@ class Bank:
         return ml.SharedExpertShare(self.sgate[l].view(self.shared_inter, rb_h),
                                     self.sup[l].view(self.shared_inter, rb_h),
                                     self.sdown[l].view(self.hidden, self.shared_inter // 32 * 34),
-                                    self.hidden, self.shared_inter, share_index * share_rows, share_rows)
+                                    self.hidden, self.shared_inter, share_index * share_rows, share_rows,
+                                    packed=self.packed)
 
 
 def layer_inputs(torch, workloads, seed, layers, cols, hidden, n_expert):
@@ -290,6 +309,7 @@ def main():
 
     t0 = time.perf_counter()
     bank = Bank(moeq8, torch, L, n_local, hidden, inter, seed, cfg["shared_inter"])
+    bank.pack_gate_up(moeq8, torch)
     xs, lgs, bs = layer_inputs(torch, workloads, seed, L, cols, hidden, n_exp)
     owner = torch.from_numpy(workloads.owner_slots(n_exp, n_local)).cuda()
     side = torch.cuda.Stream()
@@ -369,7 +389,7 @@ def main():
         for l in range(L):
             w, sh = wss[l], shared[l]
             moeq8.moe_grouped_mmvq_ex(
-                moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, w.xq, w.grouping, n=inter,
+                moeq8.GATE_UP_SWIGLU_P64, experts[l].gate, experts[l].up, w.xq, w.grouping, n=inter,
                 k=hidden, n_local_expert=n_local, ncols=cols, topk=topk, out=w.h,
                 shared={"a": sh.gate, "b": sh.up, "row_stride": rb_h, "n": sh.rows, "k": hidden,
                         "k_block_offset": 0, "offset_bytes": sh.gate_offset(), "out": w.hs})
@@ -434,7 +454,7 @@ def main():
         "step_bytes": step_bytes,
         "weight_bytes": weight_bytes,
         "active_experts_mean": round(float(np.mean(n_active)), 2),
-        "roofline": {"bound": "hbm", "kernel": "k_mmvq grouped gate/up + SwiGLU (routed experts "
+        "roofline": {"bound": "hbm", "kernel": "k_mmvq grouped gate/up + SwiGLU on the 64-chunk packed layout (routed experts "
                                "and the shared expert's rows in one launch)",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
@@ -494,6 +514,7 @@ def sweep(torch, workloads, moeq8, ml, args):
     hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
     reps = 4
     bank = Bank(moeq8, torch, reps, n_exp, hidden, inter, 4)
+    bank.pack_gate_up(moeq8, torch)
     sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
     out = []
     for cols in (1, 2, 4, 5, 8):
@@ -519,7 +540,7 @@ def sweep(torch, workloads, moeq8, ml, args):
 
         def gate_up_only():
             for l in range(reps):
-                moeq8.moe_grouped_mmvq(moeq8.GATE_UP_SWIGLU, experts[l].gate, experts[l].up, wss[l].xq,
+                moeq8.moe_grouped_mmvq_ex(moeq8.GATE_UP_SWIGLU_P64, experts[l].gate, experts[l].up, wss[l].xq,
                                        wss[l].grouping, n=inter, k=hidden, n_local_expert=n_exp,
                                        ncols=cols, topk=topk, out=wss[l].h)
 

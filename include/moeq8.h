@@ -97,6 +97,19 @@ int q8_1_quantize_rows(const float* x, int64_t n_rows, int64_t k, int64_t x_row_
 int q8_0_quantize_rows(const float* w, int64_t n_rows, int64_t k, int64_t w_row_stride,
                        void* wq, void* stream);
 
+/* Repack Q8_0 rows into the 64-chunk packed layout read by
+ * MOEQ8_GATE_UP_SWIGLU_P64.  A row of k values (k a multiple of 4096) is k/4096
+ * segments of 64 two-block chunks (4352 bytes, 1088 dwords); within a segment
+ * dword d < 16 of chunk c (plain dword 17c + d) moves to dword
+ * 256*(d/4) + 4c + d%4 and dword 16 of chunk c to dword 1024 + c.  Same bytes,
+ * permuted within each segment, so a wave whose lane c reads chunk c fetches
+ * each 16-byte piece of its chunks with one contiguous load across the wave.
+ *   src  Q8_0 rows [n_rows], src_row_stride_bytes apart
+ *   dst  packed rows [n_rows], dst_row_stride_bytes apart; must not overlap src
+ * Strides >= k/32*34 bytes, pointers and strides multiples of 4 bytes. */
+int q8_0_pack64_rows(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes,
+                     void* dst, int64_t dst_row_stride_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * a3 (+a10): single Q8_0 x q8_1 product, y[c][i] = sum over the k/32 blocks b of
  * row i of d_w * d_x * sum(qw * qx).
@@ -182,7 +195,8 @@ int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_
  * bit-identical to mmvq_q8_0 (DOWN) or mmvq_q8_0_glu_pair's h (GATE_UP) on that
  * expert and that route's activation row.
  * ------------------------------------------------------------------------- */
-enum moeq8_stage { MOEQ8_GATE_UP_SWIGLU = 0, MOEQ8_DOWN = 1, MOEQ8_DOWN_F32_ACT = 2 };
+enum moeq8_stage { MOEQ8_GATE_UP_SWIGLU = 0, MOEQ8_DOWN = 1, MOEQ8_DOWN_F32_ACT = 2,
+                   MOEQ8_GATE_UP_SWIGLU_P64 = 3 };
 int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
                      int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
                      int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
@@ -207,6 +221,15 @@ int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
  *     Each s_out element is bit-identical to mmvq_q8_0_glu_pair / mmvq_q8_0 on
  *     that slice.  A dense part whose s_k differs from k, or whose slice spans a
  *     different number of 16-chunk rounds, is MOEQ8_EUNSUPPORTED (call it apart).
+ *   - stage MOEQ8_GATE_UP_SWIGLU_P64: the gate/up stage on weights repacked by
+ *     q8_0_pack64_rows (the routed experts and the dense part alike).  Each
+ *     lane's chunk arrives through four 16-byte and one 4-byte nontemporal
+ *     loads that read one contiguous span across the wave.  Requires
+ *     k == 4096 (one packed segment a row; a dense slice starting at a
+ *     multiple of 128 blocks) else MOEQ8_EUNSUPPORTED, and 16-byte aligned
+ *     weight pointers, row strides and expert stride else MOEQ8_EALIGN.
+ *     Every output is bit-identical to MOEQ8_GATE_UP_SWIGLU on the unpacked
+ *     weights.
  * act_row_stride is ignored for the q8_1 stages.
  * ------------------------------------------------------------------------- */
 int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,

@@ -101,8 +101,12 @@ __device__ __forceinline__ float chain_groups(float v, int lane) {
     }
 }
 
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4>
+// P64: the weights are in the 64-chunk packed layout (moeq8_device.hpp); the
+// launch reads one 64-chunk segment a row (K = 4096 at a segment boundary),
+// so with four lane groups a row (G = 4) lane L holds chunk L of the segment.
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false>
 __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
+    static_assert(!P64 || (G == 4 && !Q4 && !ACT_F32 && !STX), "the packed layout serves the q8_1 four-group rows");
     // weight chunk: two Q8_0 blocks (68 B) or two 4-bit blocks (36 B); the
     // chunk's value has the same form either way, so the reduction order and
     // every launch shape are shared
@@ -229,7 +233,10 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                 const int64_t off = ok[u] ? row * row_stride + (int64_t)crel * WCB : 0;
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
-                    if (UNCOND || ok[u]) {
+                    if constexpr (P64) {
+                        if (ok[u]) load_w_chunk_p64(wc[u][m], (m == 0 ? w0 : w1) + row * row_stride, crel);
+                        else zero_w_chunk(wc[u][m]);
+                    } else if (UNCOND || ok[u]) {
                         load_w_chunk(wc[u][m], (m == 0 ? w0 : w1) + off);
                     } else {
                         zero_w_chunk(wc[u][m]);
@@ -446,10 +453,10 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 
 // One work item = one row block: of one active expert (grouped), of the dense
 // extra matrix (grouped launches with a shared part), or of the one matrix.
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4>
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false>
 __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_act[];
-    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX, Q4>(p, blockIdx.x, lds_act);
+    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX, Q4, P64>(p, blockIdx.x, lds_act);
 }
 
 __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, float* h) {
@@ -509,6 +516,17 @@ int launch_shape(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, 
         case 2: hipLaunchKernelGGL((k_mmvq<2, NMAT, U, GROUPED, ACT_F32, STX, Q4>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
         default: hipLaunchKernelGGL((k_mmvq<4, NMAT, U, GROUPED, ACT_F32, STX, Q4>), dim3((uint32_t)grid), block, lds_bytes, stream, p); break;
     }
+    return check_launch();
+}
+
+// the grouped gate/up pair on 64-chunk packed weights (four lane groups a row)
+int launch_pair_p64(MmvqParams& p, const Shape& s, int64_t grid, hipStream_t stream) {
+    p.nsteps = s.nsteps;
+    if (grid <= 0) return MOEQ8_OK;
+    if (grid > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    constexpr int U = u_for(2, false, false);
+    hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), dim3((uint32_t)grid),
+                       dim3(64 * WAVES_PER_WG), 0, stream, p);
     return check_launch();
 }
 
@@ -633,9 +651,12 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
                  int64_t s_k_block_offset, const void* s_act,
                  int64_t s_act_row_stride, float* s_out, void* stream) {
     const int64_t bb = q4 ? Q4_BYTES : Q80_BYTES;
-    if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_DOWN_F32_ACT)
+    if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_DOWN_F32_ACT &&
+        stage != MOEQ8_GATE_UP_SWIGLU_P64)
         return MOEQ8_EINVAL;
-    const bool pair = stage == MOEQ8_GATE_UP_SWIGLU;
+    const bool p64 = stage == MOEQ8_GATE_UP_SWIGLU_P64;
+    if (p64 && q4) return MOEQ8_EINVAL;
+    const bool pair = stage == MOEQ8_GATE_UP_SWIGLU || p64;
     const bool f32 = stage == MOEQ8_DOWN_F32_ACT;
     int st = validate_matrix(w_a, w_row_stride_bytes, n, k, 0, bb);
     if (st) return st;
@@ -669,6 +690,16 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
         if ((uintptr_t)s_act & 3u) return MOEQ8_EALIGN;
         const Shape a = pick_shape(0, k / 64), b = pick_shape(s_k_block_offset / 2, k / 64);
         if (a.G != b.G || a.nsteps != b.nsteps) return MOEQ8_EUNSUPPORTED;
+    }
+    if (p64) {
+        // one 64-chunk segment a row, 16-byte aligned segments
+        if (k != P64_CHUNKS * 2 * QK) return MOEQ8_EUNSUPPORTED;
+        if (((uintptr_t)w_a | (uintptr_t)w_b | (uint64_t)w_row_stride_bytes | (uint64_t)expert_stride_bytes) & 15u)
+            return MOEQ8_EALIGN;
+        if (has_s) {
+            if (s_k_block_offset % (P64_CHUNKS * 2) != 0) return MOEQ8_EALIGN;
+            if (((uintptr_t)s_a | (uintptr_t)s_b | (uint64_t)s_row_stride_bytes) & 15u) return MOEQ8_EALIGN;
+        }
     }
     if (n == 0 && (!has_s || s_n == 0)) return MOEQ8_OK;
 
@@ -720,6 +751,7 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
         if (f32) return launch_mmvq<1, true, true, true>(p, s, grid, lds, hs);
         return launch_mmvq<1, true, false, true>(p, s, grid, 0, hs);
     }
+    if (p64) return launch_pair_p64(p, s, grid, hs);
     if (pair) return launch_mmvq<2, true, false, false>(p, s, grid, 0, hs);
     if (f32) return launch_mmvq<1, true, true, false>(p, s, grid, lds, hs);
     return launch_mmvq<1, true, false, false>(p, s, grid, 0, hs);

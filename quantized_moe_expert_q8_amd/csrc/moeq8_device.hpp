@@ -140,6 +140,39 @@ __device__ __forceinline__ void load_x_chunk_lds(XChunk& x, const uint8_t* p) {
     }
 }
 
+// The 64-chunk packed layout (P64) of Q8_0 rows whose length is a multiple
+// of 4096 values: each 4352-byte segment of 64 chunks (two blocks each) is
+// stored with dword d < 16 of chunk c at dword 256 * (d / 4) + 4 * c + d % 4
+// and dword 16 of chunk c at dword 1024 + c.  Lane c of a wave that reads the
+// segment's chunk c then fetches its 68 bytes as four 16-byte loads at
+// 1024-byte steps and one 4-byte load, each load of the wave reading one
+// contiguous span (every cache line consumed by one instruction), and holds
+// the same 17 dwords as with the plain layout.
+typedef uint32_t u32x4a16 __attribute__((ext_vector_type(4), aligned(16)));
+constexpr int P64_CHUNKS = 64;
+constexpr int P64_SEGMENT_BYTES = P64_CHUNKS * W_CHUNK_BYTES;      // 4352
+constexpr int P64_SEGMENT_DWORDS = P64_SEGMENT_BYTES / 4;          // 1088
+
+// Chunk c of a packed segment (16-byte aligned), with nontemporal loads: the
+// weights are read once.
+__device__ __forceinline__ void load_w_chunk_p64(WChunk& w, const uint8_t* seg, int c) {
+    const u32x4a16* q = reinterpret_cast<const u32x4a16*>(seg) + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4a16 t = __builtin_nontemporal_load(q + 64 * i);
+        w.v[4 * i + 0] = t.x;
+        w.v[4 * i + 1] = t.y;
+        w.v[4 * i + 2] = t.z;
+        w.v[4 * i + 3] = t.w;
+    }
+    w.v[16] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(seg + 4096) + c);
+}
+
+// Source dword (index 17 c + d of the plain segment) of packed dword p.
+__host__ __device__ constexpr int p64_source_dword(int p) {
+    return p < 1024 ? 17 * ((p & 255) >> 2) + 4 * (p >> 8) + (p & 3) : 17 * (p - 1024) + 16;
+}
+
 __device__ __forceinline__ void zero_w_chunk(WChunk& w) {
 #pragma unroll
     for (int i = 0; i < W_CHUNK_DWORDS; ++i) w.v[i] = 0u;

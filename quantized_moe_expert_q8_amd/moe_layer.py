@@ -36,7 +36,9 @@ class RoutedExperts:
     """Local experts of one layer, each [rows][k/32] blocks, experts
     ``expert_stride`` bytes apart (views into larger tensors are fine).
     fmt: "q8_0" (34-byte blocks) or "q4" (18-byte 4-bit blocks, for
-    bandwidth-only expert weights)."""
+    bandwidth-only expert weights).  packed: gate and up are in the 64-chunk
+    packed layout (ops.q8_0_pack64_rows; hidden 4096), read by the fused
+    path's gate/up launch."""
     gate: torch.Tensor       # uint8, n_local x inter x hidden/32 blocks
     up: torch.Tensor
     down: torch.Tensor       # uint8, n_local x hidden x inter/32 blocks
@@ -44,6 +46,7 @@ class RoutedExperts:
     hidden: int
     inter: int
     fmt: str = "q8_0"
+    packed: bool = False
 
 
 @dataclass
@@ -58,6 +61,7 @@ class SharedExpertShare:
     inter_full: int
     row0: int
     rows: int
+    packed: bool = False     # gate and up in the 64-chunk packed layout
 
     def gate_offset(self) -> int:
         return self.row0 * (self.hidden // QK) * Q80
@@ -123,6 +127,11 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     Both give the same bits.  ``hook(name, phase)`` (unfused only) is called
     around each launch."""
     add = add_shared and shared is not None
+    if experts.packed or (shared is not None and shared.packed):
+        if not fused or experts.fmt != "q8_0":
+            raise ValueError("packed gate/up weights run on the fused Q8_0 path")
+        if shared is not None and shared.packed != experts.packed:
+            raise ValueError("routed and shared gate/up weights must share one layout")
     if experts.fmt == "q4":
         return _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add)
     if experts.fmt != "q8_0":
@@ -216,7 +225,8 @@ def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared,
             sh_dn = {"a": shared.down, "row_stride": (shared.inter_full // QK) * Q80,
                      "n": hidden, "k": shared.rows, "k_block_offset": kb,
                      "offset_bytes": kb * Q80, "out": ws.ys, "act": ws.hs}
-    ops.moe_grouped_mmvq_ex(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping,
+    gate_up = ops.GATE_UP_SWIGLU_P64 if experts.packed else ops.GATE_UP_SWIGLU
+    ops.moe_grouped_mmvq_ex(gate_up, experts.gate, experts.up, ws.xq, ws.grouping,
                             n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
                             out=ws.h, shared=sh_gu)
     ops.moe_grouped_mmvq_ex(ops.DOWN_F32_ACT, experts.down, None, ws.h.view(R, inter), ws.grouping,
@@ -314,6 +324,25 @@ def _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws
                       out=ws.ys)
     ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out, shared=ws.ys if add else None)
     return ws.out, ws.ys
+
+
+def pack_gate_up(experts: RoutedExperts, shared: SharedExpertShare | None = None):
+    """Copies of the gate and up matrices in the 64-chunk packed layout
+    (allocated here; down stays as it is).  Returns (experts, shared)."""
+    if experts.fmt != "q8_0" or experts.packed:
+        raise ValueError("pack_gate_up takes plain Q8_0 experts")
+    rows = experts.n_local * experts.inter
+    pe = RoutedExperts(ops.q8_0_pack64_rows(experts.gate, rows, experts.hidden),
+                       ops.q8_0_pack64_rows(experts.up, rows, experts.hidden), experts.down,
+                       experts.n_local, experts.hidden, experts.inter, packed=True)
+    ps = None
+    if shared is not None:
+        rb = shared.hidden // QK * Q80
+        g = ops.q8_0_pack64_rows(shared.gate, shared.inter_full, shared.hidden).view(shared.inter_full, rb)
+        u = ops.q8_0_pack64_rows(shared.up, shared.inter_full, shared.hidden).view(shared.inter_full, rb)
+        ps = SharedExpertShare(g, u, shared.down, shared.hidden, shared.inter_full, shared.row0, shared.rows,
+                               packed=True)
+    return pe, ps
 
 
 def expert_bytes_q4(hidden: int, inter: int) -> int:

@@ -23,6 +23,8 @@ MAX_COLS = 8
 GATE_UP_SWIGLU = 0
 DOWN = 1
 DOWN_F32_ACT = 2
+GATE_UP_SWIGLU_P64 = 3      # gate/up on weights repacked by q8_0_pack64_rows
+P64_K = 4096                # values in one packed segment
 
 
 def _stream(t: torch.Tensor):
@@ -85,6 +87,24 @@ def q8_0_quantize_rows(w: torch.Tensor, out: torch.Tensor | None = None) -> torc
     _cuda(out, "out", torch.uint8)
     _need(out, "out", rows * (k // QK) * Q8_0_BLOCK_BYTES)
     call("q8_0_quantize_rows", _ptr(w), rows, k, w.stride(0), _ptr(out), _stream(w))
+    return out
+
+
+def q8_0_pack64_rows(src: torch.Tensor, rows: int, k: int, out: torch.Tensor | None = None,
+                     src_row_stride_bytes: int | None = None,
+                     out_row_stride_bytes: int | None = None) -> torch.Tensor:
+    """Q8_0 rows (uint8, rows of k/32*34 bytes) -> the same rows in the 64-chunk
+    packed layout that GATE_UP_SWIGLU_P64 reads; k a multiple of 4096."""
+    row_bytes = k // QK * Q8_0_BLOCK_BYTES
+    ss = row_bytes if src_row_stride_bytes is None else src_row_stride_bytes
+    ds = row_bytes if out_row_stride_bytes is None else out_row_stride_bytes
+    _cuda(src, "src", torch.uint8)
+    _need(src, "src", _weight_extent(rows, k, ss))
+    if out is None:
+        out = torch.empty(rows * ds, dtype=torch.uint8, device=src.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", _weight_extent(rows, k, ds))
+    call("q8_0_pack64_rows", _ptr(src), rows, k, ss, _ptr(out), ds, _stream(src))
     return out
 
 
@@ -508,7 +528,7 @@ def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
     _cuda(w_a, "w_a", torch.uint8)
     _need(w_a, "w_a", extent)
     act_row_stride = 0
-    if stage == GATE_UP_SWIGLU:
+    if stage in (GATE_UP_SWIGLU, GATE_UP_SWIGLU_P64):
         _cuda(w_b, "w_b", torch.uint8)
         _need(w_b, "w_b", extent)
         _act_rows(act, "act", ncols, k)
@@ -535,7 +555,7 @@ def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
         sa, sout = shared["a"], shared["out"]
         _cuda(sa, "shared a", torch.uint8)
         _need(sa, "shared a", _weight_extent(s_n, s_k, s_stride), s_off)
-        if stage == GATE_UP_SWIGLU:
+        if stage in (GATE_UP_SWIGLU, GATE_UP_SWIGLU_P64):
             sb = shared["b"]
             _cuda(sb, "shared b", torch.uint8)
             _need(sb, "shared b", _weight_extent(s_n, s_k, s_stride), s_off)

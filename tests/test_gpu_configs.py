@@ -249,6 +249,7 @@ def test_ep_share_l43_e128_c8():
     share = cfg["shared_inter"] // cfg["shared_share"]
     say("config ep_share_l43_e128_c8: allocating the 43-layer share")
     bank = bench.Bank(moeq8, torch, L, n_local, H, I, seed, cfg["shared_inter"])
+    bank.pack_gate_up(moeq8, torch)         # the launch configuration the bench times
     xs, lgs, bs = bench.layer_inputs(torch, workloads, seed, L, c, H, E)
     owner_np = workloads.owner_slots(E, n_local)
     owner = to_dev(owner_np)
@@ -344,7 +345,13 @@ def test_ep_share_l43_e128_c8():
                                       w_row_stride_bytes=cfg["shared_inter"] // 32 * 34)
             ys_full = moeq8.mmvq_q8_0(shared[l].down, full_pad, H, cfg["shared_inter"])
             assert bits_equal(ys_half, ys_full)
-        hs_full = moeq8.mmvq_q8_0_glu_pair(shared[l].gate, shared[l].up, w.xq, cfg["shared_inter"], H)
+        # (the bank's gate/up are packed; the dense pair reads the plain rows,
+        # drawn again from the same generator)
+        rb_h = H // 32 * 34
+        plain = [torch.empty(cfg["shared_inter"] * rb_h, dtype=torch.uint8, device=DEV) for _ in range(2)]
+        for t, m in zip(plain, (3, 4)):
+            moeq8.synth_q8_0_fill(t, 1, cfg["shared_inter"] * H // 32, 1, seed, l, 0, m)
+        hs_full = moeq8.mmvq_q8_0_glu_pair(plain[0], plain[1], w.xq, cfg["shared_inter"], H)
         assert bits_equal(hs_full[:, :share].contiguous(), w.hs)
     del g, bank
     torch.cuda.empty_cache()

@@ -618,6 +618,142 @@ def test_fused_layer_all_routes_masked():
 
 
 # ---------------------------------------------------------------------------
+# the 64-chunk packed layout of the gate/up weights
+# ---------------------------------------------------------------------------
+
+def _p64_reference(raw: np.ndarray, rows: int, k: int) -> np.ndarray:
+    """The packed layout restated on the host: within each 4352-byte segment of
+    a row, dword 17c + d moves to 256*(d//4) + 4c + d%4 (d < 16) and dword
+    17c + 16 to 1024 + c."""
+    w = np.ascontiguousarray(raw).reshape(-1).view(np.uint32).reshape(rows, k // 4096, 1088)
+    out = np.empty_like(w)
+    c = np.arange(64)
+    for d in range(16):
+        out[:, :, 256 * (d // 4) + 4 * c + d % 4] = w[:, :, 17 * c + d]
+    out[:, :, 1024 + c] = w[:, :, 17 * c + 16]
+    return out.reshape(-1).view(np.uint8)
+
+
+@pytest.mark.parametrize("rows,k", [(1, 4096), (3, 8192), (64, 4096)])
+def test_pack64_layout(rows, k):
+    raw = np.random.default_rng(rows + k).integers(0, 256, size=rows * (k // 32) * 34, dtype=np.uint8)
+    got = host(moeq8.q8_0_pack64_rows(to_dev(raw), rows, k))
+    assert np.array_equal(got, _p64_reference(raw, rows, k))
+    # and every byte is kept: the packing only permutes within a segment
+    assert np.array_equal(np.sort(got.reshape(rows, -1), axis=1), np.sort(raw.reshape(rows, -1), axis=1))
+
+
+def _synth_dev(seed, n_mats, rows, k, matrix, layer=0):
+    t = torch.empty(n_mats * rows * (k // 32) * 34, dtype=torch.uint8, device=DEV)
+    moeq8.synth_q8_0_fill(t, n_mats, rows * k // 32, n_mats, seed, layer, 0, matrix)
+    return t
+
+
+@pytest.mark.parametrize("c,n_exp,local,inter,share_rows,half", [(1, 32, 32, 256, 0, 0),
+                                                                 (5, 64, 32, 512, 256, 1),
+                                                                 (8, 32, 16, 1024, 512, 0),
+                                                                 (3, 16, 16, 72, 40, 1)])
+def test_grouped_gate_up_p64_equals_plain(c, n_exp, local, inter, share_rows, half):
+    """GATE_UP_SWIGLU_P64 on packed copies against GATE_UP_SWIGLU on the plain
+    weights, every written h and hs row bit for bit (owner mask, ragged row
+    counts, the shared rows at either half)."""
+    say(f"p64 gate/up c={c} E={n_exp} local={local} inter={inter} share={share_rows} half={half}")
+    H, topk, seed = 4096, 8, 60 + c
+    wg, wu = _synth_dev(seed, local, inter, H, 0), _synth_dev(seed, local, inter, H, 1)
+    pg = moeq8.q8_0_pack64_rows(wg, local * inter, H)
+    pu = moeq8.q8_0_pack64_rows(wu, local * inter, H)
+    x = to_dev(workloads.activations(seed, c, H))
+    xq = moeq8.q8_1_quantize_rows(x)
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    ids, w, grouping = moeq8.moe_route_topk(lg, topk, bias=to_dev(workloads.router_bias(seed, n_exp)),
+                                            owner_slot=to_dev(workloads.owner_slots(n_exp, local)),
+                                            n_local_expert=local)
+    rb = H // 32 * 34
+    outs = []
+    for stage, a, b in ((moeq8.GATE_UP_SWIGLU, wg, wu), (moeq8.GATE_UP_SWIGLU_P64, pg, pu)):
+        h = torch.full((c, topk, inter), float("nan"), device=DEV)
+        sh = None
+        hs = None
+        if share_rows:
+            full = 2 * share_rows
+            sgp, sup = _synth_dev(seed, 1, full, H, 3), _synth_dev(seed, 1, full, H, 4)
+            if stage == moeq8.GATE_UP_SWIGLU_P64:
+                sgp, sup = moeq8.q8_0_pack64_rows(sgp, full, H), moeq8.q8_0_pack64_rows(sup, full, H)
+            hs = torch.full((c, share_rows), float("nan"), device=DEV)
+            sh = {"a": sgp, "b": sup, "row_stride": rb, "n": share_rows, "k": H, "k_block_offset": 0,
+                  "offset_bytes": half * share_rows * rb, "out": hs}
+        moeq8.moe_grouped_mmvq_ex(stage, a, b, xq, grouping, n=inter, k=H, n_local_expert=local, ncols=c,
+                                  topk=topk, out=h, shared=sh)
+        outs.append((h, hs))
+    torch.cuda.synchronize()
+    valid = host(ids) >= 0
+    h0, h1 = host(outs[0][0]), host(outs[1][0])
+    for j in range(c):
+        for s in range(topk):
+            if valid[j, s]:
+                assert np.array_equal(h0[j, s].view(np.int32), h1[j, s].view(np.int32)), (j, s)
+            else:
+                assert np.isnan(h1[j, s]).all()          # masked rows untouched
+    if share_rows:
+        assert bits_equal(outs[0][1], outs[1][1])
+
+
+def test_p64_rejects_what_it_cannot_read():
+    """Host checks of the packed stage: K other than 4096, a weight pointer or
+    a shared slice off the 16-byte / segment grid."""
+    c, topk, local, inter = 2, 4, 8, 64
+    lg = to_dev(workloads.router_logits(9, c, local))
+    ids, w, grouping = moeq8.moe_route_topk(lg, topk)
+    h = torch.zeros((c, topk, inter), device=DEV)
+    for H, off, status in ((2048, 0, -3), (4096, 4, -2)):
+        wt = torch.zeros(local * inter * (H // 32) * 34 + 64, dtype=torch.uint8, device=DEV)
+        xq = torch.zeros((c, H // 32 * 36), dtype=torch.uint8, device=DEV)
+        a = wt[off:]
+        with pytest.raises(moeq8.MoeQ8Error) as ei:
+            moeq8.moe_grouped_mmvq_ex(moeq8.GATE_UP_SWIGLU_P64, a, a, xq, grouping, n=inter, k=H,
+                                      n_local_expert=local, ncols=c, topk=topk, out=h)
+        assert ei.value.status == status
+
+
+@pytest.mark.parametrize("c,n_exp", [(1, 16), (5, 32), (8, 32)])
+def test_fused_layer_packed_equals_unfused(c, n_exp):
+    """The four-launch layer with packed gate/up (routed and shared) against the
+    nine separate calls on the plain weights: every output bit for bit."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    say(f"packed fused layer c={c} E={n_exp}")
+    H, I, topk, share_rows = 4096, 256, 8, 256
+    seed = 80 + c
+    wg, wu, wd = _synth_dev(seed, n_exp, I, H, 0), _synth_dev(seed, n_exp, I, H, 1), _synth_dev(seed, n_exp, H, I, 2)
+    full = 2 * share_rows
+    rb_h, rb_f = H // 32 * 34, full // 32 * 34
+    sg = _synth_dev(seed, 1, full, H, 3).view(full, rb_h)
+    su = _synth_dev(seed, 1, full, H, 4).view(full, rb_h)
+    sd = _synth_dev(seed, 1, H, full, 5).view(H, rb_f)
+    experts = ml.RoutedExperts(wg, wu, wd, n_exp, H, I)
+    shared = ml.SharedExpertShare(sg, su, sd, H, full, share_rows, share_rows)
+    pe, ps = ml.pack_gate_up(experts, shared)
+    x = to_dev(workloads.activations(seed, c, H))
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    b = to_dev(workloads.router_bias(seed, n_exp))
+    own = to_dev(workloads.owner_slots(n_exp, n_exp // 2))
+    for add in (False, True):
+        wa = ml.Workspace(c, H, I, topk, share_rows, DEV)
+        wb = ml.Workspace(c, H, I, topk, share_rows, DEV)
+        ml.forward(x, lg, b, own, n_exp // 2, experts, shared, wa, fused=False, add_shared=add)
+        ml.forward(x, lg, b, own, n_exp // 2, pe, ps, wb, fused=True, add_shared=add)
+        torch.cuda.synchronize()
+        assert bits_equal(wa.out, wb.out) and bits_equal(wa.ys, wb.ys) and bits_equal(wa.hs, wb.hs)
+        valid = host(wa.ids) >= 0
+        ha, hb = host(wa.h), host(wb.h)
+        for j in range(c):
+            for s in range(topk):
+                if valid[j, s]:
+                    assert np.array_equal(ha[j, s].view(np.int32), hb[j, s].view(np.int32))
+    with pytest.raises(ValueError):
+        ml.forward(x, lg, b, own, n_exp // 2, pe, ps, wb, fused=False)
+
+
+# ---------------------------------------------------------------------------
 # benchmark helper: the streaming-read ceiling reads every word once
 # ---------------------------------------------------------------------------
 
