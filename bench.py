@@ -99,18 +99,21 @@ class Bank:
 
     packed = False
 
-    def pack_gate_up(self, moeq8, torch):
-        """Repack every layer's routed (and shared) gate and up matrices into the
-        64-chunk packed layout the fused gate/up launch reads, in place through
-        one layer-sized buffer."""
-        for banks, rows in (((self.gate, self.up), self.n_local * self.inter),
-                            ((getattr(self, "sgate", None), getattr(self, "sup", None)), self.shared_inter)):
-            if not rows or banks[0] is None:
-                continue
+    def pack_weights(self, moeq8, torch):
+        """Repack every layer's weights into the packed layouts the fused
+        launches read, in place through one layer-sized buffer: routed (and
+        shared) gate and up in the 64-chunk layout, down in the round-major
+        four-row one."""
+        jobs = [((self.gate, self.up), moeq8.q8_0_pack64_rows, self.n_local * self.inter, self.hidden),
+                ((self.down,), moeq8.q8_0_pack64_rounds, self.n_local * self.hidden, self.inter)]
+        if self.shared_inter:
+            jobs += [((self.sgate, self.sup), moeq8.q8_0_pack64_rows, self.shared_inter, self.hidden),
+                     ((self.sdown,), moeq8.q8_0_pack64_rounds, self.hidden, self.shared_inter)]
+        for banks, pack, rows, k in jobs:
             tmp = torch.empty_like(banks[0][0])
             for bank in banks:
                 for l in range(self.layers):
-                    moeq8.q8_0_pack64_rows(bank[l], rows, self.hidden, out=tmp)
+                    pack(bank[l], rows, k, out=tmp)
                     bank[l].copy_(tmp)
             del tmp
         self.packed = True
@@ -309,7 +312,7 @@ def main():
 
     t0 = time.perf_counter()
     bank = Bank(moeq8, torch, L, n_local, hidden, inter, seed, cfg["shared_inter"])
-    bank.pack_gate_up(moeq8, torch)
+    bank.pack_weights(moeq8, torch)
     xs, lgs, bs = layer_inputs(torch, workloads, seed, L, cols, hidden, n_exp)
     owner = torch.from_numpy(workloads.owner_slots(n_exp, n_local)).cuda()
     side = torch.cuda.Stream()
@@ -399,10 +402,11 @@ def main():
             w, sh = wss[l], shared[l]
             kb = sh.down_block_offset()
             moeq8.moe_grouped_mmvq_ex(
-                moeq8.DOWN_F32_ACT, experts[l].down, None, w.h.view(cols * topk, inter), w.grouping,
+                moeq8.DOWN_F32_ACT_P64, experts[l].down, None, w.h.view(cols * topk, inter), w.grouping,
                 n=hidden, k=inter, n_local_expert=n_local, ncols=cols, topk=topk, out=w.y,
-                shared={"a": sh.down, "row_stride": sh.inter_full // 32 * 34, "n": hidden,
-                        "k": sh.rows, "k_block_offset": kb, "offset_bytes": kb * 34,
+                shared={"a": sh.down, "row_stride": moeq8.ops.ROUND_BYTES, "n": hidden,
+                        "k": sh.rows, "k_block_offset": 0,
+                        "offset_bytes": kb // 32 * hidden * moeq8.ops.ROUND_BYTES,
                         "out": w.ys, "act": w.hs})
 
     gu_us = time_graph(torch, gate_up_only, args.steps) / L * 1e3
@@ -514,7 +518,7 @@ def sweep(torch, workloads, moeq8, ml, args):
     hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
     reps = 4
     bank = Bank(moeq8, torch, reps, n_exp, hidden, inter, 4)
-    bank.pack_gate_up(moeq8, torch)
+    bank.pack_weights(moeq8, torch)
     sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
     out = []
     for cols in (1, 2, 4, 5, 8):

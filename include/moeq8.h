@@ -110,6 +110,17 @@ int q8_0_quantize_rows(const float* w, int64_t n_rows, int64_t k, int64_t w_row_
 int q8_0_pack64_rows(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes,
                      void* dst, int64_t dst_row_stride_bytes, void* stream);
 
+/* The round-major four-row packed layout read by MOEQ8_DOWN_F32_ACT_P64: round
+ * r (values [1024 r, 1024 r + 1024), 1088 bytes) of every row goes to the
+ * matrix dst + r * n_rows * 1088, whose rows are contiguous; there each quad of
+ * rows 4q .. 4q+3 (4352 bytes) is permuted as one q8_0_pack64_rows segment,
+ * chunk 16g + l of the segment being chunk l of row 4q + g.  A column-range
+ * slice at a multiple of 32 blocks is then the matrix of its round.  n_rows a
+ * multiple of 4, k a multiple of 1024; dst holds n_rows * k/32 * 34 bytes and
+ * must not overlap src.  Otherwise as q8_0_pack64_rows. */
+int q8_0_pack64_rounds(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes, void* dst,
+                       void* stream);
+
 /* ---------------------------------------------------------------------------
  * a3 (+a10): single Q8_0 x q8_1 product, y[c][i] = sum over the k/32 blocks b of
  * row i of d_w * d_x * sum(qw * qx).
@@ -196,7 +207,7 @@ int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_
  * expert and that route's activation row.
  * ------------------------------------------------------------------------- */
 enum moeq8_stage { MOEQ8_GATE_UP_SWIGLU = 0, MOEQ8_DOWN = 1, MOEQ8_DOWN_F32_ACT = 2,
-                   MOEQ8_GATE_UP_SWIGLU_P64 = 3 };
+                   MOEQ8_GATE_UP_SWIGLU_P64 = 3, MOEQ8_DOWN_F32_ACT_P64 = 4 };
 int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
                      int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
                      int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
@@ -230,6 +241,16 @@ int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
  *     weight pointers, row strides and expert stride else MOEQ8_EALIGN.
  *     Every output is bit-identical to MOEQ8_GATE_UP_SWIGLU on the unpacked
  *     weights.
+ *   - stage MOEQ8_DOWN_F32_ACT_P64: MOEQ8_DOWN_F32_ACT on weights repacked by
+ *     q8_0_pack64_rounds (the routed experts and the dense part alike): k must
+ *     be 1024 with rows of 1088 bytes (w_row_stride_bytes and
+ *     s_row_stride_bytes 1088), n and s_n multiples of 4, else
+ *     MOEQ8_EUNSUPPORTED; 16-byte aligned pointers and expert stride else
+ *     MOEQ8_EALIGN.  The dense part is the round's matrix (s_a at round r of
+ *     the packed shared matrix, s_k_block_offset 0): its products equal those
+ *     of the column-range slice at block 32 r of the plain matrix, since a
+ *     one-round slice's lane sums do not depend on its round.  Every output is
+ *     bit-identical to MOEQ8_DOWN_F32_ACT on the unpacked weights.
  * act_row_stride is ignored for the q8_1 stages.
  * ------------------------------------------------------------------------- */
 int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,

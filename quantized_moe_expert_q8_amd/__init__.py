@@ -11,12 +11,14 @@ from .ops import (  # noqa: F401
     DOWN,
     DOWN_F32_ACT,
     GATE_UP_SWIGLU_P64,
+    DOWN_F32_ACT_P64,
     P64_K,
     Q8_0_BLOCK_BYTES,
     Q8_1_BLOCK_BYTES,
     q8_1_quantize_rows,
     q8_0_quantize_rows,
     q8_0_pack64_rows,
+    q8_0_pack64_rounds,
     mmvq_q8_0,
     mmvq_q8_0_glu_pair,
     swiglu_ds4,

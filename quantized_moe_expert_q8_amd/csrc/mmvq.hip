@@ -101,12 +101,17 @@ __device__ __forceinline__ float chain_groups(float v, int lane) {
     }
 }
 
-// P64: the weights are in the 64-chunk packed layout (moeq8_device.hpp); the
-// launch reads one 64-chunk segment a row (K = 4096 at a segment boundary),
-// so with four lane groups a row (G = 4) lane L holds chunk L of the segment.
+// P64: the weights are in a 64-chunk packed layout (moeq8_device.hpp).  With
+// four lane groups a row (G = 4) the launch reads one 64-chunk segment a row
+// (K = 4096 at a segment boundary) and lane L holds chunk L of it.  With one
+// lane group a row (G = 1, the down launch with fp32 activations, K = 1024
+// contiguous rows of 1088 bytes) a row set is a quad of rows, 4352 contiguous
+// bytes packed as one segment whose chunk L (chunk L % 16 of row L / 16) is
+// again lane L's.
 template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false>
 __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
-    static_assert(!P64 || (G == 4 && !Q4 && !ACT_F32 && !STX), "the packed layout serves the q8_1 four-group rows");
+    static_assert(!P64 || (!Q4 && !STX && ((G == 4 && !ACT_F32) || (G == 1 && NMAT == 1 && ACT_F32))),
+                  "the packed layouts serve the four-group gate/up rows and the one-group down quads");
     // weight chunk: two Q8_0 blocks (68 B) or two 4-bit blocks (36 B); the
     // chunk's value has the same form either way, so the reduction order and
     // every launch shape are shared
@@ -233,7 +238,13 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                 const int64_t off = ok[u] ? row * row_stride + (int64_t)crel * WCB : 0;
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
-                    if constexpr (P64) {
+                    if constexpr (P64 && G == 1) {
+                        // the quad of this row set (n % 4 == 0: a quad is inside
+                        // the matrix or wholly past it, and then reads the first
+                        // quad and adds +0, as every unconditional load does)
+                        const int64_t quad = ok[u] ? row - rslot : 0;
+                        load_w_chunk_p64(wc[u][m], w0 + quad * row_stride, lane);
+                    } else if constexpr (P64) {
                         if (ok[u]) load_w_chunk_p64(wc[u][m], (m == 0 ? w0 : w1) + row * row_stride, crel);
                         else zero_w_chunk(wc[u][m]);
                     } else if (UNCOND || ok[u]) {
@@ -519,14 +530,22 @@ int launch_shape(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, 
     return check_launch();
 }
 
-// the grouped gate/up pair on 64-chunk packed weights (four lane groups a row)
-int launch_pair_p64(MmvqParams& p, const Shape& s, int64_t grid, hipStream_t stream) {
+// the grouped gate/up pair on 64-chunk packed weights (four lane groups a
+// row), and the grouped down with fp32 activations on quad-packed weights (one
+// lane group a row)
+int launch_p64(bool down, MmvqParams& p, const Shape& s, int64_t grid, size_t lds, hipStream_t stream) {
     p.nsteps = s.nsteps;
     if (grid <= 0) return MOEQ8_OK;
     if (grid > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
-    constexpr int U = u_for(2, false, false);
-    hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), dim3((uint32_t)grid),
-                       dim3(64 * WAVES_PER_WG), 0, stream, p);
+    if (down) {
+        constexpr int U = u_for(1, true, false);
+        hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true>), dim3((uint32_t)grid),
+                           dim3(64 * WAVES_PER_WG), lds, stream, p);
+    } else {
+        constexpr int U = u_for(2, false, false);
+        hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), dim3((uint32_t)grid),
+                           dim3(64 * WAVES_PER_WG), 0, stream, p);
+    }
     return check_launch();
 }
 
@@ -652,12 +671,13 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
                  int64_t s_act_row_stride, float* s_out, void* stream) {
     const int64_t bb = q4 ? Q4_BYTES : Q80_BYTES;
     if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_DOWN_F32_ACT &&
-        stage != MOEQ8_GATE_UP_SWIGLU_P64)
+        stage != MOEQ8_GATE_UP_SWIGLU_P64 && stage != MOEQ8_DOWN_F32_ACT_P64)
         return MOEQ8_EINVAL;
     const bool p64 = stage == MOEQ8_GATE_UP_SWIGLU_P64;
-    if (p64 && q4) return MOEQ8_EINVAL;
+    const bool p64d = stage == MOEQ8_DOWN_F32_ACT_P64;
+    if ((p64 || p64d) && q4) return MOEQ8_EINVAL;
     const bool pair = stage == MOEQ8_GATE_UP_SWIGLU || p64;
-    const bool f32 = stage == MOEQ8_DOWN_F32_ACT;
+    const bool f32 = stage == MOEQ8_DOWN_F32_ACT || p64d;
     int st = validate_matrix(w_a, w_row_stride_bytes, n, k, 0, bb);
     if (st) return st;
     if (pair) {
@@ -700,6 +720,15 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
             if (s_k_block_offset % (P64_CHUNKS * 2) != 0) return MOEQ8_EALIGN;
             if (((uintptr_t)s_a | (uintptr_t)s_b | (uint64_t)s_row_stride_bytes) & 15u) return MOEQ8_EALIGN;
         }
+    }
+    if (p64d) {
+        // contiguous rows of one 16-chunk round (a quad is one 4352-byte
+        // packed unit), 16-byte aligned
+        constexpr int64_t ROUND_BYTES = P64_SEGMENT_BYTES / 4;        // 1088
+        if (k != LANES_PER_ROW * 2 * QK || n % 4 != 0 || (has_s && s_n % 4 != 0)) return MOEQ8_EUNSUPPORTED;
+        if (w_row_stride_bytes != ROUND_BYTES || (has_s && (s_row_stride_bytes != ROUND_BYTES || s_k_block_offset != 0)))
+            return MOEQ8_EUNSUPPORTED;
+        if (((uintptr_t)w_a | (uint64_t)expert_stride_bytes | (uintptr_t)s_a) & 15u) return MOEQ8_EALIGN;
     }
     if (n == 0 && (!has_s || s_n == 0)) return MOEQ8_OK;
 
@@ -751,7 +780,7 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
         if (f32) return launch_mmvq<1, true, true, true>(p, s, grid, lds, hs);
         return launch_mmvq<1, true, false, true>(p, s, grid, 0, hs);
     }
-    if (p64) return launch_pair_p64(p, s, grid, hs);
+    if (p64 || p64d) return launch_p64(p64d, p, s, grid, lds, hs);
     if (pair) return launch_mmvq<2, true, false, false>(p, s, grid, 0, hs);
     if (f32) return launch_mmvq<1, true, true, false>(p, s, grid, lds, hs);
     return launch_mmvq<1, true, false, false>(p, s, grid, 0, hs);

@@ -113,3 +113,47 @@ extern "C" int q8_0_pack64_rows(const void* src, int64_t n_rows, int64_t k, int6
                        (uint32_t*)dst, dst_row_stride_bytes / 4);
     return check_launch();
 }
+
+// Repack Q8_0 rows into the round-major four-row packed layout
+// (moeq8_device.hpp): round r (16 chunks, 1088 bytes) of every row goes to
+// the matrix dst + r * n_rows * 1088 of contiguous 1088-byte rows, in which
+// rows 4q .. 4q + 3 form one 4352-byte unit permuted as a 64-chunk segment.
+// One thread per dword.
+namespace {
+__global__ void k_pack64_rounds(const uint32_t* __restrict__ src, int64_t n_rows, int64_t rounds,
+                                int64_t src_stride_dw, uint32_t* __restrict__ dst) {
+    using namespace moeq8;
+    constexpr int ROW_DW = P64_SEGMENT_DWORDS / 4;                     // 272
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_round = n_rows * ROW_DW;
+    if (t >= rounds * per_round) return;
+    const int64_t r = t / per_round;
+    const int64_t rem = t - r * per_round;                             // dword within round r's matrix
+    const int64_t q = rem / P64_SEGMENT_DWORDS;
+    const int p = (int)(rem - q * P64_SEGMENT_DWORDS);
+    const int sp = p64_source_dword(p);                                // unit dword it takes
+    dst[t] = src[(4 * q + sp / ROW_DW) * src_stride_dw + r * ROW_DW + sp % ROW_DW];
+}
+}  // namespace
+
+extern "C" int q8_0_pack64_rounds(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes,
+                                  void* dst, void* stream) {
+    using namespace moeq8;
+    constexpr int64_t ROUND_VALUES = LANES_PER_ROW * 2 * QK;          // 1024
+    if (!src || !dst || n_rows < 0 || n_rows % 4 != 0 || k <= 0 || k % ROUND_VALUES != 0) return MOEQ8_EINVAL;
+    const int64_t row_bytes = k / QK * Q80_BYTES;
+    if (src_row_stride_bytes < row_bytes) return MOEQ8_EINVAL;
+    if (((uintptr_t)src | (uintptr_t)dst | (uint64_t)src_row_stride_bytes) & 3u) return MOEQ8_EALIGN;
+    const uint8_t* s8 = (const uint8_t*)src;
+    const uint8_t* d8 = (const uint8_t*)dst;
+    const int64_t span_s = n_rows == 0 ? 0 : (n_rows - 1) * src_row_stride_bytes + row_bytes;
+    const int64_t span_d = n_rows * row_bytes;
+    if (s8 < d8 + span_d && d8 < s8 + span_s) return MOEQ8_EINVAL;     // no overlap (not in place)
+    const int64_t total = n_rows * (row_bytes / 4);
+    if (total == 0) return MOEQ8_OK;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_pack64_rounds, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint32_t*)src, n_rows, k / ROUND_VALUES, src_row_stride_bytes / 4, (uint32_t*)dst);
+    return check_launch();
+}

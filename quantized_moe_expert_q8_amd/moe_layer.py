@@ -37,8 +37,10 @@ class RoutedExperts:
     ``expert_stride`` bytes apart (views into larger tensors are fine).
     fmt: "q8_0" (34-byte blocks) or "q4" (18-byte 4-bit blocks, for
     bandwidth-only expert weights).  packed: gate and up are in the 64-chunk
-    packed layout (ops.q8_0_pack64_rows; hidden 4096), read by the fused
-    path's gate/up launch."""
+    packed layout (ops.q8_0_pack64_rows; hidden 4096) and down in the
+    round-major four-row packed layout (ops.q8_0_pack64_rounds; inter 1024),
+    read by the fused
+    path's gate/up and down launches (pack_experts makes them)."""
     gate: torch.Tensor       # uint8, n_local x inter x hidden/32 blocks
     up: torch.Tensor
     down: torch.Tensor       # uint8, n_local x hidden x inter/32 blocks
@@ -61,7 +63,7 @@ class SharedExpertShare:
     inter_full: int
     row0: int
     rows: int
-    packed: bool = False     # gate and up in the 64-chunk packed layout
+    packed: bool = False     # gate/up 64-chunk packed, down round-major four-row packed
 
     def gate_offset(self) -> int:
         return self.row0 * (self.hidden // QK) * Q80
@@ -129,9 +131,9 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     add = add_shared and shared is not None
     if experts.packed or (shared is not None and shared.packed):
         if not fused or experts.fmt != "q8_0":
-            raise ValueError("packed gate/up weights run on the fused Q8_0 path")
+            raise ValueError("packed weights run on the fused Q8_0 path")
         if shared is not None and shared.packed != experts.packed:
-            raise ValueError("routed and shared gate/up weights must share one layout")
+            raise ValueError("routed and shared weights must share one layout")
     if experts.fmt == "q4":
         return _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add)
     if experts.fmt != "q8_0":
@@ -221,7 +223,16 @@ def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared,
                  "k": hidden, "k_block_offset": 0, "offset_bytes": shared.gate_offset(),
                  "out": ws.hs}
         kb = shared.down_block_offset()
-        if _same_round_span(kb, shared.rows, inter):
+        if shared.packed:
+            # the round-major packed matrix of the share's round (a one-round
+            # slice's products do not depend on its round)
+            if shared.rows != ops.ROUND_BYTES // Q80 * QK or kb % (shared.rows // QK) != 0:
+                raise ValueError("a packed shared down share must be one whole 1024-value round")
+            rnd = kb // (shared.rows // QK)
+            sh_dn = {"a": shared.down, "row_stride": ops.ROUND_BYTES, "n": hidden, "k": shared.rows,
+                     "k_block_offset": 0, "offset_bytes": rnd * hidden * ops.ROUND_BYTES,
+                     "out": ws.ys, "act": ws.hs}
+        elif _same_round_span(kb, shared.rows, inter):
             sh_dn = {"a": shared.down, "row_stride": (shared.inter_full // QK) * Q80,
                      "n": hidden, "k": shared.rows, "k_block_offset": kb,
                      "offset_bytes": kb * Q80, "out": ws.ys, "act": ws.hs}
@@ -229,10 +240,13 @@ def _forward_fused(x, logits, bias, owner_slot, n_local_expert, experts, shared,
     ops.moe_grouped_mmvq_ex(gate_up, experts.gate, experts.up, ws.xq, ws.grouping,
                             n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
                             out=ws.h, shared=sh_gu)
-    ops.moe_grouped_mmvq_ex(ops.DOWN_F32_ACT, experts.down, None, ws.h.view(R, inter), ws.grouping,
+    down = ops.DOWN_F32_ACT_P64 if experts.packed else ops.DOWN_F32_ACT
+    ops.moe_grouped_mmvq_ex(down, experts.down, None, ws.h.view(R, inter), ws.grouping,
                             n=hidden, k=inter, n_local_expert=experts.n_local, ncols=c, topk=topk,
                             out=ws.y, shared=sh_dn)
     if shared is not None and sh_dn is None:
+        if shared.packed:
+            raise ValueError("a packed shared down must ride in the down launch (same slice shape)")
         kb = shared.down_block_offset()
         ops.q8_1_quantize_rows(ws.hs, out=ws.hsq)
         ops.mmvq_q8_0(shared.down, ws.hsq, hidden, shared.rows, ncols=c, k_block_offset=kb,
@@ -326,21 +340,26 @@ def _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws
     return ws.out, ws.ys
 
 
-def pack_gate_up(experts: RoutedExperts, shared: SharedExpertShare | None = None):
-    """Copies of the gate and up matrices in the 64-chunk packed layout
-    (allocated here; down stays as it is).  Returns (experts, shared)."""
+def pack_experts(experts: RoutedExperts, shared: SharedExpertShare | None = None):
+    """Copies of the weights in the packed layouts the fused launches read
+    (allocated here): gate and up in the 64-chunk layout, down in the
+    round-major four-row layout (the shared share's down slice is then the
+    matrix of its round).  Returns (experts, shared)."""
     if experts.fmt != "q8_0" or experts.packed:
-        raise ValueError("pack_gate_up takes plain Q8_0 experts")
+        raise ValueError("pack_experts takes plain Q8_0 experts")
     rows = experts.n_local * experts.inter
     pe = RoutedExperts(ops.q8_0_pack64_rows(experts.gate, rows, experts.hidden),
-                       ops.q8_0_pack64_rows(experts.up, rows, experts.hidden), experts.down,
+                       ops.q8_0_pack64_rows(experts.up, rows, experts.hidden),
+                       ops.q8_0_pack64_rounds(experts.down, experts.n_local * experts.hidden, experts.inter),
                        experts.n_local, experts.hidden, experts.inter, packed=True)
     ps = None
     if shared is not None:
         rb = shared.hidden // QK * Q80
+        rd = shared.inter_full // QK * Q80
         g = ops.q8_0_pack64_rows(shared.gate, shared.inter_full, shared.hidden).view(shared.inter_full, rb)
         u = ops.q8_0_pack64_rows(shared.up, shared.inter_full, shared.hidden).view(shared.inter_full, rb)
-        ps = SharedExpertShare(g, u, shared.down, shared.hidden, shared.inter_full, shared.row0, shared.rows,
+        d = ops.q8_0_pack64_rounds(shared.down, shared.hidden, shared.inter_full).view(shared.hidden, rd)
+        ps = SharedExpertShare(g, u, d, shared.hidden, shared.inter_full, shared.row0, shared.rows,
                                packed=True)
     return pe, ps
 

@@ -24,6 +24,8 @@ GATE_UP_SWIGLU = 0
 DOWN = 1
 DOWN_F32_ACT = 2
 GATE_UP_SWIGLU_P64 = 3      # gate/up on weights repacked by q8_0_pack64_rows
+DOWN_F32_ACT_P64 = 4        # down (fp32 h) on weights repacked by q8_0_pack64_rounds
+ROUND_BYTES = 1088          # a 1024-value round of Q8_0 blocks
 P64_K = 4096                # values in one packed segment
 
 
@@ -105,6 +107,23 @@ def q8_0_pack64_rows(src: torch.Tensor, rows: int, k: int, out: torch.Tensor | N
     _cuda(out, "out", torch.uint8)
     _need(out, "out", _weight_extent(rows, k, ds))
     call("q8_0_pack64_rows", _ptr(src), rows, k, ss, _ptr(out), ds, _stream(src))
+    return out
+
+
+def q8_0_pack64_rounds(src: torch.Tensor, rows: int, k: int, out: torch.Tensor | None = None,
+                       src_row_stride_bytes: int | None = None) -> torch.Tensor:
+    """Q8_0 rows -> the round-major four-row packed layout DOWN_F32_ACT_P64
+    reads: k/1024 matrices [rows][1088 bytes] (round r at byte r*rows*1088);
+    rows a multiple of 4, k a multiple of 1024."""
+    row_bytes = k // QK * Q8_0_BLOCK_BYTES
+    ss = row_bytes if src_row_stride_bytes is None else src_row_stride_bytes
+    _cuda(src, "src", torch.uint8)
+    _need(src, "src", _weight_extent(rows, k, ss))
+    if out is None:
+        out = torch.empty(rows * row_bytes, dtype=torch.uint8, device=src.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", rows * row_bytes)
+    call("q8_0_pack64_rounds", _ptr(src), rows, k, ss, _ptr(out), _stream(src))
     return out
 
 
@@ -534,7 +553,7 @@ def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
         _act_rows(act, "act", ncols, k)
     elif stage == DOWN:
         _act_rows(act, "act", ncols * topk, k)
-    elif stage == DOWN_F32_ACT:
+    elif stage in (DOWN_F32_ACT, DOWN_F32_ACT_P64):
         _cuda(act, "act", torch.float32)
         if act.dim() != 2 or act.stride(1) != 1:
             raise ValueError("fp32 act must be 2-D with unit inner stride")
@@ -561,7 +580,7 @@ def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
             _need(sb, "shared b", _weight_extent(s_n, s_k, s_stride), s_off)
         _cuda(sout, "shared out", torch.float32)
         _need(sout, "shared out", ncols * s_n * 4)
-        if stage == DOWN_F32_ACT:
+        if stage in (DOWN_F32_ACT, DOWN_F32_ACT_P64):
             sact = shared["act"]
             _cuda(sact, "shared act", torch.float32)
             s_act_stride = sact.stride(0)

@@ -249,7 +249,7 @@ def test_ep_share_l43_e128_c8():
     share = cfg["shared_inter"] // cfg["shared_share"]
     say("config ep_share_l43_e128_c8: allocating the 43-layer share")
     bank = bench.Bank(moeq8, torch, L, n_local, H, I, seed, cfg["shared_inter"])
-    bank.pack_gate_up(moeq8, torch)         # the launch configuration the bench times
+    bank.pack_weights(moeq8, torch)         # the launch configuration the bench times
     xs, lgs, bs = bench.layer_inputs(torch, workloads, seed, L, c, H, E)
     owner_np = workloads.owner_slots(E, n_local)
     owner = to_dev(owner_np)
@@ -306,7 +306,11 @@ def test_ep_share_l43_e128_c8():
         hq_dev = moeq8.q8_1_quantize_rows(to_dev(h_ref32))
         hq_ref = oracle.quantize_q8_1(h_ref32)
         assert host(hq_dev).tobytes() == hq_ref.tobytes()
-        y = host(moeq8.moe_grouped_mmvq(moeq8.DOWN, bank.down[l], None, hq_dev, w.grouping, n=H,
+        # (the bank is packed; the plain-layout calls below read the layer's
+        # matrices drawn again from the same generator)
+        plain_down = torch.empty_like(bank.down[l])
+        moeq8.synth_q8_0_fill(plain_down, n_local, H * I // 32, n_local, seed, l, 0, 2)
+        y = host(moeq8.moe_grouped_mmvq(moeq8.DOWN, plain_down, None, hq_dev, w.grouping, n=H,
                                         k=I, n_local_expert=n_local, ncols=c, topk=topk))
         for j in range(c):
             for s in range(topk):
@@ -328,7 +332,9 @@ def test_ep_share_l43_e128_c8():
         hsq_ref = oracle.quantize_q8_1(hs_ref.astype(np.float32))
         hsq_dev = moeq8.q8_1_quantize_rows(to_dev(hs_ref.astype(np.float32)))
         assert host(hsq_dev).tobytes() == hsq_ref.tobytes()
-        ys = moeq8.mmvq_q8_0(shared[l].down, hsq_dev, H, share, k_block_offset=0,
+        plain_sd = torch.empty(H * (cfg["shared_inter"] // 32 * 34), dtype=torch.uint8, device=DEV)
+        moeq8.synth_q8_0_fill(plain_sd, 1, H * cfg["shared_inter"] // 32, 1, seed, l, 0, 5)
+        ys = moeq8.mmvq_q8_0(plain_sd, hsq_dev, H, share, k_block_offset=0,
                              w_row_stride_bytes=cfg["shared_inter"] // 32 * 34)
         assert_close(host(ys), oracle.mmvq_column_range(sd, hsq_ref, 0), PROD_TOL, f"layer {l} shared down")
         # column-range slices of the shared down (both halves) equal the full row
@@ -340,10 +346,10 @@ def test_ep_share_l43_e128_c8():
             full_pad.zero_()
             full_pad[:, half * rbq:(half + 1) * rbq] = hsq_dev
             kb = half * share // 32
-            ys_half = moeq8.mmvq_q8_0(shared[l].down, hsq_dev, H, share, k_block_offset=kb,
+            ys_half = moeq8.mmvq_q8_0(plain_sd, hsq_dev, H, share, k_block_offset=kb,
                                       w_offset_bytes=kb * 34,
                                       w_row_stride_bytes=cfg["shared_inter"] // 32 * 34)
-            ys_full = moeq8.mmvq_q8_0(shared[l].down, full_pad, H, cfg["shared_inter"])
+            ys_full = moeq8.mmvq_q8_0(plain_sd, full_pad, H, cfg["shared_inter"])
             assert bits_equal(ys_half, ys_full)
         # (the bank's gate/up are packed; the dense pair reads the plain rows,
         # drawn again from the same generator)

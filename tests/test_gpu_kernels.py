@@ -643,6 +643,34 @@ def test_pack64_layout(rows, k):
     assert np.array_equal(np.sort(got.reshape(rows, -1), axis=1), np.sort(raw.reshape(rows, -1), axis=1))
 
 
+def _rounds_reference(raw: np.ndarray, rows: int, k: int, stride: int) -> np.ndarray:
+    """The round-major four-row packed layout restated on the host: round r of
+    every row goes to matrix r of contiguous 1088-byte rows, where the 4352
+    bytes of rows 4q..4q+3 are permuted as one 64-chunk segment (packed dword
+    256*(d//4) + 4c + d%4 takes unit dword 17c + d, packed dword 1024 + c takes
+    17c + 16; unit dword 272g + i is dword i of row 4q + g's round)."""
+    src = np.ascontiguousarray(raw).reshape(-1).view(np.uint32).reshape(rows, stride // 4)
+    c = np.arange(64)
+    perm = np.empty(1088, np.int64)
+    for d in range(16):
+        perm[256 * (d // 4) + 4 * c + d % 4] = 17 * c + d
+    perm[1024 + c] = 17 * c + 16
+    out = []
+    for r in range(k // 1024):
+        rnd = src[:, r * 272:(r + 1) * 272]                   # [rows][272]
+        units = rnd.reshape(rows // 4, 1088)
+        out.append(units[:, perm].reshape(-1))
+    return np.concatenate(out).view(np.uint8)
+
+
+@pytest.mark.parametrize("rows,k,extra", [(4, 1024, 0), (8, 2048, 0), (12, 1024, 1088)])
+def test_pack64_rounds_layout(rows, k, extra):
+    stride = k // 32 * 34 + extra
+    raw = np.random.default_rng(rows + k + extra).integers(0, 256, size=rows * stride, dtype=np.uint8)
+    got = host(moeq8.q8_0_pack64_rounds(to_dev(raw), rows, k, src_row_stride_bytes=stride))
+    assert np.array_equal(got, _rounds_reference(raw, rows, k, stride))
+
+
 def _synth_dev(seed, n_mats, rows, k, matrix, layer=0):
     t = torch.empty(n_mats * rows * (k // 32) * 34, dtype=torch.uint8, device=DEV)
     moeq8.synth_q8_0_fill(t, n_mats, rows * k // 32, n_mats, seed, layer, 0, matrix)
@@ -698,6 +726,52 @@ def test_grouped_gate_up_p64_equals_plain(c, n_exp, local, inter, share_rows, ha
         assert bits_equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("c,n_exp,local,hidden,half", [(1, 32, 32, 1024, 0), (5, 64, 32, 4096, 1),
+                                                      (8, 32, 16, 516, 0), (3, 16, 16, 256, 1)])
+def test_grouped_down_p64_equals_plain(c, n_exp, local, hidden, half):
+    """DOWN_F32_ACT_P64 on round-major packed copies (routed experts, and the
+    shared matrix's round for its column-range share) against DOWN_F32_ACT on
+    the plain weights with the column-range slice, every written y and ys row
+    bit for bit (owner mask, a row count that is not a multiple of the
+    workgroup's rows)."""
+    say(f"p64 down c={c} E={n_exp} local={local} hidden={hidden} half={half}")
+    topk, seed, inter = 8, 70 + c, 1024
+    wd = _synth_dev(seed, local, hidden, inter, 2)
+    pd = moeq8.q8_0_pack64_rounds(wd, local * hidden, inter)
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    ids, w, grouping = moeq8.moe_route_topk(lg, topk, owner_slot=to_dev(workloads.owner_slots(n_exp, local)),
+                                            n_local_expert=local)
+    h = to_dev(workloads.normal_f32(seed + 1, (c * topk, inter), 2.0))
+    hs = to_dev(workloads.normal_f32(seed + 2, (c, inter), 2.0))
+    full = 2 * inter
+    rbf = full // 32 * 34
+    sd = _synth_dev(seed, 1, hidden, full, 5)
+    psd = moeq8.q8_0_pack64_rounds(sd, hidden, full)
+    kb = half * inter // 32
+    rb = moeq8.ops.ROUND_BYTES
+    outs = []
+    for stage, a, sh in ((moeq8.DOWN_F32_ACT, wd, {"a": sd, "row_stride": rbf, "k_block_offset": kb,
+                                                   "offset_bytes": kb * 34}),
+                         (moeq8.DOWN_F32_ACT_P64, pd, {"a": psd, "row_stride": rb, "k_block_offset": 0,
+                                                       "offset_bytes": half * hidden * rb})):
+        y = torch.full((c, topk, hidden), float("nan"), device=DEV)
+        ys = torch.full((c, hidden), float("nan"), device=DEV)
+        moeq8.moe_grouped_mmvq_ex(stage, a, None, h, grouping, n=hidden, k=inter, n_local_expert=local,
+                                  ncols=c, topk=topk, out=y,
+                                  shared=dict(sh, n=hidden, k=inter, out=ys, act=hs))
+        outs.append((y, ys))
+    torch.cuda.synchronize()
+    valid = host(ids) >= 0
+    y0, y1 = host(outs[0][0]), host(outs[1][0])
+    for j in range(c):
+        for s in range(topk):
+            if valid[j, s]:
+                assert np.array_equal(y0[j, s].view(np.int32), y1[j, s].view(np.int32)), (j, s)
+            else:
+                assert np.isnan(y1[j, s]).all()
+    assert bits_equal(outs[0][1], outs[1][1])
+
+
 def test_p64_rejects_what_it_cannot_read():
     """Host checks of the packed stage: K other than 4096, a weight pointer or
     a shared slice off the 16-byte / segment grid."""
@@ -713,6 +787,15 @@ def test_p64_rejects_what_it_cannot_read():
             moeq8.moe_grouped_mmvq_ex(moeq8.GATE_UP_SWIGLU_P64, a, a, xq, grouping, n=inter, k=H,
                                       n_local_expert=local, ncols=c, topk=topk, out=h)
         assert ei.value.status == status
+    # the quad-packed down: k read by more than one lane group a row, n not a multiple of 4
+    for n, K, status in ((64, 2048, -3), (62, 1024, -3)):
+        wt = torch.zeros(local * n * (K // 32) * 34, dtype=torch.uint8, device=DEV)
+        hh = torch.zeros((c * topk, K), device=DEV)
+        y = torch.zeros((c, topk, n), device=DEV)
+        with pytest.raises(moeq8.MoeQ8Error) as ei:
+            moeq8.moe_grouped_mmvq_ex(moeq8.DOWN_F32_ACT_P64, wt, None, hh, grouping, n=n, k=K,
+                                      n_local_expert=local, ncols=c, topk=topk, out=y)
+        assert ei.value.status == status
 
 
 @pytest.mark.parametrize("c,n_exp", [(1, 16), (5, 32), (8, 32)])
@@ -721,7 +804,7 @@ def test_fused_layer_packed_equals_unfused(c, n_exp):
     nine separate calls on the plain weights: every output bit for bit."""
     from quantized_moe_expert_q8_amd import moe_layer as ml
     say(f"packed fused layer c={c} E={n_exp}")
-    H, I, topk, share_rows = 4096, 256, 8, 256
+    H, I, topk, share_rows = 4096, 1024, 8, 1024     # the packed down reads whole 1024-value rounds
     seed = 80 + c
     wg, wu, wd = _synth_dev(seed, n_exp, I, H, 0), _synth_dev(seed, n_exp, I, H, 1), _synth_dev(seed, n_exp, H, I, 2)
     full = 2 * share_rows
@@ -731,7 +814,7 @@ def test_fused_layer_packed_equals_unfused(c, n_exp):
     sd = _synth_dev(seed, 1, H, full, 5).view(H, rb_f)
     experts = ml.RoutedExperts(wg, wu, wd, n_exp, H, I)
     shared = ml.SharedExpertShare(sg, su, sd, H, full, share_rows, share_rows)
-    pe, ps = ml.pack_gate_up(experts, shared)
+    pe, ps = ml.pack_experts(experts, shared)
     x = to_dev(workloads.activations(seed, c, H))
     lg = to_dev(workloads.router_logits(seed, c, n_exp))
     b = to_dev(workloads.router_bias(seed, n_exp))
