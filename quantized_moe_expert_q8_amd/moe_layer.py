@@ -291,6 +291,8 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
     allocated.  products="gemm" runs the grouped products on the int8 matrix
     cores (moe_grouped_gemm), "mmvq" runs the grouped MMVQ in passes of 8
     columns, "auto" picks by the mean routes per expert.  Returns ws.out."""
+    if experts.packed:
+        raise ValueError("forward_wide reads the plain Q8_0 layout (its GEMM does not take packed weights)")
     if products == "auto":
         products = wide_products_for(ws.ncols, ws.topk, experts.n_local)
     if products not in ("gemm", "mmvq"):

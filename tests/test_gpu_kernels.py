@@ -834,6 +834,8 @@ def test_fused_layer_packed_equals_unfused(c, n_exp):
                     assert np.array_equal(ha[j, s].view(np.int32), hb[j, s].view(np.int32))
     with pytest.raises(ValueError):
         ml.forward(x, lg, b, own, n_exp // 2, pe, ps, wb, fused=False)
+    with pytest.raises(ValueError):                  # the wide path reads the plain layout only
+        ml.forward_wide(x, lg, b, own, n_exp // 2, pe, ml.WideWorkspace(c, H, I, topk, DEV))
 
 
 # ---------------------------------------------------------------------------
