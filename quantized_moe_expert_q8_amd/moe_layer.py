@@ -290,13 +290,16 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
     grouped down, combine; seven launches on the current stream, nothing
     allocated.  products="gemm" runs the grouped products on the int8 matrix
     cores (moe_grouped_gemm), "mmvq" runs the grouped MMVQ in passes of 8
-    columns, "auto" picks by the mean routes per expert.  Returns ws.out."""
-    if experts.packed:
-        raise ValueError("forward_wide reads the plain Q8_0 layout (its GEMM does not take packed weights)")
+    columns, "auto" picks by the mean routes per expert.  Packed experts
+    (pack_experts) run the MMVQ passes on the packed stages, the down
+    quantising h in its launch (six launches, the same bits); the GEMM reads
+    the plain layout only.  Returns ws.out."""
     if products == "auto":
-        products = wide_products_for(ws.ncols, ws.topk, experts.n_local)
+        products = "mmvq" if experts.packed else wide_products_for(ws.ncols, ws.topk, experts.n_local)
     if products not in ("gemm", "mmvq"):
         raise ValueError("products must be 'gemm', 'mmvq' or 'auto'")
+    if experts.packed and products == "gemm":
+        raise ValueError("the wide GEMM reads the plain Q8_0 layout, not packed weights")
     grouped = ops.moe_grouped_gemm if products == "gemm" else ops.moe_grouped_mmvq
     c, topk = ws.ncols, ws.topk
     hidden, inter = experts.hidden, experts.inter
@@ -304,11 +307,19 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
     ops.moe_route_topk_wide(logits, topk, bias=bias, owner_slot=owner_slot,
                             n_local_expert=n_local_expert, ids=ws.ids, weights=ws.weights)
     ops.moe_group_routes(ws.ids, experts.n_local, grouping=ws.grouping)
-    grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
-            n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
-    ops.q8_1_quantize_rows(ws.h.view(c * topk, inter), out=ws.hq)
-    grouped(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
-            n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
+    if experts.packed:
+        ops.moe_grouped_mmvq_ex(ops.GATE_UP_SWIGLU_P64, experts.gate, experts.up, ws.xq, ws.grouping,
+                                n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
+                                out=ws.h)
+        ops.moe_grouped_mmvq_ex(ops.DOWN_F32_ACT_P64, experts.down, None, ws.h.view(c * topk, inter),
+                                ws.grouping, n=hidden, k=inter, n_local_expert=experts.n_local, ncols=c,
+                                topk=topk, out=ws.y)
+    else:
+        grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
+                n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
+        ops.q8_1_quantize_rows(ws.h.view(c * topk, inter), out=ws.hq)
+        grouped(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
+                n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
     ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
     return ws.out
 

@@ -834,8 +834,30 @@ def test_fused_layer_packed_equals_unfused(c, n_exp):
                     assert np.array_equal(ha[j, s].view(np.int32), hb[j, s].view(np.int32))
     with pytest.raises(ValueError):
         ml.forward(x, lg, b, own, n_exp // 2, pe, ps, wb, fused=False)
-    with pytest.raises(ValueError):                  # the wide path reads the plain layout only
-        ml.forward_wide(x, lg, b, own, n_exp // 2, pe, ml.WideWorkspace(c, H, I, topk, DEV))
+    with pytest.raises(ValueError):                  # the wide GEMM reads the plain layout only
+        ml.forward_wide(x, lg, b, own, n_exp // 2, pe, ml.WideWorkspace(c, H, I, topk, DEV), products="gemm")
+
+
+@pytest.mark.parametrize("c", [3, 40])
+def test_wide_mmvq_packed_equals_plain(c):
+    """forward_wide's MMVQ passes on packed experts (the packed stages, h
+    quantised inside the down launch) against the plain MMVQ passes: every
+    output bit for bit, at a wide grouping of several passes of 8 columns."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    say(f"wide mmvq packed c={c}")
+    H, I, topk, n_exp, seed = 4096, 1024, 8, 16, 90 + c
+    wg, wu, wd = _synth_dev(seed, n_exp, I, H, 0), _synth_dev(seed, n_exp, I, H, 1), _synth_dev(seed, n_exp, H, I, 2)
+    experts = ml.RoutedExperts(wg, wu, wd, n_exp, H, I)
+    pe, _ = ml.pack_experts(experts)
+    x = to_dev(workloads.activations(seed, c, H))
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    b = to_dev(workloads.router_bias(seed, n_exp))
+    wa, wb = ml.WideWorkspace(c, H, I, topk, DEV), ml.WideWorkspace(c, H, I, topk, DEV)
+    ml.forward_wide(x, lg, b, None, n_exp, experts, wa, products="mmvq")
+    ml.forward_wide(x, lg, b, None, n_exp, pe, wb)                # auto: the MMVQ passes
+    torch.cuda.synchronize()
+    assert torch.equal(wa.ids, wb.ids)
+    assert bits_equal(wa.h, wb.h) and bits_equal(wa.y, wb.y) and bits_equal(wa.out, wb.out)
 
 
 # ---------------------------------------------------------------------------
