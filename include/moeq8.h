@@ -15,7 +15,8 @@
  *     and route sum in one launch, products and sums rounded separately;
  *     clamped routed SwiGLU;
  *   - the review finding on moe_combine_masked_kernel: a route masked to -1 is
- *     skipped and its slot never read.
+ *     skipped: nothing it indexes is read, and its slot's value (unwritten,
+ *     possibly NaN) never enters the sum.
  *
  * Formats (the pages name them and print no layout; this is the layout used):
  *   Q8_0 block, 34 bytes: fp16 d (little-endian), int8 qs[32]; value = d * q.
@@ -321,8 +322,11 @@ int moe_group_routes(const int32_t* ids, int64_t ncols, int32_t topk, int64_t n_
  * a9: weighted masked combine.
  *   out[j][i] = sum over slots s ascending with ids[j][s] >= 0 of
  *               fl(weights[j][s] * y[j][s][i])  (fp32: each product rounded, then
- *               added in slot order; masked slots are never read)
- *   y fp32 [ncols][topk][n]; ids int32 [ncols][topk]; weights fp32 [ncols][topk];
+ *               added in slot order; a masked slot's y row is loaded with the
+ *               others, all in bounds, and its value, NaN included, is
+ *               selected away, never added)
+ *   y fp32 [ncols][topk][n] (every row allocated; masked rows may hold
+ *   anything); ids int32 [ncols][topk]; weights fp32 [ncols][topk];
  *   out fp32 [ncols][n] (fully overwritten; all-masked columns give 0).
  * ------------------------------------------------------------------------- */
 int moe_combine(const float* y, const int32_t* ids, const float* weights, int64_t ncols,

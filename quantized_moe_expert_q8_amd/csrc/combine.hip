@@ -7,10 +7,12 @@
 
 namespace moeq8 {
 
-// All slots' ids and weights are read first (one round trip of scalar
-// loads), then the y values of the unmasked slots, all issued before any is
-// used (a second round trip, instead of one per slot).  A masked slot's y row
-// is never read, and the sum skips it by selection.
+// Every load is issued before any is used: the slots' ids and weights
+// (scalar loads), every slot's y value and the add term, so the combine
+// waits for one round trip to memory.  A masked slot's y element (in bounds:
+// y has a row for every route) is loaded but never used: the sum skips the
+// slot by selection, so whatever that row holds (NaN, stale values) never
+// reaches the output.
 // add (nullable): the shared expert's output [ncols][n], added once after
 // the routed sum; it may be out itself (each element is read, then written,
 // by the same thread).
@@ -26,21 +28,19 @@ __global__ void k_combine(const float* __restrict__ y, const int32_t* __restrict
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) {
         const int r = j * topk + min(s, topk - 1);      // in range for every s
-        id[s] = s < topk ? ids[r] : -1;
+        const int idr = ids[r];                          // loaded for every s, then masked
+        id[s] = s < topk ? idr : -1;
         wt[s] = w[r];
+        yv[s] = y[(int64_t)r * n + i];
     }
-#pragma unroll
-    for (int s = 0; s < KMAX; ++s) {
-        yv[s] = 0.0f;
-        if (id[s] >= 0) yv[s] = y[(int64_t)(j * topk + s) * n + i];
-    }
+    const float addv = add ? add[(int64_t)j * n + i] : 0.0f;
     float acc = 0.0f;  // +0 then the valid products in slot order
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) {
         const float sum = acc + wt[s] * yv[s];
         acc = id[s] >= 0 ? sum : acc;
     }
-    if (add) acc = acc + add[(int64_t)j * n + i];
+    if (add) acc = acc + addv;
     out[(int64_t)j * n + i] = acc;
 }
 

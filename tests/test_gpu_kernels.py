@@ -382,7 +382,7 @@ def test_grouped_gate_up_down_combine(c, n_exp, local, hidden, inter):
                                  w_offset_bytes=int(e) * hidden * row_d, w_row_stride_bytes=row_d)
             assert bits_equal(y[j, s:s + 1].contiguous(), ys)
 
-    # combine on the oracle's y and weights (masked slots hold NaN and are never read)
+    # combine on the oracle's y and weights (masked slots hold NaN, which must not reach the output)
     y32 = np.where(ids_ref[..., None] >= 0, y_ref, np.nan).astype(np.float32)
     w32 = w_ref.astype(np.float32)
     out = host(moeq8.moe_combine(to_dev(y32), ids, to_dev(w32)))
