@@ -587,7 +587,8 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
     launch over all experts reads far more than the 256 MB Infinity Cache).
     Per column count: the seven-launch layer with the grouped products on the
     matrix cores and with the grouped MMVQ, and each grouped product alone
-    (graphs, HIP events), against a plain streaming read of as many bytes."""
+    (graphs, HIP events), against a plain streaming read of as many bytes;
+    then the MMVQ passes on the packed layouts."""
     cfg = workloads.CONFIGS["wide_e256"]
     hidden, inter, topk, n_exp, seed = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"], cfg["seed"]
     bank = Bank(moeq8, torch, 1, n_exp, hidden, inter, seed)
@@ -639,6 +640,40 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
         rec["gemm"]["gate_up_frac_of_ceiling"] = round(rec["gemm"]["gate_up_gbps"] / rec["ceiling_gbps"], 4)
         log(f"wide {rec}")
         out.append(rec)
+        del ws, x, lg, bs
+    # The MMVQ passes again on the packed layouts (the bank repacked in place):
+    # the six-launch layer, the packed gate/up and the down that quantises h
+    # in its launch, each alone.
+    bank.pack_weights(moeq8, torch)
+    experts = bank.experts(ml, 0)
+    for rec in out:
+        cols = rec["cols"]
+        x = torch.from_numpy(workloads.activations(seed, cols, hidden)).cuda()
+        lg = torch.from_numpy(workloads.router_logits(seed, cols, n_exp)).cuda()
+        bs = torch.from_numpy(workloads.router_bias(seed, n_exp)).cuda()
+        ws = ml.WideWorkspace(cols, hidden, inter, topk, "cuda")
+        ml.forward_wide(x, lg, bs, None, n_exp, experts, ws, products="mmvq")
+        torch.cuda.synchronize()
+        reps = 10 if cols >= 512 else 20
+        words = ws.grouping.cpu().numpy().view(np.int32)
+        n_active, n_valid = int(words[0]), int(words[1])
+        layer_ms = time_graph(torch, lambda: ml.forward_wide(x, lg, bs, None, n_exp, experts, ws,
+                                                             products="mmvq"), reps)
+        gu_us = time_graph(torch, lambda: moeq8.moe_grouped_mmvq_ex(
+            moeq8.GATE_UP_SWIGLU_P64, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
+            n_local_expert=n_exp, ncols=cols, topk=topk, out=ws.h), reps) * 1e3
+        dn_us = time_graph(torch, lambda: moeq8.moe_grouped_mmvq_ex(
+            moeq8.DOWN_F32_ACT_P64, experts.down, None, ws.h.view(cols * topk, inter), ws.grouping,
+            n=hidden, k=inter, n_local_expert=n_exp, ncols=cols, topk=topk, out=ws.y), reps) * 1e3
+        gu_b = rec["gate_up_bytes"]
+        dn_b = down_launch_bytes(n_active, n_valid, hidden, inter)
+        rec["mmvq_packed"] = {"layer_us": round(layer_ms * 1e3, 1),
+                              "cols_per_s": round(cols / (layer_ms * 1e-3), 1),
+                              "gate_up_us": round(gu_us, 1),
+                              "gate_up_gbps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
+                              "down_us": round(dn_us, 1),
+                              "down_gbps": round(dn_b / (dn_us * 1e-6) / 1e9, 1)}
+        log(f"wide packed mmvq {cols}: {rec['mmvq_packed']}")
         del ws, x, lg, bs
     del bank, experts
     torch.cuda.empty_cache()
