@@ -251,6 +251,17 @@ def layer_bytes(n_active, n_valid, cols, hidden, inter, topk, shared_rows):
 # CPU baseline (oracle, bounded sample)
 # ---------------------------------------------------------------------------
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(workloads, cfg, budget_s, share_rows):
     import oracle
     seed, hidden, inter, topk = cfg["seed"], cfg["hidden"], cfg["inter"], cfg["topk"]
@@ -282,7 +293,7 @@ def cpu_baseline(workloads, cfg, budget_s, share_rows):
         if total_t >= budget_s:
             break
     return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
             "sample": f"{layers_done} of {cfg['layers']} layers of {cfg['name']} (numpy oracle, "
                       f"unfused per-route loop, single thread); {layers_done / total_t:.3f} layers/s"}
 
