@@ -235,8 +235,10 @@ int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
  *     different number of 16-chunk rounds, is MOEQ8_EUNSUPPORTED (call it apart).
  *   - stage MOEQ8_GATE_UP_SWIGLU_P64: the gate/up stage on weights repacked by
  *     q8_0_pack64_rows (the routed experts and the dense part alike).  Each
- *     lane's chunk arrives through four 16-byte and one 4-byte nontemporal
- *     loads that read one contiguous span across the wave.  Requires
+ *     lane's chunk arrives through four 16-byte and one 4-byte loads that
+ *     read one contiguous span across the wave: nontemporal when ncols <= 8
+ *     (each row is read once), ordinary for wider groupings, where an expert
+ *     with more than 8 routes passes over its rows again.  Requires
  *     k == 4096 (one packed segment a row; a dense slice starting at a
  *     multiple of 128 blocks) else MOEQ8_EUNSUPPORTED, and 16-byte aligned
  *     weight pointers, row strides and expert stride else MOEQ8_EALIGN.
@@ -250,8 +252,9 @@ int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
  *     MOEQ8_EALIGN.  The dense part is the round's matrix (s_a at round r of
  *     the packed shared matrix, s_k_block_offset 0): its products equal those
  *     of the column-range slice at block 32 r of the plain matrix, since a
- *     one-round slice's lane sums do not depend on its round.  Every output is
- *     bit-identical to MOEQ8_DOWN_F32_ACT on the unpacked weights.
+ *     one-round slice's lane sums do not depend on its round.  Loads as for
+ *     MOEQ8_GATE_UP_SWIGLU_P64.  Every output is bit-identical to
+ *     MOEQ8_DOWN_F32_ACT on the unpacked weights.
  * act_row_stride is ignored for the q8_1 stages.
  * ------------------------------------------------------------------------- */
 int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,

@@ -107,9 +107,14 @@ __device__ __forceinline__ float chain_groups(float v, int lane) {
 // lane group a row (G = 1, the down launch with fp32 activations, K = 1024
 // contiguous rows of 1088 bytes) a row set is a quad of rows, 4352 contiguous
 // bytes packed as one segment whose chunk L (chunk L % 16 of row L / 16) is
-// again lane L's.
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false>
+// again lane L's.  The packed weights are loaded nontemporally (each row is
+// read once) unless REREAD: a launch whose items make several passes of
+// MAX_COLS columns over the same rows takes ordinary loads, whose lines stay
+// in L2 for the next pass.
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false,
+          bool REREAD = false>
 __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
+    static_assert(!REREAD || P64, "REREAD selects the packed weights' load kind");
     static_assert(!P64 || (!Q4 && !STX && ((G == 4 && !ACT_F32) || (G == 1 && NMAT == 1 && ACT_F32))),
                   "the packed layouts serve the four-group gate/up rows and the one-group down quads");
     // weight chunk: two Q8_0 blocks (68 B) or two 4-bit blocks (36 B); the
@@ -243,9 +248,9 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                         // the matrix or wholly past it, and then reads the first
                         // quad and adds +0, as every unconditional load does)
                         const int64_t quad = ok[u] ? row - rslot : 0;
-                        load_w_chunk_p64(wc[u][m], w0 + quad * row_stride, lane);
+                        load_w_chunk_p64<!REREAD>(wc[u][m], w0 + quad * row_stride, lane);
                     } else if constexpr (P64) {
-                        if (ok[u]) load_w_chunk_p64(wc[u][m], (m == 0 ? w0 : w1) + row * row_stride, crel);
+                        if (ok[u]) load_w_chunk_p64<!REREAD>(wc[u][m], (m == 0 ? w0 : w1) + row * row_stride, crel);
                         else zero_w_chunk(wc[u][m]);
                     } else if (UNCOND || ok[u]) {
                         load_w_chunk(wc[u][m], (m == 0 ? w0 : w1) + off);
@@ -464,10 +469,11 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 
 // One work item = one row block: of one active expert (grouped), of the dense
 // extra matrix (grouped launches with a shared part), or of the one matrix.
-template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false>
+template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false,
+          bool REREAD = false>
 __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_act[];
-    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX, Q4, P64>(p, blockIdx.x, lds_act);
+    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX, Q4, P64, REREAD>(p, blockIdx.x, lds_act);
 }
 
 __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, float* h) {
@@ -537,14 +543,25 @@ int launch_p64(bool down, MmvqParams& p, const Shape& s, int64_t grid, size_t ld
     p.nsteps = s.nsteps;
     if (grid <= 0) return MOEQ8_OK;
     if (grid > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    // a grouping wider than one pass can give an expert several passes
+    const bool reread = p.ncols > MAX_COLS;
+    const dim3 block(64 * WAVES_PER_WG);
     if (down) {
         constexpr int U = u_for(1, true, false);
-        hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true>), dim3((uint32_t)grid),
-                           dim3(64 * WAVES_PER_WG), lds, stream, p);
+        if (reread)
+            hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, true>), dim3((uint32_t)grid),
+                               block, lds, stream, p);
+        else
+            hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true>), dim3((uint32_t)grid),
+                               block, lds, stream, p);
     } else {
         constexpr int U = u_for(2, false, false);
-        hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), dim3((uint32_t)grid),
-                           dim3(64 * WAVES_PER_WG), 0, stream, p);
+        if (reread)
+            hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, true>), dim3((uint32_t)grid),
+                               block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), dim3((uint32_t)grid),
+                               block, 0, stream, p);
     }
     return check_launch();
 }

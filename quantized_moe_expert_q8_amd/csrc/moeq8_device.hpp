@@ -153,19 +153,24 @@ constexpr int P64_CHUNKS = 64;
 constexpr int P64_SEGMENT_BYTES = P64_CHUNKS * W_CHUNK_BYTES;      // 4352
 constexpr int P64_SEGMENT_DWORDS = P64_SEGMENT_BYTES / 4;          // 1088
 
-// Chunk c of a packed segment (16-byte aligned), with nontemporal loads: the
-// weights are read once.
+// Chunk c of a packed segment (16-byte aligned).  NT: nontemporal loads, for
+// weights read once; otherwise ordinary loads.
+template <bool NT = true>
 __device__ __forceinline__ void load_w_chunk_p64(WChunk& w, const uint8_t* seg, int c) {
     const u32x4a16* q = reinterpret_cast<const u32x4a16*>(seg) + c;
+    const uint32_t* tail = reinterpret_cast<const uint32_t*>(seg + 4096) + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const u32x4a16 t = __builtin_nontemporal_load(q + 64 * i);
+        u32x4a16 t;
+        if constexpr (NT) t = __builtin_nontemporal_load(q + 64 * i);
+        else t = q[64 * i];
         w.v[4 * i + 0] = t.x;
         w.v[4 * i + 1] = t.y;
         w.v[4 * i + 2] = t.z;
         w.v[4 * i + 3] = t.w;
     }
-    w.v[16] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(seg + 4096) + c);
+    if constexpr (NT) w.v[16] = __builtin_nontemporal_load(tail);
+    else w.v[16] = *tail;
 }
 
 // Source dword (index 17 c + d of the plain segment) of packed dword p.
