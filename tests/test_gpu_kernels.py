@@ -677,14 +677,26 @@ def _synth_dev(seed, n_mats, rows, k, matrix, layer=0):
     return t
 
 
+def _route_any(lg, topk, c, n_exp, local, bias=None):
+    """ids, weights and the grouping of c columns: one launch up to 8 columns,
+    the wide router and the grouping launch beyond."""
+    own = to_dev(workloads.owner_slots(n_exp, local))
+    if c <= 8:
+        return moeq8.moe_route_topk(lg, topk, bias=bias, owner_slot=own, n_local_expert=local)
+    ids, w = moeq8.moe_route_topk_wide(lg, topk, bias=bias, owner_slot=own, n_local_expert=local)
+    return ids, w, moeq8.moe_group_routes(ids, local)
+
+
 @pytest.mark.parametrize("c,n_exp,local,inter,share_rows,half", [(1, 32, 32, 256, 0, 0),
                                                                  (5, 64, 32, 512, 256, 1),
                                                                  (8, 32, 16, 1024, 512, 0),
-                                                                 (3, 16, 16, 72, 40, 1)])
+                                                                 (3, 16, 16, 72, 40, 1),
+                                                                 (24, 16, 8, 256, 256, 1)])
 def test_grouped_gate_up_p64_equals_plain(c, n_exp, local, inter, share_rows, half):
     """GATE_UP_SWIGLU_P64 on packed copies against GATE_UP_SWIGLU on the plain
     weights, every written h and hs row bit for bit (owner mask, ragged row
-    counts, the shared rows at either half)."""
+    counts, the shared rows at either half; 24 columns: a wide grouping, whose
+    launch takes the packed kernel's ordinary-load form and several passes)."""
     say(f"p64 gate/up c={c} E={n_exp} local={local} inter={inter} share={share_rows} half={half}")
     H, topk, seed = 4096, 8, 60 + c
     wg, wu = _synth_dev(seed, local, inter, H, 0), _synth_dev(seed, local, inter, H, 1)
@@ -693,9 +705,7 @@ def test_grouped_gate_up_p64_equals_plain(c, n_exp, local, inter, share_rows, ha
     x = to_dev(workloads.activations(seed, c, H))
     xq = moeq8.q8_1_quantize_rows(x)
     lg = to_dev(workloads.router_logits(seed, c, n_exp))
-    ids, w, grouping = moeq8.moe_route_topk(lg, topk, bias=to_dev(workloads.router_bias(seed, n_exp)),
-                                            owner_slot=to_dev(workloads.owner_slots(n_exp, local)),
-                                            n_local_expert=local)
+    ids, w, grouping = _route_any(lg, topk, c, n_exp, local, bias=to_dev(workloads.router_bias(seed, n_exp)))
     rb = H // 32 * 34
     outs = []
     for stage, a, b in ((moeq8.GATE_UP_SWIGLU, wg, wu), (moeq8.GATE_UP_SWIGLU_P64, pg, pu)):
@@ -727,20 +737,20 @@ def test_grouped_gate_up_p64_equals_plain(c, n_exp, local, inter, share_rows, ha
 
 
 @pytest.mark.parametrize("c,n_exp,local,hidden,half", [(1, 32, 32, 1024, 0), (5, 64, 32, 4096, 1),
-                                                      (8, 32, 16, 516, 0), (3, 16, 16, 256, 1)])
+                                                      (8, 32, 16, 516, 0), (3, 16, 16, 256, 1),
+                                                      (24, 16, 8, 256, 0)])
 def test_grouped_down_p64_equals_plain(c, n_exp, local, hidden, half):
     """DOWN_F32_ACT_P64 on round-major packed copies (routed experts, and the
     shared matrix's round for its column-range share) against DOWN_F32_ACT on
     the plain weights with the column-range slice, every written y and ys row
     bit for bit (owner mask, a row count that is not a multiple of the
-    workgroup's rows)."""
+    workgroup's rows; 24 columns: a wide grouping, the ordinary-load form)."""
     say(f"p64 down c={c} E={n_exp} local={local} hidden={hidden} half={half}")
     topk, seed, inter = 8, 70 + c, 1024
     wd = _synth_dev(seed, local, hidden, inter, 2)
     pd = moeq8.q8_0_pack64_rounds(wd, local * hidden, inter)
     lg = to_dev(workloads.router_logits(seed, c, n_exp))
-    ids, w, grouping = moeq8.moe_route_topk(lg, topk, owner_slot=to_dev(workloads.owner_slots(n_exp, local)),
-                                            n_local_expert=local)
+    ids, w, grouping = _route_any(lg, topk, c, n_exp, local)
     h = to_dev(workloads.normal_f32(seed + 1, (c * topk, inter), 2.0))
     hs = to_dev(workloads.normal_f32(seed + 2, (c, inter), 2.0))
     full = 2 * inter
