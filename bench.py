@@ -486,6 +486,11 @@ def main():
                                 round(float(np.percentile(step_ms, 90)), 4)],
         "grouped_down": {"mean_launch_us": round(dn_us, 2), "gbps": round(dn_gbps, 1),
                          "bytes_per_launch": int(dn_bytes)},
+        # the routed-expert MMVQ as a whole: both grouped launches' bytes over
+        # their summed times (the shared expert's rows ride in both launches)
+        "gate_up_plus_down": {"gbps": round((gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9, 1),
+                              "frac_of_peak": round((gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9
+                                                    / HBM_PEAK_GBPS, 4)},
     }
 
     if args.pmc_copy:
@@ -523,8 +528,10 @@ def sweep(torch, workloads, moeq8, ml, args):
     """Routed layer, 256 experts, top-8, at 1..8 columns; 4 weight replicas
     (13.7 GB) rotate so the 256 MB Infinity Cache cannot serve the reads.
     Per column count: the layer (graph of the four-launch layers), the grouped
-    gate/up launch alone (graph of its launches, HIP events) and the
-    streaming-read ceiling for the same bytes per launch."""
+    gate/up launch and the grouped down launch alone (graphs of their
+    launches, HIP events), the two together as the routed-expert MMVQ (their
+    bytes over their summed times), and the streaming-read ceiling for the
+    gate/up's bytes per launch."""
     cfg = workloads.CONFIGS["verify_e256_c5"]
     hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
     reps = 4
@@ -566,15 +573,28 @@ def sweep(torch, workloads, moeq8, ml, args):
             for l in range(reps):
                 moeq8.stream_read(bank.gate[l], read_b[l], sink)
 
+        def down_only():
+            for l in range(reps):
+                moeq8.moe_grouped_mmvq_ex(moeq8.DOWN_F32_ACT_P64, experts[l].down, None,
+                                       wss[l].h.view(cols * topk, inter), wss[l].grouping, n=hidden,
+                                       k=inter, n_local_expert=n_exp, ncols=cols, topk=topk, out=wss[l].y)
+
+        dn_b = [down_launch_bytes(n_active[l], n_valid[l], hidden, inter) for l in range(reps)]
         gu_us = time_graph(torch, gate_up_only, n) / reps * 1e3
+        dn_us = time_graph(torch, down_only, n) / reps * 1e3
         st_us = time_graph(torch, stream_only, n) / reps * 1e3
         gu_gbps = float(np.mean(gu_b)) / (gu_us * 1e-6) / 1e9
+        dn_gbps = float(np.mean(dn_b)) / (dn_us * 1e-6) / 1e9
+        both_gbps = float(np.mean(gu_b) + np.mean(dn_b)) / ((gu_us + dn_us) * 1e-6) / 1e9
         st_gbps = float(np.mean(read_b)) / (st_us * 1e-6) / 1e9
         rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2),
                "layer_us": round(ms * 1e3, 2), "layers_per_s": round(1e3 / ms, 1),
                "effective_gbps": round(lb / (ms * 1e-3) / 1e9, 1),
                "gate_up_us": round(gu_us, 2), "gate_up_gbps": round(gu_gbps, 1),
                "gate_up_frac_of_peak": round(gu_gbps / HBM_PEAK_GBPS, 4),
+               "down_us": round(dn_us, 2), "down_gbps": round(dn_gbps, 1),
+               "routed_mmvq_gbps": round(both_gbps, 1),
+               "routed_mmvq_frac_of_peak": round(both_gbps / HBM_PEAK_GBPS, 4),
                "ceiling_gbps": round(st_gbps, 1), "gate_up_frac_of_ceiling": round(gu_gbps / st_gbps, 4)}
         log(f"sweep {rec}")
         out.append(rec)
