@@ -848,11 +848,13 @@ def test_fused_layer_packed_equals_unfused(c, n_exp):
         ml.forward_wide(x, lg, b, own, n_exp // 2, pe, ml.WideWorkspace(c, H, I, topk, DEV), products="gemm")
 
 
-@pytest.mark.parametrize("c", [3, 40])
+@pytest.mark.parametrize("c", [3, 40, 1024])
 def test_wide_mmvq_packed_equals_plain(c):
     """forward_wide's MMVQ passes on packed experts (the packed stages, h
     quantised inside the down launch) against the plain MMVQ passes: every
-    output bit for bit, at a wide grouping of several passes of 8 columns."""
+    output bit for bit, at wide groupings of several passes of 8 columns up
+    to the widest (1024 columns: about 64 passes an expert, the packed
+    kernels' ordinary-load form)."""
     from quantized_moe_expert_q8_amd import moe_layer as ml
     say(f"wide mmvq packed c={c}")
     H, I, topk, n_exp, seed = 4096, 1024, 8, 16, 90 + c
