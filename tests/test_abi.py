@@ -143,6 +143,41 @@ def test_other_validation():
     assert L.moeq8_stream_read(P, 0, P, None) == 0
 
 
+def test_packed_layout_validation():
+    """The packers and the packed stages reject on the host what they cannot
+    read or write (no kernel runs: every case returns before a launch)."""
+    L = moeq8.lib()
+    Q = 0x10000000                                                               # far from P: no overlap
+    rows = L.q8_0_pack64_rows
+    assert rows(P, 2, 2048, 4352, Q, 4352, None) == -1                           # k % 4096
+    assert rows(P, 2, 4096, 4000, Q, 8704, None) == -1                           # stride shorter than a row
+    assert rows(P + 2, 2, 4096, 8704, Q, 8704, None) == -2
+    assert rows(P, 2, 4096, 8704, P + 100, 8704, None) == -1                     # overlapping
+    assert rows(P, 0, 4096, 8704, Q, 8704, None) == 0
+    rounds = L.q8_0_pack64_rounds
+    assert rounds(P, 6, 1024, 1088, Q, None) == -1                               # rows % 4
+    assert rounds(P, 4, 1000, 1088, Q, None) == -1                               # k % 1024
+    assert rounds(P, 4, 1024, 1000, Q, None) == -1                               # stride shorter than a row
+    assert rounds(P + 2, 4, 1024, 1088, Q, None) == -2
+    assert rounds(P, 0, 1024, 1088, Q, None) == 0
+    ex = L.moe_grouped_mmvq_ex
+
+    def gate_up(w_a, k, stride=8704):
+        return ex(3, w_a, Q, 0, stride, 1, 4, k, P, 0, P, 1, 1, P,
+                  None, None, 0, 0, 0, 0, None, 0, None, None)
+
+    def down(n, k, stride):
+        return ex(4, P, None, 0, stride, 1, n, k, P, k, P, 1, 1, P,
+                  None, None, 0, 0, 0, 0, None, 0, None, None)
+
+    assert gate_up(P, 2048) == -3                                                # one 4096-value segment a row
+    assert gate_up(P + 4, 4096) == -2                                            # 16-byte aligned segments
+    assert gate_up(P, 4096, 8708) == -2
+    assert down(4, 2048, 2176) == -3                                             # k must be one 1024 round
+    assert down(62, 1024, 1088) == -3                                            # whole quads of rows
+    assert down(4, 1024, 2176) == -3                                             # contiguous 1088-byte rows
+
+
 def test_ops_reject_out_of_bounds_views():
     """The torch layer refuses views that would read past a tensor (CPU tensors
     are refused first, so this needs no GPU)."""
