@@ -687,3 +687,130 @@ def test_mutation_q4_mistakes_caught():
     assert not np.array_equal(swapped, q)
     no_offset = np.concatenate([qs & 0xF, qs >> 4])
     assert not np.array_equal(no_offset, q)
+
+
+def _unit_q4(codes_rows):
+    """Q4 rows of unit scale from signed values in [-8, 7] (value i < 16 in the
+    low nibble of byte i, value i + 16 in the high one)."""
+    v = np.asarray(codes_rows, np.int32)
+    rows, k = v.shape
+    c = (v + 8).reshape(rows, k // 32, 32).astype(np.uint8)
+    w = np.zeros((rows, k // 32), oracle.Q4_DTYPE)
+    w["d"] = 1.0
+    w["qs"] = c[..., :16] | (c[..., 16:] << 4)
+    return w
+
+
+def test_q4_glu_pair_closed_form():
+    # Unit scales make the two products integer dots that can be read off:
+    # gate row 0 picks x value 0, up row 0 picks twice x value 1, and the
+    # SwiGLU-DS4 closed form of (g, u) follows (gate clamped above at 7 only,
+    # up clamped to +-7).  The RDNA4 Q8_0 gate/up pair commit of PR #826
+    # defines the pair as the two separate products followed by the GLU.
+    k = 64
+    gate = np.zeros((4, k), np.int32)
+    up = np.zeros((4, k), np.int32)
+    gate[0, 0], up[0, 1] = 1, 2            # g = x0,       u = 2 x1
+    gate[1, 2], up[1, 3] = 3, 7            # g = 3 x2,     u = 7 x3
+    gate[2, 4], up[2, 5] = -5, 1           # g = -5 x4,    u = x5
+    gate[3, 40], up[3, 33] = 7, -6         # second block
+    xq = np.zeros((1, k // 32), oracle.Q8_1_DTYPE)
+    xq["d"] = 1.0
+    q = np.zeros(k, np.int32)
+    q[[0, 1, 2, 3, 4, 5, 33, 40]] = [1, 2, 3, 2, 1, 9, 1, 2]
+    xq["qs"][0] = q.reshape(k // 32, 32)
+    h, g, u = oracle.glu_pair_q4(_unit_q4(gate), _unit_q4(up), xq)
+    assert list(g[0]) == [1.0, 9.0, -5.0, 14.0]
+    assert list(u[0]) == [4.0, 14.0, 9.0, -6.0]
+
+    def silu(z):
+        return z / (1.0 + math.exp(-z))
+    want = [silu(1.0) * 4.0, silu(7.0) * 7.0, silu(-5.0) * 7.0, silu(7.0) * -6.0]
+    for a, b in zip(h[0], want):
+        assert abs(a - b) <= 1e-15 * max(1.0, abs(b))
+
+
+def test_q4_glu_pair_matches_dequantized_products():
+    # the pair equals dequantise-then-fp64 products of each matrix followed by
+    # SwiGLU-DS4, gate through the first operand and up through the second
+    rng = np.random.default_rng(16)
+    wg = oracle.quantize_q4(rng.normal(0, 0.02, (20, 512)).astype(np.float32))
+    wu = oracle.quantize_q4(rng.normal(0, 0.02, (20, 512)).astype(np.float32))
+    xq = oracle.quantize_q8_1(rng.normal(0, 1, (3, 512)).astype(np.float32) * 40)
+    h, g, u = oracle.glu_pair_q4(wg, wu, xq)
+    xd = oracle.dequantize(xq)
+    gb = xd @ oracle.dequantize_q4(wg).T
+    ub = xd @ oracle.dequantize_q4(wu).T
+    np.testing.assert_allclose(g, gb, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(u, ub, rtol=1e-12, atol=1e-12)
+    assert np.abs(gb).max() > 7 and np.abs(ub).max() > 7      # both clamps are exercised
+    gc = np.minimum(gb, 7.0)
+    hb = gc / (1.0 + np.exp(-gc)) * np.clip(ub, -7.0, 7.0)
+    np.testing.assert_allclose(h, hb, rtol=1e-12, atol=1e-12)
+
+
+def test_mutation_q4_glu_pair_caught():
+    # planted mistakes in copies of the pair: gate and up swapped, the Q8_0
+    # product called on 4-bit blocks, the offset -8 dropped
+    rng = np.random.default_rng(17)
+    wg = oracle.quantize_q4(rng.normal(0, 0.02, (8, 256)).astype(np.float32))
+    wu = oracle.quantize_q4(rng.normal(0, 0.02, (8, 256)).astype(np.float32))
+    xq = oracle.quantize_q8_1(rng.normal(0, 1, (2, 256)).astype(np.float32) * 40)
+    h = oracle.glu_pair_q4(wg, wu, xq)[0]
+    swapped = oracle.swiglu_ds4(oracle.mmvq_q4(wu, xq), oracle.mmvq_q4(wg, xq))
+    assert not np.allclose(swapped, h, rtol=1e-6, atol=1e-9)
+    with pytest.raises(Exception):
+        oracle.mmvq(wg, xq)                                 # 16 code bytes are not 32 quants
+    def no_offset(w):
+        qs = w["qs"].astype(np.int64)
+        v = np.concatenate([qs & 0xF, qs >> 4], axis=-1)
+        return np.einsum("nb,cb,cnbk,->cn", w["d"].astype(np.float64), xq["d"].astype(np.float64),
+                         v[None] * xq["qs"].astype(np.int64)[:, None], 1.0)
+    bad = oracle.swiglu_ds4(no_offset(wg), no_offset(wu))
+    assert not np.allclose(bad, h, rtol=1e-6, atol=1e-9)
+
+
+def test_glu_pair_and_expert_ffn_match_dequantized_products():
+    # the Q8_0 pair and the one-column expert FFN by dequantise-then-fp64
+    # brute force: g through the first matrix, u through the second, SwiGLU-DS4
+    # written out, h rounded to fp32 before its q8_1 (R8), then the down
+    rng = np.random.default_rng(18)
+    wg = oracle.quantize_q8_0(rng.normal(0, 0.02, (16, 256)).astype(np.float32))
+    wu = oracle.quantize_q8_0(rng.normal(0, 0.02, (16, 256)).astype(np.float32))
+    wd = oracle.quantize_q8_0(rng.normal(0, 0.02, (256, 32)).astype(np.float32))
+    xq = oracle.quantize_q8_1(rng.normal(0, 1, (2, 256)).astype(np.float32) * 40)
+    h, g, u = oracle.glu_pair(wg, wu, xq)
+    xd = oracle.dequantize(xq)
+    gb, ub = xd @ oracle.dequantize(wg).T, xd @ oracle.dequantize(wu).T
+    np.testing.assert_allclose(g, gb, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(u, ub, rtol=1e-12, atol=1e-12)
+    assert np.abs(gb).max() > 7 and np.abs(ub).max() > 7
+    gc = np.minimum(gb, 7.0)
+    hb = gc / (1.0 + np.exp(-gc)) * np.clip(ub, -7.0, 7.0)
+    np.testing.assert_allclose(h, hb, rtol=1e-12, atol=1e-12)
+    swapped = oracle.swiglu_ds4(ub, gb)                    # planted: gate and up swapped
+    assert not np.allclose(swapped, h, rtol=1e-6, atol=1e-9)
+    # expert_ffn at an intermediate size of one block (32 values)
+    wg2 = oracle.quantize_q8_0(rng.normal(0, 0.02, (32, 256)).astype(np.float32))
+    wu2 = oracle.quantize_q8_0(rng.normal(0, 0.02, (32, 256)).astype(np.float32))
+    r = oracle.expert_ffn(wg2, wu2, wd, xq[1:2])
+    g2 = oracle.dequantize(wg2) @ xd[1]
+    u2 = oracle.dequantize(wu2) @ xd[1]
+    g2c = np.minimum(g2, 7.0)
+    h2 = (g2c / (1.0 + np.exp(-g2c)) * np.clip(u2, -7.0, 7.0)).astype(np.float32)
+    hq2 = oracle.quantize_q8_1(h2[None])
+    assert r["hq"].tobytes() == hq2[0].tobytes()
+    np.testing.assert_allclose(r["y"], oracle.dequantize(wd) @ oracle.dequantize(hq2)[0],
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_every_oracle_function_is_pinned_here():
+    # every public function of the oracle module is exercised by a pin in this
+    # file (a function no CPU test calls would be trusted unchecked)
+    import inspect
+    with open(__file__) as f:
+        src = f.read()
+    names = [n for n, fn in inspect.getmembers(ref, inspect.isfunction)
+             if fn.__module__ == ref.__name__ and not n.startswith("_")]
+    missing = [n for n in names if f"oracle.{n}(" not in src and f"ref.{n}(" not in src]
+    assert not missing, missing
