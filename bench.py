@@ -57,6 +57,11 @@ def parse():
                     help="skip the 8-bit exchange codec measurement")
     ap.add_argument("--no-q4", action="store_true",
                     help="skip the 4-bit expert-weight sweep")
+    ap.add_argument("--sweep-cols", default="",
+                    help="comma-separated column counts of the sweep (default 1,2,4,5,8)")
+    ap.add_argument("--only-sweep", action="store_true",
+                    help="run the column sweep alone (profiling runs); the JSON line then "
+                         "carries the sweep only")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the oracle sample")
     ap.add_argument("--pmc-copy", action="store_true",
@@ -73,19 +78,22 @@ class Bank:
     """Routed experts of L layers x E local experts, plus optional shared
     expert (full matrices per layer), filled with synthetic Q8_0 blocks."""
 
-    def __init__(self, moeq8, torch, layers, n_local, hidden, inter, seed, shared_inter=0):
+    def __init__(self, moeq8, torch, layers, n_local, hidden, inter, seed, shared_inter=0, layer0=0):
         self.layers, self.n_local, self.hidden, self.inter = layers, n_local, hidden, inter
         rb_h = hidden // 32 * 34
         rb_i = inter // 32 * 34
         self.expert_gu = inter * rb_h
         self.expert_d = hidden * rb_i
         dev = "cuda"
-        self.gate = torch.empty((layers, n_local * self.expert_gu), dtype=torch.uint8, device=dev)
-        self.up = torch.empty_like(self.gate)
+        # a layer's gate and up banks are adjacent (one region for a streaming read)
+        self.gu = torch.empty((layers, 2, n_local * self.expert_gu), dtype=torch.uint8, device=dev)
+        self.gate = self.gu[:, 0]
+        self.up = self.gu[:, 1]
         self.down = torch.empty((layers, n_local * self.expert_d), dtype=torch.uint8, device=dev)
         for t, m, blocks in ((self.gate, 0, inter * hidden // 32), (self.up, 1, inter * hidden // 32),
                              (self.down, 2, hidden * inter // 32)):
-            moeq8.synth_q8_0_fill(t, layers * n_local, blocks, n_local, seed, 0, 0, m)
+            for l in range(layers):
+                moeq8.synth_q8_0_fill(t[l], n_local, blocks, n_local, seed, layer0 + l, 0, m)
         self.shared_inter = shared_inter
         if shared_inter:
             self.sgate = torch.empty((layers, shared_inter * rb_h), dtype=torch.uint8, device=dev)
@@ -316,6 +324,10 @@ def main():
     from quantized_moe_expert_q8_amd import moe_layer as ml
 
     torch.cuda.init()
+    if args.only_sweep:
+        print(json.dumps({"metric": "routed-expert MMVQ column sweep (profiling run)",
+                          "sweep": sweep(torch, workloads, moeq8, ml, args)}), flush=True)
+        return
     cfg = dict(workloads.CONFIGS["ep_share_l43_e128_c8"], name="ep_share_l43_e128_c8")
     L, n_local, n_exp = cfg["layers"], cfg["local_experts"], cfg["experts"]
     hidden, inter, topk, seed, cols = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["seed"], cfg["cols"][0]
@@ -524,82 +536,147 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+ROTATION_BYTES = 1.0e9      # bytes every timed sweep graph reads per replay, at least
+
+
+def best_ceiling(torch, moeq8, regions, reps, sink):
+    """The streaming-read ceiling of a graph of launches: regions is one
+    (tensor, bytes) per launch; each shape of the plain read is timed as a
+    graph of one read per region, and the fastest mean per launch (us) and its
+    shape are returned."""
+    best = None
+    for wg in moeq8.STREAM_READ_SHAPES:
+        def fn(wg=wg):
+            for t, b in regions:
+                moeq8.stream_read_shape(t, b, wg, sink)
+        us = time_graph(torch, fn, reps) / len(regions) * 1e3
+        if best is None or us < best[0]:
+            best = (us, wg)
+    return best
+
+
+def sweep_replicas(torch, workloads, moeq8, cols, hidden, inter, topk, n_exp, seed):
+    """Replica layers of the 256-expert routed layer at `cols` columns until
+    the down launches of one rotation read at least ROTATION_BYTES.  Each
+    replica draws its own x, logits and bias (seeded by its index) and is
+    routed once here; its bank stores only the experts that routing selects,
+    in slots 0..D-1, and its owner map sends those experts to their slots and
+    every other expert to -1.  The top-k runs over all 256 experts whatever
+    the owner map says, so the layer selects, weights and computes exactly as
+    with all 256 experts stored, and its launches read the same bytes; the
+    replicas only stop the 256 MB Infinity Cache from serving a rotation."""
+    dn_expert = hidden * (inter // 32 * 34)
+    reps, total = [], 0
+    while total < ROTATION_BYTES:
+        l = len(reps)
+        x = torch.from_numpy(workloads.activations(seed, cols, hidden, layer=l)).cuda()
+        lg = torch.from_numpy(workloads.router_logits(seed, cols, n_exp, layer=l)).cuda()
+        bs = torch.from_numpy(workloads.router_bias(seed, n_exp, layer=l)).cuda()
+        ids, _, _ = moeq8.moe_route_topk(lg, topk, bias=bs)
+        sel = sorted(set(int(e) for e in ids.cpu().numpy().reshape(-1)))
+        owner = np.full(n_exp, -1, np.int32)
+        owner[sel] = np.arange(len(sel), dtype=np.int32)
+        reps.append({"x": x, "logits": lg, "bias": bs, "owner": torch.from_numpy(owner).cuda(),
+                     "n_local": len(sel)})
+        total += len(sel) * dn_expert
+    return reps
+
+
 def sweep(torch, workloads, moeq8, ml, args):
-    """Routed layer, 256 experts, top-8, at 1..8 columns; 4 weight replicas
-    (13.7 GB) rotate so the 256 MB Infinity Cache cannot serve the reads.
-    Per column count: the layer (graph of the four-launch layers), the grouped
-    gate/up launch and the grouped down launch alone (graphs of their
-    launches, HIP events), the two together as the routed-expert MMVQ (their
-    bytes over their summed times), and the streaming-read ceiling for the
-    gate/up's bytes per launch."""
+    """Routed layer, 256 experts, top-8, at 1..8 columns, on replica layers
+    that rotate at least ROTATION_BYTES through every timed graph (the down
+    launches, the smallest, included), so the 256 MB Infinity Cache cannot
+    serve the reads.  Per column count: the layer (graph of the four-launch
+    layers), the grouped gate/up launch and the grouped down launch alone
+    (graphs of their launches, HIP events), the two together as the
+    routed-expert MMVQ (their bytes over their summed times), and
+    streaming-read ceilings of the same buffers at the gate/up's and the
+    down's bytes per launch (best of the read shapes)."""
     cfg = workloads.CONFIGS["verify_e256_c5"]
     hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
-    reps = 4
-    bank = Bank(moeq8, torch, reps, n_exp, hidden, inter, 4)
-    bank.pack_weights(moeq8, torch)
+    cols_list = [int(c) for c in args.sweep_cols.split(",")] if args.sweep_cols else (1, 2, 4, 5, 8)
     sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    rb_h, rb_i = hidden // 32 * 34, inter // 32 * 34
     out = []
-    for cols in (1, 2, 4, 5, 8):
-        xs, lgs, bs = layer_inputs(torch, workloads, 4, reps, cols, hidden, n_exp)
-        wss = [ml.Workspace(cols, hidden, inter, topk, 0, "cuda") for _ in range(reps)]
-        experts = [bank.experts(ml, l) for l in range(reps)]
+    for cols in cols_list:
+        reps = sweep_replicas(torch, workloads, moeq8, cols, hidden, inter, topk, n_exp, 4)
+        R = len(reps)
+        banks = []
+        for l, rp in enumerate(reps):
+            b = Bank(moeq8, torch, 1, rp["n_local"], hidden, inter, 4, layer0=l)
+            b.pack_weights(moeq8, torch)
+            banks.append(b)
+        wss = [ml.Workspace(cols, hidden, inter, topk, 0, "cuda") for _ in range(R)]
+        experts = [b.experts(ml, 0) for b in banks]
 
         def step():
-            for l in range(reps):
-                ml.forward(xs[l], lgs[l], bs[l], None, n_exp, experts[l], None, wss[l])
+            for l in range(R):
+                rp = reps[l]
+                ml.forward(rp["x"], rp["logits"], rp["bias"], rp["owner"], rp["n_local"], experts[l], None,
+                           wss[l])
 
         step()
         torch.cuda.synchronize()
         n_active, n_valid = [], []
-        for l in range(reps):
+        for l in range(R):
             words = wss[l].grouping.cpu().numpy().view(np.int32)
             n_active.append(int(words[0]))
             n_valid.append(int(words[1]))
+            assert n_active[l] == reps[l]["n_local"]
         n = max(20, args.steps)
-        ms = time_graph(torch, step, n) / reps
+        ms = time_graph(torch, step, n) / R
         lb = float(np.mean([layer_bytes(n_active[l], n_valid[l], cols, hidden, inter, topk, 0)
-                            for l in range(reps)]))
+                            for l in range(R)]))
 
         def gate_up_only():
-            for l in range(reps):
+            for l in range(R):
                 moeq8.moe_grouped_mmvq_ex(moeq8.GATE_UP_SWIGLU_P64, experts[l].gate, experts[l].up, wss[l].xq,
-                                       wss[l].grouping, n=inter, k=hidden, n_local_expert=n_exp,
-                                       ncols=cols, topk=topk, out=wss[l].h)
-
-        gu_b = [gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter) for l in range(reps)]
-        read_b = [int(b) // 16 * 16 for b in gu_b]
-
-        def stream_only():
-            for l in range(reps):
-                moeq8.stream_read(bank.gate[l], read_b[l], sink)
+                                          wss[l].grouping, n=inter, k=hidden, n_local_expert=reps[l]["n_local"],
+                                          ncols=cols, topk=topk, out=wss[l].h)
 
         def down_only():
-            for l in range(reps):
+            for l in range(R):
                 moeq8.moe_grouped_mmvq_ex(moeq8.DOWN_F32_ACT_P64, experts[l].down, None,
-                                       wss[l].h.view(cols * topk, inter), wss[l].grouping, n=hidden,
-                                       k=inter, n_local_expert=n_exp, ncols=cols, topk=topk, out=wss[l].y)
+                                          wss[l].h.view(cols * topk, inter), wss[l].grouping, n=hidden,
+                                          k=inter, n_local_expert=reps[l]["n_local"], ncols=cols, topk=topk,
+                                          out=wss[l].y)
 
-        dn_b = [down_launch_bytes(n_active[l], n_valid[l], hidden, inter) for l in range(reps)]
-        gu_us = time_graph(torch, gate_up_only, n) / reps * 1e3
-        dn_us = time_graph(torch, down_only, n) / reps * 1e3
-        st_us = time_graph(torch, stream_only, n) / reps * 1e3
+        gu_b = [gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter) for l in range(R)]
+        dn_b = [down_launch_bytes(n_active[l], n_valid[l], hidden, inter) for l in range(R)]
+        gu_us = time_graph(torch, gate_up_only, n) / R * 1e3
+        dn_us = time_graph(torch, down_only, n) / R * 1e3
+        # ceilings: one plain read per launch of the replica's own weights
+        # (its gate and up banks, adjacent, in one read; its down bank)
+        gu_w = [n_active[l] * inter * rb_h for l in range(R)]
+        dn_w = [n_active[l] * hidden * rb_i for l in range(R)]
+        st_gu_us, st_gu_wg = best_ceiling(
+            torch, moeq8, [(banks[l].gu[0], 2 * gu_w[l] // 16 * 16) for l in range(R)], n, sink)
+        st_dn_us, st_dn_wg = best_ceiling(
+            torch, moeq8, [(banks[l].down[0], dn_w[l] // 16 * 16) for l in range(R)], n, sink)
         gu_gbps = float(np.mean(gu_b)) / (gu_us * 1e-6) / 1e9
         dn_gbps = float(np.mean(dn_b)) / (dn_us * 1e-6) / 1e9
         both_gbps = float(np.mean(gu_b) + np.mean(dn_b)) / ((gu_us + dn_us) * 1e-6) / 1e9
-        st_gbps = float(np.mean(read_b)) / (st_us * 1e-6) / 1e9
-        rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2),
+        st_gu_gbps = 2 * float(np.mean(gu_w)) / (st_gu_us * 1e-6) / 1e9
+        st_dn_gbps = float(np.mean(dn_w)) / (st_dn_us * 1e-6) / 1e9
+        rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2), "replicas": R,
+               "rotation_bytes": {"layer": int(sum(n_active[l] * ml.expert_bytes(hidden, inter) for l in range(R))),
+                                  "gate_up": int(sum(gu_b)), "down": int(sum(dn_b))},
                "layer_us": round(ms * 1e3, 2), "layers_per_s": round(1e3 / ms, 1),
                "effective_gbps": round(lb / (ms * 1e-3) / 1e9, 1),
                "gate_up_us": round(gu_us, 2), "gate_up_gbps": round(gu_gbps, 1),
                "gate_up_frac_of_peak": round(gu_gbps / HBM_PEAK_GBPS, 4),
                "down_us": round(dn_us, 2), "down_gbps": round(dn_gbps, 1),
+               "down_frac_of_peak": round(dn_gbps / HBM_PEAK_GBPS, 4),
                "routed_mmvq_gbps": round(both_gbps, 1),
                "routed_mmvq_frac_of_peak": round(both_gbps / HBM_PEAK_GBPS, 4),
-               "ceiling_gbps": round(st_gbps, 1), "gate_up_frac_of_ceiling": round(gu_gbps / st_gbps, 4)}
+               "gate_up_ceiling_gbps": round(st_gu_gbps, 1), "gate_up_ceiling_wg_bytes": st_gu_wg,
+               "gate_up_frac_of_ceiling": round(gu_gbps / st_gu_gbps, 4),
+               "down_ceiling_gbps": round(st_dn_gbps, 1), "down_ceiling_wg_bytes": st_dn_wg,
+               "down_frac_of_ceiling": round(dn_gbps / st_dn_gbps, 4)}
         log(f"sweep {rec}")
         out.append(rec)
-    del bank
-    torch.cuda.empty_cache()
+        del banks, experts, wss, reps
+        torch.cuda.empty_cache()
     return out
 
 

@@ -54,6 +54,14 @@ int moeq8_synth_q8_0_fill(void* dst, int64_t n_mats, int64_t blocks_per_mat,
  * on `stream`; returns 0 or a negative moeq8 status. */
 int moeq8_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
+/* The same read with `wg_bytes` (8192, 16384, 32768 or 65536) bytes a
+ * workgroup; moeq8_stream_read is wg_bytes = 65536.  Which shape reads a given
+ * byte count fastest depends on the count (ramp and tail against the number of
+ * workgroups), so a ceiling is taken as the best of the shapes.  Other
+ * wg_bytes values are MOEQ8_EINVAL. */
+int moeq8_stream_read_shape(const void* buf, int64_t bytes, int64_t wg_bytes, uint32_t* sink,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

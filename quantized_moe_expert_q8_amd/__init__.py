@@ -42,4 +42,6 @@ from .ops import (  # noqa: F401
     moe_grouped_mmvq_q4,
     synth_q8_0_fill,
     stream_read,
+    stream_read_shape,
+    STREAM_READ_SHAPES,
 )

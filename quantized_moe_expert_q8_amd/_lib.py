@@ -54,6 +54,7 @@ SIGNATURES = {
     "moeq8_synth_q8_0_fill": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_u32, c_u32, c_u32,
                                              c_u32, c_vp]),
     "moeq8_stream_read": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp]),
+    "moeq8_stream_read_shape": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp]),
 }
 
 _LIB = None

@@ -1,9 +1,9 @@
 // The 8-bit block exchange codec of the prefill partials (lucebox PR #826,
 // the 8-bit prefill exchange commit): a partial is sent as blocks of 32 int8
-// values with one f32 scale (1.125 bytes a value against 2 for bf16), the
-// blocks of every rank are gathered, and every rank sums the ranks'
-// dequantized values in rank order, so all ranks get the same result.  The
-// gather itself crosses devices and is not here; these are the two HBM-bound
+// values with one f32 scale (1.125 bytes a value against 2 for bf16), all
+// ranks' blocks are gathered, and the decode adds the per-rank fp32 products
+// in ascending rank order from +0, which gives identical bits on every rank.
+// The gather itself crosses devices and is not here; these are the two HBM-bound
 // kernels on either side of it.
 //
 // Block: {f32 d; int8 qs[32]} (36 bytes).  d = amax / 127 in fp32 (kept in

@@ -76,32 +76,48 @@ extern "C" int moeq8_synth_q8_0_fill(void* dst, int64_t n_mats, int64_t blocks_p
 namespace {
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-constexpr int64_t STREAM_WG_BYTES = 64 * 1024;
 
+// WG_BYTES bytes a workgroup of 256 threads, every load issued before the
+// first use, nontemporal 16-byte loads.
+template <int WG_BYTES>
 __global__ __launch_bounds__(256) void k_stream_read(const u32x4v* __restrict__ p, int64_t n16,
                                                      uint32_t* sink) {
-    const int64_t base = (int64_t)blockIdx.x * (STREAM_WG_BYTES / 16);
-    u32x4v v[STREAM_WG_BYTES / 16 / 256];
+    constexpr int PER = WG_BYTES / 16 / 256;
+    const int64_t base = (int64_t)blockIdx.x * (WG_BYTES / 16);
+    u32x4v v[PER];
 #pragma unroll
-    for (int i = 0; i < STREAM_WG_BYTES / 16 / 256; ++i) {
+    for (int i = 0; i < PER; ++i) {
         const int64_t idx = base + i * 256 + threadIdx.x;
         v[i] = idx < n16 ? __builtin_nontemporal_load(p + idx) : u32x4v{0u, 0u, 0u, 0u};
     }
     uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < STREAM_WG_BYTES / 16 / 256; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    for (int i = 0; i < PER; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
 }  // namespace
 
-extern "C" int moeq8_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+extern "C" int moeq8_stream_read_shape(const void* buf, int64_t bytes, int64_t wg_bytes, uint32_t* sink,
+                                       void* stream) {
     if (!buf || !sink || bytes < 0) return MOEQ8_EINVAL;
+    if (wg_bytes != 8192 && wg_bytes != 16384 && wg_bytes != 32768 && wg_bytes != 65536) return MOEQ8_EINVAL;
     if ((((uintptr_t)buf) & 15u) || (bytes & 15) || (((uintptr_t)sink) & 3u)) return MOEQ8_EALIGN;
     if (bytes == 0) return MOEQ8_OK;
-    const int64_t blocks = (bytes + STREAM_WG_BYTES - 1) / STREAM_WG_BYTES;
+    const int64_t blocks = (bytes + wg_bytes - 1) / wg_bytes;
     if (blocks > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
-    hipLaunchKernelGGL(k_stream_read, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream,
-                       (const u32x4v*)buf, bytes / 16, sink);
+    const dim3 grid((uint32_t)blocks), block(256);
+    const hipStream_t s = (hipStream_t)stream;
+    const u32x4v* p = (const u32x4v*)buf;
+    switch (wg_bytes) {
+        case 8192: hipLaunchKernelGGL(k_stream_read<8192>, grid, block, 0, s, p, bytes / 16, sink); break;
+        case 16384: hipLaunchKernelGGL(k_stream_read<16384>, grid, block, 0, s, p, bytes / 16, sink); break;
+        case 32768: hipLaunchKernelGGL(k_stream_read<32768>, grid, block, 0, s, p, bytes / 16, sink); break;
+        default: hipLaunchKernelGGL(k_stream_read<65536>, grid, block, 0, s, p, bytes / 16, sink); break;
+    }
     return moeq8::check_launch();
+}
+
+extern "C" int moeq8_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    return moeq8_stream_read_shape(buf, bytes, 65536, sink, stream);
 }

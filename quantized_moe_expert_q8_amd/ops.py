@@ -645,3 +645,16 @@ def stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, offset_bytes
     _need(buf, "buf", nbytes, offset_bytes)
     _need(sink, "sink", 4)
     call("moeq8_stream_read", _ptr(buf, offset_bytes), nbytes, _ptr(sink), _stream(buf))
+
+
+STREAM_READ_SHAPES = (8192, 16384, 32768, 65536)
+
+
+def stream_read_shape(buf: torch.Tensor, nbytes: int, wg_bytes: int, sink: torch.Tensor,
+                      offset_bytes: int = 0):
+    """stream_read with wg_bytes (one of STREAM_READ_SHAPES) bytes a workgroup."""
+    _cuda(buf, "buf")
+    _cuda(sink, "sink")
+    _need(buf, "buf", nbytes, offset_bytes)
+    _need(sink, "sink", 4)
+    call("moeq8_stream_read_shape", _ptr(buf, offset_bytes), nbytes, wg_bytes, _ptr(sink), _stream(buf))

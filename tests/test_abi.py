@@ -141,6 +141,9 @@ def test_other_validation():
     assert L.moeq8_stream_read(P + 4, 64, P, None) == -2                         # misaligned buffer
     assert L.moeq8_stream_read(P, 24, P, None) == -2                             # bytes % 16
     assert L.moeq8_stream_read(P, 0, P, None) == 0
+    assert L.moeq8_stream_read_shape(P, 64, 4096, P, None) == -1                # not a read shape
+    assert L.moeq8_stream_read_shape(P, 24, 8192, P, None) == -2                # bytes % 16
+    assert L.moeq8_stream_read_shape(P, 0, 16384, P, None) == 0
 
 
 def test_packed_layout_validation():

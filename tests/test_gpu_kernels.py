@@ -896,6 +896,15 @@ def test_stream_read_reads_every_word(where):
     moeq8.stream_read(buf, n - 16, clean, offset_bytes=16 if where == "first" else 0)
     torch.cuda.synchronize()
     assert int(host(clean.view(torch.int32))[0]) == 0
+    # every read shape, the same way
+    for wg in moeq8.STREAM_READ_SHAPES:
+        sink.zero_()
+        clean.zero_()
+        moeq8.stream_read_shape(buf, n, wg, sink)
+        moeq8.stream_read_shape(buf, n - 16, wg, clean, offset_bytes=16 if where == "first" else 0)
+        torch.cuda.synchronize()
+        assert int(host(sink.view(torch.int32))[0]) == 0x9E3779B9 - (1 << 32), wg
+        assert int(host(clean.view(torch.int32))[0]) == 0, wg
 
 
 # ---------------------------------------------------------------------------
