@@ -85,11 +85,13 @@ class Bank:
         self.expert_gu = inter * rb_h
         self.expert_d = hidden * rb_i
         dev = "cuda"
-        # a layer's gate and up banks are adjacent (one region for a streaming read)
-        self.gu = torch.empty((layers, 2, n_local * self.expert_gu), dtype=torch.uint8, device=dev)
-        self.gate = self.gu[:, 0]
-        self.up = self.gu[:, 1]
-        self.down = torch.empty((layers, n_local * self.expert_d), dtype=torch.uint8, device=dev)
+        # a layer's gate, up and down banks are adjacent (one region for a
+        # streaming read of any leading part)
+        ng, nd = n_local * self.expert_gu, n_local * self.expert_d
+        self.w = torch.empty((layers, 2 * ng + nd), dtype=torch.uint8, device=dev)
+        self.gate = self.w[:, :ng]
+        self.up = self.w[:, ng:2 * ng]
+        self.down = self.w[:, 2 * ng:]
         for t, m, blocks in ((self.gate, 0, inter * hidden // 32), (self.up, 1, inter * hidden // 32),
                              (self.down, 2, hidden * inter // 32)):
             for l in range(layers):
@@ -650,14 +652,18 @@ def sweep(torch, workloads, moeq8, ml, args):
         gu_w = [n_active[l] * inter * rb_h for l in range(R)]
         dn_w = [n_active[l] * hidden * rb_i for l in range(R)]
         st_gu_us, st_gu_wg = best_ceiling(
-            torch, moeq8, [(banks[l].gu[0], 2 * gu_w[l] // 16 * 16) for l in range(R)], n, sink)
+            torch, moeq8, [(banks[l].w[0], 2 * gu_w[l] // 16 * 16) for l in range(R)], n, sink)
         st_dn_us, st_dn_wg = best_ceiling(
             torch, moeq8, [(banks[l].down[0], dn_w[l] // 16 * 16) for l in range(R)], n, sink)
+        st_all_us, st_all_wg = best_ceiling(
+            torch, moeq8, [(banks[l].w[0], (2 * gu_w[l] + dn_w[l]) // 16 * 16) for l in range(R)], n, sink)
         gu_gbps = float(np.mean(gu_b)) / (gu_us * 1e-6) / 1e9
         dn_gbps = float(np.mean(dn_b)) / (dn_us * 1e-6) / 1e9
         both_gbps = float(np.mean(gu_b) + np.mean(dn_b)) / ((gu_us + dn_us) * 1e-6) / 1e9
         st_gu_gbps = 2 * float(np.mean(gu_w)) / (st_gu_us * 1e-6) / 1e9
         st_dn_gbps = float(np.mean(dn_w)) / (st_dn_us * 1e-6) / 1e9
+        st_all_gbps = float(np.mean(gu_w) * 2 + np.mean(dn_w)) / (st_all_us * 1e-6) / 1e9
+        st_pair_gbps = float(np.mean(gu_w) * 2 + np.mean(dn_w)) / ((st_gu_us + st_dn_us) * 1e-6) / 1e9
         rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2), "replicas": R,
                "rotation_bytes": {"layer": int(sum(n_active[l] * ml.expert_bytes(hidden, inter) for l in range(R))),
                                   "gate_up": int(sum(gu_b)), "down": int(sum(dn_b))},
@@ -672,7 +678,13 @@ def sweep(torch, workloads, moeq8, ml, args):
                "gate_up_ceiling_gbps": round(st_gu_gbps, 1), "gate_up_ceiling_wg_bytes": st_gu_wg,
                "gate_up_frac_of_ceiling": round(gu_gbps / st_gu_gbps, 4),
                "down_ceiling_gbps": round(st_dn_gbps, 1), "down_ceiling_wg_bytes": st_dn_wg,
-               "down_frac_of_ceiling": round(dn_gbps / st_dn_gbps, 4)}
+               "down_frac_of_ceiling": round(dn_gbps / st_dn_gbps, 4),
+               # the two launches' ceilings together, and one read of all
+               # three matrices' bytes in a single launch (what any split of
+               # the work over launches is bounded by)
+               "pair_ceiling_gbps": round(st_pair_gbps, 1),
+               "routed_mmvq_frac_of_pair_ceiling": round(both_gbps / st_pair_gbps, 4),
+               "one_read_ceiling_gbps": round(st_all_gbps, 1), "one_read_ceiling_wg_bytes": st_all_wg}
         log(f"sweep {rec}")
         out.append(rec)
         del banks, experts, wss, reps

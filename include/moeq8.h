@@ -265,6 +265,45 @@ int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,
                         int64_t s_n, int64_t s_k, int64_t s_k_block_offset, const void* s_act,
                         int64_t s_act_row_stride, float* s_out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * a6 + a7 + a8, the routed FFN product after routing, in one call: the grouped
+ * gate/up + SwiGLU-DS4 of MOEQ8_GATE_UP_SWIGLU_P64 writing h, then the grouped
+ * down of MOEQ8_DOWN_F32_ACT_P64 quantising h to q8_1 in its launch, with the
+ * shared expert's share as extra work items of both (two launches on
+ * `stream`; the pages' fused decode kernels commit runs one expert grouping
+ * for gate, up and down).
+ *   w_gate, w_up   routed experts' gate and up, packed by q8_0_pack64_rows,
+ *                  [n_local_expert][inter][hidden/32 blocks] (rows hidden/32*34
+ *                  bytes apart), experts gate_up_expert_stride_bytes apart
+ *   w_down         routed experts' down, packed by q8_0_pack64_rounds,
+ *                  [n_local_expert][hidden] rows of 1088 bytes, experts
+ *                  down_expert_stride_bytes apart
+ *   hidden == 4096, inter == 1024 (the packed layouts' shapes), else
+ *   MOEQ8_EUNSUPPORTED; 1 <= ncols <= MOEQ8_MAX_COLS
+ *   xq             q8_1 rows of x [ncols][hidden/32]
+ *   grouping       from moe_route_topk / moe_route_topk_quantize for ncols, topk
+ *   h              fp32 [ncols*topk][inter] workspace: SwiGLU-DS4 of each route
+ *                  (written by the first launch, read by the second; masked
+ *                  routes' rows not written)
+ *   y              fp32 [ncols][topk][hidden] out (masked routes' rows not
+ *                  written)
+ *   shared share (s_gate == NULL: none): s_gate, s_up rows [0, s_rows) of the
+ *                  packed shared gate/up, s_row_stride_bytes apart; s_down the
+ *                  packed shared down's round matrix of this share ([hidden]
+ *                  rows of 1088 bytes); s_rows == inter; hs fp32 [ncols][s_rows]
+ *                  workspace and ys fp32 [ncols][hidden] out, as in
+ *                  moe_grouped_mmvq_ex
+ * Both stages are checked before either is launched.  Every output is
+ * bit-identical to moe_grouped_mmvq_ex with MOEQ8_GATE_UP_SWIGLU_P64 and then
+ * MOEQ8_DOWN_F32_ACT_P64 on the same arguments.
+ * ------------------------------------------------------------------------- */
+int moe_grouped_ffn_p64(const void* w_gate, const void* w_up, const void* w_down,
+                        int64_t gate_up_expert_stride_bytes, int64_t down_expert_stride_bytes,
+                        int64_t n_local_expert, int64_t hidden, int64_t inter, const void* xq,
+                        const void* grouping, int64_t ncols, int32_t topk, float* h, float* y,
+                        const void* s_gate, const void* s_up, int64_t s_row_stride_bytes,
+                        int64_t s_rows, const void* s_down, float* hs, float* ys, void* stream);
+
 /* a1 + a4 + a5 in one launch (the layer prologue): q8_1 quantisation of the
  * ncols rows of x [ncols][x_row_stride] into xq [ncols][k/32], and
  * moe_route_topk on the logits.  Outputs are bit-identical to calling
@@ -346,10 +385,11 @@ int moe_combine_shared(const float* y, const int32_t* ids, const float* weights,
 
 /* ---------------------------------------------------------------------------
  * 8-bit block exchange codec for prefill-sized partials (PR #826, the 8-bit
- * prefill exchange commit: partials travel as blocks of 32 int8 values with
- * one f32 scale, 1.125 bytes a value, are gathered from every rank, and every
- * rank sums the ranks' dequantized values in rank order so all ranks get the
- * same result).  The gather crosses devices and is not part of this library.
+ * prefill exchange commit: a partial is carried as 32-value int8 blocks with
+ * an f32 scale each, 1.125 bytes a value; after the gather, the decode adds
+ * the per-rank fp32 products in ascending rank order from +0, so every rank
+ * computes identical bits).  The gather crosses devices and is not part of
+ * this library.
  *
  * Block: {f32 d; int8 qs[32]}, MOEQ8_EXCHANGE_BLOCK_BYTES = 36 bytes.
  *

@@ -32,6 +32,7 @@ from .ops import (  # noqa: F401
     moe_grouped_mmvq_ex,
     moe_route_topk_quantize,
     moe_combine,
+    moe_grouped_ffn_p64,
     EXCHANGE_BLOCK_BYTES,
     q8_block_encode,
     q8_block_decode_sum,

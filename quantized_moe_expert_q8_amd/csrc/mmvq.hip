@@ -111,9 +111,15 @@ __device__ __forceinline__ float chain_groups(float v, int lane) {
 // read once) unless REREAD: a launch whose items make several passes of
 // MAX_COLS columns over the same rows takes ordinary loads, whose lines stay
 // in L2 for the next pass.
+//
+// MC: the columns of one pass (accumulators are kept for MC columns).  A
+// launch whose groups hold at most MC routes each runs one pass; decode
+// launches take the smallest of 1, 2, 4, 8 that covers their columns, so
+// fewer registers are held and more waves fit on a SIMD.
 template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false,
-          bool REREAD = false>
+          bool REREAD = false, int MC = MAX_COLS>
 __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
+    static_assert(MC == MAX_COLS || (P64 && !REREAD), "narrow passes serve the packed decode stages");
     static_assert(!REREAD || P64, "REREAD selects the packed weights' load kind");
     static_assert(!P64 || (!Q4 && !STX && ((G == 4 && !ACT_F32) || (G == 1 && NMAT == 1 && ACT_F32))),
                   "the packed layouts serve the four-group gate/up rows and the one-group down quads");
@@ -210,11 +216,11 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
     }
     const int64_t row_base = row_block * rows_per_wg + (int64_t)wave * (U * RPW) + rslot;
 
-    for (int c0 = 0; c0 < ncols; c0 += MAX_COLS) {
-        const int nc = min(ncols - c0, MAX_COLS);
-        float acc[MAX_COLS][U][NMAT];
+    for (int c0 = 0; c0 < ncols; c0 += MC) {
+        const int nc = min(ncols - c0, MC);
+        float acc[MC][U][NMAT];
 #pragma unroll
-        for (int c = 0; c < MAX_COLS; ++c)
+        for (int c = 0; c < MC; ++c)
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -266,22 +272,22 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
         if constexpr (!ACT_F32) load_weights(0);
 
         // output row and activation row of each column of this pass
-        int orow[MAX_COLS];
-        int arow[MAX_COLS];
+        int orow[MC];
+        int arow[MC];
         int8w w8 = {};
         if constexpr (GROUPED) {
             // the route entries of this pass as one eight-word read (words
             // past the pass's nc columns are read but not used)
             if (routed) w8 = grouping_words8(grouping, 4 + 2 * R + 1 + route_begin + c0);
 #pragma unroll
-            for (int c = 0; c < MAX_COLS; ++c) {
+            for (int c = 0; c < MC; ++c) {
                 const int r = (c >= nc || w8[c] < 0 || w8[c] >= R) ? -1 : w8[c];
                 orow[c] = routed ? r : c0 + c;
                 arow[c] = routed ? (r < 0 ? 0 : (int)(((uint64_t)r * act_route_mul) >> 32)) : c0 + c;
             }
         } else {
 #pragma unroll
-            for (int c = 0; c < MAX_COLS; ++c) {
+            for (int c = 0; c < MC; ++c) {
                 orow[c] = c0 + c;
                 arow[c] = c0 + c;
             }
@@ -302,7 +308,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                 const int pos = k * 1024 + lane * 16;
                 int c = 0;
 #pragma unroll
-                for (int q = 1; q < MAX_COLS; ++q) c += (pos >= q * (int)act_row_bytes) ? 1 : 0;
+                for (int q = 1; q < MC; ++q) c += (pos >= q * (int)act_row_bytes) ? 1 : 0;
                 int ar = c0 + c;
                 if (routed) {
                     const int r = w8[c];                   // c < nc wherever pos < total
@@ -369,7 +375,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
         for (int s = 0; s < nsteps; ++s) {
             if (s > 0) load_weights(s);
 #pragma unroll
-            for (int c = 0; c < MAX_COLS; ++c) {
+            for (int c = 0; c < MC; ++c) {
                 if (c < nc) {
                     XChunk xc;
                     if constexpr (ACT_F32 || STX) {
@@ -396,7 +402,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 
         // reduce: chain the groups of a row in round order, then the 16-lane tree
         float* out = (GROUPED && !routed) ? s_out : out0;
-        if constexpr (MAX_COLS * U <= 16) {
+        if constexpr (MC * U <= 16) {
             // Every lane of the 16 ends the tree with every (column, row set)
             // value, and each such pair has a lane of its own (lane c*U + u):
             // each lane keeps its pair's values and finishes it alone, so the
@@ -408,7 +414,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             int sel_orow = -1;
             int sel_u = 0;
 #pragma unroll
-            for (int c = 0; c < MAX_COLS; ++c) {
+            for (int c = 0; c < MC; ++c) {
                 if (c < nc) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -439,7 +445,7 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
             continue;
         }
 #pragma unroll
-        for (int c = 0; c < MAX_COLS; ++c) {
+        for (int c = 0; c < MC; ++c) {
             if (c < nc) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -470,10 +476,10 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
 // One work item = one row block: of one active expert (grouped), of the dense
 // extra matrix (grouped launches with a shared part), or of the one matrix.
 template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4, bool P64 = false,
-          bool REREAD = false>
+          bool REREAD = false, int MC = MAX_COLS>
 __global__ __launch_bounds__(64 * WAVES_PER_WG) void k_mmvq(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_act[];
-    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX, Q4, P64, REREAD>(p, blockIdx.x, lds_act);
+    mmvq_item<G, NMAT, U, GROUPED, ACT_F32, STX, Q4, P64, REREAD, MC>(p, blockIdx.x, lds_act);
 }
 
 __global__ void k_swiglu_ds4(const float* g, const float* u, int64_t count, float* h) {
@@ -546,22 +552,25 @@ int launch_p64(bool down, MmvqParams& p, const Shape& s, int64_t grid, size_t ld
     // a grouping wider than one pass can give an expert several passes
     const bool reread = p.ncols > MAX_COLS;
     const dim3 block(64 * WAVES_PER_WG);
+    const dim3 g((uint32_t)grid);
+    // a decode grouping's groups hold at most ncols routes (top-k picks
+    // distinct experts per column), so one pass of the next power of two
+    // covers them
+    const int mc = p.ncols <= 1 ? 1 : p.ncols <= 2 ? 2 : p.ncols <= 4 ? 4 : 8;
     if (down) {
         constexpr int U = u_for(1, true, false);
-        if (reread)
-            hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, true>), dim3((uint32_t)grid),
-                               block, lds, stream, p);
-        else
-            hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true>), dim3((uint32_t)grid),
-                               block, lds, stream, p);
+        if (reread) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, true>), g, block, lds, stream, p);
+        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, false, 1>), g, block, lds, stream, p);
+        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, false, 2>), g, block, lds, stream, p);
+        else if (mc == 4) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, false, 4>), g, block, lds, stream, p);
+        else hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true>), g, block, lds, stream, p);
     } else {
         constexpr int U = u_for(2, false, false);
-        if (reread)
-            hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, true>), dim3((uint32_t)grid),
-                               block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), dim3((uint32_t)grid),
-                               block, 0, stream, p);
+        if (reread) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, true>), g, block, 0, stream, p);
+        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, false, 1>), g, block, 0, stream, p);
+        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, false, 2>), g, block, 0, stream, p);
+        else if (mc == 4) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, false, 4>), g, block, 0, stream, p);
+        else hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), g, block, 0, stream, p);
     }
     return check_launch();
 }
@@ -678,14 +687,23 @@ extern "C" int swiglu_ds4(const float* g, const float* u, int64_t count, float* 
 
 namespace moeq8 {
 namespace {
-int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
-                 int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
-                 int64_t n_local_expert, int64_t n, int64_t k, const void* act,
-                 int64_t act_row_stride, const void* grouping, int64_t ncols,
-                 int32_t topk, float* out, const void* s_a, const void* s_b,
-                 int64_t s_row_stride_bytes, int64_t s_n, int64_t s_k,
-                 int64_t s_k_block_offset, const void* s_act,
-                 int64_t s_act_row_stride, float* s_out, void* stream) {
+// A grouped launch's parameters, grid and LDS, after the host checks.
+struct GroupedLaunch {
+    MmvqParams p;
+    Shape s;
+    int64_t grid;
+    size_t lds;
+    bool pair, f32, p64, p64d;
+};
+
+int prepare_grouped(GroupedLaunch& L, bool q4, int32_t stage, const void* w_a, const void* w_b,
+                    int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                    int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                    int64_t act_row_stride, const void* grouping, int64_t ncols,
+                    int32_t topk, float* out, const void* s_a, const void* s_b,
+                    int64_t s_row_stride_bytes, int64_t s_n, int64_t s_k,
+                    int64_t s_k_block_offset, const void* s_act,
+                    int64_t s_act_row_stride, float* s_out) {
     const int64_t bb = q4 ? Q4_BYTES : Q80_BYTES;
     if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_DOWN_F32_ACT &&
         stage != MOEQ8_GATE_UP_SWIGLU_P64 && stage != MOEQ8_DOWN_F32_ACT_P64)
@@ -747,6 +765,7 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
             return MOEQ8_EUNSUPPORTED;
         if (((uintptr_t)w_a | (uint64_t)expert_stride_bytes | (uintptr_t)s_a) & 15u) return MOEQ8_EALIGN;
     }
+    L.grid = 0;                                    // nothing to launch unless set below
     if (n == 0 && (!has_s || s_n == 0)) return MOEQ8_OK;
 
     MmvqParams p = {};
@@ -791,19 +810,92 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
     }
     const size_t lds = f32 ? (size_t)MAX_COLS * (size_t)p.act_row_bytes : 0;
     if (lds > 64 * 1024) return MOEQ8_EUNSUPPORTED;
+    p.nsteps = s.nsteps;
+    L.p = p;
+    L.s = s;
+    L.grid = grid;
+    L.lds = lds;
+    L.pair = pair;
+    L.f32 = f32;
+    L.p64 = p64;
+    L.p64d = p64d;
+    return MOEQ8_OK;
+}
+
+int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
+                 int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
+                 int64_t n_local_expert, int64_t n, int64_t k, const void* act,
+                 int64_t act_row_stride, const void* grouping, int64_t ncols,
+                 int32_t topk, float* out, const void* s_a, const void* s_b,
+                 int64_t s_row_stride_bytes, int64_t s_n, int64_t s_k,
+                 int64_t s_k_block_offset, const void* s_act,
+                 int64_t s_act_row_stride, float* s_out, void* stream) {
+    GroupedLaunch L;
+    const int st = prepare_grouped(L, q4, stage, w_a, w_b, expert_stride_bytes, w_row_stride_bytes,
+                                   n_local_expert, n, k, act, act_row_stride, grouping, ncols, topk, out,
+                                   s_a, s_b, s_row_stride_bytes, s_n, s_k, s_k_block_offset, s_act,
+                                   s_act_row_stride, s_out);
+    if (st != MOEQ8_OK) return st;
+    if (n == 0 && (!s_a || s_n == 0)) return MOEQ8_OK;
+    MmvqParams& p = L.p;
+    const Shape& s = L.s;
+    const int64_t grid = L.grid;
+    const size_t lds = L.lds;
     const hipStream_t hs = (hipStream_t)stream;
     if (q4) {
-        if (pair) return launch_mmvq<2, true, false, true>(p, s, grid, 0, hs);
-        if (f32) return launch_mmvq<1, true, true, true>(p, s, grid, lds, hs);
+        if (L.pair) return launch_mmvq<2, true, false, true>(p, s, grid, 0, hs);
+        if (L.f32) return launch_mmvq<1, true, true, true>(p, s, grid, lds, hs);
         return launch_mmvq<1, true, false, true>(p, s, grid, 0, hs);
     }
-    if (p64 || p64d) return launch_p64(p64d, p, s, grid, lds, hs);
-    if (pair) return launch_mmvq<2, true, false, false>(p, s, grid, 0, hs);
-    if (f32) return launch_mmvq<1, true, true, false>(p, s, grid, lds, hs);
+    if (L.p64 || L.p64d) return launch_p64(L.p64d, p, s, grid, lds, hs);
+    if (L.pair) return launch_mmvq<2, true, false, false>(p, s, grid, 0, hs);
+    if (L.f32) return launch_mmvq<1, true, true, false>(p, s, grid, lds, hs);
     return launch_mmvq<1, true, false, false>(p, s, grid, 0, hs);
+}
+
+// The routed FFN product after routing: the packed gate/up stage (h written
+// to the caller's buffer), then the packed down stage reading h, two launches
+// on the caller's stream.
+int ffn_impl(const void* w_gate, const void* w_up, const void* w_down, int64_t gate_up_expert_stride_bytes,
+             int64_t down_expert_stride_bytes, int64_t n_local_expert, int64_t hidden, int64_t inter,
+             const void* xq, const void* grouping, int64_t ncols, int32_t topk, float* h, float* y,
+             const void* s_gate, const void* s_up, int64_t s_row_stride_bytes, int64_t s_rows,
+             const void* s_down, float* hs, float* ys, void* stream) {
+    if (ncols < 1 || ncols > MAX_COLS || hidden <= 0 || inter <= 0) return MOEQ8_EINVAL;
+    if (!w_down || !h || !y) return MOEQ8_EINVAL;
+    const bool has_s = s_gate != nullptr;
+    if (has_s && (!s_up || !s_down || !hs || !ys || s_rows < 1)) return MOEQ8_EINVAL;
+    constexpr int64_t ROUND_BYTES = P64_SEGMENT_BYTES / 4;           // 1088
+    // both stages are checked before either is launched
+    GroupedLaunch G, D;
+    int st = prepare_grouped(G, false, MOEQ8_GATE_UP_SWIGLU_P64, w_gate, w_up, gate_up_expert_stride_bytes,
+                             (hidden / QK) * Q80_BYTES, n_local_expert, inter, hidden, xq, 0, grouping, ncols,
+                             topk, h, s_gate, s_up, s_row_stride_bytes, has_s ? s_rows : 0, hidden, 0, nullptr, 0,
+                             has_s ? hs : nullptr);
+    if (st != MOEQ8_OK) return st;
+    st = prepare_grouped(D, false, MOEQ8_DOWN_F32_ACT_P64, w_down, nullptr, down_expert_stride_bytes, ROUND_BYTES,
+                         n_local_expert, hidden, inter, h, inter, grouping, ncols, topk, y, has_s ? s_down : nullptr,
+                         nullptr, ROUND_BYTES, has_s ? hidden : 0, has_s ? s_rows : 0, 0, has_s ? hs : nullptr,
+                         has_s ? s_rows : 0, has_s ? ys : nullptr);
+    if (st != MOEQ8_OK) return st;
+    const hipStream_t hs_ = (hipStream_t)stream;
+    st = launch_p64(false, G.p, G.s, G.grid, G.lds, hs_);
+    if (st != MOEQ8_OK) return st;
+    return launch_p64(true, D.p, D.s, D.grid, D.lds, hs_);
 }
 }  // namespace
 }  // namespace moeq8
+
+extern "C" int moe_grouped_ffn_p64(const void* w_gate, const void* w_up, const void* w_down,
+                                   int64_t gate_up_expert_stride_bytes, int64_t down_expert_stride_bytes,
+                                   int64_t n_local_expert, int64_t hidden, int64_t inter, const void* xq,
+                                   const void* grouping, int64_t ncols, int32_t topk, float* h, float* y,
+                                   const void* s_gate, const void* s_up, int64_t s_row_stride_bytes,
+                                   int64_t s_rows, const void* s_down, float* hs, float* ys, void* stream) {
+    return ffn_impl(w_gate, w_up, w_down, gate_up_expert_stride_bytes, down_expert_stride_bytes, n_local_expert,
+                    hidden, inter, xq, grouping, ncols, topk, h, y, s_gate, s_up, s_row_stride_bytes, s_rows,
+                    s_down, hs, ys, stream);
+}
 
 extern "C" int moe_grouped_mmvq_ex(int32_t stage, const void* w_a, const void* w_b,
                                    int64_t expert_stride_bytes, int64_t w_row_stride_bytes,

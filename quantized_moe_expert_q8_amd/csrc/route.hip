@@ -568,3 +568,4 @@ extern "C" int moe_group_routes(const int32_t* ids, int64_t ncols, int32_t topk,
                        (int)topk, (int)n_local_expert, (int32_t*)grouping);
     return check_launch();
 }
+

@@ -595,6 +595,54 @@ def moe_grouped_mmvq_ex(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
     return out
 
 
+def moe_grouped_ffn_p64(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, xq: torch.Tensor,
+                        grouping: torch.Tensor, *, hidden: int, inter: int, n_local_expert: int, ncols: int,
+                        topk: int, h: torch.Tensor, y: torch.Tensor, shared: dict | None = None):
+    """The routed FFN product after routing: grouped gate/up + SwiGLU into the
+    workspace h, then the grouped down quantising h in its launch, on packed
+    experts (contiguous: gate/up experts inter rows of hidden/32 blocks, down
+    experts hidden rows of 1088 bytes).
+
+    shared = {"gate", "up" (packed rows of the shared gate/up), "row_stride",
+              "rows" (== inter), "offset_bytes" (of the share's first row),
+              "down" (the packed shared down), "down_offset_bytes" (of the
+              share's round matrix), "hs" (fp32 [ncols, rows]), "ys" (fp32
+              [ncols, hidden])}."""
+    rb_h = (hidden // QK) * Q8_0_BLOCK_BYTES
+    gu_stride = inter * rb_h
+    dn_stride = hidden * ROUND_BYTES
+    for t, name, nb in ((w_gate, "w_gate", gu_stride), (w_up, "w_up", gu_stride), (w_down, "w_down", dn_stride)):
+        _cuda(t, name, torch.uint8)
+        _need(t, name, n_local_expert * nb)
+    _act_rows(xq, "xq", ncols, hidden)
+    _cuda(grouping, "grouping", torch.uint8)
+    _need(grouping, "grouping", moe_grouping_bytes(ncols, topk))
+    _cuda(h, "h", torch.float32)
+    _need(h, "h", ncols * topk * inter * 4)
+    _cuda(y, "y", torch.float32)
+    _need(y, "y", ncols * topk * hidden * 4)
+    sg = su = sd = hs = ys = None
+    s_stride = s_rows = s_off = d_off = 0
+    if shared is not None:
+        sg, su, sd = shared["gate"], shared["up"], shared["down"]
+        s_stride, s_rows = shared["row_stride"], shared["rows"]
+        s_off, d_off = shared.get("offset_bytes", 0), shared.get("down_offset_bytes", 0)
+        hs, ys = shared["hs"], shared["ys"]
+        for t, name in ((sg, "shared gate"), (su, "shared up")):
+            _cuda(t, name, torch.uint8)
+            _need(t, name, _weight_extent(s_rows, hidden, s_stride), s_off)
+        _cuda(sd, "shared down", torch.uint8)
+        _need(sd, "shared down", hidden * ROUND_BYTES, d_off)
+        _cuda(hs, "hs", torch.float32)
+        _need(hs, "hs", ncols * s_rows * 4)
+        _cuda(ys, "ys", torch.float32)
+        _need(ys, "ys", ncols * hidden * 4)
+    call("moe_grouped_ffn_p64", _ptr(w_gate), _ptr(w_up), _ptr(w_down), gu_stride, dn_stride, n_local_expert,
+         hidden, inter, _ptr(xq), _ptr(grouping), ncols, topk, _ptr(h), _ptr(y), _ptr(sg, s_off), _ptr(su, s_off),
+         s_stride, s_rows, _ptr(sd, d_off), _ptr(hs), _ptr(ys), _stream(w_gate))
+    return y
+
+
 def moe_combine(y: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor,
                 out: torch.Tensor | None = None, shared: torch.Tensor | None = None) -> torch.Tensor:
     """out fp32 [ncols, n] = sum over unmasked slots of weights * y, plus

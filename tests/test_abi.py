@@ -141,6 +141,18 @@ def test_other_validation():
     assert L.moeq8_stream_read(P + 4, 64, P, None) == -2                         # misaligned buffer
     assert L.moeq8_stream_read(P, 24, P, None) == -2                             # bytes % 16
     assert L.moeq8_stream_read(P, 0, P, None) == 0
+    # the routed FFN entry: columns, shapes of the packed layouts, alignment
+    gu_s, dn_s = 1024 * 4352, 4096 * 1088
+    assert L.moe_grouped_ffn_p64(P, P, P, gu_s, dn_s, 2, 4096, 1024, P, P, 0, 8, P, P,
+                                 None, None, 0, 0, None, None, None, None) == -1            # no columns
+    assert L.moe_grouped_ffn_p64(P, P, P, gu_s, dn_s, 2, 4096, 1024, P, P, 9, 8, P, P,
+                                 None, None, 0, 0, None, None, None, None) == -1            # past 8 columns
+    assert L.moe_grouped_ffn_p64(P, P, P, gu_s // 2, dn_s, 2, 2048, 1024, P, P, 1, 8, P, P,
+                                 None, None, 0, 0, None, None, None, None) == -3            # not one segment a row
+    assert L.moe_grouped_ffn_p64(P, P, P + 4, gu_s, dn_s, 2, 4096, 1024, P, P, 1, 8, P, P,
+                                 None, None, 0, 0, None, None, None, None) == -2            # down off 16 bytes
+    assert L.moe_grouped_ffn_p64(P, P, P, gu_s, dn_s, 2, 4096, 1024, P, P, 1, 8, P, P,
+                                 P, None, 4352, 1024, P, P, P, None) == -1                  # shared up missing
     assert L.moeq8_stream_read_shape(P, 64, 4096, P, None) == -1                # not a read shape
     assert L.moeq8_stream_read_shape(P, 24, 8192, P, None) == -2                # bytes % 16
     assert L.moeq8_stream_read_shape(P, 0, 16384, P, None) == 0

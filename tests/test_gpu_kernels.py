@@ -1288,3 +1288,94 @@ def test_grouped_gemm_takes_the_decode_grouping():
     for e, routes in oracle.group_routes(ids_ref):
         ref = oracle.glu_pair(wg[e], wu[e], xo[[r // topk for r in routes]])[0]
         assert_close(hh[routes], ref, EPI_TOL, f"gemm on decode grouping, expert {e}")
+
+
+# ---------------------------------------------------------------------------
+# the routed FFN product after routing in one call (moe_grouped_ffn_p64)
+# ---------------------------------------------------------------------------
+
+def _packed_ffn_layer(seed, local, share):
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    H, I = 4096, 1024
+    wg, wu, wd = _synth_dev(seed, local, I, H, 0), _synth_dev(seed, local, I, H, 1), _synth_dev(seed, local, H, I, 2)
+    experts = ml.RoutedExperts(wg, wu, wd, local, H, I)
+    shared = None
+    if share:
+        full = 2 * I
+        rb_h, rb_f = H // 32 * 34, full // 32 * 34
+        shared = ml.SharedExpertShare(_synth_dev(seed, 1, full, H, 3).view(full, rb_h),
+                                      _synth_dev(seed, 1, full, H, 4).view(full, rb_h),
+                                      _synth_dev(seed, 1, H, full, 5).view(H, rb_f), H, full, I, I)
+    return ml.pack_experts(experts, shared)
+
+
+@pytest.mark.parametrize("c,n_exp,local,share", [(1, 16, 16, True), (2, 32, 16, False), (3, 32, 32, True),
+                                                 (5, 64, 32, True), (8, 128, 48, False)])
+def test_grouped_ffn_equals_its_two_stages(c, n_exp, local, share):
+    """moe_grouped_ffn_p64 against GATE_UP_SWIGLU_P64 then DOWN_F32_ACT_P64:
+    h, y (and hs, ys) bit for bit, masked rows untouched; every column count
+    class of the launch (1, 2, up to 4, up to 8 columns a pass)."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    say(f"grouped ffn c={c} E={n_exp} local={local} share={share}")
+    H, I, topk, seed = 4096, 1024, 8, 110 + c
+    pe, ps = _packed_ffn_layer(seed, local, share)
+    x = to_dev(workloads.activations(seed, c, H))
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    b = to_dev(workloads.router_bias(seed, n_exp))
+    own = to_dev(workloads.owner_slots(n_exp, local))
+    ws = [ml.Workspace(c, H, I, topk, I if share else 0, DEV) for _ in range(2)]
+    for w in ws:
+        moeq8.moe_route_topk_quantize(x, lg, topk, bias=b, owner_slot=own, n_local_expert=local, xq=w.xq,
+                                      ids=w.ids, weights=w.weights, grouping=w.grouping)
+        for t in (w.h, w.y) + ((w.hs, w.ys) if share else ()):
+            t.fill_(float("nan"))
+    rb = H // 32 * 34
+    wa, wb = ws
+    gu = dn = one = None
+    if share:
+        rnd = ps.down_block_offset() // (ps.rows // 32)
+        doff = rnd * H * moeq8.ops.ROUND_BYTES
+        gu = {"a": ps.gate, "b": ps.up, "row_stride": rb, "n": ps.rows, "k": H, "k_block_offset": 0,
+              "offset_bytes": ps.gate_offset(), "out": wa.hs}
+        dn = {"a": ps.down, "row_stride": moeq8.ops.ROUND_BYTES, "n": H, "k": ps.rows, "k_block_offset": 0,
+              "offset_bytes": doff, "out": wa.ys, "act": wa.hs}
+        one = {"gate": ps.gate, "up": ps.up, "row_stride": rb, "rows": ps.rows, "offset_bytes": ps.gate_offset(),
+               "down": ps.down, "down_offset_bytes": doff, "hs": wb.hs, "ys": wb.ys}
+    moeq8.moe_grouped_mmvq_ex(moeq8.GATE_UP_SWIGLU_P64, pe.gate, pe.up, wa.xq, wa.grouping, n=I, k=H,
+                              n_local_expert=local, ncols=c, topk=topk, out=wa.h, shared=gu)
+    moeq8.moe_grouped_mmvq_ex(moeq8.DOWN_F32_ACT_P64, pe.down, None, wa.h.view(c * topk, I), wa.grouping,
+                              n=H, k=I, n_local_expert=local, ncols=c, topk=topk, out=wa.y, shared=dn)
+    moeq8.moe_grouped_ffn_p64(pe.gate, pe.up, pe.down, wb.xq, wb.grouping, hidden=H, inter=I,
+                              n_local_expert=local, ncols=c, topk=topk, h=wb.h, y=wb.y, shared=one)
+    torch.cuda.synchronize()
+    valid = host(wa.ids) >= 0
+    ha, hb, ya, yb = host(wa.h), host(wb.h), host(wa.y), host(wb.y)
+    for j in range(c):
+        for s in range(topk):
+            if valid[j, s]:
+                assert np.array_equal(ha[j, s].view(np.int32), hb[j, s].view(np.int32)), (j, s)
+                assert np.array_equal(ya[j, s].view(np.int32), yb[j, s].view(np.int32)), (j, s)
+            else:
+                assert np.isnan(hb[j, s]).all() and np.isnan(yb[j, s]).all()
+    if share:
+        assert bits_equal(wa.hs, wb.hs) and bits_equal(wa.ys, wb.ys)
+
+
+def test_grouped_ffn_rejects_before_launching():
+    """A bad down stage is found before the gate/up stage is launched: h keeps
+    its contents."""
+    say("grouped ffn host checks")
+    c, topk, local, H, I = 2, 8, 4, 4096, 1024
+    lg = to_dev(workloads.router_logits(3, c, local))
+    ids, w, grouping = moeq8.moe_route_topk(lg, 4)
+    g = torch.zeros(local * I * (H // 32) * 34, dtype=torch.uint8, device=DEV)
+    d = torch.zeros(local * H * 1088 + 16, dtype=torch.uint8, device=DEV)
+    xq = torch.zeros((c, H // 32 * 36), dtype=torch.uint8, device=DEV)
+    h = torch.full((c, 4, I), 7.0, device=DEV)
+    y = torch.zeros((c, 4, H), device=DEV)
+    with pytest.raises(moeq8.MoeQ8Error) as ei:         # down weights off the 16-byte grid
+        moeq8.moe_grouped_ffn_p64(g, g, d[4:], xq, grouping, hidden=H, inter=I, n_local_expert=local, ncols=c,
+                                  topk=4, h=h, y=y)
+    assert ei.value.status == -2
+    torch.cuda.synchronize()
+    assert bool((h == 7.0).all())
