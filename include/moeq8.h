@@ -304,6 +304,25 @@ int moe_grouped_ffn_p64(const void* w_gate, const void* w_up, const void* w_down
                         const void* s_gate, const void* s_up, int64_t s_row_stride_bytes,
                         int64_t s_rows, const void* s_down, float* hs, float* ys, void* stream);
 
+/* moe_grouped_ffn_p64 for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid it): the
+ * same product and the same bits, with h and hs held in
+ * MOEQ8_FFN_SCRATCH_BYTES of device memory the library keeps on each GPU it
+ * runs on, from its first call there until the process ends.  The call
+ * itself allocates nothing.  Arguments as moe_grouped_ffn_p64 without h and
+ * hs; `stream` must belong to the current device.  Sizes beyond that memory
+ * (ncols * topk * inter * 4 > 524288 bytes, or ncols * s_rows * 4 > 32768)
+ * are MOEQ8_EUNSUPPORTED, nothing enqueued.  Every call on one GPU uses the
+ * same memory, and each leaves its h there: calls that overlap on one GPU
+ * (other streams, other host threads) race and must not be made. */
+#define MOEQ8_FFN_SCRATCH_BYTES 557056
+int moe_grouped_ffn_p64_noalloc(const void* w_gate, const void* w_up, const void* w_down,
+                                int64_t gate_up_expert_stride_bytes, int64_t down_expert_stride_bytes,
+                                int64_t n_local_expert, int64_t hidden, int64_t inter, const void* xq,
+                                const void* grouping, int64_t ncols, int32_t topk, float* y,
+                                const void* s_gate, const void* s_up, int64_t s_row_stride_bytes,
+                                int64_t s_rows, const void* s_down, float* ys, void* stream);
+
 /* a1 + a4 + a5 in one launch (the layer prologue): q8_1 quantisation of the
  * ncols rows of x [ncols][x_row_stride] into xq [ncols][k/32], and
  * moe_route_topk on the logits.  Outputs are bit-identical to calling

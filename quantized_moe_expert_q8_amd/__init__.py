@@ -33,6 +33,7 @@ from .ops import (  # noqa: F401
     moe_route_topk_quantize,
     moe_combine,
     moe_grouped_ffn_p64,
+    moe_grouped_ffn_p64_noalloc,
     EXCHANGE_BLOCK_BYTES,
     q8_block_encode,
     q8_block_decode_sum,

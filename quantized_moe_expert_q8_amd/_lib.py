@@ -39,6 +39,9 @@ SIGNATURES = {
     "moe_grouped_ffn_p64": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp,
                                            c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
                                            c_vp, c_vp, c_vp, c_vp]),
+    "moe_grouped_ffn_p64_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp,
+                                                   c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                   c_vp, c_vp, c_vp]),
     "moe_combine": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]),
     "moe_combine_shared": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "q8_block_encode": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),

@@ -25,6 +25,7 @@
 #include "moeq8_device.hpp"
 #include "moeq8_host.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace moeq8 {
@@ -892,6 +893,69 @@ extern "C" int moe_grouped_ffn_p64(const void* w_gate, const void* w_up, const v
                                    const void* grouping, int64_t ncols, int32_t topk, float* h, float* y,
                                    const void* s_gate, const void* s_up, int64_t s_row_stride_bytes,
                                    int64_t s_rows, const void* s_down, float* hs, float* ys, void* stream) {
+    return ffn_impl(w_gate, w_up, w_down, gate_up_expert_stride_bytes, down_expert_stride_bytes, n_local_expert,
+                    hidden, inter, xq, grouping, ncols, topk, h, y, s_gate, s_up, s_row_stride_bytes, s_rows,
+                    s_down, hs, ys, stream);
+}
+
+// ---- the routed FFN product with its workspace in library-held memory ----
+// h (and the shared share's hs) live in `scratch`, a device array of this
+// file that every GPU the library runs on holds until the process ends.  Host
+// code reaches it only through the per-device address hipGetSymbolAddress
+// returns (the array's name is a host-side stand-in, not a device address).
+namespace moeq8 {
+namespace {
+constexpr size_t FFN_SCRATCH_H_BYTES = (size_t)MAX_COLS * MOEQ8_MAX_TOPK * 1024 * 4;   // routes x inter 1024
+constexpr size_t FFN_SCRATCH_HS_BYTES = (size_t)MAX_COLS * 1024 * 4;                  // columns x share rows
+static_assert(FFN_SCRATCH_H_BYTES + FFN_SCRATCH_HS_BYTES == MOEQ8_FFN_SCRATCH_BYTES, "scratch size in the header");
+}  // namespace
+}  // namespace moeq8
+
+static __device__ __align__(256) uint8_t scratch[MOEQ8_FFN_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current (the caller's), or an error status.
+int scratch_for_current_device(uint8_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOEQ8_EHIP;
+    }
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return MOEQ8_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return MOEQ8_EHIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = (uint8_t*)g_scratch_ptr[dev];
+    return MOEQ8_OK;
+}
+}  // namespace
+
+extern "C" int moe_grouped_ffn_p64_noalloc(const void* w_gate, const void* w_up, const void* w_down,
+                                           int64_t gate_up_expert_stride_bytes, int64_t down_expert_stride_bytes,
+                                           int64_t n_local_expert, int64_t hidden, int64_t inter, const void* xq,
+                                           const void* grouping, int64_t ncols, int32_t topk, float* y,
+                                           const void* s_gate, const void* s_up, int64_t s_row_stride_bytes,
+                                           int64_t s_rows, const void* s_down, float* ys, void* stream) {
+    // sizes beyond what the library holds are refused before anything else
+    if (ncols < 1 || ncols > MAX_COLS || topk < 1 || topk > MOEQ8_MAX_TOPK || inter <= 0) return MOEQ8_EINVAL;
+    if ((size_t)(ncols * topk) * (size_t)inter * 4 > FFN_SCRATCH_H_BYTES) return MOEQ8_EUNSUPPORTED;
+    if (s_gate && (s_rows < 1 || (size_t)ncols * (size_t)s_rows * 4 > FFN_SCRATCH_HS_BYTES)) return MOEQ8_EUNSUPPORTED;
+    uint8_t* base = nullptr;
+    const int st = scratch_for_current_device(&base);
+    if (st != MOEQ8_OK) return st;
+    float* h = (float*)base;
+    float* hs = s_gate ? (float*)(base + FFN_SCRATCH_H_BYTES) : nullptr;
     return ffn_impl(w_gate, w_up, w_down, gate_up_expert_stride_bytes, down_expert_stride_bytes, n_local_expert,
                     hidden, inter, xq, grouping, ncols, topk, h, y, s_gate, s_up, s_row_stride_bytes, s_rows,
                     s_down, hs, ys, stream);

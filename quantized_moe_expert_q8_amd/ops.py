@@ -643,6 +643,44 @@ def moe_grouped_ffn_p64(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.
     return y
 
 
+def moe_grouped_ffn_p64_noalloc(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                                xq: torch.Tensor, grouping: torch.Tensor, *, hidden: int, inter: int,
+                                n_local_expert: int, ncols: int, topk: int, y: torch.Tensor,
+                                shared: dict | None = None):
+    """moe_grouped_ffn_p64 with h and hs in the library's own device memory:
+    the same arguments without h and hs (shared: the same dict without "hs").
+    Calls on one GPU must not overlap."""
+    rb_h = (hidden // QK) * Q8_0_BLOCK_BYTES
+    gu_stride = inter * rb_h
+    dn_stride = hidden * ROUND_BYTES
+    for t, name, nb in ((w_gate, "w_gate", gu_stride), (w_up, "w_up", gu_stride), (w_down, "w_down", dn_stride)):
+        _cuda(t, name, torch.uint8)
+        _need(t, name, n_local_expert * nb)
+    _act_rows(xq, "xq", ncols, hidden)
+    _cuda(grouping, "grouping", torch.uint8)
+    _need(grouping, "grouping", moe_grouping_bytes(ncols, topk))
+    _cuda(y, "y", torch.float32)
+    _need(y, "y", ncols * topk * hidden * 4)
+    sg = su = sd = ys = None
+    s_stride = s_rows = s_off = d_off = 0
+    if shared is not None:
+        sg, su, sd = shared["gate"], shared["up"], shared["down"]
+        s_stride, s_rows = shared["row_stride"], shared["rows"]
+        s_off, d_off = shared.get("offset_bytes", 0), shared.get("down_offset_bytes", 0)
+        ys = shared["ys"]
+        for t, name in ((sg, "shared gate"), (su, "shared up")):
+            _cuda(t, name, torch.uint8)
+            _need(t, name, _weight_extent(s_rows, hidden, s_stride), s_off)
+        _cuda(sd, "shared down", torch.uint8)
+        _need(sd, "shared down", hidden * ROUND_BYTES, d_off)
+        _cuda(ys, "ys", torch.float32)
+        _need(ys, "ys", ncols * hidden * 4)
+    call("moe_grouped_ffn_p64_noalloc", _ptr(w_gate), _ptr(w_up), _ptr(w_down), gu_stride, dn_stride,
+         n_local_expert, hidden, inter, _ptr(xq), _ptr(grouping), ncols, topk, _ptr(y), _ptr(sg, s_off),
+         _ptr(su, s_off), s_stride, s_rows, _ptr(sd, d_off), _ptr(ys), _stream(w_gate))
+    return y
+
+
 def moe_combine(y: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor,
                 out: torch.Tensor | None = None, shared: torch.Tensor | None = None) -> torch.Tensor:
     """out fp32 [ncols, n] = sum over unmasked slots of weights * y, plus

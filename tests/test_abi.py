@@ -153,6 +153,13 @@ def test_other_validation():
                                  None, None, 0, 0, None, None, None, None) == -2            # down off 16 bytes
     assert L.moe_grouped_ffn_p64(P, P, P, gu_s, dn_s, 2, 4096, 1024, P, P, 1, 8, P, P,
                                  P, None, 4352, 1024, P, P, P, None) == -1                  # shared up missing
+    # its no-alloc form refuses what its memory cannot hold before anything else
+    assert L.moe_grouped_ffn_p64_noalloc(P, P, P, gu_s, dn_s, 2, 4096, 2048, P, P, 8, 16, P,
+                                         None, None, 0, 0, None, None, None) == -3          # h past 512 KiB
+    assert L.moe_grouped_ffn_p64_noalloc(P, P, P, gu_s, dn_s, 2, 4096, 1024, P, P, 8, 8, P,
+                                         P, P, 4352, 2048, P, P, None) == -3                # hs past 32 KiB
+    assert L.moe_grouped_ffn_p64_noalloc(P, P, P, gu_s, dn_s, 2, 4096, 1024, P, P, 0, 8, P,
+                                         None, None, 0, 0, None, None, None) == -1          # no columns
     assert L.moeq8_stream_read_shape(P, 64, 4096, P, None) == -1                # not a read shape
     assert L.moeq8_stream_read_shape(P, 24, 8192, P, None) == -2                # bytes % 16
     assert L.moeq8_stream_read_shape(P, 0, 16384, P, None) == 0
