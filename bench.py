@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--only-sweep", action="store_true",
                     help="run the column sweep alone (profiling runs); the JSON line then "
                          "carries the sweep only")
+    ap.add_argument("--cpu-procs", type=int, default=min(16, os.cpu_count() or 1),
+                    help="processes of the multi-process oracle leg (the host's CPU share; 1 = none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the oracle sample")
     ap.add_argument("--pmc-copy", action="store_true",
@@ -272,6 +274,112 @@ def host_cpu_model():
     return None
 
 
+def _cpu_layer_work(oracle, workloads, cfg, share_rows, l, mats, shared_mats, own):
+    """The oracle on layer l, as the single-thread leg runs it: the routed
+    layer (q8_1 of x, routing, each route's expert FFN, the weighted combine)
+    and the shared expert's share."""
+    seed, hidden, topk, n_exp, cols = cfg["seed"], cfg["hidden"], cfg["topk"], cfg["experts"], cfg["cols"][0]
+    x = workloads.activations(seed, cols, hidden, layer=l)
+    lg = workloads.router_logits(seed, cols, n_exp, layer=l)
+    bias = workloads.router_bias(seed, n_exp, layer=l)
+    r = oracle.moe_layer(x, lg, bias, own, lambda e: mats[(l, e)], topk)
+    sg, su, sd = shared_mats[l]
+    h, _, _ = oracle.glu_pair(sg, su, r["xq"])
+    hq = oracle.quantize_q8_1(h.astype(np.float32))
+    oracle.mmvq(sd[:, :share_rows // 32], hq)
+
+
+def _cpu_worker(rank, nproc, cfg, share_rows, root, start_evt, barrier, results):
+    """One process of the multi-process oracle leg: waits until the GPU part
+    is done, draws the inputs of its contiguous share of the layers, meets the
+    others at a barrier, then runs the oracle on its layers."""
+    import sys as _sys
+    import time as _time
+    if root not in _sys.path:
+        _sys.path.insert(0, root)
+    import oracle
+    import workloads
+    if not start_evt.wait(3600):
+        return
+    try:
+        _cpu_worker_body(rank, nproc, cfg, share_rows, barrier, results, oracle, workloads, _time)
+    except Exception as exc:                           # reported to the parent, never left hanging
+        results.put((rank, None, None, f"{type(exc).__name__}: {exc}"))
+
+
+def _cpu_worker_body(rank, nproc, cfg, share_rows, barrier, results, oracle, workloads, _time):
+    seed, hidden, inter, topk = cfg["seed"], cfg["hidden"], cfg["inter"], cfg["topk"]
+    cols, L, n_exp = cfg["cols"][0], cfg["layers"], cfg["experts"]
+    own = workloads.owner_slots(n_exp, cfg["local_experts"])
+    mine = list(range(rank * L // nproc, (rank + 1) * L // nproc))
+    mats, shared_mats = {}, {}
+    for l in mine:
+        lg = workloads.router_logits(seed, cols, n_exp, layer=l)
+        ids, _, _ = oracle.route_topk(lg, workloads.router_bias(seed, n_exp, layer=l), own, topk)
+        for e in (int(v) for v in ids.reshape(-1) if v >= 0):
+            if (l, e) not in mats:
+                mats[(l, e)] = tuple(workloads.synth_q8_0_matrix(seed, l, e, m, r_, k_)
+                                     for m, r_, k_ in ((0, inter, hidden), (1, inter, hidden), (2, hidden, inter)))
+        if l not in shared_mats:
+            shared_mats[l] = (workloads.synth_q8_0_matrix(seed, l, 0, 3, cfg["shared_inter"], hidden, 0, share_rows),
+                              workloads.synth_q8_0_matrix(seed, l, 0, 4, cfg["shared_inter"], hidden, 0, share_rows),
+                              workloads.synth_q8_0_matrix(seed, l, 0, 5, hidden, cfg["shared_inter"]))
+    barrier.wait(600)
+    t0 = _time.perf_counter()
+    for l in mine:
+        _cpu_layer_work(oracle, workloads, cfg, share_rows, l, mats, shared_mats, own)
+    t1 = _time.perf_counter()
+    results.put((rank, t0, t1, len(mine)))
+
+
+class CpuPool:
+    """The multi-process oracle leg's processes, started before the GPU is
+    touched (spawned children of a process that has not initialised the GPU)
+    and idle until run() releases them after the GPU part."""
+
+    def __init__(self, nproc, cfg, share_rows):
+        import multiprocessing as mp
+        ctx = mp.get_context("spawn")
+        self.nproc, self.cfg, self.share_rows = nproc, cfg, share_rows
+        self.start_evt = ctx.Event()
+        self.barrier = ctx.Barrier(nproc)
+        self.results = ctx.Queue()
+        self.procs = [ctx.Process(target=_cpu_worker, args=(r, nproc, cfg, share_rows, ROOT, self.start_evt,
+                                                             self.barrier, self.results), daemon=True)
+                      for r in range(nproc)]
+        # one thread a process (the children read these when numpy loads)
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+        os.environ.update({k: "1" for k in saved})
+        try:
+            for p in self.procs:
+                p.start()
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+
+    def run(self, workloads):
+        """All layers of the workload over the processes; throughput over the
+        span from the first process's start to the last one's end."""
+        self.start_evt.set()
+        got = [self.results.get(timeout=900) for _ in range(self.nproc)]
+        for p in self.procs:
+            p.join(timeout=60)
+        bad = [g for g in got if g[1] is None]
+        if bad:
+            raise RuntimeError(f"multi-process oracle leg failed: {bad[0][3]}")
+        span = max(g[2] for g in got) - min(g[1] for g in got)
+        return span
+
+    def close(self):
+        self.start_evt.set()
+        for p in self.procs:
+            if p.is_alive():
+                p.terminate()
+
+
 def cpu_baseline(workloads, cfg, budget_s, share_rows):
     import oracle
     seed, hidden, inter, topk = cfg["seed"], cfg["hidden"], cfg["inter"], cfg["topk"]
@@ -319,9 +427,22 @@ def main():
                                    "expert FFN is not built (one process per GPU would each run this "
                                    "step on its own expert share)", "n_gpus": args.gpus}))
         sys.exit(2)
+    import workloads
+    pool = None
+    if not args.no_cpu_baseline and not args.only_sweep and args.cpu_procs > 1:
+        c5 = dict(workloads.CONFIGS["ep_share_l43_e128_c8"], name="ep_share_l43_e128_c8")
+        # the processes start before anything touches the GPU
+        pool = CpuPool(args.cpu_procs, c5, c5["shared_inter"] // c5["shared_share"])
+    try:
+        _main_gpu(args, workloads, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def _main_gpu(args, workloads, pool):
     import torch
 
-    import workloads
     import quantized_moe_expert_q8_amd as moeq8
     from quantized_moe_expert_q8_amd import moe_layer as ml
 
@@ -535,6 +656,18 @@ def main():
         t0 = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(workloads, cfg, args.cpu_seconds, share_rows)
         log(f"cpu baseline {time.perf_counter() - t0:.1f}s: {result['cpu_baseline']}")
+        if pool is not None:
+            t0 = time.perf_counter()
+            span = pool.run(workloads)
+            all_bytes = step_bytes                     # every layer of the step, as the GPU's value
+            leg = {"value": round(all_bytes / span / 1e9, 4), "unit": "GB/s", "cores": pool.nproc,
+                   "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
+                   "sample": f"all {L} layers of {cfg['name']} in contiguous shares over {pool.nproc} "
+                             f"processes (numpy oracle, one thread each; the span of the compute from the "
+                             f"first start to the last end after a barrier); {L / span:.3f} layers/s"}
+            result["cpu_baseline"] = {**result["cpu_baseline"], "single_thread": dict(result["cpu_baseline"]),
+                                      "multi_process": leg}
+            log(f"cpu baseline, {pool.nproc} processes, {time.perf_counter() - t0:.1f}s: {leg}")
     print(json.dumps(result), flush=True)
 
 
