@@ -1080,6 +1080,44 @@ def test_grouped_gemm_integer_dots_unit_scale():
         assert np.array_equal(hh[r], exact.astype(np.float32)), r
 
 
+def _off_alignment(t: torch.Tensor, shift: int = 4) -> torch.Tensor:
+    """A copy of t's bytes that starts `shift` bytes past a 16-byte boundary."""
+    raw = t.reshape(-1).view(torch.uint8)
+    buf = torch.zeros(raw.numel() + 32, dtype=torch.uint8, device=DEV)
+    view = buf[16 + shift:16 + shift + raw.numel()]
+    view.copy_(raw)
+    assert view.data_ptr() % 16 == shift
+    return view
+
+
+@pytest.mark.parametrize("c,n_exp,local,topk,hidden,inter", [
+    (200, 16, 16, 8, 1024, 512),     # ~100 routes an expert: a full and a ragged 64-route unit
+    (130, 64, 40, 8, 2048, 256),     # owner mask (masked routes)
+    (64, 4, 4, 4, 4096, 256),        # 16 K steps; every column routes to all 4 experts
+    (1, 8, 8, 8, 256, 256),          # one column, one K step: nothing to prefetch
+])
+def test_staged_gemm_equals_register_gemm(c, n_exp, local, topk, hidden, inter):
+    """With k % 256 == 0 and 16-byte aligned operands the grouped gate/up
+    product stages its operands in LDS; the same call on weights copied 4
+    bytes off that alignment runs the register-fed form.  Both take the same
+    integer dots, scale products and accumulation order, so every output (and
+    every untouched row of a masked route) has the same bits."""
+    say(f"staged vs register gemm c={c} E={n_exp} local={local} k={topk} H={hidden} I={inter}")
+    (wg, wu, wd), (wgd, wud, wdd), x, ids_ref, ids, g = _gemm_case(c, n_exp, local, topk, hidden, inter,
+                                                                   3 * c + hidden)
+    xo, xd = quantized_pair(x)
+    outs = []
+    for a, b in ((wgd, wud), (_off_alignment(wgd), _off_alignment(wud))):
+        h = torch.full((c, topk, inter), float("nan"), device=DEV)
+        moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU, a, b, xd, g, n=inter, k=hidden, n_local_expert=local,
+                               ncols=c, topk=topk, out=h)
+        outs.append(h)
+    assert bits_equal(outs[0], outs[1])
+    live = torch.from_numpy(ids_ref.reshape(-1) >= 0).to(DEV)
+    assert not torch.isnan(outs[0].reshape(c * topk, -1)[live]).any()
+    assert torch.isnan(outs[0].reshape(c * topk, -1)[~live]).all()
+
+
 # ---------------------------------------------------------------------------
 # 8-bit block exchange codec: bytes and sums bit for bit against the oracle
 # ---------------------------------------------------------------------------
