@@ -448,8 +448,11 @@ def _main_gpu(args, workloads, pool):
 
     torch.cuda.init()
     if args.only_sweep:
-        print(json.dumps({"metric": "routed-expert MMVQ column sweep (profiling run)",
-                          "sweep": sweep(torch, workloads, moeq8, ml, args)}), flush=True)
+        rec = sweep(torch, workloads, moeq8, ml, args)
+        if args.pmc_copy:
+            pmc_reference_copy(torch)
+        print(json.dumps({"metric": "routed-expert MMVQ column sweep (profiling run)", "sweep": rec}),
+              flush=True)
         return
     cfg = dict(workloads.CONFIGS["ep_share_l43_e128_c8"], name="ep_share_l43_e128_c8")
     L, n_local, n_exp = cfg["layers"], cfg["local_experts"], cfg["experts"]
@@ -629,14 +632,7 @@ def _main_gpu(args, workloads, pool):
     }
 
     if args.pmc_copy:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log("pmc reference: copied 536870912 bytes device to device")
-        del src, dst
+        pmc_reference_copy(torch)
 
     # release the big bank before the sweep
     del g, bank, experts, shared, wss
@@ -715,6 +711,19 @@ def sweep_replicas(torch, workloads, moeq8, cols, hidden, inter, topk, n_exp, se
                      "n_local": len(sel)})
         total += len(sel) * dn_expert
     return reps
+
+
+def pmc_reference_copy(torch):
+    """A 512 MiB device-to-device copy of known size: what FETCH_SIZE and
+    WRITE_SIZE read for it scales their readings of the other kernels."""
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log("pmc reference: copied 536870912 bytes device to device")
+    del src, dst
 
 
 def sweep(torch, workloads, moeq8, ml, args):
@@ -802,6 +811,8 @@ def sweep(torch, workloads, moeq8, ml, args):
                                   "gate_up": int(sum(gu_b)), "down": int(sum(dn_b))},
                "layer_us": round(ms * 1e3, 2), "layers_per_s": round(1e3 / ms, 1),
                "effective_gbps": round(lb / (ms * 1e-3) / 1e9, 1),
+               "gate_up_bytes_per_launch": round(float(np.mean(gu_b))),
+               "down_bytes_per_launch": round(float(np.mean(dn_b))),
                "gate_up_us": round(gu_us, 2), "gate_up_gbps": round(gu_gbps, 1),
                "gate_up_frac_of_peak": round(gu_gbps / HBM_PEAK_GBPS, 4),
                "down_us": round(dn_us, 2), "down_gbps": round(dn_gbps, 1),
