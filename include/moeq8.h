@@ -191,6 +191,16 @@ int moe_route_topk(const float* logits, const float* bias, const int32_t* owner_
                    int64_t ncols, int64_t n_expert, int64_t n_local_expert, int32_t topk,
                    int32_t* ids, float* weights, void* grouping, void* stream);
 
+/* a4's score function alone (the scores the router of PR #826's fused DS4.1
+ * decode kernels commit selects and weights by): scores[i] = the router's score
+ * of logits[i] (the sigmoid evaluated in fp64 and rounded once to fp32), by the same
+ * device expression the router uses, for n >= 0 fp32 values (device pointers,
+ * 4-byte aligned; n = 0 enqueues nothing).  For checking that rounding against
+ * a reference over any set of logits; the selection itself is moe_route_topk.
+ * Returns MOEQ8_EINVAL for a null pointer or n < 0, MOEQ8_EALIGN for a
+ * misaligned pointer. */
+int moe_router_scores(const float* logits, int64_t n, float* scores, void* stream);
+
 /* ---------------------------------------------------------------------------
  * a6 / a8: grouped per-expert MMVQ over the routed experts, one launch per
  * projection, using the grouping written by moe_route_topk.

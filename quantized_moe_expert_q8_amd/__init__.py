@@ -31,6 +31,7 @@ from .ops import (  # noqa: F401
     moe_grouped_gemm,
     moe_grouped_mmvq_ex,
     moe_route_topk_quantize,
+    moe_router_scores,
     moe_combine,
     moe_grouped_ffn_p64,
     moe_grouped_ffn_p64_noalloc,

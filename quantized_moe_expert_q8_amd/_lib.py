@@ -25,6 +25,7 @@ SIGNATURES = {
                                           c_vp, c_vp, c_vp, c_vp]),
     "swiglu_ds4": (ctypes.c_int, [c_vp, c_vp, c_i64, c_vp, c_vp]),
     "moe_grouping_bytes": (c_size, [c_i64, c_i32]),
+    "moe_router_scores": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp]),
     "moe_route_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp,
                                       c_vp, c_vp]),
     "moe_grouped_mmvq": (ctypes.c_int, [c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,

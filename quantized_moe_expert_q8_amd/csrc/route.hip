@@ -31,6 +31,12 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The router's score of a logit: the sigmoid evaluated in fp64 and rounded
+// once to fp32 (one expression for the router and for moe_router_scores).
+__device__ __forceinline__ float router_score(float logit) {
+    return (float)(1.0 / (1.0 + exp(-(double)logit)));
+}
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
     const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
@@ -94,7 +100,7 @@ __device__ __forceinline__ void route_body(
             // sigmoid in fp64, rounded once to fp32; key = score + bias in fp32.
             // An expert past n_expert gets key 0, below every real key (the
             // ordered image of a finite float is positive).
-            score[i] = (float)(1.0 / (1.0 + exp(-(double)lg[i])));
+            score[i] = router_score(lg[i]);
             key[i] = ((valid >> i) & 1u) ? ordered_key(bias ? score[i] + bs[i] : score[i]) : 0u;
         }
         // Sort the lane's entries once by key, descending: odd-even
@@ -438,6 +444,11 @@ __global__ __launch_bounds__(64 * ROUTE_MAX_COLS) void k_route_quantize(
     quantize_block<true>(x + r * x_stride + b * QK, xq + gid * Q81_BYTES);
 }
 
+__global__ void k_router_scores(const float* __restrict__ logits, int64_t n, float* __restrict__ scores) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) scores[i] = router_score(logits[i]);
+}
+
 }  // namespace moeq8
 
 using namespace moeq8;
@@ -569,3 +580,13 @@ extern "C" int moe_group_routes(const int32_t* ids, int64_t ncols, int32_t topk,
     return check_launch();
 }
 
+extern "C" int moe_router_scores(const float* logits, int64_t n, float* scores, void* stream) {
+    if (!logits || !scores || n < 0) return MOEQ8_EINVAL;
+    if (((uintptr_t)logits | (uintptr_t)scores) & 3u) return MOEQ8_EALIGN;
+    if (n == 0) return MOEQ8_OK;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_router_scores, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream, logits, n,
+                       scores);
+    return check_launch();
+}

@@ -483,6 +483,20 @@ def moe_grouped_gemm(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, ac
                          ncols, topk, expert_stride_bytes, w_row_stride_bytes, out)
 
 
+def moe_router_scores(logits: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The router's score of every logit (fp64 sigmoid rounded once to fp32),
+    by the router's own device expression; any shape, fp32, contiguous."""
+    _cuda(logits, "logits", torch.float32)
+    if not logits.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    if out is None:
+        out = torch.empty_like(logits)
+    _cuda(out, "out", torch.float32)
+    _need(out, "out", logits.numel() * 4)
+    call("moe_router_scores", _ptr(logits), logits.numel(), _ptr(out), _stream(logits))
+    return out
+
+
 def moe_route_topk_quantize(x: torch.Tensor, logits: torch.Tensor, topk: int, *,
                             bias: torch.Tensor | None = None,
                             owner_slot: torch.Tensor | None = None,

@@ -163,6 +163,10 @@ def test_other_validation():
     assert L.moeq8_stream_read_shape(P, 64, 4096, P, None) == -1                # not a read shape
     assert L.moeq8_stream_read_shape(P, 24, 8192, P, None) == -2                # bytes % 16
     assert L.moeq8_stream_read_shape(P, 0, 16384, P, None) == 0
+    assert L.moe_router_scores(None, 4, P, None) == -1
+    assert L.moe_router_scores(P, -1, P, None) == -1
+    assert L.moe_router_scores(P, 4, P + 2, None) == -2
+    assert L.moe_router_scores(P, 0, P, None) == 0                                # nothing to do
 
 
 def test_packed_layout_validation():

@@ -946,6 +946,27 @@ def test_group_routes_vs_oracle(c, topk, n_local):
     _check_grouping(_grouping_words(g), np.where(ids < n_local, ids, -1).astype(np.int32))
 
 
+def test_router_scores_dense_sweep():
+    """Every key the router sorts is score + bias with score = the fp64
+    sigmoid rounded once to fp32 (the router's own device expression).  Over a
+    dense sweep (2^24 logits evenly spaced over [-24, 24], 2^21 consecutive fp32
+    values upward from 0.5 and from -3, and special values) the GPU's scores
+    equal the oracle's bit for bit; the two fp64 exp implementations could only
+    part where an fp64 sigmoid lies within an ulp or two of an fp32 rounding
+    boundary."""
+    say("router scores: dense sweep")
+    even = np.linspace(-24.0, 24.0, 1 << 24).astype(np.float32)
+    runs = [(np.arange(1 << 21, dtype=np.int64) + np.int64(np.float32(v).view(np.int32))).astype(np.int32)
+            .view(np.float32) for v in (0.5, -3.0)]
+    special = np.array([0.0, -0.0, 1e-30, -1e-30, 1e-45, 16.635532, 88.0, -88.0, 100.0, -100.0, -103.97,
+                        1e30, -1e30], np.float32)
+    lg = np.concatenate([even] + runs + [special])
+    got = host(moeq8.moe_router_scores(to_dev(lg)))
+    ref = oracle.sigmoid_f32(lg)
+    bad = np.flatnonzero(got.view(np.int32) != ref.view(np.int32))
+    assert bad.size == 0, (bad[:8], lg[bad[:8]], got[bad[:8]], ref[bad[:8]])
+
+
 @pytest.mark.parametrize("c,n_exp,hidden,inter", [(40, 32, 1024, 256), (130, 64, 512, 256)])
 def test_wide_grouped_products_vs_oracle(c, n_exp, hidden, inter):
     """Grouped gate/up and down over a wide grouping (items take their routes
