@@ -686,7 +686,7 @@ def best_ceiling(torch, moeq8, regions, reps, sink):
     return best
 
 
-def sweep_replicas(torch, workloads, moeq8, cols, hidden, inter, topk, n_exp, seed):
+def sweep_replicas(torch, workloads, moeq8, cols, hidden, inter, topk, n_exp, seed, block_bytes=34):
     """Replica layers of the 256-expert routed layer at `cols` columns until
     the down launches of one rotation read at least ROTATION_BYTES.  Each
     replica draws its own x, logits and bias (seeded by its index) and is
@@ -695,8 +695,9 @@ def sweep_replicas(torch, workloads, moeq8, cols, hidden, inter, topk, n_exp, se
     every other expert to -1.  The top-k runs over all 256 experts whatever
     the owner map says, so the layer selects, weights and computes exactly as
     with all 256 experts stored, and its launches read the same bytes; the
-    replicas only stop the 256 MB Infinity Cache from serving a rotation."""
-    dn_expert = hidden * (inter // 32 * 34)
+    replicas only stop the 256 MB Infinity Cache from serving a rotation.
+    block_bytes is the weight format's bytes per 32 values (34: Q8_0)."""
+    dn_expert = hidden * (inter // 32 * block_bytes)
     reps, total = [], 0
     while total < ROTATION_BYTES:
         l = len(reps)
@@ -976,82 +977,85 @@ def codec_bench(torch, workloads, moeq8, args):
 
 def q4_sweep(torch, workloads, moeq8, ml, args):
     """The sweep's routed layer (256 experts, top-8, no shared expert) with
-    4-bit expert weights: N(0, 0.02^2) weights drawn on the GPU (torch, seeded)
-    and quantised by q4_quantize_rows, 4 rotating replicas (5.4 GB).  Per
-    column count: the four-launch layer, the grouped gate/up alone, and the
-    streaming ceiling for the same bytes."""
+    4-bit expert weights, on replica layers as in the sweep (each stores only
+    the experts its routing selects; every rotation reads at least
+    ROTATION_BYTES of 4-bit down weights, so the Infinity Cache cannot serve
+    it).  Weights are N(0, 0.02^2) drawn on the GPU (torch, seeded) and
+    quantised by q4_quantize_rows.  Per column count: the four-launch layer,
+    the grouped gate/up alone, and the streaming-read ceiling of the same
+    bytes per launch from the replicas' gate and up banks (best read shape)."""
     cfg = workloads.CONFIGS["verify_e256_c5"]
     hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
-    reps = 4
     q4b = 18
     gen = torch.Generator(device="cuda").manual_seed(44)
-    per_gu = inter * (hidden // 32) * q4b
-    per_d = hidden * (inter // 32) * q4b
-    banks = []
-    for _ in range(reps):
-        t = {}
-        for name, rows, k, per in (("gate", inter, hidden, per_gu), ("up", inter, hidden, per_gu),
-                                   ("down", hidden, inter, per_d)):
-            buf = torch.empty(n_exp * per, dtype=torch.uint8, device="cuda")
-            for e in range(n_exp):
-                w = torch.randn((rows, k), generator=gen, device="cuda") * 0.02
-                moeq8.q4_quantize_rows(w, out=buf[e * per:(e + 1) * per].view(rows, -1))
-            t[name] = buf
-        banks.append(t)
-    torch.cuda.synchronize()
-    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
     row_gu = (hidden // 32) * q4b
+    per_gu = inter * row_gu
+    per_d = hidden * (inter // 32) * q4b
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
     out = []
     for cols in (1, 2, 4, 5, 8):
-        xs, lgs, bs = layer_inputs(torch, workloads, 4, reps, cols, hidden, n_exp)
-        wss = [ml.Workspace(cols, hidden, inter, topk, 0, "cuda") for _ in range(reps)]
-        experts = [ml.RoutedExperts(b["gate"], b["up"], b["down"], n_exp, hidden, inter, fmt="q4")
-                   for b in banks]
+        reps = sweep_replicas(torch, workloads, moeq8, cols, hidden, inter, topk, n_exp, 4, block_bytes=q4b)
+        R = len(reps)
+        banks = []
+        for rp in reps:
+            d = rp["n_local"]
+            # gate then up in one buffer, so that one plain read covers both
+            w = torch.empty(2 * d * per_gu, dtype=torch.uint8, device="cuda")
+            down = torch.empty(d * per_d, dtype=torch.uint8, device="cuda")
+            for buf, base, rows, k, per in ((w, 0, inter, hidden, per_gu), (w, d * per_gu, inter, hidden, per_gu),
+                                            (down, 0, hidden, inter, per_d)):
+                for e in range(d):
+                    x = torch.randn((rows, k), generator=gen, device="cuda") * 0.02
+                    moeq8.q4_quantize_rows(x, out=buf[base + e * per:base + (e + 1) * per].view(rows, -1))
+            banks.append({"w": w, "gate": w[:d * per_gu], "up": w[d * per_gu:], "down": down})
+        torch.cuda.synchronize()
+        wss = [ml.Workspace(cols, hidden, inter, topk, 0, "cuda") for _ in range(R)]
+        experts = [ml.RoutedExperts(b["gate"], b["up"], b["down"], reps[l]["n_local"], hidden, inter, fmt="q4")
+                   for l, b in enumerate(banks)]
 
         def step():
-            for l in range(reps):
-                ml.forward(xs[l], lgs[l], bs[l], None, n_exp, experts[l], None, wss[l])
+            for l in range(R):
+                rp = reps[l]
+                ml.forward(rp["x"], rp["logits"], rp["bias"], rp["owner"], rp["n_local"], experts[l], None,
+                           wss[l])
 
         step()
         torch.cuda.synchronize()
         n_active, n_valid = [], []
-        for l in range(reps):
+        for l in range(R):
             words = wss[l].grouping.cpu().numpy().view(np.int32)
             n_active.append(int(words[0]))
             n_valid.append(int(words[1]))
+            assert n_active[l] == reps[l]["n_local"]
         n = max(20, args.steps)
-        ms = time_graph(torch, step, n) / reps
+        ms = time_graph(torch, step, n) / R
 
         def gate_up_only():
-            for l in range(reps):
+            for l in range(R):
                 moeq8.moe_grouped_mmvq_q4(moeq8.GATE_UP_SWIGLU, banks[l]["gate"], banks[l]["up"], wss[l].xq,
-                                          wss[l].grouping, n=inter, k=hidden, n_local_expert=n_exp,
+                                          wss[l].grouping, n=inter, k=hidden, n_local_expert=reps[l]["n_local"],
                                           ncols=cols, topk=topk, out=wss[l].h)
 
         gu_b = [n_active[l] * 2 * inter * row_gu + cols * (hidden // 32 * 36) + n_valid[l] * inter * 4
-                for l in range(reps)]
-        read_b = [int(b) // 16 * 16 for b in gu_b]
-
-        def stream_only():
-            for l in range(reps):
-                moeq8.stream_read(banks[l]["gate"], min(read_b[l], banks[l]["gate"].numel() // 16 * 16), sink)
-
-        gu_us = time_graph(torch, gate_up_only, n) / reps * 1e3
-        st_us = time_graph(torch, stream_only, n) / reps * 1e3
+                for l in range(R)]
+        gu_us = time_graph(torch, gate_up_only, n) / R * 1e3
+        gu_w = [n_active[l] * 2 * per_gu for l in range(R)]
+        st_us, st_wg = best_ceiling(torch, moeq8, [(banks[l]["w"], gu_w[l] // 16 * 16) for l in range(R)], n, sink)
         gu_gbps = float(np.mean(gu_b)) / (gu_us * 1e-6) / 1e9
-        st_bytes = float(np.mean([min(b, banks[0]["gate"].numel() // 16 * 16) for b in read_b]))
-        st_gbps = st_bytes / (st_us * 1e-6) / 1e9
-        weights = float(np.mean([n_active[l] * ml.expert_bytes_q4(hidden, inter) for l in range(reps)]))
-        rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2),
+        st_gbps = float(np.mean(gu_w)) / (st_us * 1e-6) / 1e9
+        weights = float(np.mean([n_active[l] * ml.expert_bytes_q4(hidden, inter) for l in range(R)]))
+        rec = {"cols": cols, "active_experts": round(float(np.mean(n_active)), 2), "replicas": R,
+               "rotation_bytes": int(sum(n_active[l] * ml.expert_bytes_q4(hidden, inter) for l in range(R))),
                "layer_us": round(ms * 1e3, 2), "layers_per_s": round(1e3 / ms, 1),
                "expert_weight_gbps": round(weights / (ms * 1e-3) / 1e9, 1),
                "gate_up_us": round(gu_us, 2), "gate_up_gbps": round(gu_gbps, 1),
                "gate_up_frac_of_peak": round(gu_gbps / HBM_PEAK_GBPS, 4),
-               "ceiling_gbps": round(st_gbps, 1), "gate_up_frac_of_ceiling": round(gu_gbps / st_gbps, 4)}
+               "ceiling_gbps": round(st_gbps, 1), "ceiling_wg_bytes": st_wg,
+               "gate_up_frac_of_ceiling": round(gu_gbps / st_gbps, 4)}
         log(f"q4 {rec}")
         out.append(rec)
-    del banks
-    torch.cuda.empty_cache()
+        del banks, experts, wss, reps
+        torch.cuda.empty_cache()
     return out
 
 

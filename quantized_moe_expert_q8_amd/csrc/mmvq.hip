@@ -390,11 +390,15 @@ __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uin
                     } else {
                         zero_x_chunk(xc);
                     }
+                    [[maybe_unused]] XBias xb{0, 0};
+                    if constexpr (Q4) xb = q4_x_bias(xc);      // once per column, for every row set
 #pragma unroll
                     for (int u = 0; u < U; ++u)
 #pragma unroll
                         for (int m = 0; m < NMAT; ++m) {
-                            const float d = chunk_dot(wc[u][m], xc);
+                            float d;
+                            if constexpr (Q4) d = chunk_dot(wc[u][m], xc, xb);
+                            else d = chunk_dot(wc[u][m], xc);
                             acc[c][u][m] += ((UNCOND || STX) && !ok[u]) ? 0.0f : d;
                         }
                 }

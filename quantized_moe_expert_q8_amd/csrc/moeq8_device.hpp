@@ -319,26 +319,38 @@ __device__ __forceinline__ void zero_w_chunk(W4Chunk& w) {
     for (int i = 0; i < W4_CHUNK_DWORDS; ++i) w.v[i] = 0u;
 }
 
-// Four codes (one per byte, 0..15) -> four signed bytes code - 8, with no
-// borrow between bytes: (c | 0x80) - 8 stays in 120..135, and flipping bit 7
-// back gives c - 8 modulo 256.
-__device__ __forceinline__ int signed_nibbles(uint32_t c4) {
-    return (int)(((c4 | 0x80808080u) - 0x08080808u) ^ 0x80808080u);
+// -8 times the quant sum of each block of a q8_1 chunk (v_dot4 against -8 in
+// every byte): the term that turns a dot product of raw 4-bit codes (0..15,
+// valid signed bytes) into one of code - 8.  Computed once per activation
+// chunk and shared by every weight chunk it meets.
+struct XBias { int b0, b1; };
+
+__device__ __forceinline__ XBias q4_x_bias(const XChunk& x) {
+    constexpr int M8 = (int)0xF8F8F8F8u;                            // four int8 -8
+    int b0 = 0, b1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        b0 = __builtin_amdgcn_sdot4(M8, (int)x.v[1 + i], b0, false);
+        b1 = __builtin_amdgcn_sdot4(M8, (int)x.v[10 + i], b1, false);
+    }
+    return {b0, b1};
 }
 
 // Value of a 4-bit chunk against a q8_1 chunk, in the same form as the Q8_0
 // chunk: (d_w * d_x) * sumi per block, then the sum of the two blocks.  sumi
-// is the exact integer sum of (code - 8) * q.
-__device__ __forceinline__ float chunk_dot(const W4Chunk& w, const XChunk& x) {
-    int s0 = 0, s1 = 0;
+// is the exact integer sum of (code - 8) * q, taken as sum(code * q) started
+// from the block's -8 * sum(q) (xb, from q4_x_bias of the same chunk): the same
+// integer as summing (code - 8) * q term by term.
+__device__ __forceinline__ float chunk_dot(const W4Chunk& w, const XChunk& x, const XBias& xb) {
+    int s0 = xb.b0, s1 = xb.b1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t c0 = (w.v[i] >> 16) | (w.v[i + 1] << 16);   // block 0, bytes 4i .. 4i+3
-        s0 = __builtin_amdgcn_sdot4(signed_nibbles(c0 & 0x0f0f0f0fu), (int)x.v[1 + i], s0, false);
-        s0 = __builtin_amdgcn_sdot4(signed_nibbles((c0 >> 4) & 0x0f0f0f0fu), (int)x.v[5 + i], s0, false);
+        s0 = __builtin_amdgcn_sdot4((int)(c0 & 0x0f0f0f0fu), (int)x.v[1 + i], s0, false);
+        s0 = __builtin_amdgcn_sdot4((int)((c0 >> 4) & 0x0f0f0f0fu), (int)x.v[5 + i], s0, false);
         const uint32_t c1 = w.v[5 + i];                             // block 1
-        s1 = __builtin_amdgcn_sdot4(signed_nibbles(c1 & 0x0f0f0f0fu), (int)x.v[10 + i], s1, false);
-        s1 = __builtin_amdgcn_sdot4(signed_nibbles((c1 >> 4) & 0x0f0f0f0fu), (int)x.v[14 + i], s1, false);
+        s1 = __builtin_amdgcn_sdot4((int)(c1 & 0x0f0f0f0fu), (int)x.v[10 + i], s1, false);
+        s1 = __builtin_amdgcn_sdot4((int)((c1 >> 4) & 0x0f0f0f0fu), (int)x.v[14 + i], s1, false);
     }
     const float dw0 = half_bits_to_float(w.v[0]);
     const float dw1 = half_bits_to_float(w.v[4] >> 16);
