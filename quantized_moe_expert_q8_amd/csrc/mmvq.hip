@@ -536,6 +536,9 @@ constexpr int u_for(int nmat, bool act_f32, bool q4 = false) {
 
 int rows_per_wg_for(const Shape& s, int u) { return WAVES_PER_WG * u * (4 / s.G); }
 
+// row sets a wave of the packed gate/up takes for passes of 1-2 columns
+constexpr int P64_SMALL_U = 1;
+
 template <int NMAT, bool GROUPED, bool ACT_F32, bool STX, bool Q4, int U = u_for(NMAT, ACT_F32, Q4)>
 int launch_shape(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, hipStream_t stream) {
     const dim3 block(64 * WAVES_PER_WG);
@@ -571,9 +574,10 @@ int launch_p64(bool down, MmvqParams& p, const Shape& s, int64_t grid, size_t ld
         else hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true>), g, block, lds, stream, p);
     } else {
         constexpr int U = u_for(2, false, false);
+        constexpr int US = P64_SMALL_U;                 // passes of 1-2 columns (the host sized the grid so)
         if (reread) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, true>), g, block, 0, stream, p);
-        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, false, 1>), g, block, 0, stream, p);
-        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, false, 2>), g, block, 0, stream, p);
+        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<4, 2, US, true, false, false, false, true, false, 1>), g, block, 0, stream, p);
+        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<4, 2, US, true, false, false, false, true, false, 2>), g, block, 0, stream, p);
         else if (mc == 4) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, false, 4>), g, block, 0, stream, p);
         else hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), g, block, 0, stream, p);
     }
@@ -775,7 +779,11 @@ int prepare_grouped(GroupedLaunch& L, bool q4, int32_t stage, const void* w_a, c
 
     MmvqParams p = {};
     const Shape s = pick_shape(0, k / 64);
-    p.rows_per_wg = rows_per_wg_for(s, u_for(pair ? 2 : 1, f32, q4));
+    // the packed gate/up takes one row set a wave for passes of 1-2 columns
+    // (twice the workgroups, each finishing sooner: 13.08 -> 12.85 us at one
+    // column, 23.29 -> 22.61 at two); the down keeps two at every width (one
+    // measured 7.72 -> 8.30 us at one column)
+    p.rows_per_wg = rows_per_wg_for(s, (p64 && ncols <= 2) ? P64_SMALL_U : u_for(pair ? 2 : 1, f32, q4));
     p.m = make_desc(w_a, w_b, w_row_stride_bytes, n, k, 0, p.rows_per_wg);
     p.expert_stride = expert_stride_bytes;
     p.n_local = n_local_expert;
