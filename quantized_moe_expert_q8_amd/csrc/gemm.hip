@@ -43,6 +43,7 @@
 #include "moeq8_device.hpp"
 #include "moeq8_host.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace moeq8 {
@@ -133,51 +134,68 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
     return v;
 }
 
-// The work unit of this workgroup: units are (group, row tile, chunk of up
-// to CHUNK of the group's routes), numbered chunk-fastest; unit u runs on XCD
-// u / ceil(units / 8) (workgroups are dispatched to the 8 XCDs round-robin),
-// so the chunks that read the same weight rows run on one XCD close together
-// in time.  Returns false when this workgroup has no unit.  Every lane of the
-// workgroup gets the same answer (wave-uniform values only).
+// Work units are (group, row tile, chunk of up to CHUNK of the group's
+// routes), numbered chunk-fastest; the units are dealt to the 8 XCDs in
+// contiguous ranges (workgroups are dispatched to the XCDs round-robin), so
+// the chunks that read the same weight rows run on one XCD close together in
+// time.  Every lane of a workgroup computes the same values (wave-uniform
+// loads and scans only).
+
+// The grouping's number of active groups and of units; false for a grouping
+// that does not match the launch.
 template <int CHUNK>
-__device__ __forceinline__ bool find_unit(const GemmParams& p, int l, int& e, int& rbegin, int& nr, uint32_t& t) {
+__device__ __forceinline__ bool grouping_units(const GemmParams& p, int l, int& n_active, uint32_t& total) {
     const int Rk = p.ncols * p.topk;
     const int4w hdr = grouping_words4(p.grouping, 0);
     if ((hdr[2] != p.ncols) | (hdr[3] != p.topk) | (hdr[0] < 0) | (hdr[0] > Rk) | (hdr[1] < 0) |
         (hdr[1] > Rk))
         return false;
-    const int n_active = hdr[0];
+    n_active = hdr[0];
     const uint32_t tiles = (uint32_t)p.tiles;
-    const uint32_t xcd = blockIdx.x % XCDS;
-    const uint32_t slot = blockIdx.x / XCDS;
-    // chunks <= n_active + n_valid / CHUNK, so slots past this bound have nothing
-    const uint32_t bound = ((uint32_t)n_active + (uint32_t)hdr[1] / CHUNK) * tiles;
-    if (slot >= (bound + XCDS - 1) / XCDS) return false;
-
     const int4* table = reinterpret_cast<const int4*>(p.grouping + grouping_table_word(Rk));
-    auto units_of = [&](int a, int4& g) -> uint32_t {
-        if (a >= n_active) return 0u;
-        g = table[a];
-        const bool ok = (g.x >= 0) & (g.x < p.n_local) & (g.y >= 0) & (g.z >= g.y) & (g.z <= Rk);
-        return ok ? (uint32_t)((g.z - g.y + CHUNK - 1) / CHUNK) * tiles : 0u;
-    };
-    uint32_t total = 0;
+    total = 0;
     for (int b0 = 0; b0 < n_active; b0 += 64) {
-        int4 g;
-        const uint32_t s = wave_incl_scan(units_of(b0 + l, g), l);
+        uint32_t un = 0;
+        const int a = b0 + l;
+        if (a < n_active) {
+            const int4 g = table[a];
+            const bool ok = (g.x >= 0) & (g.x < p.n_local) & (g.y >= 0) & (g.z >= g.y) & (g.z <= Rk);
+            un = ok ? (uint32_t)((g.z - g.y + CHUNK - 1) / CHUNK) * tiles : 0u;
+        }
+        const uint32_t s = wave_incl_scan(un, l);
         total += (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
     }
-    const uint32_t per = total / XCDS, extra = total % XCDS;
-    if (slot >= per + (xcd < extra ? 1u : 0u)) return false;
-    const uint32_t u = xcd * per + min(xcd, extra) + slot;
+    return true;
+}
+
+// Unit u (< the total): its local expert e, first route entry rbegin, route
+// count nr (1..CHUNK) and row tile t; false if its group is empty.
+template <int CHUNK>
+__device__ __forceinline__ bool unit_at(const GemmParams& p, int l, int n_active, uint32_t u, int& e, int& rbegin,
+                                        int& nr, uint32_t& t) {
+    const int Rk = p.ncols * p.topk;
+    const uint32_t tiles = (uint32_t)p.tiles;
+    const int4* table = reinterpret_cast<const int4*>(p.grouping + grouping_table_word(Rk));
     int gbegin = 0, gend = 0;
     uint32_t ubase = 0;
     e = 0;
-    {
-        uint32_t carry = 0;
-        for (int b0 = 0; b0 < n_active; b0 += 64) {
-            int4 g = make_int4(0, 0, 0, 0);
-            const uint32_t un = units_of(b0 + l, g);
+    uint32_t carry = 0;
+    bool found = false;
+    // 256 groups at a time: their records are read before any is scanned
+    for (int b0 = 0; b0 < n_active && !found; b0 += 256) {
+        int4 gq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int a = b0 + 64 * k + l;
+            gq[k] = a < n_active ? table[a] : make_int4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (found || b0 + 64 * k >= n_active) break;
+            const int4 g = gq[k];
+            const bool ok = (b0 + 64 * k + l < n_active) & (g.x >= 0) & (g.x < p.n_local) & (g.y >= 0) &
+                            (g.z >= g.y) & (g.z <= Rk);
+            const uint32_t un = ok ? (uint32_t)((g.z - g.y + CHUNK - 1) / CHUNK) * tiles : 0u;
             const uint32_t incl = wave_incl_scan(un, l) + carry;
             const bool hit = (un > 0) & (incl - un <= u) & (u < incl);
             const uint64_t m = __ballot(hit);
@@ -187,9 +205,10 @@ __device__ __forceinline__ bool find_unit(const GemmParams& p, int l, int& e, in
                 gbegin = __builtin_amdgcn_readlane(g.y, src);
                 gend = __builtin_amdgcn_readlane(g.z, src);
                 ubase = (uint32_t)__builtin_amdgcn_readlane((int)(incl - un), src);
-                break;
+                found = true;
+            } else {
+                carry = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
             }
-            carry = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
         }
     }
     if (gend <= gbegin) return false;
@@ -199,6 +218,34 @@ __device__ __forceinline__ bool find_unit(const GemmParams& p, int l, int& e, in
     rbegin = gbegin + (int)(rem - t * nchunk) * CHUNK;
     nr = min(gend - rbegin, CHUNK);                    // routes of this unit, 1..CHUNK
     return true;
+}
+
+// The units of XCD x: [first, end) of the total, contiguous.
+__device__ __forceinline__ void xcd_range(uint32_t total, uint32_t x, uint32_t& first, uint32_t& end) {
+    const uint32_t per = total / XCDS, extra = total % XCDS;
+    first = x * per + min(x, extra);
+    end = first + per + (x < extra ? 1u : 0u);
+}
+
+// The one unit of this workgroup in a grid of one workgroup per unit (the
+// grid covers an upper bound of the units; the excess returns false).
+template <int CHUNK>
+__device__ __forceinline__ bool find_unit(const GemmParams& p, int l, int& e, int& rbegin, int& nr, uint32_t& t) {
+    {
+        // units <= (active groups + valid routes / CHUNK) * tiles: slots past
+        // that bound leave before the scan
+        const int4w hdr = grouping_words4(p.grouping, 0);
+        const uint32_t bound = ((uint32_t)max(hdr[0], 0) + (uint32_t)max(hdr[1], 0) / CHUNK) * (uint32_t)p.tiles;
+        if (blockIdx.x / XCDS >= (bound + XCDS - 1) / XCDS) return false;
+    }
+    int n_active;
+    uint32_t total;
+    if (!grouping_units<CHUNK>(p, l, n_active, total)) return false;
+    uint32_t first, end;
+    xcd_range(total, blockIdx.x % XCDS, first, end);
+    const uint32_t u = first + blockIdx.x / XCDS;
+    if (u >= end) return false;
+    return unit_at<CHUNK>(p, l, n_active, u, e, rbegin, nr, t);
 }
 
 template <bool PAIR>
@@ -371,54 +418,51 @@ __global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(nt
     }
 }
 
-// Staged gate/up pair (k % 256 == 0, n % 32 == 0, 16-byte aligned operands):
-// a workgroup of eight waves stages each K step of 8 blocks (256 values) of
-// 32 rows of the gate and of the up matrix and of its routes' activations in
-// LDS with direct 16-byte global-to-LDS loads (no registers on the way), the
-// next step in flight while one is computed, and every wave reads its
-// matrix-core fragments from there: a staged weight row serves all four
-// route tiles and a staged activation row both row groups, so each byte is
-// fetched once per workgroup (the register-fed form above fetches each
-// activation once per wave).  Only whole 16-route tiles that hold routes are
-// staged and run.  Wave w runs rows 16 (w & 1) + [0, 16) of both matrices
-// against route tile w >> 1.
+// Staged form (k % 256 == 0, whole row tiles, 16-byte aligned operands): a
+// workgroup of eight waves stages each K step of 8 blocks (256 values) of its
+// unit's 64 weight rows (gate/up: 32 rows of each matrix) and of up to 64
+// routes' activations in LDS with direct 16-byte global-to-LDS loads (no
+// registers on the way), and every wave reads its matrix-core fragments from
+// there: a staged weight row serves every route tile and a staged activation
+// row every row group, so each byte is fetched once per workgroup (the
+// register-fed form above fetches each activation once per wave).  Only whole
+// 16-route tiles that hold routes are staged and run.
+//   gate/up: wave w runs rows 16 (w & 1) + [0, 16) of both matrices against
+//            route tile w >> 1;  down: rows 16 (w & 3) + [0, 16) against route
+//            tiles 2 (w >> 2) and 2 (w >> 2) + 1.
+// The grid is two workgroups a CU; each takes every S-th unit of its XCD's
+// range (S = workgroups an XCD), and the steps of its units form one
+// pipeline: the next step's loads, the next unit's first step included, are
+// in flight while a step is computed, and the next unit's lookup and route
+// entries are read while its first step loads, so a unit costs its steps and
+// not a fresh fill (the down has only a few steps a unit).
 //   LDS per step: weights 64 rows x 272 bytes (a row's 8 blocks, as stored),
 //   activations 64 routes x 288 bytes; per wave, fp32 activation scales of
 //   its route slots.  Every wave issues the same six loads a step (pieces it
-//   has no use for go to a scratch area of LDS), so the wait for a step is a
-//   fixed count of loads still in flight.  A weight row's quants sit 2 bytes
-//   into each 34-byte block, so a fragment of an even block is cut from three
-//   aligned dwords.
+//   has no use for go to a scratch area of LDS).  A weight row's quants sit 2
+//   bytes into each 34-byte block, so a fragment of an even block is cut from
+//   three aligned dwords.
 // Arithmetic and order are those of the form above: acc = fma(float(sumi),
 // d_w * d_x, acc), blocks ascending from +0, so both forms give the same bits.
 // The form is bound by that per-block scaling (three VALU operations per
-// output, row and block) and its LDS reads more than by the loads; with the
-// down product's short K (a few steps) the pipeline fill outweighs the shared
-// staging, so the down product stays on the register-fed form.
+// output, row and block) and its LDS reads more than by its loads.
 constexpr int S_THREADS = 512;
+constexpr int S_WG_PER_CU = 2;                   // the LDS below holds two
 constexpr int S_CHUNK = 64;                      // routes per unit
 constexpr int S_STEP_BLOCKS = 8;                 // blocks per K step
 constexpr int S_WROW = S_STEP_BLOCKS * Q80_BYTES;   // 272
 constexpr int S_AROW = S_STEP_BLOCKS * Q81_BYTES;   // 288
-constexpr int S_W = 64 * S_WROW;                 // 17408: 32 gate rows, then 32 up rows
+constexpr int S_W = 64 * S_WROW;                 // 17408: 64 weight rows
 constexpr int S_A = S_CHUNK * S_AROW;            // 18432: 64 routes
 constexpr int S_STAGE = S_W + S_A;               // 35840
-constexpr int S_STAGES = 2;                      // steps staged at once
-constexpr int S_DX = S_STAGES * S_STAGE;         // per wave: fp32 [8 blocks][16 slots]
-constexpr int S_DX_WAVE = S_STEP_BLOCKS * 16 * 4;    // 512
+constexpr int S_DX = 2 * S_STAGE;                // per wave: fp32 [8 blocks][32 slots]
+constexpr int S_DX_WAVE = S_STEP_BLOCKS * 32 * 4;    // 1024
 constexpr int S_JUNK = S_DX + 8 * S_DX_WAVE;     // 1 KB target of the loads no wave needs
-constexpr int S_LDS = S_JUNK + 1024;             // 76800: two workgroups a CU
+constexpr int S_LDS = S_JUNK + 1024;             // 80896
 constexpr int S_W_LOADS = S_W / 1024;            // 17 wave-loads of 1 KB
 constexpr int S_A_LOADS = S_A / 1024;            // 18
 constexpr int S_SLOTS = (S_A_LOADS + 7) / 8;     // 3 wave-loads of each kind per wave
-constexpr int S_LOADS = 2 * S_SLOTS;             // loads every wave issues a step
-
-// s_waitcnt with vmcnt(n) alone (n < 64; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
+static_assert(S_WG_PER_CU * S_LDS <= 160 * 1024, "LDS of a CU");
 
 // Workgroup barrier over LDS only: waits for this wave's LDS operations, not
 // for its global loads, so a step's loads stay in flight across it (the
@@ -440,6 +484,8 @@ __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
                  :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) alone
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* b, int off) {
     return *reinterpret_cast<const uint32_t*>(b + off);
@@ -467,157 +513,268 @@ __device__ __forceinline__ long a_frag(const uint8_t* ar, int q8) {
     return (long)(((uint64_t)hi << 32) | lo);
 }
 
-__global__ __launch_bounds__(S_THREADS) void k_grouped_gemm_pair_staged(const GemmParams p) {
-    __shared__ __align__(16) uint8_t lds[S_LDS];
-    const int wave = threadIdx.x >> 6;
-    const int l = threadIdx.x & 63;
-    const int c = l & 15;
-    const int q8 = (l >> 4) * 8;
+// Where this lane's pieces of a step come from and go to, the same for every
+// unit and step: weight piece j of the wave is row wrow, 16-byte part wpart
+// of the stage's weight rows (gate/up: rows 0..31 gate, 32..63 up);
+// activation piece j is route slot aslot (-1: past the stage), part apart.
+struct StageGeometry {
+    int w_off[S_SLOTS];                                // wrow' * row_stride + 16 wpart (wrow' = row in its matrix)
+    uint32_t w_up;                                     // bit j: piece j is of the second matrix
+    int a_slot[S_SLOTS];
+    int a_part[S_SLOTS];                               // 16 apart
+};
 
-    const int Rk = p.ncols * p.topk;
-    int e, rbegin, nr;
-    uint32_t t;
-    if (!find_unit<S_CHUNK>(p, l, e, rbegin, nr, t)) return;
-    const int64_t r0 = (int64_t)t * 32;                // first row of the unit in each matrix
-    const int32_t* route = p.grouping + 4 + 2 * (int64_t)Rk + 1;
-    const int nslot = (nr + 15) & ~15;                 // staged route slots: whole tiles
-    const int rh = (wave & 1) * 16;                    // this wave's rows (of each matrix)
-    const int slot0 = (wave >> 1) * 16;                // and route slots
-    const bool live = slot0 < nslot;                   // the tile holds routes
-
-    // per-lane sources of this wave's loads (the same for every K step).  A
-    // wave-load past the stage goes to the scratch area; a lane whose piece
-    // is past the staged route slots reads the unit's first activation piece
-    // (one cached line for all such lanes) into an unused slot.
-    const uint8_t* wsrc[S_SLOTS];
-    const uint8_t* asrc[S_SLOTS];
-    const uint8_t* a_first;
-    {
-        const int rt = route[rbegin];
-        const int rr = (rt >= 0 && rt < Rk) ? rt : 0;
-        a_first = p.act + (int64_t)(((uint64_t)(uint32_t)rr * p.act_route_mul) >> 32) * p.act_row_bytes;
-    }
+template <bool PAIR>
+__device__ __forceinline__ void stage_geometry(const GemmParams& p, int wave, int l, StageGeometry& G) {
+    G.w_up = 0;
 #pragma unroll
     for (int j = 0; j < S_SLOTS; ++j) {
         const int i = 8 * j + wave;                    // wave-load index
         const int piece = min(i, S_W_LOADS - 1) * 64 + l;
         const int wrow = piece / 17, part = piece - wrow * 17;
-        wsrc[j] = (wrow < 32 ? p.w0 : p.w1) + (int64_t)e * p.expert_stride + (r0 + wrow % 32) * p.row_stride +
-                  part * 16;
+        const int m = PAIR ? wrow / 32 : 0;
+        const int r = PAIR ? wrow % 32 : wrow;
+        G.w_off[j] = r * (int)p.row_stride + part * 16;
+        G.w_up |= (uint32_t)m << j;
         const int apiece = min(i, S_A_LOADS - 1) * 64 + l;
-        const int slot = apiece / 18, apart = apiece - slot * 18;
-        if (i < S_A_LOADS && slot < nslot) {
-            const int rt = route[rbegin + min(slot, nr - 1)];
-            const int rr = (rt >= 0 && rt < Rk) ? rt : 0;
-            const int64_t arow = (int64_t)(((uint64_t)(uint32_t)rr * p.act_route_mul) >> 32);
-            asrc[j] = p.act + arow * p.act_row_bytes + apart * 16;
-        } else {
-            asrc[j] = a_first;
-        }
+        const int slot = apiece / 18;
+        G.a_slot[j] = i < S_A_LOADS ? slot : -1;
+        G.a_part[j] = (apiece - slot * 18) * 16;
     }
+}
+
+// The activation sources of a unit: byte offsets into the activations of
+// this lane's pieces (a piece past the unit's staged route slots reads the
+// unit's first activation piece, one cached line for all such lanes).
+__device__ __forceinline__ void stage_act(const GemmParams& p, const StageGeometry& G, int rbegin, int nr,
+                                          int (&a_off)[S_SLOTS]) {
+    const int Rk = p.ncols * p.topk;
+    const int32_t* route = p.grouping + 4 + 2 * (int64_t)Rk + 1;
+    const int nslot = (nr + 15) & ~15;                 // staged route slots: whole tiles
+    auto row_off = [&](int rt) {
+        const int rr = (rt >= 0 && rt < Rk) ? rt : 0;
+        return (int)(((uint64_t)(uint32_t)rr * p.act_route_mul) >> 32) * (int)p.act_row_bytes;
+    };
+    // every entry read at an index inside the unit, all before the first use
+    const int r_first = route[rbegin];
+    int rts[S_SLOTS];
+#pragma unroll
+    for (int j = 0; j < S_SLOTS; ++j) rts[j] = route[rbegin + min(max(G.a_slot[j], 0), nr - 1)];
+    const int first = row_off(r_first);
+#pragma unroll
+    for (int j = 0; j < S_SLOTS; ++j) {
+        const int slot = G.a_slot[j];
+        a_off[j] = (slot >= 0 && slot < nslot) ? row_off(rts[j]) + G.a_part[j] : first;
+    }
+}
+
+template <bool PAIR>
+__global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_gemm_staged(
+    const GemmParams p) {
+    __shared__ __align__(16) uint8_t lds[S_LDS];
+    constexpr int NM = PAIR ? 2 : 1;                   // weight fragments a wave reads a block
+    constexpr int NR = PAIR ? 1 : 2;                   // route tiles a wave runs
+    constexpr int TILE_ROWS = PAIR ? 32 : 64;
+    const int wave = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int c = l & 15;
+    const int q8 = (l >> 4) * 8;
+    const int rh = PAIR ? (wave & 1) * 16 : (wave & 3) * 16;   // this wave's rows (of each matrix)
+    const int tile0 = PAIR ? (wave >> 1) : (wave >> 2) * 2;    // and first route tile
+    const int Rk = p.ncols * p.topk;
+    const int32_t* route = p.grouping + 4 + 2 * (int64_t)Rk + 1;
+
+    int n_active;
+    uint32_t total;
+    if (!grouping_units<S_CHUNK>(p, l, n_active, total)) return;
+    uint32_t first, end;
+    xcd_range(total, blockIdx.x % XCDS, first, end);
+    const uint32_t stride = gridDim.x / XCDS;          // workgroups an XCD (the grid is a multiple of 8)
+    uint32_t u = first + blockIdx.x / XCDS;
+    if (u >= end) return;
+    // the current unit: expert, route entries, row tile (wave-uniform)
+    int e, rbegin, nr;
+    uint32_t t;
+    if (!unit_at<S_CHUNK>(p, l, n_active, u, e, rbegin, nr, t)) return;   // before any load
+
+    StageGeometry G;
+    stage_geometry<PAIR>(p, wave, l, G);
+    int a_off[S_SLOTS];
+    stage_act(p, G, rbegin, nr, a_off);
+
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    auto load_step = [&](int s, int b) {
+    // step s of the unit of expert ee, row tile tt, activation offsets ao, into buffer b
+    auto load_step = [&](int ee, uint32_t tt, const int (&ao)[S_SLOTS], int s, int b) {
+        const int64_t wb = (int64_t)ee * p.expert_stride + (int64_t)tt * TILE_ROWS * p.row_stride + (int64_t)s * S_WROW;
+        const uint8_t* w0 = p.w0 + wb;
+        const uint8_t* w1 = PAIR ? p.w1 + wb : w0;
+        const uint8_t* act = p.act + (int64_t)s * S_AROW;
         const uint32_t base = lds0 + b * S_STAGE;
 #pragma unroll
         for (int j = 0; j < S_SLOTS; ++j) {
             const int i = 8 * j + wave;
-            load_lds16(wsrc[j] + (int64_t)s * S_WROW, i < S_W_LOADS ? base + i * 1024 : lds0 + S_JUNK);
-            load_lds16(asrc[j] + (int64_t)s * S_AROW, i < S_A_LOADS ? base + S_W + i * 1024 : lds0 + S_JUNK);
+            load_lds16(((G.w_up >> j) & 1u ? w1 : w0) + G.w_off[j], i < S_W_LOADS ? base + i * 1024 : lds0 + S_JUNK);
+            load_lds16(act + ao[j], i < S_A_LOADS ? base + S_W + i * 1024 : lds0 + S_JUNK);
         }
     };
-
-    float acc[2][4];                                   // [gate, up][route slot slot0 + 4q + i]
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][i] = 0.0f;
-
-    float* dxt = reinterpret_cast<float*>(lds + S_DX + wave * S_DX_WAVE);   // [8 blocks][16 slots]
+    float* dxt = reinterpret_cast<float*>(lds + S_DX + wave * S_DX_WAVE);   // [8 blocks][32 slots]
     const int nsteps = p.nb / S_STEP_BLOCKS;
-#pragma unroll
-    for (int st = 0; st < S_STAGES - 1; ++st)
-        if (st < nsteps) load_step(st, st);
-    for (int s = 0; s < nsteps; ++s) {
-        const int b = s % S_STAGES;
-        // step s is in LDS once this wave's loads of the steps after it are
-        // all that is left in flight (loads complete in order) and every
-        // wave has passed this barrier; every wave is then also done with
-        // step s - 1, whose buffer takes step s + S_STAGES - 1
-        static_assert(S_STAGES >= 2 && S_STAGES <= 4, "the waits below cover up to two steps ahead");
-        const int ahead = min(S_STAGES - 2, nsteps - 1 - s);
-        if (ahead >= 2) wait_vm<2 * S_LOADS>();
-        else if (ahead == 1) wait_vm<S_LOADS>();
-        else wait_vm<0>();
-        lds_barrier();
-        if (s + S_STAGES - 1 < nsteps) load_step(s + S_STAGES - 1, (s + S_STAGES - 1) % S_STAGES);
-        if (!live) continue;
-        const uint8_t* W = lds + b * S_STAGE;
-        const uint8_t* A = W + S_W;
-        // this wave's activation scales, fp32 (read back by this wave only)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ent = h * 64 + l;
-            const int k = ent >> 4, sl = ent & 15;
-            dxt[k * 16 + sl] = half_bits_to_float(
-                *reinterpret_cast<const uint16_t*>(A + (slot0 + sl) * S_AROW + k * Q81_BYTES));
-        }
-        const uint8_t* wg = W + (rh + c) * S_WROW;
-        const uint8_t* wu = W + (32 + rh + c) * S_WROW;
-        const uint8_t* ar = A + (slot0 + c) * S_AROW;
-        // two blocks at a time: fragments of both, then the matrix-core
-        // products of both, then the scaled sums in block order (block K
-        // enters every accumulator before block K + 1)
-        auto two_blocks = [&](auto kc) {
-            constexpr int K0 = 2 * decltype(kc)::value;
-            long wb[2][2], xa[2];
-            float dwv[2][2];
-            float4 dx4[2];
-            i32x4 d[2][2];
-            wb[0][0] = w_frag<K0>(wg, q8);
-            wb[0][1] = w_frag<K0>(wu, q8);
-            wb[1][0] = w_frag<K0 + 1>(wg, q8);
-            wb[1][1] = w_frag<K0 + 1>(wu, q8);
-            dwv[0][0] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wg + K0 * Q80_BYTES));
-            dwv[0][1] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wu + K0 * Q80_BYTES));
-            dwv[1][0] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wg + (K0 + 1) * Q80_BYTES));
-            dwv[1][1] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wu + (K0 + 1) * Q80_BYTES));
-            xa[0] = a_frag<K0>(ar, q8);
-            xa[1] = a_frag<K0 + 1>(ar, q8);
-            dx4[0] = *reinterpret_cast<const float4*>(dxt + K0 * 16 + q8 / 2);
-            dx4[1] = *reinterpret_cast<const float4*>(dxt + (K0 + 1) * 16 + q8 / 2);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const i32x4 z = {0, 0, 0, 0};
-                    d[kk][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa[kk], wb[kk][m], z, 0, 0, 0);
-                }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const float dxv[4] = {dx4[kk].x, dx4[kk].y, dx4[kk].z, dx4[kk].w};
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[m][i] = fmaf((float)d[kk][m][i], dwv[kk][m] * dxv[i], acc[m][i]);
-            }
-        };
-        two_blocks(std::integral_constant<int, 0>{});
-        two_blocks(std::integral_constant<int, 1>{});
-        two_blocks(std::integral_constant<int, 2>{});
-        two_blocks(std::integral_constant<int, 3>{});
-    }
 
-    // lane (c, q) holds row rh + c of both matrices for route slots slot0 + 4q + i
-    if (!live) return;
+    load_step(e, t, a_off, 0, 0);
+    int g = 0;                                         // steps of this workgroup so far
+    for (;;) {
+        // this lane's output rows (route slots 16 tile + 4q + i), read while
+        // the unit's first step loads
+        int out_route[NR][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int slotr = slot0 + q8 / 2 + i;
-        if (slotr >= nr) continue;
-        const int r = route[rbegin + slotr];
-        if (r < 0 || r >= Rk) continue;
-        p.out[(int64_t)r * p.n + r0 + rh + c] = swiglu_ds4_f32(acc[0][i], acc[1][i]);
+        for (int rt = 0; rt < NR; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int slotr = (tile0 + rt) * 16 + q8 / 2 + i;
+                const int r = route[rbegin + min(slotr, nr - 1)];   // an entry of the unit either way
+                out_route[rt][i] = (slotr < nr && r >= 0 && r < Rk) ? r : -1;
+            }
+        const int nslot = (nr + 15) & ~15;
+        bool live[NR];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) live[rt] = (tile0 + rt) * 16 < nslot;
+        float acc[NR][NM][4];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[rt][m][i] = 0.0f;
+
+        // one step from LDS buffer b
+        auto compute = [&](int b) {
+            const uint8_t* W = lds + b * S_STAGE;
+            const uint8_t* A = W + S_W;
+            // this wave's activation scales, fp32 (read back by this wave only)
+#pragma unroll
+            for (int h = 0; h < 2 * NR; ++h) {
+                const int ent = h * 64 + l;
+                const int k = ent / (16 * NR), sl = ent % (16 * NR);
+                dxt[k * 32 + sl] = half_bits_to_float(
+                    *reinterpret_cast<const uint16_t*>(A + (tile0 * 16 + sl) * S_AROW + k * Q81_BYTES));
+            }
+            // two blocks at a time: fragments of both, then the matrix-core
+            // products of both, then the scaled sums in block order (block K
+            // enters every accumulator before block K + 1)
+            auto run_step = [&](auto nlive) {
+                constexpr int NL = decltype(nlive)::value;   // live route tiles of this wave
+                auto two_blocks = [&](auto kc) {
+                    constexpr int K0 = 2 * decltype(kc)::value;
+                    long wb[2][NM], xa[2][NL];
+                    float dwv[2][NM];
+                    float4 dx4[2][NL];
+                    i32x4 d[2][NL][NM];
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        const uint8_t* wr = W + (m * 32 + rh + c) * S_WROW;
+                        wb[0][m] = w_frag<K0>(wr, q8);
+                        wb[1][m] = w_frag<K0 + 1>(wr, q8);
+                        dwv[0][m] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wr + K0 * Q80_BYTES));
+                        dwv[1][m] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wr + (K0 + 1) * Q80_BYTES));
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < NL; ++rt) {
+                        const uint8_t* ar = A + ((tile0 + rt) * 16 + c) * S_AROW;
+                        xa[0][rt] = a_frag<K0>(ar, q8);
+                        xa[1][rt] = a_frag<K0 + 1>(ar, q8);
+                        dx4[0][rt] = *reinterpret_cast<const float4*>(dxt + K0 * 32 + rt * 16 + q8 / 2);
+                        dx4[1][rt] = *reinterpret_cast<const float4*>(dxt + (K0 + 1) * 32 + rt * 16 + q8 / 2);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int rt = 0; rt < NL; ++rt)
+#pragma unroll
+                            for (int m = 0; m < NM; ++m) {
+                                const i32x4 z = {0, 0, 0, 0};
+                                d[kk][rt][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa[kk][rt], wb[kk][m], z, 0, 0, 0);
+                            }
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int rt = 0; rt < NL; ++rt) {
+                            const float dxv[4] = {dx4[kk][rt].x, dx4[kk][rt].y, dx4[kk][rt].z, dx4[kk][rt].w};
+#pragma unroll
+                            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    acc[rt][m][i] = fmaf((float)d[kk][rt][m][i], dwv[kk][m] * dxv[i], acc[rt][m][i]);
+                        }
+                };
+                two_blocks(std::integral_constant<int, 0>{});
+                two_blocks(std::integral_constant<int, 1>{});
+                two_blocks(std::integral_constant<int, 2>{});
+                two_blocks(std::integral_constant<int, 3>{});
+            };
+            if (NR == 2 && live[NR - 1]) run_step(std::integral_constant<int, NR>{});
+            else run_step(std::integral_constant<int, 1>{});
+        };
+
+        // step s is in LDS once every wave has waited for its own loads and
+        // passed the barrier; every wave is then also done with the step
+        // before, whose buffer takes the next step's loads
+        for (int s = 0; s + 1 < nsteps; ++s, ++g) {
+            wait_vm0();
+            lds_barrier();
+            load_step(e, t, a_off, s + 1, (g & 1) ^ 1);
+            if (live[0]) compute(g & 1);
+        }
+        // the last step: the next unit's lookup and activation sources are
+        // read while this step's data arrives, and its first step loads while
+        // this one is computed
+        const uint32_t un = u + stride;
+        int ne = 0, nrb = 0, nnr = 0;
+        uint32_t nt = 0;
+        const bool has_next = un < end && unit_at<S_CHUNK>(p, l, n_active, un, ne, nrb, nnr, nt);
+        if (has_next) stage_act(p, G, nrb, nnr, a_off);   // this unit's are no longer needed
+        wait_vm0();
+        lds_barrier();
+        if (has_next) load_step(ne, nt, a_off, 0, (g & 1) ^ 1);
+        if (live[0]) compute(g & 1);
+        ++g;
+
+        // lane (c, q) holds row rh + c (of each matrix) of route slots 16 tile + 4q + i
+        const int64_t r0 = (int64_t)t * TILE_ROWS;
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            if (!live[rt]) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = out_route[rt][i];
+                if (r < 0) continue;
+                float* o = p.out + (int64_t)r * p.n + r0 + rh + c;
+                if constexpr (PAIR) o[0] = swiglu_ds4_f32(acc[rt][0][i], acc[rt][1][i]);
+                else o[0] = acc[rt][0][i];
+            }
+        }
+        if (!has_next) break;                          // no load is in flight
+        u = un;
+        e = ne;
+        rbegin = nrb;
+        nr = nnr;
+        t = nt;
     }
+}
+
+// CUs of the current device (cached per device; 0 if HIP cannot tell).
+int compute_units() {
+    constexpr int MAX_DEVICES = 64;
+    static std::atomic<int> cached[MAX_DEVICES] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < MAX_DEVICES) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < MAX_DEVICES && cus > 0) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 int validate_weights(const void* w, int64_t row_stride, int64_t k) {
@@ -673,18 +830,35 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
     p.act_row_bytes = (k / QK) * Q81_BYTES;
     p.grouping = (const int32_t*)grouping;
     p.out = out;
-    // the staged gate/up pair: whole 8-block steps, 16-byte aligned rows and
-    // steps (every staged piece is one aligned 16-byte load); n % 32 == 0 holds
-    const bool staged = pair && k % (S_STEP_BLOCKS * QK) == 0 &&
+    // the staged form: whole 8-block steps, whole row tiles, 16-byte aligned
+    // rows and steps (every staged piece is one aligned 16-byte load), piece
+    // offsets within 32 bits (a tile's rows, the activation rows); the down
+    // from 8 steps a unit on (k >= 2048: measured at hidden 4096 and 7168,
+    // 815 against 1013 us and 1397 against 1761 at 1024 columns), the
+    // register-fed form below it (k = 1024, four steps: 507 against 499 us)
+    const int srows = pair ? 32 : 64;
+    const int64_t act_rows = pair ? ncols : R;
+    const bool staged = (pair || k >= 8 * S_STEP_BLOCKS * QK) && k % (S_STEP_BLOCKS * QK) == 0 &&
+                        n % srows == 0 &&
+                        64 * w_row_stride_bytes < ((int64_t)1 << 31) &&
+                        act_rows * p.act_row_bytes < ((int64_t)1 << 31) &&
                         (((uintptr_t)w_a | (uintptr_t)w_b | (uintptr_t)act_q | (uint64_t)w_row_stride_bytes |
                           (uint64_t)expert_stride_bytes | (uint64_t)p.act_row_bytes) & 15u) == 0;
     if (staged) {
-        const int64_t tiles = n / 32;
+        const int64_t tiles = n / srows;
+        // an upper bound of the units; the grid is at most two workgroups a
+        // CU, a multiple of the XCDs, each taking its units in turn
         const int64_t units = (std::min<int64_t>(R, n_local_expert) + R / S_CHUNK) * tiles;
-        const int64_t grid = (units + XCDS - 1) / XCDS * XCDS;
-        if (grid > 0x7fffffff || units > 0xffffffffLL) return MOEQ8_EUNSUPPORTED;
+        if (units > 0xffffffffLL) return MOEQ8_EUNSUPPORTED;
+        const int cus = compute_units();
+        if (cus < 1) return MOEQ8_EHIP;
+        const int64_t cap = (int64_t)S_WG_PER_CU * cus;
+        const int64_t grid = (std::min<int64_t>(units, cap) + XCDS - 1) / XCDS * XCDS;
         p.tiles = (int32_t)tiles;
-        hipLaunchKernelGGL(k_grouped_gemm_pair_staged, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+        if (pair)
+            hipLaunchKernelGGL(k_grouped_gemm_staged<true>, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+        else
+            hipLaunchKernelGGL(k_grouped_gemm_staged<false>, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
         return check_launch();
     }
     const int wg_rows = (pair ? 16 : 32) * GEMM_WAVES;

@@ -1033,6 +1033,7 @@ def _gemm_case(c, n_exp, local, topk, hidden, inter, seed):
     (130, 64, 40, 8, 320, 128),      # owner mask (masked routes); down n = 320: a half-empty row tile
     (3, 16, 16, 8, 128, 64),         # K = 128 and 64: fewer block pairs than a step holds
     (1, 4, 4, 4, 64, 64),
+    (24, 8, 8, 8, 256, 2048),        # down K = 2048: the down staged in LDS too
 ])
 def test_grouped_gemm_vs_oracle(c, n_exp, local, topk, hidden, inter):
     """moe_grouped_gemm gate/up (h) and down (y) against the oracle route by
@@ -1113,20 +1114,25 @@ def _off_alignment(t: torch.Tensor, shift: int = 4) -> torch.Tensor:
 
 @pytest.mark.parametrize("c,n_exp,local,topk,hidden,inter", [
     (200, 16, 16, 8, 1024, 512),     # ~100 routes an expert: a full and a ragged 64-route unit
-    (130, 64, 40, 8, 2048, 256),     # owner mask (masked routes)
+    (130, 64, 40, 8, 2048, 256),     # owner mask (masked routes); down: one K step, nothing to prefetch
     (64, 4, 4, 4, 4096, 256),        # 16 K steps; every column routes to all 4 experts
-    (1, 8, 8, 8, 256, 256),          # one column, one K step: nothing to prefetch
+    (1, 8, 8, 8, 256, 256),          # one column, one K step
+    (256, 64, 64, 8, 1024, 512),     # ~1024 units: workgroups take several units in turn
+    (64, 8, 8, 8, 256, 2048),        # down K = 2048 (8 steps): the down staged too
+    (256, 64, 64, 8, 1024, 2048),    # ~1024 down units of 8 steps each
 ])
 def test_staged_gemm_equals_register_gemm(c, n_exp, local, topk, hidden, inter):
-    """With k % 256 == 0 and 16-byte aligned operands the grouped gate/up
-    product stages its operands in LDS; the same call on weights copied 4
-    bytes off that alignment runs the register-fed form.  Both take the same
-    integer dots, scale products and accumulation order, so every output (and
-    every untouched row of a masked route) has the same bits."""
+    """With k % 256 == 0, whole row tiles and 16-byte aligned operands the
+    grouped GEMM stages its operands in LDS (persistent workgroups, the steps
+    of their units in one pipeline; the down from k = 2048 on); the same call
+    on weights copied 4 bytes off that alignment runs the register-fed form.  Both take the same integer
+    dots, scale products and accumulation order, so every output (and every
+    untouched row of a masked route) has the same bits."""
     say(f"staged vs register gemm c={c} E={n_exp} local={local} k={topk} H={hidden} I={inter}")
     (wg, wu, wd), (wgd, wud, wdd), x, ids_ref, ids, g = _gemm_case(c, n_exp, local, topk, hidden, inter,
                                                                    3 * c + hidden)
     xo, xd = quantized_pair(x)
+    live = torch.from_numpy(ids_ref.reshape(-1) >= 0).to(DEV)
     outs = []
     for a, b in ((wgd, wud), (_off_alignment(wgd), _off_alignment(wud))):
         h = torch.full((c, topk, inter), float("nan"), device=DEV)
@@ -1134,7 +1140,16 @@ def test_staged_gemm_equals_register_gemm(c, n_exp, local, topk, hidden, inter):
                                ncols=c, topk=topk, out=h)
         outs.append(h)
     assert bits_equal(outs[0], outs[1])
-    live = torch.from_numpy(ids_ref.reshape(-1) >= 0).to(DEV)
+    assert not torch.isnan(outs[0].reshape(c * topk, -1)[live]).any()
+    assert torch.isnan(outs[0].reshape(c * topk, -1)[~live]).all()
+    hq = moeq8.q8_1_quantize_rows(torch.nan_to_num(outs[0]).reshape(c * topk, inter))
+    outs = []
+    for a in (wdd, _off_alignment(wdd)):
+        y = torch.full((c, topk, hidden), float("nan"), device=DEV)
+        moeq8.moe_grouped_gemm(moeq8.DOWN, a, None, hq, g, n=hidden, k=inter, n_local_expert=local,
+                               ncols=c, topk=topk, out=y)
+        outs.append(y)
+    assert bits_equal(outs[0], outs[1])
     assert not torch.isnan(outs[0].reshape(c * topk, -1)[live]).any()
     assert torch.isnan(outs[0].reshape(c * topk, -1)[~live]).all()
 
