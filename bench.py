@@ -983,7 +983,10 @@ def q4_sweep(torch, workloads, moeq8, ml, args):
     it).  Weights are N(0, 0.02^2) drawn on the GPU (torch, seeded) and
     quantised by q4_quantize_rows.  Per column count: the four-launch layer,
     the grouped gate/up alone, and the streaming-read ceiling of the same
-    bytes per launch from the replicas' gate and up banks (best read shape)."""
+    bytes per launch from the replicas' gate and up banks (best read shape);
+    then the layer and the gate/up again on packed copies of the banks
+    (pack_experts: the 64-chunk packed stages), after the plain banks are
+    freed."""
     cfg = workloads.CONFIGS["verify_e256_c5"]
     hidden, inter, topk, n_exp = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"]
     q4b = 18
@@ -1052,9 +1055,37 @@ def q4_sweep(torch, workloads, moeq8, ml, args):
                "gate_up_frac_of_peak": round(gu_gbps / HBM_PEAK_GBPS, 4),
                "ceiling_gbps": round(st_gbps, 1), "ceiling_wg_bytes": st_wg,
                "gate_up_frac_of_ceiling": round(gu_gbps / st_gbps, 4)}
+        # the packed stages on packed copies (the plain banks freed first)
+        packed = []
+        for l in range(R):
+            packed.append(ml.pack_experts(experts[l])[0])
+            banks[l] = None
+            experts[l] = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+        def step_packed():
+            for l in range(R):
+                rp = reps[l]
+                ml.forward(rp["x"], rp["logits"], rp["bias"], rp["owner"], rp["n_local"], packed[l], None,
+                           wss[l])
+
+        def gate_up_packed():
+            for l in range(R):
+                moeq8.moe_grouped_mmvq_q4(moeq8.GATE_UP_SWIGLU_P64, packed[l].gate, packed[l].up, wss[l].xq,
+                                          wss[l].grouping, n=inter, k=hidden, n_local_expert=reps[l]["n_local"],
+                                          ncols=cols, topk=topk, out=wss[l].h)
+
+        pms = time_graph(torch, step_packed, n) / R
+        pgu_us = time_graph(torch, gate_up_packed, n) / R * 1e3
+        pgu_gbps = float(np.mean(gu_b)) / (pgu_us * 1e-6) / 1e9
+        rec["packed"] = {"layer_us": round(pms * 1e3, 2), "expert_weight_gbps": round(weights / (pms * 1e-3) / 1e9, 1),
+                         "gate_up_us": round(pgu_us, 2), "gate_up_gbps": round(pgu_gbps, 1),
+                         "gate_up_frac_of_peak": round(pgu_gbps / HBM_PEAK_GBPS, 4),
+                         "gate_up_frac_of_ceiling": round(pgu_gbps / st_gbps, 4)}
         log(f"q4 {rec}")
         out.append(rec)
-        del banks, experts, wss, reps
+        del banks, experts, wss, reps, packed
         torch.cuda.empty_cache()
     return out
 

@@ -456,7 +456,9 @@ int q8_block_decode_sum(const void* gathered, int32_t nranks, int64_t rank_strid
  *   and codes 8.  w 4-byte aligned, wq 2-byte aligned.
  * mmvq_q4, mmvq_q4_glu_pair, moe_grouped_mmvq_q4: the products of mmvq_q8_0,
  *   mmvq_q8_0_glu_pair and moe_grouped_mmvq_ex (no shared part; stages
- *   MOEQ8_GATE_UP_SWIGLU, MOEQ8_DOWN, MOEQ8_DOWN_F32_ACT) with Q4 weights, on
+ *   MOEQ8_GATE_UP_SWIGLU, MOEQ8_DOWN, MOEQ8_DOWN_F32_ACT, and the packed
+ *   MOEQ8_GATE_UP_SWIGLU_P64 / MOEQ8_DOWN_F32_ACT_P64 on weights repacked by
+ *   q4_pack64_rows, with the shapes those stages take) with Q4 weights, on
  *   q8_1 activations; the same arguments, with row strides of at least
  *   k/32 * 18 bytes (a multiple of 4).  A block contributes
  *   (d_w * d_x) * sum((code - 8) * q), with the same reduction order as the
@@ -476,6 +478,20 @@ int moe_grouped_mmvq_q4(int32_t stage, const void* w_a, const void* w_b,
                         int64_t n_local_expert, int64_t n, int64_t k, const void* act,
                         int64_t act_row_stride, const void* grouping, int64_t ncols, int32_t topk,
                         float* out, void* stream);
+
+/* Repack Q4 rows into the 64-chunk packed layout the packed 4-bit stages
+ * read (the same bytes, permuted within each segment).  A row of k values (k a
+ * multiple of 4096) is k/4096 segments of 64 two-block chunks (2304 bytes, 576
+ * dwords); within a segment dword d < 8 of chunk c (plain dword 9c + d) moves to
+ * dword 256*(d/4) + 4c + d%4 and dword 8 of chunk c to dword 512 + c.  For
+ * MOEQ8_DOWN_F32_ACT_P64 (k = 1024, rows 576 bytes apart) pass each quad of
+ * four consecutive rows as one row of 4096 values (n_rows / 4 rows, 2304
+ * bytes apart).
+ *   src  Q4 rows [n_rows], src_row_stride_bytes apart
+ *   dst  packed rows [n_rows], dst_row_stride_bytes apart; must not overlap src
+ * Strides >= k/32*18 bytes, pointers and strides multiples of 4 bytes. */
+int q4_pack64_rows(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes,
+                   void* dst, int64_t dst_row_stride_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,7 @@ from .ops import (  # noqa: F401
     q8_0_quantize_rows,
     q8_0_pack64_rows,
     q8_0_pack64_rounds,
+    q4_pack64_rows,
     mmvq_q8_0,
     mmvq_q8_0_glu_pair,
     swiglu_ds4,

@@ -122,7 +122,7 @@ template <int G, int NMAT, int U, bool GROUPED, bool ACT_F32, bool STX, bool Q4,
 __device__ __forceinline__ void mmvq_item(const MmvqParams& p, int64_t item, uint8_t* lds_act) {
     static_assert(MC == MAX_COLS || (P64 && !REREAD), "narrow passes serve the packed decode stages");
     static_assert(!REREAD || P64, "REREAD selects the packed weights' load kind");
-    static_assert(!P64 || (!Q4 && !STX && ((G == 4 && !ACT_F32) || (G == 1 && NMAT == 1 && ACT_F32))),
+    static_assert(!P64 || (!STX && ((G == 4 && !ACT_F32) || (G == 1 && NMAT == 1 && ACT_F32))),
                   "the packed layouts serve the four-group gate/up rows and the one-group down quads");
     // weight chunk: two Q8_0 blocks (68 B) or two 4-bit blocks (36 B); the
     // chunk's value has the same form either way, so the reduction order and
@@ -553,6 +553,7 @@ int launch_shape(MmvqParams& p, const Shape& s, int64_t grid, size_t lds_bytes, 
 // the grouped gate/up pair on 64-chunk packed weights (four lane groups a
 // row), and the grouped down with fp32 activations on quad-packed weights (one
 // lane group a row)
+template <bool Q4>
 int launch_p64(bool down, MmvqParams& p, const Shape& s, int64_t grid, size_t lds, hipStream_t stream) {
     p.nsteps = s.nsteps;
     if (grid <= 0) return MOEQ8_OK;
@@ -566,20 +567,20 @@ int launch_p64(bool down, MmvqParams& p, const Shape& s, int64_t grid, size_t ld
     // covers them
     const int mc = p.ncols <= 1 ? 1 : p.ncols <= 2 ? 2 : p.ncols <= 4 ? 4 : 8;
     if (down) {
-        constexpr int U = u_for(1, true, false);
-        if (reread) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, true>), g, block, lds, stream, p);
-        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, false, 1>), g, block, lds, stream, p);
-        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, false, 2>), g, block, lds, stream, p);
-        else if (mc == 4) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true, false, 4>), g, block, lds, stream, p);
-        else hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, false, true>), g, block, lds, stream, p);
+        constexpr int U = u_for(1, true, Q4);
+        if (reread) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, Q4, true, true>), g, block, lds, stream, p);
+        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, Q4, true, false, 1>), g, block, lds, stream, p);
+        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, Q4, true, false, 2>), g, block, lds, stream, p);
+        else if (mc == 4) hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, Q4, true, false, 4>), g, block, lds, stream, p);
+        else hipLaunchKernelGGL((k_mmvq<1, 1, U, true, true, false, Q4, true>), g, block, lds, stream, p);
     } else {
-        constexpr int U = u_for(2, false, false);
+        constexpr int U = u_for(2, false, Q4);
         constexpr int US = P64_SMALL_U;                 // passes of 1-2 columns (the host sized the grid so)
-        if (reread) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, true>), g, block, 0, stream, p);
-        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<4, 2, US, true, false, false, false, true, false, 1>), g, block, 0, stream, p);
-        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<4, 2, US, true, false, false, false, true, false, 2>), g, block, 0, stream, p);
-        else if (mc == 4) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true, false, 4>), g, block, 0, stream, p);
-        else hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, false, true>), g, block, 0, stream, p);
+        if (reread) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, Q4, true, true>), g, block, 0, stream, p);
+        else if (mc == 1) hipLaunchKernelGGL((k_mmvq<4, 2, US, true, false, false, Q4, true, false, 1>), g, block, 0, stream, p);
+        else if (mc == 2) hipLaunchKernelGGL((k_mmvq<4, 2, US, true, false, false, Q4, true, false, 2>), g, block, 0, stream, p);
+        else if (mc == 4) hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, Q4, true, false, 4>), g, block, 0, stream, p);
+        else hipLaunchKernelGGL((k_mmvq<4, 2, U, true, false, false, Q4, true>), g, block, 0, stream, p);
     }
     return check_launch();
 }
@@ -719,7 +720,6 @@ int prepare_grouped(GroupedLaunch& L, bool q4, int32_t stage, const void* w_a, c
         return MOEQ8_EINVAL;
     const bool p64 = stage == MOEQ8_GATE_UP_SWIGLU_P64;
     const bool p64d = stage == MOEQ8_DOWN_F32_ACT_P64;
-    if ((p64 || p64d) && q4) return MOEQ8_EINVAL;
     const bool pair = stage == MOEQ8_GATE_UP_SWIGLU || p64;
     const bool f32 = stage == MOEQ8_DOWN_F32_ACT || p64d;
     int st = validate_matrix(w_a, w_row_stride_bytes, n, k, 0, bb);
@@ -766,9 +766,9 @@ int prepare_grouped(GroupedLaunch& L, bool q4, int32_t stage, const void* w_a, c
         }
     }
     if (p64d) {
-        // contiguous rows of one 16-chunk round (a quad is one 4352-byte
-        // packed unit), 16-byte aligned
-        constexpr int64_t ROUND_BYTES = P64_SEGMENT_BYTES / 4;        // 1088
+        // contiguous rows of one 16-chunk round (a quad is one 64-chunk
+        // packed segment: 4352 bytes in Q8_0, 2304 in 4-bit), 16-byte aligned
+        const int64_t ROUND_BYTES = (q4 ? P64Q4_SEGMENT_BYTES : P64_SEGMENT_BYTES) / 4;   // 1088 / 576
         if (k != LANES_PER_ROW * 2 * QK || n % 4 != 0 || (has_s && s_n % 4 != 0)) return MOEQ8_EUNSUPPORTED;
         if (w_row_stride_bytes != ROUND_BYTES || (has_s && (s_row_stride_bytes != ROUND_BYTES || s_k_block_offset != 0)))
             return MOEQ8_EUNSUPPORTED;
@@ -856,11 +856,12 @@ int grouped_impl(bool q4, int32_t stage, const void* w_a, const void* w_b,
     const size_t lds = L.lds;
     const hipStream_t hs = (hipStream_t)stream;
     if (q4) {
+        if (L.p64 || L.p64d) return launch_p64<true>(L.p64d, p, s, grid, lds, hs);
         if (L.pair) return launch_mmvq<2, true, false, true>(p, s, grid, 0, hs);
         if (L.f32) return launch_mmvq<1, true, true, true>(p, s, grid, lds, hs);
         return launch_mmvq<1, true, false, true>(p, s, grid, 0, hs);
     }
-    if (L.p64 || L.p64d) return launch_p64(L.p64d, p, s, grid, lds, hs);
+    if (L.p64 || L.p64d) return launch_p64<false>(L.p64d, p, s, grid, lds, hs);
     if (L.pair) return launch_mmvq<2, true, false, false>(p, s, grid, 0, hs);
     if (L.f32) return launch_mmvq<1, true, true, false>(p, s, grid, lds, hs);
     return launch_mmvq<1, true, false, false>(p, s, grid, 0, hs);
@@ -892,9 +893,9 @@ int ffn_impl(const void* w_gate, const void* w_up, const void* w_down, int64_t g
                          has_s ? s_rows : 0, has_s ? ys : nullptr);
     if (st != MOEQ8_OK) return st;
     const hipStream_t hs_ = (hipStream_t)stream;
-    st = launch_p64(false, G.p, G.s, G.grid, G.lds, hs_);
+    st = launch_p64<false>(false, G.p, G.s, G.grid, G.lds, hs_);
     if (st != MOEQ8_OK) return st;
-    return launch_p64(true, D.p, D.s, D.grid, D.lds, hs_);
+    return launch_p64<false>(true, D.p, D.s, D.grid, D.lds, hs_);
 }
 }  // namespace
 }  // namespace moeq8

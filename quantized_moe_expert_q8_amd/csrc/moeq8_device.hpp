@@ -319,6 +319,38 @@ __device__ __forceinline__ void zero_w_chunk(W4Chunk& w) {
     for (int i = 0; i < W4_CHUNK_DWORDS; ++i) w.v[i] = 0u;
 }
 
+// The 64-chunk packed layout of 4-bit rows (the P64 rule for 9-dword chunks):
+// each 2304-byte segment of 64 chunks stores dword d < 8 of chunk c at dword
+// 256 * (d / 4) + 4 * c + d % 4 and dword 8 at dword 512 + c, so lane c
+// fetches its 36 bytes as two 16-byte loads 1024 bytes apart and one 4-byte
+// load, each load of the wave one contiguous span, and holds the same 9
+// dwords as with the plain layout.
+constexpr int P64Q4_SEGMENT_BYTES = P64_CHUNKS * W4_CHUNK_BYTES;    // 2304
+constexpr int P64Q4_SEGMENT_DWORDS = P64Q4_SEGMENT_BYTES / 4;       // 576
+
+template <bool NT = true>
+__device__ __forceinline__ void load_w_chunk_p64(W4Chunk& w, const uint8_t* seg, int c) {
+    const u32x4a16* q = reinterpret_cast<const u32x4a16*>(seg) + c;
+    const uint32_t* tail = reinterpret_cast<const uint32_t*>(seg + 2048) + c;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        u32x4a16 t;
+        if constexpr (NT) t = __builtin_nontemporal_load(q + 64 * i);
+        else t = q[64 * i];
+        w.v[4 * i + 0] = t.x;
+        w.v[4 * i + 1] = t.y;
+        w.v[4 * i + 2] = t.z;
+        w.v[4 * i + 3] = t.w;
+    }
+    if constexpr (NT) w.v[8] = __builtin_nontemporal_load(tail);
+    else w.v[8] = *tail;
+}
+
+// Source dword (index 9 c + d of the plain segment) of packed dword p.
+__host__ __device__ constexpr int p64q4_source_dword(int p) {
+    return p < 512 ? 9 * ((p & 255) >> 2) + 4 * (p >> 8) + (p & 3) : 9 * (p - 512) + 8;
+}
+
 // -8 times the quant sum of each block of a q8_1 chunk (v_dot4 against -8 in
 // every byte): the term that turns a dot product of raw 4-bit codes (0..15,
 // valid signed bytes) into one of code - 8.  Computed once per activation

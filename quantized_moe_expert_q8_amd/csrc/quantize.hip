@@ -114,6 +114,47 @@ extern "C" int q8_0_pack64_rows(const void* src, int64_t n_rows, int64_t k, int6
     return check_launch();
 }
 
+// Repack 4-bit rows into their 64-chunk packed layout (moeq8_device.hpp):
+// one thread per destination dword.
+namespace {
+__global__ void k_pack64_q4(const uint32_t* __restrict__ src, int64_t n_rows, int64_t segs,
+                            int64_t src_stride_dw, uint32_t* __restrict__ dst, int64_t dst_stride_dw) {
+    using namespace moeq8;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_row = segs * P64Q4_SEGMENT_DWORDS;
+    if (t >= n_rows * per_row) return;
+    const int64_t row = t / per_row;
+    const int64_t rem = t - row * per_row;
+    const int64_t seg = rem / P64Q4_SEGMENT_DWORDS;
+    const int p = (int)(rem - seg * P64Q4_SEGMENT_DWORDS);
+    dst[row * dst_stride_dw + seg * P64Q4_SEGMENT_DWORDS + p] =
+        src[row * src_stride_dw + seg * P64Q4_SEGMENT_DWORDS + p64q4_source_dword(p)];
+}
+}  // namespace
+
+extern "C" int q4_pack64_rows(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes,
+                              void* dst, int64_t dst_row_stride_bytes, void* stream) {
+    using namespace moeq8;
+    if (!src || !dst || n_rows < 0 || k <= 0 || k % (P64_CHUNKS * 2 * QK) != 0) return MOEQ8_EINVAL;
+    const int64_t row_bytes = k / QK * Q4_BYTES;
+    if (src_row_stride_bytes < row_bytes || dst_row_stride_bytes < row_bytes) return MOEQ8_EINVAL;
+    if (((uintptr_t)src | (uintptr_t)dst | (uint64_t)src_row_stride_bytes | (uint64_t)dst_row_stride_bytes) & 3u)
+        return MOEQ8_EALIGN;
+    const uint8_t* s8 = (const uint8_t*)src;
+    const uint8_t* d8 = (const uint8_t*)dst;
+    const int64_t span_s = n_rows == 0 ? 0 : (n_rows - 1) * src_row_stride_bytes + row_bytes;
+    const int64_t span_d = n_rows == 0 ? 0 : (n_rows - 1) * dst_row_stride_bytes + row_bytes;
+    if (s8 < d8 + span_d && d8 < s8 + span_s) return MOEQ8_EINVAL;     // no overlap (not in place)
+    const int64_t total = n_rows * (row_bytes / 4);
+    if (total == 0) return MOEQ8_OK;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_pack64_q4, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint32_t*)src, n_rows, k / (P64_CHUNKS * 2 * QK), src_row_stride_bytes / 4,
+                       (uint32_t*)dst, dst_row_stride_bytes / 4);
+    return check_launch();
+}
+
 // Repack Q8_0 rows into the round-major four-row packed layout
 // (moeq8_device.hpp): round r (16 chunks, 1088 bytes) of every row goes to
 // the matrix dst + r * n_rows * 1088 of contiguous 1088-byte rows, in which

@@ -40,7 +40,8 @@ class RoutedExperts:
     packed layout (ops.q8_0_pack64_rows; hidden 4096) and down in the
     round-major four-row packed layout (ops.q8_0_pack64_rounds; inter 1024),
     read by the fused
-    path's gate/up and down launches (pack_experts makes them)."""
+    path's gate/up and down launches (pack_experts makes them); with 4-bit
+    weights both are ops.q4_pack64_rows (down: each quad of rows as one row)."""
     gate: torch.Tensor       # uint8, n_local x inter x hidden/32 blocks
     up: torch.Tensor
     down: torch.Tensor       # uint8, n_local x hidden x inter/32 blocks
@@ -130,10 +131,14 @@ def forward(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
     around each launch."""
     add = add_shared and shared is not None
     if experts.packed or (shared is not None and shared.packed):
-        if not fused or experts.fmt != "q8_0":
-            raise ValueError("packed weights run on the fused Q8_0 path")
-        if shared is not None and shared.packed != experts.packed:
-            raise ValueError("routed and shared weights must share one layout")
+        if experts.fmt == "q4":
+            if shared is not None and shared.packed:
+                raise ValueError("the 4-bit layer runs its Q8_0 shared share on the plain layout")
+        else:
+            if not fused:
+                raise ValueError("packed weights run on the fused path")
+            if shared is not None and shared.packed != experts.packed:
+                raise ValueError("routed and shared weights must share one layout")
     if experts.fmt == "q4":
         return _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add)
     if experts.fmt != "q8_0":
@@ -326,18 +331,21 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
 
 def _forward_q4(x, logits, bias, owner_slot, n_local_expert, experts, shared, ws, add):
     """The layer with 4-bit routed experts: prologue, grouped gate/up,
-    grouped down quantising h in the launch, combine (four launches); a shared
-    expert (Q8_0) runs as its own pair, quantisation and down calls."""
+    grouped down quantising h in the launch, combine (four launches), on the
+    plain or (experts.packed) the 64-chunk packed stages; a shared expert
+    (Q8_0, plain layout) runs as its own pair, quantisation and down calls."""
     c, topk = ws.ncols, ws.topk
     hidden, inter = experts.hidden, experts.inter
     ops.moe_route_topk_quantize(x, logits, topk, bias=bias, owner_slot=owner_slot,
                                 n_local_expert=n_local_expert, xq=ws.xq, ids=ws.ids,
                                 weights=ws.weights, grouping=ws.grouping)
     R = c * topk
-    ops.moe_grouped_mmvq_q4(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping,
+    gate_up = ops.GATE_UP_SWIGLU_P64 if experts.packed else ops.GATE_UP_SWIGLU
+    down = ops.DOWN_F32_ACT_P64 if experts.packed else ops.DOWN_F32_ACT
+    ops.moe_grouped_mmvq_q4(gate_up, experts.gate, experts.up, ws.xq, ws.grouping,
                             n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
                             out=ws.h)
-    ops.moe_grouped_mmvq_q4(ops.DOWN_F32_ACT, experts.down, None, ws.h.view(R, inter), ws.grouping,
+    ops.moe_grouped_mmvq_q4(down, experts.down, None, ws.h.view(R, inter), ws.grouping,
                             n=hidden, k=inter, n_local_expert=experts.n_local, ncols=c, topk=topk,
                             out=ws.y)
     if shared is not None:
@@ -357,10 +365,21 @@ def pack_experts(experts: RoutedExperts, shared: SharedExpertShare | None = None
     """Copies of the weights in the packed layouts the fused launches read
     (allocated here): gate and up in the 64-chunk layout, down in the
     round-major four-row layout (the shared share's down slice is then the
-    matrix of its round).  Returns (experts, shared)."""
-    if experts.fmt != "q8_0" or experts.packed:
-        raise ValueError("pack_experts takes plain Q8_0 experts")
+    matrix of its round).  4-bit experts take ops.q4_pack64_rows for all three
+    (down: each quad of four rows packed as one row of 4096 values), and their
+    layer's Q8_0 shared share stays plain.  Returns (experts, shared)."""
+    if experts.fmt not in ("q8_0", "q4") or experts.packed:
+        raise ValueError("pack_experts takes plain Q8_0 or 4-bit experts")
     rows = experts.n_local * experts.inter
+    if experts.fmt == "q4":
+        if experts.hidden != ops.P64_K or experts.inter != 1024:
+            raise ValueError("the packed 4-bit stages take hidden 4096 and inter 1024")
+        pe = RoutedExperts(ops.q4_pack64_rows(experts.gate, rows, experts.hidden),
+                           ops.q4_pack64_rows(experts.up, rows, experts.hidden),
+                           ops.q4_pack64_rows(experts.down, experts.n_local * experts.hidden // 4,
+                                              4 * experts.inter),
+                           experts.n_local, experts.hidden, experts.inter, fmt="q4", packed=True)
+        return pe, shared
     pe = RoutedExperts(ops.q8_0_pack64_rows(experts.gate, rows, experts.hidden),
                        ops.q8_0_pack64_rows(experts.up, rows, experts.hidden),
                        ops.q8_0_pack64_rounds(experts.down, experts.n_local * experts.hidden, experts.inter),

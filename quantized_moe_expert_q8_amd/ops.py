@@ -127,6 +127,26 @@ def q8_0_pack64_rounds(src: torch.Tensor, rows: int, k: int, out: torch.Tensor |
     return out
 
 
+def q4_pack64_rows(src: torch.Tensor, rows: int, k: int, out: torch.Tensor | None = None,
+                   src_row_stride_bytes: int | None = None,
+                   out_row_stride_bytes: int | None = None) -> torch.Tensor:
+    """4-bit rows (uint8, rows of k/32*18 bytes) -> the same rows in the 64-chunk
+    packed layout the 4-bit GATE_UP_SWIGLU_P64 reads; k a multiple of 4096.  The
+    4-bit DOWN_F32_ACT_P64 (k = 1024) takes each quad of four consecutive rows
+    packed as one row of 4096 values: rows/4 rows, k = 4096."""
+    row_bytes = k // QK * Q4_BLOCK_BYTES
+    ss = row_bytes if src_row_stride_bytes is None else src_row_stride_bytes
+    ds = row_bytes if out_row_stride_bytes is None else out_row_stride_bytes
+    _cuda(src, "src", torch.uint8)
+    _need(src, "src", _weight_extent(rows, k, ss, Q4_BLOCK_BYTES))
+    if out is None:
+        out = torch.empty(rows * ds, dtype=torch.uint8, device=src.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", _weight_extent(rows, k, ds, Q4_BLOCK_BYTES))
+    call("q4_pack64_rows", _ptr(src), rows, k, ss, _ptr(out), ds, _stream(src))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # 8-bit block exchange codec
 # ---------------------------------------------------------------------------
@@ -287,7 +307,8 @@ def moe_grouped_mmvq_q4(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
                         expert_stride_bytes: int | None = None) -> torch.Tensor:
     """Grouped per-expert products with Q4 expert weights [n_local][n][k/32]:
     stages GATE_UP_SWIGLU and DOWN on q8_1 rows, DOWN_F32_ACT on fp32 h rows
-    [ncols*topk, k].  Returns out fp32 [ncols, topk, n]."""
+    [ncols*topk, k]; GATE_UP_SWIGLU_P64 and DOWN_F32_ACT_P64 the same on weights
+    repacked by q4_pack64_rows.  Returns out fp32 [ncols, topk, n]."""
     row_stride = (k // QK) * Q4_BLOCK_BYTES
     if expert_stride_bytes is None:
         expert_stride_bytes = n * row_stride
@@ -295,7 +316,7 @@ def moe_grouped_mmvq_q4(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
     _cuda(w_a, "w_a", torch.uint8)
     _need(w_a, "w_a", extent)
     act_stride = 0
-    if stage == GATE_UP_SWIGLU:
+    if stage in (GATE_UP_SWIGLU, GATE_UP_SWIGLU_P64):
         if w_b is None:
             raise ValueError("the gate/up stage needs w_b")
         _cuda(w_b, "w_b", torch.uint8)
@@ -303,12 +324,12 @@ def moe_grouped_mmvq_q4(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None,
         _act_rows(act, "act", ncols, k)
     elif stage == DOWN:
         _act_rows(act, "act", ncols * topk, k)
-    elif stage == DOWN_F32_ACT:
+    elif stage in (DOWN_F32_ACT, DOWN_F32_ACT_P64):
         _cuda(act, "act", torch.float32)
         _contig_rows(act, "act", ncols * topk, k)
         act_stride = act.stride(0)
     else:
-        raise ValueError("stage must be GATE_UP_SWIGLU, DOWN or DOWN_F32_ACT")
+        raise ValueError("stage must be GATE_UP_SWIGLU, DOWN, DOWN_F32_ACT or a packed one")
     _cuda(grouping, "grouping", torch.uint8)
     _need(grouping, "grouping", moe_grouping_bytes_wide(ncols, topk))
     if out is None:

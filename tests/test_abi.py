@@ -130,7 +130,7 @@ def test_other_validation():
     assert L.mmvq_q4(P, 32, 4, 64, 0, P, 1, P, None) == -1                       # row shorter than a row
     assert L.mmvq_q4(P, 36, 4, 96, 0, P, 1, P, None) == -1                       # k % 64
     assert L.mmvq_q4_glu_pair(P, None, 36, 4, 64, 0, P, 1, P, None, None, None) == -1
-    assert L.moe_grouped_mmvq_q4(3, P, P, 144, 36, 1, 4, 64, P, 0, P, 1, 1, P, None) == -1   # bad stage
+    assert L.moe_grouped_mmvq_q4(5, P, P, 144, 36, 1, 4, 64, P, 0, P, 1, 1, P, None) == -1   # bad stage
     assert L.moe_grouped_mmvq_q4(0, P, None, 144, 36, 1, 4, 64, P, 0, P, 1, 1, P, None) == -1  # no up
     assert L.moe_combine(P, P, P, 0, 8, 16, P, None) == -1
     assert L.moe_combine(P, P, P, 1, 8, 0, P, None) == 0
@@ -202,6 +202,27 @@ def test_packed_layout_validation():
     assert down(4, 2048, 2176) == -3                                             # k must be one 1024 round
     assert down(62, 1024, 1088) == -3                                            # whole quads of rows
     assert down(4, 1024, 2176) == -3                                             # contiguous 1088-byte rows
+    q4 = L.q4_pack64_rows
+    assert q4(P, 2, 2048, 1152, Q, 1152, None) == -1                             # k % 4096
+    assert q4(P, 2, 4096, 2300, Q, 4608, None) == -1                             # stride shorter than a row
+    assert q4(P + 2, 2, 4096, 2304, Q, 2304, None) == -2
+    assert q4(P, 2, 4096, 2304, Q, 2306, None) == -2                             # dword row strides
+    assert q4(P, 2, 4096, 2304, P + 100, 2304, None) == -1                       # overlapping
+    assert q4(P, 0, 4096, 2304, Q, 2304, None) == 0
+    g4 = L.moe_grouped_mmvq_q4
+
+    def gate_up4(w_a, k, stride=4608):
+        return g4(3, w_a, Q, 0, stride, 1, 4, k, P, 0, P, 1, 1, P, None)
+
+    def down4(n, k, stride):
+        return g4(4, P, None, 0, stride, 1, n, k, P, k, P, 1, 1, P, None)
+
+    assert gate_up4(P, 2048) == -3                                               # one 4096-value segment a row
+    assert gate_up4(P + 4, 4096) == -2                                           # 16-byte aligned segments
+    assert gate_up4(P, 4096, 4612) == -2
+    assert down4(4, 2048, 1152) == -3                                            # k must be one 1024 round
+    assert down4(62, 1024, 576) == -3                                            # whole quads of rows
+    assert down4(4, 1024, 1152) == -3                                            # contiguous 576-byte rows
 
 
 def test_ops_reject_out_of_bounds_views():

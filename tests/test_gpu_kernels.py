@@ -1341,6 +1341,117 @@ def test_q4_layer_equals_its_calls():
     assert bits_equal(out, moeq8.moe_combine(y, ids, w))
 
 
+def _p64q4_reference(raw: np.ndarray, rows: int, k: int) -> np.ndarray:
+    """The 4-bit packed layout restated on the host: within each 2304-byte
+    segment of a row, dword 9c + d moves to 256*(d//4) + 4c + d%4 (d < 8) and
+    dword 9c + 8 to 512 + c."""
+    w = np.ascontiguousarray(raw).reshape(-1).view(np.uint32).reshape(rows, k // 4096, 576)
+    out = np.empty_like(w)
+    c = np.arange(64)
+    for d in range(8):
+        out[:, :, 256 * (d // 4) + 4 * c + d % 4] = w[:, :, 9 * c + d]
+    out[:, :, 512 + c] = w[:, :, 9 * c + 8]
+    return out.reshape(-1).view(np.uint8)
+
+
+@pytest.mark.parametrize("rows,k,extra", [(1, 4096, 0), (3, 8192, 0), (64, 4096, 16)])
+def test_q4_pack64_layout(rows, k, extra):
+    say(f"q4 pack64 rows={rows} k={k} extra={extra}")
+    row_bytes = k // 32 * 18
+    stride = row_bytes + extra
+    raw = np.random.default_rng(rows + k + extra).integers(0, 256, size=rows * stride, dtype=np.uint8)
+    got = host(moeq8.q4_pack64_rows(to_dev(raw), rows, k, src_row_stride_bytes=stride))
+    want = _p64q4_reference(raw.reshape(rows, stride)[:, :row_bytes], rows, k)
+    assert np.array_equal(got, want)
+    # every byte is kept: the packing only permutes within a segment
+    assert np.array_equal(np.sort(got.reshape(rows, -1), axis=1),
+                          np.sort(raw.reshape(rows, stride)[:, :row_bytes], axis=1))
+
+
+_Q4_BANK = {}
+
+
+def _q4_bank(local, H=4096, I=1024):
+    """Plain and packed 4-bit gate, up and down of `local` experts (device)."""
+    if local not in _Q4_BANK:
+        mats = []
+        for m, (rows, k) in enumerate(((local * I, H), (local * I, H), (local * H, I))):
+            mats.append(moeq8.q4_quantize_rows(to_dev(workloads.normal_f32(900 + m, (rows, k), 0.02))).view(-1))
+        wg, wu, wd = mats
+        packed = (moeq8.q4_pack64_rows(wg, local * I, H), moeq8.q4_pack64_rows(wu, local * I, H),
+                  moeq8.q4_pack64_rows(wd, local * H // 4, 4 * I))
+        _Q4_BANK.clear()
+        _Q4_BANK[local] = ((wg, wu, wd), packed)
+    return _Q4_BANK[local]
+
+
+@pytest.mark.parametrize("c", [1, 2, 5, 8, 24])
+def test_q4_grouped_p64_equals_plain(c):
+    """The packed 4-bit stages (gate/up on 64-chunk packed rows, down on
+    quad-packed rows, h quantised in the launch) against the plain 4-bit
+    stages: every written h and y row bit for bit, masked routes untouched
+    (half the experts local; 24 columns: a wide grouping, which the packed
+    kernels serve with their ordinary-load form in passes of 8 columns)."""
+    say(f"q4 p64 grouped c={c}")
+    H, I, topk, n_exp, local, seed = 4096, 1024, 8, 16, 8, 140 + c
+    (wg, wu, wd), (pg, pu, pd) = _q4_bank(local)
+    x = to_dev(workloads.activations(seed, c, H))
+    xq = moeq8.q8_1_quantize_rows(x)
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    ids, _, grouping = _route_any(lg, topk, c, n_exp, local, bias=to_dev(workloads.router_bias(seed, n_exp)))
+    h_in = to_dev(workloads.normal_f32(seed + 1, (c * topk, I), 2.0))
+    hs, ys = [], []
+    for (gu, dn), (a, b, d) in (((moeq8.GATE_UP_SWIGLU, moeq8.DOWN_F32_ACT), (wg, wu, wd)),
+                                ((moeq8.GATE_UP_SWIGLU_P64, moeq8.DOWN_F32_ACT_P64), (pg, pu, pd))):
+        h = torch.full((c, topk, I), float("nan"), device=DEV)
+        y = torch.full((c, topk, H), float("nan"), device=DEV)
+        moeq8.moe_grouped_mmvq_q4(gu, a, b, xq, grouping, n=I, k=H, n_local_expert=local, ncols=c, topk=topk,
+                                  out=h)
+        moeq8.moe_grouped_mmvq_q4(dn, d, None, h_in, grouping, n=H, k=I, n_local_expert=local, ncols=c,
+                                  topk=topk, out=y)
+        hs.append(host(h))
+        ys.append(host(y))
+    valid = host(ids) >= 0
+    assert valid.any() and not valid.all()
+    for j in range(c):
+        for s in range(topk):
+            if valid[j, s]:
+                assert np.array_equal(hs[0][j, s].view(np.int32), hs[1][j, s].view(np.int32)), (j, s)
+                assert np.array_equal(ys[0][j, s].view(np.int32), ys[1][j, s].view(np.int32)), (j, s)
+            else:
+                assert np.isnan(hs[1][j, s]).all() and np.isnan(ys[1][j, s]).all()
+
+
+@pytest.mark.parametrize("c", [1, 8])
+def test_q4_layer_packed_equals_plain(c):
+    """moe_layer.forward with packed 4-bit experts (pack_experts) and a plain
+    Q8_0 shared share gives the bits of the plain 4-bit layer."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    say(f"q4 packed layer c={c}")
+    H, I, topk, n_exp, local, share_rows, seed = 4096, 1024, 8, 16, 8, 256, 150 + c
+    (wg, wu, wd), _ = _q4_bank(local)
+    experts = ml.RoutedExperts(wg, wu, wd, local, H, I, fmt="q4")
+    full = 2 * share_rows
+    sg = _synth_dev(seed, 1, full, H, 3).view(full, H // 32 * 34)
+    su = _synth_dev(seed, 1, full, H, 4).view(full, H // 32 * 34)
+    sd = _synth_dev(seed, 1, H, full, 5).view(H, full // 32 * 34)
+    shared = ml.SharedExpertShare(sg, su, sd, H, full, share_rows, share_rows)
+    pe, ps = ml.pack_experts(experts, shared)
+    assert pe.packed and pe.fmt == "q4" and ps is shared
+    x = to_dev(workloads.activations(seed, c, H))
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    own = to_dev(workloads.owner_slots(n_exp, local))
+    wa = ml.Workspace(c, H, I, topk, share_rows, DEV)
+    wb = ml.Workspace(c, H, I, topk, share_rows, DEV)
+    ml.forward(x, lg, None, own, local, experts, shared, wa, add_shared=True)
+    ml.forward(x, lg, None, own, local, pe, ps, wb, add_shared=True)
+    torch.cuda.synchronize()
+    assert bits_equal(wa.out, wb.out) and bits_equal(wa.ys, wb.ys)
+    with pytest.raises(ValueError):                  # the 4-bit layer's shared share stays plain
+        ml.forward(x, lg, None, own, local, pe, ml.SharedExpertShare(sg, su, sd, H, full, share_rows,
+                                                                     share_rows, packed=True), wb)
+
+
 def test_grouped_gemm_takes_the_decode_grouping():
     """moe_grouped_gemm on the grouping moe_route_topk writes (8 columns, owner
     mask) gives the oracle's products, like the grouped MMVQ on it."""
