@@ -558,8 +558,25 @@ def _main_gpu(args, workloads, pool):
                         "offset_bytes": kb // 32 * hidden * moeq8.ops.ROUND_BYTES,
                         "out": w.ys, "act": w.hs})
 
+    # the two small launches of the layer, each alone in a graph of 43 (a
+    # kernel trace lengthens such short kernels; the graphs time them as the
+    # step issues them)
+    def prologue_only():
+        for l in range(L):
+            w = wss[l]
+            moeq8.moe_route_topk_quantize(xs[l], lgs[l], topk, bias=bs[l], owner_slot=owner,
+                                          n_local_expert=n_local, xq=w.xq, ids=w.ids, weights=w.weights,
+                                          grouping=w.grouping)
+
+    def combine_only():
+        for l in range(L):
+            w = wss[l]
+            moeq8.moe_combine(w.y, w.ids, w.weights, out=w.out, shared=w.ys)
+
     gu_us = time_graph(torch, gate_up_only, args.steps) / L * 1e3
     dn_us = time_graph(torch, down_only, args.steps) / L * 1e3
+    pro_us = time_graph(torch, prologue_only, args.steps) / L * 1e3
+    cmb_us = time_graph(torch, combine_only, args.steps) / L * 1e3
     gu_bytes = float(np.mean([gate_up_launch_bytes(n_active[l], n_valid[l], cols, hidden, inter)
                               for l in range(L)])) + shared_gate_up_bytes(cols, hidden, share_rows)
     dn_bytes = float(np.mean([down_launch_bytes(n_active[l], n_valid[l], hidden, inter)
@@ -624,6 +641,12 @@ def _main_gpu(args, workloads, pool):
                                 round(float(np.percentile(step_ms, 90)), 4)],
         "grouped_down": {"mean_launch_us": round(dn_us, 2), "gbps": round(dn_gbps, 1),
                          "bytes_per_launch": int(dn_bytes)},
+        # per layer: each launch kind alone in a graph of 43, against the
+        # step's time per layer (the rest is the dependent launches' gaps)
+        "layer_breakdown_us": {"prologue": round(pro_us, 2), "gate_up": round(gu_us, 2),
+                               "down": round(dn_us, 2), "combine": round(cmb_us, 2),
+                               "sum": round(pro_us + gu_us + dn_us + cmb_us, 2),
+                               "step_per_layer": round(ms_per_step / L * 1e3, 2)},
         # the routed-expert MMVQ as a whole: both grouped launches' bytes over
         # their summed times (the shared expert's rows ride in both launches)
         "gate_up_plus_down": {"gbps": round((gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9, 1),
