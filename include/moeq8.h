@@ -374,9 +374,15 @@ size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk);
  *   the oracle's product to rounding; it is NOT bit-identical to
  *   moe_grouped_mmvq, whose reduction order differs.
  *   Requires n % 32 == 0 and k % 64 == 0 (MOEQ8_EINVAL otherwise).  Rows of
- *   masked routes are not written.  Work is split into (expert, 16-route
+ *   masked routes are not written.  Work is split into (expert, route
  *   chunk, row tile) units, so an expert with many routes spreads over many
- *   workgroups. */
+ *   workgroups.
+ *   Concurrency: when k is a multiple of 256 (gate/up; down from k = 2048)
+ *   and the operands are 16-byte aligned, the workgroups take their units
+ *   from one of 256 work counters of the library on the device, handed to
+ *   the calls in turn and left at zero when a call ends: at most 256 calls
+ *   may be in flight on one device at once, and a captured graph keeps its
+ *   counters, so one graph must not be replayed on two streams at once. */
 int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
                      int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
                      int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,

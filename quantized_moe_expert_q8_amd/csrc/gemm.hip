@@ -97,6 +97,7 @@ struct GemmParams {
     int64_t act_row_bytes;      // nb * 36
     const int32_t* grouping;
     float* out;                 // [ncols * topk][n]
+    int32_t ticket_slot;        // the staged form's work counters (below)
 };
 
 struct W68 { uint32_t v[17]; };          // one weight pair as loaded
@@ -464,6 +465,17 @@ constexpr int S_A_LOADS = S_A / 1024;            // 18
 constexpr int S_SLOTS = (S_A_LOADS + 7) / 8;     // 3 wave-loads of each kind per wave
 static_assert(S_WG_PER_CU * S_LDS <= 160 * 1024, "LDS of a CU");
 
+// Work counters of the staged form: the workgroups of one XCD take that XCD's
+// units in the order they ask for them (one counter a call slot and XCD, 128
+// bytes apart), so the chunks of one row tile, consecutive units, start
+// together and the later ones find the rows in L2 whatever each unit's
+// length.  The draw that takes a counter's last value (units + workgroups -
+// 1: every workgroup ends with one draw past the units) sets it back to zero,
+// so a slot is zero between calls.  The host hands the slots out in turn: up
+// to S_TICKET_SLOTS calls may be in flight on one device at once.
+constexpr int S_TICKET_SLOTS = 256;
+__device__ uint32_t g_tickets[S_TICKET_SLOTS * XCDS * 32];
+
 // Workgroup barrier over LDS only: waits for this wave's LDS operations, not
 // for its global loads, so a step's loads stay in flight across it (the
 // barrier of __syncthreads also waits for every outstanding global load).
@@ -586,16 +598,38 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
 
     int n_active;
     uint32_t total;
-    if (!grouping_units<S_CHUNK>(p, l, n_active, total)) return;
+    if (!grouping_units<S_CHUNK>(p, l, n_active, total)) return;   // every workgroup alike: no draw
+    const uint32_t x = blockIdx.x % XCDS;
     uint32_t first, end;
-    xcd_range(total, blockIdx.x % XCDS, first, end);
-    const uint32_t stride = gridDim.x / XCDS;          // workgroups an XCD (the grid is a multiple of 8)
-    uint32_t u = first + blockIdx.x / XCDS;
+    xcd_range(total, x, first, end);
+    const uint32_t cnt = end - first;                  // units of this XCD
+    const uint32_t nwg = gridDim.x / XCDS;             // its workgroups (the grid is a multiple of 8)
+    uint32_t* const ctr = g_tickets + ((uint32_t)p.ticket_slot * XCDS + x) * 32;
+    __shared__ uint32_t s_tick;                        // thread 0's last draw, for every wave
+    auto draw = [&]() -> uint32_t {
+        const uint32_t v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v == cnt + nwg - 1) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return v;
+    };
+    // a unit that cannot be looked up (a grouping changed under the call) is
+    // skipped with the rest of the workgroup's draws, so the counter still
+    // returns to zero
+    auto drain = [&]() {
+        if (threadIdx.x == 0)
+            while (draw() < cnt) {
+            }
+    };
+    if (threadIdx.x == 0) s_tick = draw();
+    __syncthreads();
+    uint32_t u = first + s_tick;
     if (u >= end) return;
     // the current unit: expert, route entries, row tile (wave-uniform)
     int e, rbegin, nr;
     uint32_t t;
-    if (!unit_at<S_CHUNK>(p, l, n_active, u, e, rbegin, nr, t)) return;   // before any load
+    if (!unit_at<S_CHUNK>(p, l, n_active, u, e, rbegin, nr, t)) {   // before any load
+        drain();
+        return;
+    }
 
     StageGeometry G;
     stage_geometry<PAIR>(p, wave, l, G);
@@ -718,19 +752,31 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
         // step s is in LDS once every wave has waited for its own loads and
         // passed the barrier; every wave is then also done with the step
         // before, whose buffer takes the next step's loads
+        // the next unit's ticket: drawn two steps before the last (its
+        // result is in after the next step's wait), published by the barrier
+        // of the step after; a unit of one or two steps draws at its last
+        // step and waits for it
+        uint32_t t_pend = 0;
         for (int s = 0; s + 1 < nsteps; ++s, ++g) {
             wait_vm0();
+            if (nsteps >= 3 && s == nsteps - 2 && threadIdx.x == 0) s_tick = t_pend;
             lds_barrier();
             load_step(e, t, a_off, s + 1, (g & 1) ^ 1);
+            if (nsteps >= 3 && s == nsteps - 3 && threadIdx.x == 0) t_pend = draw();
             if (live[0]) compute(g & 1);
+        }
+        if (nsteps < 3) {
+            if (threadIdx.x == 0) s_tick = draw();
+            lds_barrier();
         }
         // the last step: the next unit's lookup and activation sources are
         // read while this step's data arrives, and its first step loads while
         // this one is computed
-        const uint32_t un = u + stride;
+        const uint32_t un = first + s_tick;
         int ne = 0, nrb = 0, nnr = 0;
         uint32_t nt = 0;
-        const bool has_next = un < end && unit_at<S_CHUNK>(p, l, n_active, un, ne, nrb, nnr, nt);
+        const bool more = un < end;
+        const bool has_next = more && unit_at<S_CHUNK>(p, l, n_active, un, ne, nrb, nnr, nt);
         if (has_next) stage_act(p, G, nrb, nnr, a_off);   // this unit's are no longer needed
         wait_vm0();
         lds_barrier();
@@ -752,7 +798,10 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                 else o[0] = acc[rt][0][i];
             }
         }
-        if (!has_next) break;                          // no load is in flight
+        if (!has_next) {                               // no load is in flight
+            if (more) drain();
+            break;
+        }
         u = un;
         e = ne;
         rbegin = nrb;
@@ -830,6 +879,8 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
     p.act_row_bytes = (k / QK) * Q81_BYTES;
     p.grouping = (const int32_t*)grouping;
     p.out = out;
+    static std::atomic<uint32_t> next_slot{0};
+    p.ticket_slot = (int32_t)(next_slot.fetch_add(1, std::memory_order_relaxed) % S_TICKET_SLOTS);
     // the staged form: whole 8-block steps, whole row tiles, 16-byte aligned
     // rows and steps (every staged piece is one aligned 16-byte load), piece
     // offsets within 32 bits (a tile's rows, the activation rows); the down

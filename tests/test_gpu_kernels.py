@@ -1154,6 +1154,45 @@ def test_staged_gemm_equals_register_gemm(c, n_exp, local, topk, hidden, inter):
     assert torch.isnan(outs[0].reshape(c * topk, -1)[~live]).all()
 
 
+def test_staged_gemm_work_counters_return_to_zero():
+    """The staged GEMM's workgroups take their units from the library's work
+    counters (256 call slots, handed out in turn); a call leaves its counters
+    at zero.  300 calls in a row (every slot reused) with units of one, two
+    and four K steps (the next unit drawn at the last step, or two steps
+    before it) and a down of 8 steps: every call gives the bits of the
+    register-fed form (a counter left off zero would skip units, leaving NaN
+    rows)."""
+    say("staged gemm work counters, 300 calls")
+    c, n_exp, local, topk, inter = 40, 8, 8, 8, 64
+    cases = []
+    for hidden in (256, 512, 1024):
+        (_, _, _), (wgd, wud, _), x, ids_ref, ids, g = _gemm_case(c, n_exp, local, topk, hidden, inter, 7 + hidden)
+        xd = moeq8.q8_1_quantize_rows(to_dev(x))
+        ref = torch.full((c, topk, inter), float("nan"), device=DEV)
+        moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU, _off_alignment(wgd), _off_alignment(wud), xd, g, n=inter,
+                               k=hidden, n_local_expert=local, ncols=c, topk=topk, out=ref)
+        cases.append((hidden, wgd, wud, xd, g, ref))
+    (_, _, _), (_, _, wdd), _, _, _, gd = _gemm_case(c, n_exp, local, topk, 256, 2048, 11)
+    hq = moeq8.q8_1_quantize_rows(to_dev(workloads.normal_f32(12, (c * topk, 2048), 1.0)))
+    yref = torch.full((c, topk, 256), float("nan"), device=DEV)
+    moeq8.moe_grouped_gemm(moeq8.DOWN, _off_alignment(wdd), None, hq, gd, n=256, k=2048, n_local_expert=local,
+                           ncols=c, topk=topk, out=yref)
+    h = torch.empty((c, topk, inter), device=DEV)
+    y = torch.empty((c, topk, 256), device=DEV)
+    for i in range(300):
+        if i % 4 == 3:
+            y.fill_(float("nan"))
+            moeq8.moe_grouped_gemm(moeq8.DOWN, wdd, None, hq, gd, n=256, k=2048, n_local_expert=local,
+                                   ncols=c, topk=topk, out=y)
+            assert bits_equal(y, yref), i
+        else:
+            hidden, wgd, wud, xd, g, ref = cases[i % 4]
+            h.fill_(float("nan"))
+            moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU, wgd, wud, xd, g, n=inter, k=hidden, n_local_expert=local,
+                                   ncols=c, topk=topk, out=h)
+            assert bits_equal(h, ref), (i, hidden)
+
+
 # ---------------------------------------------------------------------------
 # 8-bit block exchange codec: bytes and sums bit for bit against the oracle
 # ---------------------------------------------------------------------------
