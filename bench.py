@@ -876,11 +876,14 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
     Per column count: the seven-launch layer with the grouped products on the
     matrix cores and with the grouped MMVQ, and each grouped product alone
     (graphs, HIP events), against a plain streaming read of as many bytes;
-    then the MMVQ passes on the packed layouts."""
+    the layer and the gate/up again with gate/up in the GEMM's own layout
+    (pack_gemm_experts: a second copy of gate and up); then the MMVQ passes
+    on the packed layouts."""
     cfg = workloads.CONFIGS["wide_e256"]
     hidden, inter, topk, n_exp, seed = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"], cfg["seed"]
     bank = Bank(moeq8, torch, 1, n_exp, hidden, inter, seed)
     experts = bank.experts(ml, 0)
+    ge = ml.pack_gemm_experts(experts)
     sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
     out = []
     for cols in cfg["cols"]:
@@ -912,6 +915,17 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
                          "gate_up_gbps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
                          "down_us": round(dn_us, 1),
                          "down_gbps": round(dn_b / (dn_us * 1e-6) / 1e9, 1)}
+        # gate/up in the GEMM's layout (the same bits)
+        layer_ms = time_graph(torch, lambda: ml.forward_wide(x, lg, bs, None, n_exp, ge, ws, products="gemm"),
+                              reps)
+        gu_us = time_graph(torch, lambda: moeq8.moe_grouped_gemm(
+            moeq8.GATE_UP_SWIGLU_G8, ge.gemm_gate, ge.gemm_up, ws.xq, ws.grouping, n=inter, k=hidden,
+            n_local_expert=n_exp, ncols=cols, topk=topk, out=ws.h), reps) * 1e3
+        rec["gemm_layout"] = {"layer_us": round(layer_ms * 1e3, 1),
+                              "cols_per_s": round(cols / (layer_ms * 1e-3), 1),
+                              "gate_up_us": round(gu_us, 1),
+                              "gate_up_gbps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
+                              "gate_up_frac_of_peak": round(gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
         # the ceiling: as many bytes read from the gate and up banks
         half = min(int(gu_b) // 2, bank.gate[0].numel()) // 16 * 16
 
@@ -926,9 +940,12 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
         rec["ceiling_gbps"] = round(st_bytes / (st_us * 1e-6) / 1e9, 1)
         rec["gemm"]["gate_up_frac_of_peak"] = round(rec["gemm"]["gate_up_gbps"] / HBM_PEAK_GBPS, 4)
         rec["gemm"]["gate_up_frac_of_ceiling"] = round(rec["gemm"]["gate_up_gbps"] / rec["ceiling_gbps"], 4)
+        rec["gemm_layout"]["gate_up_frac_of_ceiling"] = round(rec["gemm_layout"]["gate_up_gbps"] / rec["ceiling_gbps"], 4)
         log(f"wide {rec}")
         out.append(rec)
         del ws, x, lg, bs
+    del ge
+    torch.cuda.empty_cache()
     # The MMVQ passes again on the packed layouts (the bank repacked in place):
     # the six-launch layer, the packed gate/up and the down that quantises h
     # in its launch, each alone.

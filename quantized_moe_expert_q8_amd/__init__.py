@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     DOWN_F32_ACT,
     GATE_UP_SWIGLU_P64,
     DOWN_F32_ACT_P64,
+    GATE_UP_SWIGLU_G8,
     P64_K,
     Q8_0_BLOCK_BYTES,
     Q8_1_BLOCK_BYTES,
@@ -20,6 +21,7 @@ from .ops import (  # noqa: F401
     q8_0_pack64_rows,
     q8_0_pack64_rounds,
     q4_pack64_rows,
+    q8_0_pack_gemm_rows,
     mmvq_q8_0,
     mmvq_q8_0_glu_pair,
     swiglu_ds4,

@@ -21,6 +21,7 @@ SIGNATURES = {
     "q8_0_pack64_rows": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "q8_0_pack64_rounds": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "q4_pack64_rows": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "q8_0_pack_gemm_rows": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "mmvq_q8_0": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]),
     "mmvq_q8_0_glu_pair": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_i64,
                                           c_vp, c_vp, c_vp, c_vp]),

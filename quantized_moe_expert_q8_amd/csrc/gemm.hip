@@ -580,9 +580,16 @@ __device__ __forceinline__ void stage_act(const GemmParams& p, const StageGeomet
     }
 }
 
-template <bool PAIR>
+// G8: the weights are in the layout of q8_0_pack_gemm_rows (per 8-block
+// group, 16 bytes of scales, then 8-byte aligned quants with the 8-byte halves
+// of each 16-byte piece swapped in rows 8-15 of every 16): a lane's operand
+// piece is one aligned 8-byte read, and the 16 rows of a wave's read fall
+// into different LDS banks.  The same bytes reach the same lanes, so the
+// results are those of the plain layout.
+template <bool PAIR, bool G8 = false>
 __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_gemm_staged(
     const GemmParams p) {
+    static_assert(!G8 || PAIR, "the GEMM layout serves the gate/up stage");
     __shared__ __align__(16) uint8_t lds[S_LDS];
     constexpr int NM = PAIR ? 2 : 1;                   // weight fragments a wave reads a block
     constexpr int NR = PAIR ? 1 : 2;                   // route tiles a wave runs
@@ -706,10 +713,21 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
 #pragma unroll
                     for (int m = 0; m < NM; ++m) {
                         const uint8_t* wr = W + (m * 32 + rh + c) * S_WROW;
-                        wb[0][m] = w_frag<K0>(wr, q8);
-                        wb[1][m] = w_frag<K0 + 1>(wr, q8);
-                        dwv[0][m] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wr + K0 * Q80_BYTES));
-                        dwv[1][m] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wr + (K0 + 1) * Q80_BYTES));
+                        if constexpr (G8) {
+                            // operand piece q of block K at 16 + 32K + 8 (q ^ (row / 8 % 2));
+                            // the scales of blocks K0, K0 + 1 in one dword
+                            const int qx = q8 ^ (c & 8);
+                            wb[0][m] = *reinterpret_cast<const long*>(wr + 16 + 32 * K0 + qx);
+                            wb[1][m] = *reinterpret_cast<const long*>(wr + 16 + 32 * (K0 + 1) + qx);
+                            const uint32_t sw = *reinterpret_cast<const uint32_t*>(wr + 2 * K0);
+                            dwv[0][m] = half_bits_to_float(sw & 0xFFFFu);
+                            dwv[1][m] = half_bits_to_float(sw >> 16);
+                        } else {
+                            wb[0][m] = w_frag<K0>(wr, q8);
+                            wb[1][m] = w_frag<K0 + 1>(wr, q8);
+                            dwv[0][m] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wr + K0 * Q80_BYTES));
+                            dwv[1][m] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(wr + (K0 + 1) * Q80_BYTES));
+                        }
                     }
 #pragma unroll
                     for (int rt = 0; rt < NL; ++rt) {
@@ -843,8 +861,10 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
                                 int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
                                 const void* grouping, int64_t ncols, int32_t topk, float* out,
                                 void* stream) {
-    if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN) return MOEQ8_EINVAL;
-    const bool pair = stage == MOEQ8_GATE_UP_SWIGLU;
+    if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_GATE_UP_SWIGLU_G8)
+        return MOEQ8_EINVAL;
+    const bool g8 = stage == MOEQ8_GATE_UP_SWIGLU_G8;
+    const bool pair = stage == MOEQ8_GATE_UP_SWIGLU || g8;
     if (n < 0 || k <= 0 || k % 64 != 0 || n % 32 != 0) return MOEQ8_EINVAL;
     int st = validate_weights(w_a, w_row_stride_bytes, k);
     if (st) return st;
@@ -906,12 +926,15 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
         const int64_t cap = (int64_t)S_WG_PER_CU * cus;
         const int64_t grid = (std::min<int64_t>(units, cap) + XCDS - 1) / XCDS * XCDS;
         p.tiles = (int32_t)tiles;
-        if (pair)
+        if (g8)
+            hipLaunchKernelGGL((k_grouped_gemm_staged<true, true>), dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+        else if (pair)
             hipLaunchKernelGGL(k_grouped_gemm_staged<true>, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
         else
             hipLaunchKernelGGL(k_grouped_gemm_staged<false>, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
         return check_launch();
     }
+    if (g8) return MOEQ8_EUNSUPPORTED;                 // the GEMM layout is read by the staged form only
     const int wg_rows = (pair ? 16 : 32) * GEMM_WAVES;
     const int64_t tiles = (n + wg_rows - 1) / wg_rows;
     // units <= (groups + valid routes / 16) * tiles for any grouping of these

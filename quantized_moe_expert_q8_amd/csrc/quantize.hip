@@ -155,6 +155,65 @@ extern "C" int q4_pack64_rows(const void* src, int64_t n_rows, int64_t k, int64_
     return check_launch();
 }
 
+// Repack Q8_0 rows into the grouped GEMM's layout (q8_0_pack_gemm_rows in
+// moeq8.h): each 272-byte group of 8 blocks becomes 16 bytes of scales, then
+// the 8 blocks' quants 8-byte aligned, with the 8-byte halves of each 16-byte
+// quant piece swapped in rows i % 16 >= 8.  One thread per destination dword;
+// the four bytes of a dword come from one region and one 8-byte half.
+namespace {
+constexpr int G8_GROUP_BYTES = 8 * 34;                // 272
+constexpr int G8_GROUP_DWORDS = G8_GROUP_BYTES / 4;   // 68
+__global__ void k_pack_gemm(const uint8_t* __restrict__ src, int64_t n_rows, int64_t groups,
+                            int64_t src_stride, uint32_t* __restrict__ dst, int64_t dst_stride_dw) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_row = groups * G8_GROUP_DWORDS;
+    if (t >= n_rows * per_row) return;
+    const int64_t row = t / per_row;
+    const int64_t rem = t - row * per_row;
+    const int64_t grp = rem / G8_GROUP_DWORDS;
+    const int o = (int)(rem - grp * G8_GROUP_DWORDS) * 4;      // byte of the group
+    const uint8_t* g = src + row * src_stride + grp * G8_GROUP_BYTES;
+    int from;                                                   // source byte of byte o
+    if (o < 16) {
+        from = 34 * (o >> 1);                                   // scale of block o / 2 (o even)
+    } else {
+        const int qo = o - 16;
+        const int b = (qo & 31) ^ ((row & 15) >= 8 ? 8 : 0);
+        from = 34 * (qo >> 5) + 2 + b;
+    }
+    uint32_t v;
+    if (o < 16)   // two scales: bytes 0-1 of block o/2 and of block o/2 + 1
+        v = (uint32_t)g[from] | ((uint32_t)g[from + 1] << 8) | ((uint32_t)g[from + 34] << 16) |
+            ((uint32_t)g[from + 35] << 24);
+    else
+        v = (uint32_t)g[from] | ((uint32_t)g[from + 1] << 8) | ((uint32_t)g[from + 2] << 16) |
+            ((uint32_t)g[from + 3] << 24);
+    dst[row * dst_stride_dw + rem] = v;
+}
+}  // namespace
+
+extern "C" int q8_0_pack_gemm_rows(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes,
+                                   void* dst, int64_t dst_row_stride_bytes, void* stream) {
+    using namespace moeq8;
+    if (!src || !dst || n_rows < 0 || k <= 0 || k % (8 * QK) != 0) return MOEQ8_EINVAL;
+    const int64_t row_bytes = k / QK * Q80_BYTES;
+    if (src_row_stride_bytes < row_bytes || dst_row_stride_bytes < row_bytes) return MOEQ8_EINVAL;
+    if (((uintptr_t)src | (uintptr_t)dst | (uint64_t)src_row_stride_bytes | (uint64_t)dst_row_stride_bytes) & 3u)
+        return MOEQ8_EALIGN;
+    const uint8_t* s8 = (const uint8_t*)src;
+    const uint8_t* d8 = (const uint8_t*)dst;
+    const int64_t span_s = n_rows == 0 ? 0 : (n_rows - 1) * src_row_stride_bytes + row_bytes;
+    const int64_t span_d = n_rows == 0 ? 0 : (n_rows - 1) * dst_row_stride_bytes + row_bytes;
+    if (s8 < d8 + span_d && d8 < s8 + span_s) return MOEQ8_EINVAL;     // no overlap (not in place)
+    const int64_t total = n_rows * (row_bytes / 4);
+    if (total == 0) return MOEQ8_OK;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffff) return MOEQ8_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_pack_gemm, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream, s8, n_rows,
+                       k / (8 * QK), src_row_stride_bytes, (uint32_t*)dst, dst_row_stride_bytes / 4);
+    return check_launch();
+}
+
 // Repack Q8_0 rows into the round-major four-row packed layout
 // (moeq8_device.hpp): round r (16 chunks, 1088 bytes) of every row goes to
 // the matrix dst + r * n_rows * 1088 of contiguous 1088-byte rows, in which

@@ -50,6 +50,10 @@ class RoutedExperts:
     inter: int
     fmt: str = "q8_0"
     packed: bool = False
+    # optional copies of gate and up in the grouped GEMM's layout
+    # (pack_gemm_experts), read by forward_wide's matrix-core gate/up
+    gemm_gate: torch.Tensor | None = None
+    gemm_up: torch.Tensor | None = None
 
 
 @dataclass
@@ -298,7 +302,8 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
     columns, "auto" picks by the mean routes per expert.  Packed experts
     (pack_experts) run the MMVQ passes on the packed stages, the down
     quantising h in its launch (six launches, the same bits); the GEMM reads
-    the plain layout only.  Returns ws.out."""
+    the plain layout, its gate/up the GEMM layout when the experts carry it
+    (pack_gemm_experts; the same bits).  Returns ws.out."""
     if products == "auto":
         products = "mmvq" if experts.packed else wide_products_for(ws.ncols, ws.topk, experts.n_local)
     if products not in ("gemm", "mmvq"):
@@ -320,8 +325,13 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
                                 ws.grouping, n=hidden, k=inter, n_local_expert=experts.n_local, ncols=c,
                                 topk=topk, out=ws.y)
     else:
-        grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
-                n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
+        if products == "gemm" and experts.gemm_gate is not None:
+            ops.moe_grouped_gemm(ops.GATE_UP_SWIGLU_G8, experts.gemm_gate, experts.gemm_up, ws.xq, ws.grouping,
+                                 n=inter, k=hidden, n_local_expert=experts.n_local, ncols=c, topk=topk,
+                                 out=ws.h)
+        else:
+            grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
+                    n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
         ops.q8_1_quantize_rows(ws.h.view(c * topk, inter), out=ws.hq)
         grouped(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
                 n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
@@ -394,6 +404,20 @@ def pack_experts(experts: RoutedExperts, shared: SharedExpertShare | None = None
         ps = SharedExpertShare(g, u, d, shared.hidden, shared.inter_full, shared.row0, shared.rows,
                                packed=True)
     return pe, ps
+
+
+def pack_gemm_experts(experts: RoutedExperts) -> RoutedExperts:
+    """The experts with copies of gate and up in the grouped GEMM's layout
+    (ops.q8_0_pack_gemm_rows, allocated here) for forward_wide's matrix-core
+    gate/up; the plain matrices stay for the MMVQ passes and the down."""
+    if experts.fmt != "q8_0" or experts.packed:
+        raise ValueError("pack_gemm_experts takes plain Q8_0 experts")
+    if experts.hidden % 256 or experts.inter % 32:
+        raise ValueError("the GEMM layout takes hidden % 256 == 0 and inter % 32 == 0")
+    rows = experts.n_local * experts.inter
+    return RoutedExperts(experts.gate, experts.up, experts.down, experts.n_local, experts.hidden,
+                         experts.inter, gemm_gate=ops.q8_0_pack_gemm_rows(experts.gate, rows, experts.hidden),
+                         gemm_up=ops.q8_0_pack_gemm_rows(experts.up, rows, experts.hidden))
 
 
 def expert_bytes_q4(hidden: int, inter: int) -> int:

@@ -25,6 +25,7 @@ DOWN = 1
 DOWN_F32_ACT = 2
 GATE_UP_SWIGLU_P64 = 3      # gate/up on weights repacked by q8_0_pack64_rows
 DOWN_F32_ACT_P64 = 4        # down (fp32 h) on weights repacked by q8_0_pack64_rounds
+GATE_UP_SWIGLU_G8 = 5       # moe_grouped_gemm gate/up on weights repacked by q8_0_pack_gemm_rows
 ROUND_BYTES = 1088          # a 1024-value round of Q8_0 blocks
 P64_K = 4096                # values in one packed segment
 
@@ -124,6 +125,26 @@ def q8_0_pack64_rounds(src: torch.Tensor, rows: int, k: int, out: torch.Tensor |
     _cuda(out, "out", torch.uint8)
     _need(out, "out", rows * row_bytes)
     call("q8_0_pack64_rounds", _ptr(src), rows, k, ss, _ptr(out), _stream(src))
+    return out
+
+
+def q8_0_pack_gemm_rows(src: torch.Tensor, rows: int, k: int, out: torch.Tensor | None = None,
+                        src_row_stride_bytes: int | None = None,
+                        out_row_stride_bytes: int | None = None) -> torch.Tensor:
+    """Q8_0 rows -> the grouped GEMM's layout that GATE_UP_SWIGLU_G8 reads (per
+    8-block group: 16 bytes of scales, then the quants 8-byte aligned, the
+    8-byte halves of each 16-byte piece swapped in rows i % 16 >= 8); k a
+    multiple of 256; pack whole expert matrices from their first row."""
+    row_bytes = k // QK * Q8_0_BLOCK_BYTES
+    ss = row_bytes if src_row_stride_bytes is None else src_row_stride_bytes
+    ds = row_bytes if out_row_stride_bytes is None else out_row_stride_bytes
+    _cuda(src, "src", torch.uint8)
+    _need(src, "src", _weight_extent(rows, k, ss))
+    if out is None:
+        out = torch.empty(rows * ds, dtype=torch.uint8, device=src.device)
+    _cuda(out, "out", torch.uint8)
+    _need(out, "out", _weight_extent(rows, k, ds))
+    call("q8_0_pack_gemm_rows", _ptr(src), rows, k, ss, _ptr(out), ds, _stream(src))
     return out
 
 
@@ -460,7 +481,9 @@ def _grouped_call(fn: str, stage: int, w_a, w_b, act_q, grouping, n, k, n_local_
     extent = (n_local_expert - 1) * expert_stride_bytes + _weight_extent(n, k, w_row_stride_bytes)
     _cuda(w_a, "w_a", torch.uint8)
     _need(w_a, "w_a", extent)
-    if stage == GATE_UP_SWIGLU:
+    if stage in (GATE_UP_SWIGLU, GATE_UP_SWIGLU_G8):
+        if stage == GATE_UP_SWIGLU_G8 and fn != "moe_grouped_gemm":
+            raise ValueError("GATE_UP_SWIGLU_G8 is a stage of moe_grouped_gemm")
         if w_b is None:
             raise ValueError("the gate/up stage needs w_b")
         _cuda(w_b, "w_b", torch.uint8)
@@ -469,7 +492,7 @@ def _grouped_call(fn: str, stage: int, w_a, w_b, act_q, grouping, n, k, n_local_
     elif stage == DOWN:
         act_rows = ncols * topk
     else:
-        raise ValueError("stage must be GATE_UP_SWIGLU or DOWN")
+        raise ValueError("stage must be GATE_UP_SWIGLU, GATE_UP_SWIGLU_G8 (GEMM) or DOWN")
     _act_rows(act_q, "act_q", act_rows, k)
     _cuda(grouping, "grouping", torch.uint8)
     _need(grouping, "grouping", moe_grouping_bytes_wide(ncols, topk))
@@ -499,7 +522,9 @@ def moe_grouped_gemm(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, ac
                      w_row_stride_bytes: int | None = None,
                      out: torch.Tensor | None = None) -> torch.Tensor:
     """The grouped products on the int8 matrix cores (wide batches): same
-    arguments and results as moe_grouped_mmvq, equal to rounding (n % 32 == 0)."""
+    arguments and results as moe_grouped_mmvq, equal to rounding (n % 32 == 0).
+    Stage GATE_UP_SWIGLU_G8 takes gate/up repacked by q8_0_pack_gemm_rows (the
+    bits of GATE_UP_SWIGLU on the plain rows)."""
     return _grouped_call("moe_grouped_gemm", stage, w_a, w_b, act_q, grouping, n, k, n_local_expert,
                          ncols, topk, expert_stride_bytes, w_row_stride_bytes, out)
 

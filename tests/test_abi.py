@@ -202,6 +202,16 @@ def test_packed_layout_validation():
     assert down(4, 2048, 2176) == -3                                             # k must be one 1024 round
     assert down(62, 1024, 1088) == -3                                            # whole quads of rows
     assert down(4, 1024, 2176) == -3                                             # contiguous 1088-byte rows
+    gp = L.q8_0_pack_gemm_rows
+    assert gp(P, 2, 128, 68 * 4, Q, 68 * 4, None) == -1                          # k % 256
+    assert gp(P, 2, 256, 270, Q, 272, None) == -1                                # stride shorter than a row
+    assert gp(P + 2, 2, 256, 272, Q, 272, None) == -2
+    assert gp(P, 2, 256, 272, P + 100, 272, None) == -1                          # overlapping
+    assert gp(P, 0, 256, 272, Q, 272, None) == 0
+    gg = L.moe_grouped_gemm                                                      # the GEMM layout: staged form only
+    assert gg(5, P, Q, 0, 68 * 2, 1, 32, 128, P, P, 1, 1, P, None) == -3         # k % 256
+    assert gg(5, P + 4, Q, 0, 272, 1, 32, 256, P, P, 1, 1, P, None) == -3        # 16-byte alignment
+    assert gg(6, P, Q, 0, 272, 1, 32, 256, P, P, 1, 1, P, None) == -1            # no such stage
     q4 = L.q4_pack64_rows
     assert q4(P, 2, 2048, 1152, Q, 1152, None) == -1                             # k % 4096
     assert q4(P, 2, 4096, 2300, Q, 4608, None) == -1                             # stride shorter than a row

@@ -1193,6 +1193,77 @@ def test_staged_gemm_work_counters_return_to_zero():
             assert bits_equal(h, ref), (i, hidden)
 
 
+def _gemm_layout_reference(raw: np.ndarray, rows: int, k: int) -> np.ndarray:
+    """The grouped GEMM's weight layout restated on the host: per 272-byte
+    group of 8 blocks, the 8 scales (block j's two bytes at 2j), then block j's
+    32 quants at 16 + 32j, the two 8-byte halves of each 16-byte piece swapped
+    in rows i with i % 16 >= 8."""
+    g = k // 256
+    b = np.ascontiguousarray(raw).reshape(rows, g, 8, 34)
+    out = np.empty((rows, g, 272), np.uint8)
+    out[:, :, :16] = b[:, :, :, :2].reshape(rows, g, 16)
+    q = b[:, :, :, 2:].reshape(rows, g, 8, 4, 8).copy()          # [row, group, block, 8-byte piece, byte]
+    swap = (np.arange(rows) % 16) >= 8
+    q[swap] = q[swap][:, :, :, [1, 0, 3, 2], :]
+    out[:, :, 16:] = q.reshape(rows, g, 256)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("rows,k", [(1, 256), (40, 512), (64, 4096)])
+def test_gemm_layout_bytes(rows, k):
+    say(f"gemm layout rows={rows} k={k}")
+    raw = np.random.default_rng(rows + k).integers(0, 256, size=rows * (k // 32) * 34, dtype=np.uint8)
+    got = host(moeq8.q8_0_pack_gemm_rows(to_dev(raw), rows, k))
+    assert np.array_equal(got, _gemm_layout_reference(raw, rows, k))
+
+
+@pytest.mark.parametrize("c,n_exp,local,topk,hidden,inter", [
+    (200, 16, 16, 8, 1024, 512),     # ~100 routes an expert: a full and a ragged 64-route unit
+    (130, 64, 40, 8, 2048, 256),     # owner mask (masked routes)
+    (64, 4, 4, 4, 4096, 256),        # 16 K steps; every column routes to all 4 experts
+    (1, 8, 8, 8, 256, 256),          # one column, one K step
+    (40, 8, 8, 8, 512, 64),          # two K steps
+])
+def test_gemm_layout_equals_plain(c, n_exp, local, topk, hidden, inter):
+    """GATE_UP_SWIGLU_G8 on weights repacked by q8_0_pack_gemm_rows against
+    GATE_UP_SWIGLU on the plain rows: every output bit for bit, rows of
+    masked routes untouched."""
+    say(f"gemm layout vs plain c={c} E={n_exp} local={local} k={topk} H={hidden} I={inter}")
+    (_, _, _), (wgd, wud, _), x, ids_ref, ids, g = _gemm_case(c, n_exp, local, topk, hidden, inter, 5 * c + hidden)
+    xd = moeq8.q8_1_quantize_rows(to_dev(x))
+    pg = moeq8.q8_0_pack_gemm_rows(wgd, local * inter, hidden)
+    pu = moeq8.q8_0_pack_gemm_rows(wud, local * inter, hidden)
+    outs = []
+    for stage, a, b in ((moeq8.GATE_UP_SWIGLU, wgd, wud), (moeq8.GATE_UP_SWIGLU_G8, pg, pu)):
+        h = torch.full((c, topk, inter), float("nan"), device=DEV)
+        moeq8.moe_grouped_gemm(stage, a, b, xd, g, n=inter, k=hidden, n_local_expert=local, ncols=c,
+                               topk=topk, out=h)
+        outs.append(h)
+    assert bits_equal(outs[0], outs[1])
+    live = torch.from_numpy(ids_ref.reshape(-1) >= 0).to(DEV)
+    assert not torch.isnan(outs[1].reshape(c * topk, -1)[live]).any()
+
+
+@pytest.mark.parametrize("c", [40, 512])
+def test_wide_layer_gemm_layout_equals_plain(c):
+    """forward_wide on the matrix cores with gate/up in the GEMM layout
+    (pack_gemm_experts) against the plain layout: every output bit for bit."""
+    from quantized_moe_expert_q8_amd import moe_layer as ml
+    say(f"wide gemm layout layer c={c}")
+    H, I, topk, n_exp, seed = 4096, 1024, 8, 16, 120 + c
+    wg, wu, wd = _synth_dev(seed, n_exp, I, H, 0), _synth_dev(seed, n_exp, I, H, 1), _synth_dev(seed, n_exp, H, I, 2)
+    experts = ml.RoutedExperts(wg, wu, wd, n_exp, H, I)
+    ge = ml.pack_gemm_experts(experts)
+    x = to_dev(workloads.activations(seed, c, H))
+    lg = to_dev(workloads.router_logits(seed, c, n_exp))
+    b = to_dev(workloads.router_bias(seed, n_exp))
+    wa, wb = ml.WideWorkspace(c, H, I, topk, DEV), ml.WideWorkspace(c, H, I, topk, DEV)
+    ml.forward_wide(x, lg, b, None, n_exp, experts, wa, products="gemm")
+    ml.forward_wide(x, lg, b, None, n_exp, ge, wb, products="gemm")
+    torch.cuda.synchronize()
+    assert bits_equal(wa.h, wb.h) and bits_equal(wa.y, wb.y) and bits_equal(wa.out, wb.out)
+
+
 # ---------------------------------------------------------------------------
 # 8-bit block exchange codec: bytes and sums bit for bit against the oracle
 # ---------------------------------------------------------------------------
