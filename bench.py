@@ -876,8 +876,8 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
     Per column count: the seven-launch layer with the grouped products on the
     matrix cores and with the grouped MMVQ, and each grouped product alone
     (graphs, HIP events), against a plain streaming read of as many bytes;
-    the layer and the gate/up again with gate/up in the GEMM's own layout
-    (pack_gemm_experts: a second copy of gate and up); then the MMVQ passes
+    the layer, the gate/up and the down again on the GEMM's own layout
+    (pack_gemm_experts: a second copy of the experts); then the MMVQ passes
     on the packed layouts."""
     cfg = workloads.CONFIGS["wide_e256"]
     hidden, inter, topk, n_exp, seed = cfg["hidden"], cfg["inter"], cfg["topk"], cfg["experts"], cfg["seed"]
@@ -921,11 +921,16 @@ def wide_sweep(torch, workloads, moeq8, ml, args):
         gu_us = time_graph(torch, lambda: moeq8.moe_grouped_gemm(
             moeq8.GATE_UP_SWIGLU_G8, ge.gemm_gate, ge.gemm_up, ws.xq, ws.grouping, n=inter, k=hidden,
             n_local_expert=n_exp, ncols=cols, topk=topk, out=ws.h), reps) * 1e3
+        dn_us = time_graph(torch, lambda: moeq8.moe_grouped_gemm(
+            moeq8.DOWN_G8, ge.gemm_down, None, ws.hq, ws.grouping, n=hidden, k=inter, n_local_expert=n_exp,
+            ncols=cols, topk=topk, out=ws.y), reps) * 1e3
         rec["gemm_layout"] = {"layer_us": round(layer_ms * 1e3, 1),
                               "cols_per_s": round(cols / (layer_ms * 1e-3), 1),
                               "gate_up_us": round(gu_us, 1),
                               "gate_up_gbps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
-                              "gate_up_frac_of_peak": round(gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+                              "gate_up_frac_of_peak": round(gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                              "down_us": round(dn_us, 1),
+                              "down_gbps": round(dn_b / (dn_us * 1e-6) / 1e9, 1)}
         # the ceiling: as many bytes read from the gate and up banks
         half = min(int(gu_b) // 2, bank.gate[0].numel()) // 16 * 16
 

@@ -122,8 +122,8 @@ int q8_0_pack64_rows(const void* src, int64_t n_rows, int64_t k, int64_t src_row
 int q8_0_pack64_rounds(const void* src, int64_t n_rows, int64_t k, int64_t src_row_stride_bytes, void* dst,
                        void* stream);
 
-/* Repack Q8_0 rows into the layout MOEQ8_GATE_UP_SWIGLU_G8 of
- * moe_grouped_gemm reads.  Each 272-byte group of 8 blocks (a row of k values
+/* Repack Q8_0 rows into the layout MOEQ8_GATE_UP_SWIGLU_G8 and MOEQ8_DOWN_G8 of
+ * moe_grouped_gemm read.  Each 272-byte group of 8 blocks (a row of k values
  * is k/256 groups, k a multiple of 256) holds the 8 blocks' fp16 scales in its
  * first 16 bytes (block j at byte 2j) and then their quants, block j's 32
  * bytes at 16 + 32j, so the matrix cores' 8-byte operand pieces are 8-byte
@@ -235,7 +235,7 @@ int moe_router_scores(const float* logits, int64_t n, float* scores, void* strea
  * ------------------------------------------------------------------------- */
 enum moeq8_stage { MOEQ8_GATE_UP_SWIGLU = 0, MOEQ8_DOWN = 1, MOEQ8_DOWN_F32_ACT = 2,
                    MOEQ8_GATE_UP_SWIGLU_P64 = 3, MOEQ8_DOWN_F32_ACT_P64 = 4,
-                   MOEQ8_GATE_UP_SWIGLU_G8 = 5 /* moe_grouped_gemm only */ };
+                   MOEQ8_GATE_UP_SWIGLU_G8 = 5, MOEQ8_DOWN_G8 = 6 /* moe_grouped_gemm only */ };
 int moe_grouped_mmvq(int32_t stage, const void* w_a, const void* w_b,
                      int64_t expert_stride_bytes, int64_t w_row_stride_bytes,
                      int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
@@ -394,11 +394,12 @@ size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk);
  *   masked routes are not written.  Work is split into (expert, route
  *   chunk, row tile) units, so an expert with many routes spreads over many
  *   workgroups.
- *   stage MOEQ8_GATE_UP_SWIGLU_G8: the gate/up stage on weights repacked by
- *   q8_0_pack_gemm_rows, with the same results bit for bit.  It always takes
- *   the staged form below, so it requires k % 256 == 0, n % 32 == 0, 16-byte
- *   aligned weights, xq, row and expert strides and xq rows, else
- *   MOEQ8_EUNSUPPORTED.
+ *   stages MOEQ8_GATE_UP_SWIGLU_G8 / MOEQ8_DOWN_G8: the gate/up and down
+ *   stages on weights repacked by q8_0_pack_gemm_rows, with the same results
+ *   bit for bit.  They always take the staged form below, so they require
+ *   k % 256 == 0, n % 32 == 0 (gate/up) or n % 64 == 0 (down), 16-byte
+ *   aligned weights, activations, row and expert strides and activation
+ *   rows, else MOEQ8_EUNSUPPORTED.
  *   Concurrency: when k is a multiple of 256 (gate/up; down from k = 2048)
  *   and the operands are 16-byte aligned, the workgroups take their units
  *   from one of 256 work counters of the library on the device, handed to

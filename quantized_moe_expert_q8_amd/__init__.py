@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     GATE_UP_SWIGLU_P64,
     DOWN_F32_ACT_P64,
     GATE_UP_SWIGLU_G8,
+    DOWN_G8,
     P64_K,
     Q8_0_BLOCK_BYTES,
     Q8_1_BLOCK_BYTES,

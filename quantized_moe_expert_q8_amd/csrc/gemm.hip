@@ -580,7 +580,7 @@ __device__ __forceinline__ void stage_act(const GemmParams& p, const StageGeomet
     }
 }
 
-// G8: the weights are in the layout of q8_0_pack_gemm_rows (per 8-block
+// G8: the weights (gate/up, or down) are in the layout of q8_0_pack_gemm_rows (per 8-block
 // group, 16 bytes of scales, then 8-byte aligned quants with the 8-byte halves
 // of each 16-byte piece swapped in rows 8-15 of every 16): a lane's operand
 // piece is one aligned 8-byte read, and the 16 rows of a wave's read fall
@@ -589,7 +589,6 @@ __device__ __forceinline__ void stage_act(const GemmParams& p, const StageGeomet
 template <bool PAIR, bool G8 = false>
 __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_gemm_staged(
     const GemmParams p) {
-    static_assert(!G8 || PAIR, "the GEMM layout serves the gate/up stage");
     __shared__ __align__(16) uint8_t lds[S_LDS];
     constexpr int NM = PAIR ? 2 : 1;                   // weight fragments a wave reads a block
     constexpr int NR = PAIR ? 1 : 2;                   // route tiles a wave runs
@@ -861,10 +860,11 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
                                 int64_t n_local_expert, int64_t n, int64_t k, const void* act_q,
                                 const void* grouping, int64_t ncols, int32_t topk, float* out,
                                 void* stream) {
-    if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_GATE_UP_SWIGLU_G8)
+    if (stage != MOEQ8_GATE_UP_SWIGLU && stage != MOEQ8_DOWN && stage != MOEQ8_GATE_UP_SWIGLU_G8 &&
+        stage != MOEQ8_DOWN_G8)
         return MOEQ8_EINVAL;
-    const bool g8 = stage == MOEQ8_GATE_UP_SWIGLU_G8;
-    const bool pair = stage == MOEQ8_GATE_UP_SWIGLU || g8;
+    const bool g8 = stage == MOEQ8_GATE_UP_SWIGLU_G8 || stage == MOEQ8_DOWN_G8;
+    const bool pair = stage == MOEQ8_GATE_UP_SWIGLU || stage == MOEQ8_GATE_UP_SWIGLU_G8;
     if (n < 0 || k <= 0 || k % 64 != 0 || n % 32 != 0) return MOEQ8_EINVAL;
     int st = validate_weights(w_a, w_row_stride_bytes, k);
     if (st) return st;
@@ -909,7 +909,7 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
     // register-fed form below it (k = 1024, four steps: 507 against 499 us)
     const int srows = pair ? 32 : 64;
     const int64_t act_rows = pair ? ncols : R;
-    const bool staged = (pair || k >= 8 * S_STEP_BLOCKS * QK) && k % (S_STEP_BLOCKS * QK) == 0 &&
+    const bool staged = (pair || g8 || k >= 8 * S_STEP_BLOCKS * QK) && k % (S_STEP_BLOCKS * QK) == 0 &&
                         n % srows == 0 &&
                         64 * w_row_stride_bytes < ((int64_t)1 << 31) &&
                         act_rows * p.act_row_bytes < ((int64_t)1 << 31) &&
@@ -926,8 +926,10 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
         const int64_t cap = (int64_t)S_WG_PER_CU * cus;
         const int64_t grid = (std::min<int64_t>(units, cap) + XCDS - 1) / XCDS * XCDS;
         p.tiles = (int32_t)tiles;
-        if (g8)
+        if (g8 && pair)
             hipLaunchKernelGGL((k_grouped_gemm_staged<true, true>), dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+        else if (g8)
+            hipLaunchKernelGGL((k_grouped_gemm_staged<false, true>), dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
         else if (pair)
             hipLaunchKernelGGL(k_grouped_gemm_staged<true>, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
         else

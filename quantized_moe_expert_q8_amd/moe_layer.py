@@ -50,10 +50,11 @@ class RoutedExperts:
     inter: int
     fmt: str = "q8_0"
     packed: bool = False
-    # optional copies of gate and up in the grouped GEMM's layout
-    # (pack_gemm_experts), read by forward_wide's matrix-core gate/up
+    # optional copies of gate, up and down in the grouped GEMM's layout
+    # (pack_gemm_experts), read by forward_wide's matrix-core products
     gemm_gate: torch.Tensor | None = None
     gemm_up: torch.Tensor | None = None
+    gemm_down: torch.Tensor | None = None
 
 
 @dataclass
@@ -333,8 +334,12 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
             grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
                     n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
         ops.q8_1_quantize_rows(ws.h.view(c * topk, inter), out=ws.hq)
-        grouped(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
-                n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
+        if products == "gemm" and experts.gemm_down is not None:
+            ops.moe_grouped_gemm(ops.DOWN_G8, experts.gemm_down, None, ws.hq, ws.grouping, n=hidden, k=inter,
+                                 n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
+        else:
+            grouped(ops.DOWN, experts.down, None, ws.hq, ws.grouping, n=hidden, k=inter,
+                    n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
     ops.moe_combine(ws.y, ws.ids, ws.weights, out=ws.out)
     return ws.out
 
@@ -406,18 +411,23 @@ def pack_experts(experts: RoutedExperts, shared: SharedExpertShare | None = None
     return pe, ps
 
 
-def pack_gemm_experts(experts: RoutedExperts) -> RoutedExperts:
-    """The experts with copies of gate and up in the grouped GEMM's layout
-    (ops.q8_0_pack_gemm_rows, allocated here) for forward_wide's matrix-core
-    gate/up; the plain matrices stay for the MMVQ passes and the down."""
+def pack_gemm_experts(experts: RoutedExperts, down: bool = True) -> RoutedExperts:
+    """The experts with copies of gate, up and (with down=True) down in the
+    grouped GEMM's layout (ops.q8_0_pack_gemm_rows, allocated here) for
+    forward_wide's matrix-core products; the plain matrices stay for the
+    MMVQ passes."""
     if experts.fmt != "q8_0" or experts.packed:
         raise ValueError("pack_gemm_experts takes plain Q8_0 experts")
     if experts.hidden % 256 or experts.inter % 32:
         raise ValueError("the GEMM layout takes hidden % 256 == 0 and inter % 32 == 0")
+    if down and (experts.inter % 256 or experts.hidden % 64):
+        raise ValueError("the GEMM layout of the down takes inter % 256 == 0 and hidden % 64 == 0")
     rows = experts.n_local * experts.inter
     return RoutedExperts(experts.gate, experts.up, experts.down, experts.n_local, experts.hidden,
                          experts.inter, gemm_gate=ops.q8_0_pack_gemm_rows(experts.gate, rows, experts.hidden),
-                         gemm_up=ops.q8_0_pack_gemm_rows(experts.up, rows, experts.hidden))
+                         gemm_up=ops.q8_0_pack_gemm_rows(experts.up, rows, experts.hidden),
+                         gemm_down=(ops.q8_0_pack_gemm_rows(experts.down, experts.n_local * experts.hidden,
+                                                            experts.inter) if down else None))
 
 
 def expert_bytes_q4(hidden: int, inter: int) -> int:

@@ -26,6 +26,7 @@ DOWN_F32_ACT = 2
 GATE_UP_SWIGLU_P64 = 3      # gate/up on weights repacked by q8_0_pack64_rows
 DOWN_F32_ACT_P64 = 4        # down (fp32 h) on weights repacked by q8_0_pack64_rounds
 GATE_UP_SWIGLU_G8 = 5       # moe_grouped_gemm gate/up on weights repacked by q8_0_pack_gemm_rows
+DOWN_G8 = 6                 # moe_grouped_gemm down on weights repacked by q8_0_pack_gemm_rows
 ROUND_BYTES = 1088          # a 1024-value round of Q8_0 blocks
 P64_K = 4096                # values in one packed segment
 
@@ -489,10 +490,12 @@ def _grouped_call(fn: str, stage: int, w_a, w_b, act_q, grouping, n, k, n_local_
         _cuda(w_b, "w_b", torch.uint8)
         _need(w_b, "w_b", extent)
         act_rows = ncols
-    elif stage == DOWN:
+    elif stage in (DOWN, DOWN_G8):
+        if stage == DOWN_G8 and fn != "moe_grouped_gemm":
+            raise ValueError("DOWN_G8 is a stage of moe_grouped_gemm")
         act_rows = ncols * topk
     else:
-        raise ValueError("stage must be GATE_UP_SWIGLU, GATE_UP_SWIGLU_G8 (GEMM) or DOWN")
+        raise ValueError("stage must be GATE_UP_SWIGLU, DOWN or (GEMM) GATE_UP_SWIGLU_G8, DOWN_G8")
     _act_rows(act_q, "act_q", act_rows, k)
     _cuda(grouping, "grouping", torch.uint8)
     _need(grouping, "grouping", moe_grouping_bytes_wide(ncols, topk))
@@ -523,8 +526,8 @@ def moe_grouped_gemm(stage: int, w_a: torch.Tensor, w_b: torch.Tensor | None, ac
                      out: torch.Tensor | None = None) -> torch.Tensor:
     """The grouped products on the int8 matrix cores (wide batches): same
     arguments and results as moe_grouped_mmvq, equal to rounding (n % 32 == 0).
-    Stage GATE_UP_SWIGLU_G8 takes gate/up repacked by q8_0_pack_gemm_rows (the
-    bits of GATE_UP_SWIGLU on the plain rows)."""
+    Stages GATE_UP_SWIGLU_G8 and DOWN_G8 take weights repacked by
+    q8_0_pack_gemm_rows (the bits of GATE_UP_SWIGLU / DOWN on the plain rows)."""
     return _grouped_call("moe_grouped_gemm", stage, w_a, w_b, act_q, grouping, n, k, n_local_expert,
                          ncols, topk, expert_stride_bytes, w_row_stride_bytes, out)
 

@@ -211,7 +211,8 @@ def test_packed_layout_validation():
     gg = L.moe_grouped_gemm                                                      # the GEMM layout: staged form only
     assert gg(5, P, Q, 0, 68 * 2, 1, 32, 128, P, P, 1, 1, P, None) == -3         # k % 256
     assert gg(5, P + 4, Q, 0, 272, 1, 32, 256, P, P, 1, 1, P, None) == -3        # 16-byte alignment
-    assert gg(6, P, Q, 0, 272, 1, 32, 256, P, P, 1, 1, P, None) == -1            # no such stage
+    assert gg(6, P, None, 0, 272, 1, 32, 256, P, P, 1, 1, P, None) == -3         # down: whole 64-row tiles
+    assert gg(7, P, Q, 0, 272, 1, 32, 256, P, P, 1, 1, P, None) == -1            # no such stage
     q4 = L.q4_pack64_rows
     assert q4(P, 2, 2048, 1152, Q, 1152, None) == -1                             # k % 4096
     assert q4(P, 2, 4096, 2300, Q, 4608, None) == -1                             # stride shorter than a row

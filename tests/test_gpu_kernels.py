@@ -1225,11 +1225,11 @@ def test_gemm_layout_bytes(rows, k):
     (40, 8, 8, 8, 512, 64),          # two K steps
 ])
 def test_gemm_layout_equals_plain(c, n_exp, local, topk, hidden, inter):
-    """GATE_UP_SWIGLU_G8 on weights repacked by q8_0_pack_gemm_rows against
-    GATE_UP_SWIGLU on the plain rows: every output bit for bit, rows of
-    masked routes untouched."""
+    """GATE_UP_SWIGLU_G8 and DOWN_G8 on weights repacked by q8_0_pack_gemm_rows
+    against GATE_UP_SWIGLU and DOWN on the plain rows: every output bit for
+    bit, rows of masked routes untouched."""
     say(f"gemm layout vs plain c={c} E={n_exp} local={local} k={topk} H={hidden} I={inter}")
-    (_, _, _), (wgd, wud, _), x, ids_ref, ids, g = _gemm_case(c, n_exp, local, topk, hidden, inter, 5 * c + hidden)
+    (_, _, _), (wgd, wud, wdd), x, ids_ref, ids, g = _gemm_case(c, n_exp, local, topk, hidden, inter, 5 * c + hidden)
     xd = moeq8.q8_1_quantize_rows(to_dev(x))
     pg = moeq8.q8_0_pack_gemm_rows(wgd, local * inter, hidden)
     pu = moeq8.q8_0_pack_gemm_rows(wud, local * inter, hidden)
@@ -1242,6 +1242,19 @@ def test_gemm_layout_equals_plain(c, n_exp, local, topk, hidden, inter):
     assert bits_equal(outs[0], outs[1])
     live = torch.from_numpy(ids_ref.reshape(-1) >= 0).to(DEV)
     assert not torch.isnan(outs[1].reshape(c * topk, -1)[live]).any()
+    if inter % 256:
+        return                                       # the down's layout takes whole 8-block groups
+    # the down: DOWN_G8 (always staged) against DOWN on the plain rows
+    hq = moeq8.q8_1_quantize_rows(torch.nan_to_num(outs[0]).reshape(c * topk, inter))
+    pd = moeq8.q8_0_pack_gemm_rows(wdd, local * hidden, inter)
+    ys = []
+    for stage, a in ((moeq8.DOWN, wdd), (moeq8.DOWN_G8, pd)):
+        y = torch.full((c, topk, hidden), float("nan"), device=DEV)
+        moeq8.moe_grouped_gemm(stage, a, None, hq, g, n=hidden, k=inter, n_local_expert=local, ncols=c,
+                               topk=topk, out=y)
+        ys.append(y)
+    assert bits_equal(ys[0], ys[1])
+    assert not torch.isnan(ys[1].reshape(c * topk, -1)[live]).any()
 
 
 @pytest.mark.parametrize("c", [40, 512])
