@@ -525,6 +525,19 @@ __device__ __forceinline__ long a_frag(const uint8_t* ar, int q8) {
     return (long)(((uint64_t)hi << 32) | lo);
 }
 
+// The activation rows of a stage (288 bytes, 72 dwords apart) put slots c,
+// c + 4, c + 8, c + 12 of a 16-route tile on the same LDS banks.  With the
+// GEMM's weight layout the pieces of slots with bit 2 set are stored rotated
+// by one 16-byte place, so a tile's fragment reads meet two rows a bank group
+// instead of four (measured at 512 / 1024 columns: gate/up 458 -> 450 and
+// 602 -> 586 us, down 317 -> 286 and 460 -> 391; with the plain weight rows,
+// whose fragment reads are split and conflict on their own, the same rotation
+// measured slower: gate/up 196 -> 219 us at 32 columns).  Byte o of slot s's
+// row sits at o + 16 a_rot(s), except in the row's last piece (o >= 272),
+// which wraps to the row's start.
+template <bool ROT>
+__device__ __forceinline__ int a_rot(int slot) { return ROT ? (slot >> 2) & 1 : 0; }
+
 // Where this lane's pieces of a step come from and go to, the same for every
 // unit and step: weight piece j of the wave is row wrow, 16-byte part wpart
 // of the stage's weight rows (gate/up: rows 0..31 gate, 32..63 up);
@@ -536,7 +549,7 @@ struct StageGeometry {
     int a_part[S_SLOTS];                               // 16 apart
 };
 
-template <bool PAIR>
+template <bool PAIR, bool ROT>
 __device__ __forceinline__ void stage_geometry(const GemmParams& p, int wave, int l, StageGeometry& G) {
     G.w_up = 0;
 #pragma unroll
@@ -551,7 +564,8 @@ __device__ __forceinline__ void stage_geometry(const GemmParams& p, int wave, in
         const int apiece = min(i, S_A_LOADS - 1) * 64 + l;
         const int slot = apiece / 18;
         G.a_slot[j] = i < S_A_LOADS ? slot : -1;
-        G.a_part[j] = (apiece - slot * 18) * 16;
+        // LDS position pp of the slot's row holds piece pp - a_rot(slot) (mod 18)
+        G.a_part[j] = (apiece - slot * 18 + 18 - a_rot<ROT>(slot)) % 18 * 16;
     }
 }
 
@@ -638,7 +652,7 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
     }
 
     StageGeometry G;
-    stage_geometry<PAIR>(p, wave, l, G);
+    stage_geometry<PAIR, G8>(p, wave, l, G);
     int a_off[S_SLOTS];
     stage_act(p, G, rbegin, nr, a_off);
 
@@ -695,8 +709,8 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
             for (int h = 0; h < 2 * NR; ++h) {
                 const int ent = h * 64 + l;
                 const int k = ent / (16 * NR), sl = ent % (16 * NR);
-                dxt[k * 32 + sl] = half_bits_to_float(
-                    *reinterpret_cast<const uint16_t*>(A + (tile0 * 16 + sl) * S_AROW + k * Q81_BYTES));
+                dxt[k * 32 + sl] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(
+                    A + (tile0 * 16 + sl) * S_AROW + 16 * a_rot<G8>(sl) + k * Q81_BYTES));
             }
             // two blocks at a time: fragments of both, then the matrix-core
             // products of both, then the scaled sums in block order (block K
@@ -730,9 +744,13 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                     }
 #pragma unroll
                     for (int rt = 0; rt < NL; ++rt) {
+                        // the fragment of block 7 at q8 >= 16 lies in the row's
+                        // last piece (rotated to the row's start when a_rot)
                         const uint8_t* ar = A + ((tile0 + rt) * 16 + c) * S_AROW;
-                        xa[0][rt] = a_frag<K0>(ar, q8);
-                        xa[1][rt] = a_frag<K0 + 1>(ar, q8);
+                        const uint8_t* ar0 = ar + 16 * a_rot<G8>(c);
+                        const uint8_t* ar7 = q8 < 16 ? ar0 : a_rot<G8>(c) ? ar - 272 : ar;
+                        xa[0][rt] = a_frag<K0>(K0 == 7 ? ar7 : ar0, q8);
+                        xa[1][rt] = a_frag<K0 + 1>(K0 + 1 == 7 ? ar7 : ar0, q8);
                         dx4[0][rt] = *reinterpret_cast<const float4*>(dxt + K0 * 32 + rt * 16 + q8 / 2);
                         dx4[1][rt] = *reinterpret_cast<const float4*>(dxt + (K0 + 1) * 32 + rt * 16 + q8 / 2);
                     }

@@ -334,11 +334,12 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
             grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
                     n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
         ops.q8_1_quantize_rows(ws.h.view(c * topk, inter), out=ws.hq)
-        # the down on the GEMM layout runs the staged form, faster once the
-        # experts average 8 routes or more (256-expert layer: 317 against 336
-        # us at 512 columns, 459 against 496 at 1024); below that the plain
-        # rows' register-fed form is (117 against 124 us at 32 columns)
-        if products == "gemm" and experts.gemm_down is not None and c * topk >= 8 * experts.n_local:
+        # the down on the GEMM layout runs the staged form, as fast once the
+        # experts average 4 routes (256-expert layer: 192 against 194 us at 128
+        # columns) and faster beyond (289 against 336 at 512, 389 against 496
+        # at 1024); with fewer the plain rows' register-fed form is (117
+        # against 120 us at 32 columns)
+        if products == "gemm" and experts.gemm_down is not None and c * topk >= 4 * experts.n_local:
             ops.moe_grouped_gemm(ops.DOWN_G8, experts.gemm_down, None, ws.hq, ws.grouping, n=hidden, k=inter,
                                  n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
         else:
