@@ -50,6 +50,14 @@ namespace moeq8 {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// fp16 bits h as element 0 of a 4-vector, the rest +0.
+__device__ __forceinline__ f16x4 half4_lo(uint32_t h) {
+    const uint64_t v = h;
+    return __builtin_bit_cast(f16x4, v);
+}
 
 #ifndef MOEQ8_GEMM_WAVES
 #define MOEQ8_GEMM_WAVES 2
@@ -704,9 +712,10 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
         auto compute = [&](int b) {
             const uint8_t* W = lds + b * S_STAGE;
             const uint8_t* A = W + S_W;
-            // this wave's activation scales, fp32 (read back by this wave only)
+            // this wave's activation scales, fp32 (read back by this wave only;
+            // the plain layout's forms)
 #pragma unroll
-            for (int h = 0; h < 2 * NR; ++h) {
+            for (int h = 0; h < (G8 ? 0 : 2 * NR); ++h) {
                 const int ent = h * 64 + l;
                 const int k = ent / (16 * NR), sl = ent % (16 * NR);
                 dxt[k * 32 + sl] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(
@@ -723,6 +732,13 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                     float dwv[2][NM];
                     float4 dx4[2][NL];
                     i32x4 d[2][NL][NM];
+                    // G8: the scale products d_x * d_w of each block's 16 x 16 tile
+                    // come from the matrix cores, an fp16 product whose only
+                    // nonzero K term is lane group 0's (exact in fp32: the same
+                    // values as the fp32 multiply)
+                    uint32_t dwh[2][NM], dxh[2][NL];
+                    f32x4 sc[2][NL][NM];
+                    const uint32_t kmask = (l >> 4) == 0 ? 0xFFFFu : 0u;
 #pragma unroll
                     for (int m = 0; m < NM; ++m) {
                         const uint8_t* wr = W + (m * 32 + rh + c) * S_WROW;
@@ -733,8 +749,8 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                             wb[0][m] = *reinterpret_cast<const long*>(wr + 16 + 32 * K0 + qx);
                             wb[1][m] = *reinterpret_cast<const long*>(wr + 16 + 32 * (K0 + 1) + qx);
                             const uint32_t sw = *reinterpret_cast<const uint32_t*>(wr + 2 * K0);
-                            dwv[0][m] = half_bits_to_float(sw & 0xFFFFu);
-                            dwv[1][m] = half_bits_to_float(sw >> 16);
+                            dwh[0][m] = sw & kmask;
+                            dwh[1][m] = (sw >> 16) & kmask;
                         } else {
                             wb[0][m] = w_frag<K0>(wr, q8);
                             wb[1][m] = w_frag<K0 + 1>(wr, q8);
@@ -751,8 +767,13 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                         const uint8_t* ar7 = q8 < 16 ? ar0 : a_rot<G8>(c) ? ar - 272 : ar;
                         xa[0][rt] = a_frag<K0>(K0 == 7 ? ar7 : ar0, q8);
                         xa[1][rt] = a_frag<K0 + 1>(K0 + 1 == 7 ? ar7 : ar0, q8);
-                        dx4[0][rt] = *reinterpret_cast<const float4*>(dxt + K0 * 32 + rt * 16 + q8 / 2);
-                        dx4[1][rt] = *reinterpret_cast<const float4*>(dxt + (K0 + 1) * 32 + rt * 16 + q8 / 2);
+                        if constexpr (G8) {
+                            dxh[0][rt] = *reinterpret_cast<const uint16_t*>(ar0 + K0 * Q81_BYTES) & kmask;
+                            dxh[1][rt] = *reinterpret_cast<const uint16_t*>(ar0 + (K0 + 1) * Q81_BYTES) & kmask;
+                        } else {
+                            dx4[0][rt] = *reinterpret_cast<const float4*>(dxt + K0 * 32 + rt * 16 + q8 / 2);
+                            dx4[1][rt] = *reinterpret_cast<const float4*>(dxt + (K0 + 1) * 32 + rt * 16 + q8 / 2);
+                        }
                     }
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
@@ -762,17 +783,30 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                             for (int m = 0; m < NM; ++m) {
                                 const i32x4 z = {0, 0, 0, 0};
                                 d[kk][rt][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa[kk][rt], wb[kk][m], z, 0, 0, 0);
+                                if constexpr (G8) {
+                                    const f32x4 zf = {0.0f, 0.0f, 0.0f, 0.0f};
+                                    sc[kk][rt][m] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                                        half4_lo(dxh[kk][rt]), half4_lo(dwh[kk][m]), zf, 0, 0, 0);
+                                }
                             }
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                         for (int rt = 0; rt < NL; ++rt) {
-                            const float dxv[4] = {dx4[kk][rt].x, dx4[kk][rt].y, dx4[kk][rt].z, dx4[kk][rt].w};
+                            if constexpr (G8) {
 #pragma unroll
-                            for (int m = 0; m < NM; ++m)
+                                for (int m = 0; m < NM; ++m)
 #pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    acc[rt][m][i] = fmaf((float)d[kk][rt][m][i], dwv[kk][m] * dxv[i], acc[rt][m][i]);
+                                    for (int i = 0; i < 4; ++i)
+                                        acc[rt][m][i] = fmaf((float)d[kk][rt][m][i], sc[kk][rt][m][i], acc[rt][m][i]);
+                            } else {
+                                const float dxv[4] = {dx4[kk][rt].x, dx4[kk][rt].y, dx4[kk][rt].z, dx4[kk][rt].w};
+#pragma unroll
+                                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i)
+                                        acc[rt][m][i] = fmaf((float)d[kk][rt][m][i], dwv[kk][m] * dxv[i], acc[rt][m][i]);
+                            }
                         }
                 };
                 two_blocks(std::integral_constant<int, 0>{});

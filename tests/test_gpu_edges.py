@@ -102,6 +102,42 @@ def test_products_with_zero_and_subnormal_scales(case):
                 _exact(y[j, s], oracle.mmvq(wexp[e * n:(e + 1) * n], hq[r:r + 1])[0], f"{name} ({j},{s})")
 
 
+@pytest.mark.parametrize("case", sorted(SCALE_CASES))
+def test_gemm_layout_with_zero_and_subnormal_scales(case):
+    """The grouped GEMM on its own weight layout takes each block's scale
+    product d_x * d_w from an fp16 matrix-core product: with zero and fp16
+    subnormal scales on either side the down still equals the oracle exactly
+    (scales as above), and the gate/up the plain layout's bits."""
+    say(f"edge scales, GEMM layout {case}")
+    ws, xs = SCALE_CASES[case]
+    rng = np.random.default_rng(200 + sorted(SCALE_CASES).index(case))
+    n, k, c, n_exp, topk = 64, 1024, 3, 4, 2
+    nb = k // 32
+    wexp = np.concatenate([_blocks(rng, n, nb, ws, False) for _ in range(n_exp)])
+    hq = _blocks(rng, c * topk, nb, xs, True)
+    lg = to_dev(workloads.router_logits(6, c, n_exp))
+    ids, _, grouping = moeq8.moe_route_topk(lg, topk)
+    idh = host(ids)
+    wd = to_dev(wexp)
+    y = host(moeq8.moe_grouped_gemm(moeq8.DOWN_G8, moeq8.q8_0_pack_gemm_rows(wd, n_exp * n, k), None, to_dev(hq),
+                                    grouping, n=n, k=k, n_local_expert=n_exp, ncols=c, topk=topk))
+    for j in range(c):
+        for s_ in range(topk):
+            e = int(idh[j, s_])
+            r = j * topk + s_
+            _exact(y[j, s_], oracle.mmvq(wexp[e * n:(e + 1) * n], hq[r:r + 1])[0], f"GEMM layout down ({j},{s_})")
+    # gate/up: the layout's bits against the plain rows'
+    wu = to_dev(np.concatenate([_blocks(rng, n, nb, ws, False) for _ in range(n_exp)]))
+    xq = to_dev(_blocks(rng, c, nb, xs, True))
+    outs = []
+    for stage, a, b in ((moeq8.GATE_UP_SWIGLU, wd, wu),
+                        (moeq8.GATE_UP_SWIGLU_G8, moeq8.q8_0_pack_gemm_rows(wd, n_exp * n, k),
+                         moeq8.q8_0_pack_gemm_rows(wu, n_exp * n, k))):
+        outs.append(moeq8.moe_grouped_gemm(stage, a, b, xq, grouping, n=n, k=k, n_local_expert=n_exp, ncols=c,
+                                           topk=topk))
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+
+
 # ---------------------------------------------------------------------------
 # guard canaries
 # ---------------------------------------------------------------------------
