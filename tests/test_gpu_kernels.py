@@ -1159,9 +1159,9 @@ def test_staged_gemm_work_counters_return_to_zero():
     counters (256 call slots, handed out in turn); a call leaves its counters
     at zero.  300 calls in a row (every slot reused) with units of one, two
     and four K steps (the next unit drawn at the last step, or two steps
-    before it) and a down of 8 steps: every call gives the bits of the
-    register-fed form (a counter left off zero would skip units, leaving NaN
-    rows)."""
+    before it) and a down of 8 steps, on the plain rows and the GEMM layout in
+    turn: every call gives the bits of the register-fed form (a counter left
+    off zero would skip units, leaving NaN rows)."""
     say("staged gemm work counters, 300 calls")
     c, n_exp, local, topk, inter = 40, 8, 8, 8, 64
     cases = []
@@ -1177,20 +1177,26 @@ def test_staged_gemm_work_counters_return_to_zero():
     yref = torch.full((c, topk, 256), float("nan"), device=DEV)
     moeq8.moe_grouped_gemm(moeq8.DOWN, _off_alignment(wdd), None, hq, gd, n=256, k=2048, n_local_expert=local,
                            ncols=c, topk=topk, out=yref)
+    # the GEMM layout's kernels draw from the same counters
+    packed = {hidden: (moeq8.q8_0_pack_gemm_rows(wgd, local * inter, hidden),
+                       moeq8.q8_0_pack_gemm_rows(wud, local * inter, hidden)) for hidden, wgd, wud, _, _, _ in cases}
+    pdd = moeq8.q8_0_pack_gemm_rows(wdd, local * 256, 2048)
     h = torch.empty((c, topk, inter), device=DEV)
     y = torch.empty((c, topk, 256), device=DEV)
     for i in range(300):
+        g8 = (i // 4) % 2 == 1
         if i % 4 == 3:
             y.fill_(float("nan"))
-            moeq8.moe_grouped_gemm(moeq8.DOWN, wdd, None, hq, gd, n=256, k=2048, n_local_expert=local,
-                                   ncols=c, topk=topk, out=y)
+            moeq8.moe_grouped_gemm(moeq8.DOWN_G8 if g8 else moeq8.DOWN, pdd if g8 else wdd, None, hq, gd, n=256,
+                                   k=2048, n_local_expert=local, ncols=c, topk=topk, out=y)
             assert bits_equal(y, yref), i
         else:
             hidden, wgd, wud, xd, g, ref = cases[i % 4]
+            a, b = packed[hidden] if g8 else (wgd, wud)
             h.fill_(float("nan"))
-            moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU, wgd, wud, xd, g, n=inter, k=hidden, n_local_expert=local,
-                                   ncols=c, topk=topk, out=h)
-            assert bits_equal(h, ref), (i, hidden)
+            moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU_G8 if g8 else moeq8.GATE_UP_SWIGLU, a, b, xd, g, n=inter,
+                                   k=hidden, n_local_expert=local, ncols=c, topk=topk, out=h)
+            assert bits_equal(h, ref), (i, hidden, g8)
 
 
 def _gemm_layout_reference(raw: np.ndarray, rows: int, k: int) -> np.ndarray:
