@@ -400,7 +400,7 @@ size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk);
  *   k % 256 == 0, n % 32 == 0 (gate/up) or n % 64 == 0 (down), 16-byte
  *   aligned weights, activations, row and expert strides and activation
  *   rows, else MOEQ8_EUNSUPPORTED.
- *   Concurrency: when k is a multiple of 256 (gate/up; down from k = 2048)
+ *   Concurrency: when k is a multiple of 256 (gate/up; down from k = 1024)
  *   and the operands are 16-byte aligned, the workgroups take their units
  *   from one of 256 work counters of the library on the device, handed to
  *   the calls in turn and left at zero when a call ends: at most 256 calls

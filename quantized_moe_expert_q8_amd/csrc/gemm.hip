@@ -534,13 +534,15 @@ __device__ __forceinline__ long a_frag(const uint8_t* ar, int q8) {
 }
 
 // The activation rows of a stage (288 bytes, 72 dwords apart) put slots c,
-// c + 4, c + 8, c + 12 of a 16-route tile on the same LDS banks.  With the
-// GEMM's weight layout the pieces of slots with bit 2 set are stored rotated
-// by one 16-byte place, so a tile's fragment reads meet two rows a bank group
-// instead of four (measured at 512 / 1024 columns: gate/up 458 -> 450 and
-// 602 -> 586 us, down 317 -> 286 and 460 -> 391; with the plain weight rows,
-// whose fragment reads are split and conflict on their own, the same rotation
-// measured slower: gate/up 196 -> 219 us at 32 columns).  Byte o of slot s's
+// c + 4, c + 8, c + 12 of a 16-route tile on the same LDS banks.  On the
+// GEMM's weight layout, and in the down (two route tiles a wave) on either,
+// the pieces of slots with bit 2 set are stored rotated by one 16-byte place,
+// so a tile's fragment reads meet two rows a bank group instead of four
+// (measured at 512 / 1024 columns: gate/up on the layout 458 -> 450 and
+// 602 -> 586 us, its down 317 -> 286 and 460 -> 391; the plain rows' down at
+// k = 1024 staged 294 / 407 us against 336 / 497 register-fed; the plain
+// rows' gate/up, whose weight reads are split and conflict on their own,
+// measured slower with it: 196 -> 219 us at 32 columns).  Byte o of slot s's
 // row sits at o + 16 a_rot(s), except in the row's last piece (o >= 272),
 // which wraps to the row's start.
 template <bool ROT>
@@ -660,7 +662,8 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
     }
 
     StageGeometry G;
-    stage_geometry<PAIR, G8>(p, wave, l, G);
+    constexpr bool ROT = G8 || !PAIR;
+    stage_geometry<PAIR, ROT>(p, wave, l, G);
     int a_off[S_SLOTS];
     stage_act(p, G, rbegin, nr, a_off);
 
@@ -719,7 +722,7 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                 const int ent = h * 64 + l;
                 const int k = ent / (16 * NR), sl = ent % (16 * NR);
                 dxt[k * 32 + sl] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(
-                    A + (tile0 * 16 + sl) * S_AROW + 16 * a_rot<G8>(sl) + k * Q81_BYTES));
+                    A + (tile0 * 16 + sl) * S_AROW + 16 * a_rot<ROT>(sl) + k * Q81_BYTES));
             }
             // two blocks at a time: fragments of both, then the matrix-core
             // products of both, then the scaled sums in block order (block K
@@ -763,8 +766,8 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                         // the fragment of block 7 at q8 >= 16 lies in the row's
                         // last piece (rotated to the row's start when a_rot)
                         const uint8_t* ar = A + ((tile0 + rt) * 16 + c) * S_AROW;
-                        const uint8_t* ar0 = ar + 16 * a_rot<G8>(c);
-                        const uint8_t* ar7 = q8 < 16 ? ar0 : a_rot<G8>(c) ? ar - 272 : ar;
+                        const uint8_t* ar0 = ar + 16 * a_rot<ROT>(c);
+                        const uint8_t* ar7 = q8 < 16 ? ar0 : a_rot<ROT>(c) ? ar - 272 : ar;
                         xa[0][rt] = a_frag<K0>(K0 == 7 ? ar7 : ar0, q8);
                         xa[1][rt] = a_frag<K0 + 1>(K0 + 1 == 7 ? ar7 : ar0, q8);
                         if constexpr (G8) {
@@ -956,12 +959,12 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
     // the staged form: whole 8-block steps, whole row tiles, 16-byte aligned
     // rows and steps (every staged piece is one aligned 16-byte load), piece
     // offsets within 32 bits (a tile's rows, the activation rows); the down
-    // from 8 steps a unit on (k >= 2048: measured at hidden 4096 and 7168,
-    // 815 against 1013 us and 1397 against 1761 at 1024 columns), the
-    // register-fed form below it (k = 1024, four steps: 507 against 499 us)
+    // from 4 steps a unit on (k >= 1024; at k = 1024 on the 256-expert layer
+    // 119 / 192 / 294 / 407 us at 32 / 128 / 512 / 1024 columns against 117 /
+    // 193 / 336 / 497 for the register-fed form, which takes shorter k)
     const int srows = pair ? 32 : 64;
     const int64_t act_rows = pair ? ncols : R;
-    const bool staged = (pair || g8 || k >= 8 * S_STEP_BLOCKS * QK) && k % (S_STEP_BLOCKS * QK) == 0 &&
+    const bool staged = (pair || g8 || k >= 4 * S_STEP_BLOCKS * QK) && k % (S_STEP_BLOCKS * QK) == 0 &&
                         n % srows == 0 &&
                         64 * w_row_stride_bytes < ((int64_t)1 << 31) &&
                         act_rows * p.act_row_bytes < ((int64_t)1 << 31) &&

@@ -334,12 +334,7 @@ def forward_wide(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | Non
             grouped(ops.GATE_UP_SWIGLU, experts.gate, experts.up, ws.xq, ws.grouping, n=inter, k=hidden,
                     n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.h)
         ops.q8_1_quantize_rows(ws.h.view(c * topk, inter), out=ws.hq)
-        # the down on the GEMM layout runs the staged form, as fast once the
-        # experts average 4 routes (256-expert layer: 192 against 194 us at 128
-        # columns) and faster beyond (289 against 336 at 512, 389 against 496
-        # at 1024); with fewer the plain rows' register-fed form is (117
-        # against 120 us at 32 columns)
-        if products == "gemm" and experts.gemm_down is not None and c * topk >= 4 * experts.n_local:
+        if products == "gemm" and experts.gemm_down is not None:
             ops.moe_grouped_gemm(ops.DOWN_G8, experts.gemm_down, None, ws.hq, ws.grouping, n=hidden, k=inter,
                                  n_local_expert=experts.n_local, ncols=c, topk=topk, out=ws.y)
         else:
