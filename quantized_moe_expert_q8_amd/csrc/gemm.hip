@@ -59,6 +59,17 @@ __device__ __forceinline__ f16x4 half4_lo(uint32_t h) {
     return __builtin_bit_cast(f16x4, v);
 }
 
+// The fp16 bits h of block K0 + kk's activation scale at K term (K0 + kk) % 4
+// of a 4-vector, the other terms +0.
+template <int K0>
+__device__ __forceinline__ f16x4 dx_term(uint32_t h, int kk) {
+    const int term = (K0 + kk) % 4;
+    const uint32_t v = (term & 1) ? h << 16 : h;
+    const uint64_t w = (term & 2) ? (uint64_t)v << 32 : (uint64_t)v;
+    return __builtin_bit_cast(f16x4, w);
+}
+
+
 #ifndef MOEQ8_GEMM_WAVES
 #define MOEQ8_GEMM_WAVES 2
 #endif
@@ -447,8 +458,9 @@ __global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(nt
 // not a fresh fill (the down has only a few steps a unit).
 //   LDS per step: weights 64 rows x 272 bytes (a row's 8 blocks, as stored),
 //   activations 64 routes x 288 bytes; per wave, fp32 activation scales of
-//   its route slots.  Every wave issues the same six loads a step (pieces it
-//   has no use for go to a scratch area of LDS).  A weight row's quants sit 2
+//   its route slots.  A wave issues up to six loads a step (the stage's 17
+//   weight and 18 activation wave-loads over the eight waves; the step's
+//   wait covers all of them).  A weight row's quants sit 2
 //   bytes into each 34-byte block, so a fragment of an even block is cut from
 //   three aligned dwords.
 // Arithmetic and order are those of the form above: acc = fma(float(sumi),
@@ -466,8 +478,8 @@ constexpr int S_A = S_CHUNK * S_AROW;            // 18432: 64 routes
 constexpr int S_STAGE = S_W + S_A;               // 35840
 constexpr int S_DX = 2 * S_STAGE;                // per wave: fp32 [8 blocks][32 slots]
 constexpr int S_DX_WAVE = S_STEP_BLOCKS * 32 * 4;    // 1024
-constexpr int S_JUNK = S_DX + 8 * S_DX_WAVE;     // 1 KB target of the loads no wave needs
-constexpr int S_LDS = S_JUNK + 1024;             // 80896
+constexpr int S_ZERO = S_DX + 8 * S_DX_WAVE;     // 256 zero bytes (the GEMM layout's scale operands)
+constexpr int S_LDS = S_ZERO + 256;              // 80128
 constexpr int S_W_LOADS = S_W / 1024;            // 17 wave-loads of 1 KB
 constexpr int S_A_LOADS = S_A / 1024;            // 18
 constexpr int S_SLOTS = (S_A_LOADS + 7) / 8;     // 3 wave-loads of each kind per wave
@@ -629,6 +641,7 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
     int n_active;
     uint32_t total;
     if (!grouping_units<S_CHUNK>(p, l, n_active, total)) return;   // every workgroup alike: no draw
+    if (G8 && PAIR && threadIdx.x < 64) reinterpret_cast<uint32_t*>(lds + S_ZERO)[threadIdx.x] = 0u;
     const uint32_t x = blockIdx.x % XCDS;
     uint32_t first, end;
     xcd_range(total, x, first, end);
@@ -677,9 +690,9 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
         const uint32_t base = lds0 + b * S_STAGE;
 #pragma unroll
         for (int j = 0; j < S_SLOTS; ++j) {
-            const int i = 8 * j + wave;
-            load_lds16(((G.w_up >> j) & 1u ? w1 : w0) + G.w_off[j], i < S_W_LOADS ? base + i * 1024 : lds0 + S_JUNK);
-            load_lds16(act + ao[j], i < S_A_LOADS ? base + S_W + i * 1024 : lds0 + S_JUNK);
+            const int i = 8 * j + wave;                // wave-uniform: a wave skips the pieces past the stage
+            if (i < S_W_LOADS) load_lds16(((G.w_up >> j) & 1u ? w1 : w0) + G.w_off[j], base + i * 1024);
+            if (i < S_A_LOADS) load_lds16(act + ao[j], base + S_W + i * 1024);
         }
     };
     float* dxt = reinterpret_cast<float*>(lds + S_DX + wave * S_DX_WAVE);   // [8 blocks][32 slots]
@@ -736,12 +749,19 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                     float4 dx4[2][NL];
                     i32x4 d[2][NL][NM];
                     // G8: the scale products d_x * d_w of each block's 16 x 16 tile
-                    // come from the matrix cores, an fp16 product whose only
-                    // nonzero K term is lane group 0's (exact in fp32: the same
-                    // values as the fp32 multiply)
-                    uint32_t dwh[2][NM], dxh[2][NL];
-                    f32x4 sc[2][NL][NM];
+                    // come from the matrix cores, an fp16 product with one
+                    // nonzero K term (exact in fp32: the same values as the fp32
+                    // multiply).  Gate/up: the weight operand is four of the
+                    // row's scales as stored (blocks 4 (K / 4) .. + 3 at K terms
+                    // 0..3) and the activation operand holds block K's d_x at
+                    // term K % 4, zeros elsewhere, lane groups 1..3 reading it
+                    // from a zero area, so neither needs masking.  The down (two
+                    // route tiles a wave, no registers to spare) masks both
+                    // operands to lane group 0's first term.
+                    f16x4 dws[NM];
+                    uint32_t dxh[2][NL], dwh[2][NM];
                     const uint32_t kmask = (l >> 4) == 0 ? 0xFFFFu : 0u;
+                    f32x4 sc[2][NL][NM];
 #pragma unroll
                     for (int m = 0; m < NM; ++m) {
                         const uint8_t* wr = W + (m * 32 + rh + c) * S_WROW;
@@ -751,9 +771,13 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                             const int qx = q8 ^ (c & 8);
                             wb[0][m] = *reinterpret_cast<const long*>(wr + 16 + 32 * K0 + qx);
                             wb[1][m] = *reinterpret_cast<const long*>(wr + 16 + 32 * (K0 + 1) + qx);
-                            const uint32_t sw = *reinterpret_cast<const uint32_t*>(wr + 2 * K0);
-                            dwh[0][m] = sw & kmask;
-                            dwh[1][m] = (sw >> 16) & kmask;
+                            if constexpr (PAIR) {
+                                dws[m] = *reinterpret_cast<const f16x4*>(wr + 8 * (K0 / 4));
+                            } else {
+                                const uint32_t sw = *reinterpret_cast<const uint32_t*>(wr + 2 * K0);
+                                dwh[0][m] = sw & kmask;
+                                dwh[1][m] = (sw >> 16) & kmask;
+                            }
                         } else {
                             wb[0][m] = w_frag<K0>(wr, q8);
                             wb[1][m] = w_frag<K0 + 1>(wr, q8);
@@ -771,8 +795,14 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                         xa[0][rt] = a_frag<K0>(K0 == 7 ? ar7 : ar0, q8);
                         xa[1][rt] = a_frag<K0 + 1>(K0 + 1 == 7 ? ar7 : ar0, q8);
                         if constexpr (G8) {
-                            dxh[0][rt] = *reinterpret_cast<const uint16_t*>(ar0 + K0 * Q81_BYTES) & kmask;
-                            dxh[1][rt] = *reinterpret_cast<const uint16_t*>(ar0 + (K0 + 1) * Q81_BYTES) & kmask;
+                            if constexpr (PAIR) {
+                                const uint8_t* dxa = (l >> 4) == 0 ? ar0 : lds + S_ZERO;
+                                dxh[0][rt] = *reinterpret_cast<const uint16_t*>(dxa + K0 * Q81_BYTES);
+                                dxh[1][rt] = *reinterpret_cast<const uint16_t*>(dxa + (K0 + 1) * Q81_BYTES);
+                            } else {
+                                dxh[0][rt] = *reinterpret_cast<const uint16_t*>(ar0 + K0 * Q81_BYTES) & kmask;
+                                dxh[1][rt] = *reinterpret_cast<const uint16_t*>(ar0 + (K0 + 1) * Q81_BYTES) & kmask;
+                            }
                         } else {
                             dx4[0][rt] = *reinterpret_cast<const float4*>(dxt + K0 * 32 + rt * 16 + q8 / 2);
                             dx4[1][rt] = *reinterpret_cast<const float4*>(dxt + (K0 + 1) * 32 + rt * 16 + q8 / 2);
@@ -789,7 +819,8 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
                                 if constexpr (G8) {
                                     const f32x4 zf = {0.0f, 0.0f, 0.0f, 0.0f};
                                     sc[kk][rt][m] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                                        half4_lo(dxh[kk][rt]), half4_lo(dwh[kk][m]), zf, 0, 0, 0);
+                                        PAIR ? dx_term<K0>(dxh[kk][rt], kk) : half4_lo(dxh[kk][rt]),
+                                        PAIR ? dws[m] : half4_lo(dwh[kk][m]), zf, 0, 0, 0);
                                 }
                             }
 #pragma unroll
