@@ -396,7 +396,9 @@ size_t moe_grouping_bytes_wide(int64_t ncols, int32_t topk);
  *   workgroups.
  *   stages MOEQ8_GATE_UP_SWIGLU_G8 / MOEQ8_DOWN_G8: the gate/up and down
  *   stages on weights repacked by q8_0_pack_gemm_rows, with the same results
- *   bit for bit.  They always take the staged form below, so they require
+ *   bit for bit while the weight scales are finite (an infinite or NaN fp16
+ *   weight scale makes the gate/up outputs of its row NaN where the plain
+ *   rows may give an infinity).  They always take the staged form below, so they require
  *   k % 256 == 0, n % 32 == 0 (gate/up) or n % 64 == 0 (down), 16-byte
  *   aligned weights, activations, row and expert strides and activation
  *   rows, else MOEQ8_EUNSUPPORTED.
