@@ -622,7 +622,8 @@ __device__ __forceinline__ void stage_act(const GemmParams& p, const StageGeomet
 // piece is one aligned 8-byte read, and the 16 rows of a wave's read fall
 // into different LDS banks.  The same bytes reach the same lanes, so the
 // results are those of the plain layout.
-template <bool PAIR, bool G8 = false>
+// TPU: row tiles a unit (p.tiles counts units of TPU tiles).
+template <bool PAIR, bool G8 = false, int TPU = 1>
 __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_gemm_staged(
     const GemmParams p) {
     __shared__ __align__(16) uint8_t lds[S_LDS];
@@ -673,6 +674,8 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
         drain();
         return;
     }
+    t *= (uint32_t)TPU;                                // the unit's first row tile
+    int ti = 0;                                        // row tile of the unit
 
     StageGeometry G;
     constexpr bool ROT = G8 || !PAIR;
@@ -859,28 +862,36 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
         // result is in after the next step's wait), published by the barrier
         // of the step after; a unit of one or two steps draws at its last
         // step and waits for it
+        // the next unit is drawn only in its last row tile; before that the
+        // next row tile of the same routes follows, with no lookup
+        const bool last_tile = ti + 1 == TPU;
         uint32_t t_pend = 0;
         for (int s = 0; s + 1 < nsteps; ++s, ++g) {
             wait_vm0();
-            if (nsteps >= 3 && s == nsteps - 2 && threadIdx.x == 0) s_tick = t_pend;
+            if (last_tile && nsteps >= 3 && s == nsteps - 2 && threadIdx.x == 0) s_tick = t_pend;
             lds_barrier();
             load_step(e, t, a_off, s + 1, (g & 1) ^ 1);
-            if (nsteps >= 3 && s == nsteps - 3 && threadIdx.x == 0) t_pend = draw();
+            if (last_tile && nsteps >= 3 && s == nsteps - 3 && threadIdx.x == 0) t_pend = draw();
             if (live[0]) compute(g & 1);
         }
-        if (nsteps < 3) {
+        if (last_tile && nsteps < 3) {
             if (threadIdx.x == 0) s_tick = draw();
             lds_barrier();
         }
         // the last step: the next unit's lookup and activation sources are
         // read while this step's data arrives, and its first step loads while
         // this one is computed
-        const uint32_t un = first + s_tick;
-        int ne = 0, nrb = 0, nnr = 0;
-        uint32_t nt = 0;
-        const bool more = un < end;
-        const bool has_next = more && unit_at<S_CHUNK>(p, l, n_active, un, ne, nrb, nnr, nt);
-        if (has_next) stage_act(p, G, nrb, nnr, a_off);   // this unit's are no longer needed
+        uint32_t un = 0;
+        int ne = e, nrb = rbegin, nnr = nr;
+        uint32_t nt = t + 1;
+        bool more = true, has_next = true;
+        if (last_tile) {
+            un = first + s_tick;
+            more = un < end;
+            has_next = more && unit_at<S_CHUNK>(p, l, n_active, un, ne, nrb, nnr, nt);
+            nt *= (uint32_t)TPU;
+            if (has_next) stage_act(p, G, nrb, nnr, a_off);   // this unit's are no longer needed
+        }
         wait_vm0();
         lds_barrier();
         if (has_next) load_step(ne, nt, a_off, 0, (g & 1) ^ 1);
@@ -905,7 +916,12 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
             if (more) drain();
             break;
         }
-        u = un;
+        if (last_tile) {
+            u = un;
+            ti = 0;
+        } else {
+            ++ti;
+        }
         e = ne;
         rbegin = nrb;
         nr = nnr;
@@ -1003,23 +1019,35 @@ extern "C" int moe_grouped_gemm(int32_t stage, const void* w_a, const void* w_b,
                           (uint64_t)expert_stride_bytes | (uint64_t)p.act_row_bytes) & 15u) == 0;
     if (staged) {
         const int64_t tiles = n / srows;
+        // a unit of at most 4 steps a tile (the down at k = 1024) takes two
+        // row tiles of its routes when the tiles pair up: half the unit
+        // changes, whose lookup waits on two dependent reads (the down 285 ->
+        // 261 and 386 -> 350 us at 512 / 1024 columns on 256 experts); longer
+        // units keep one, as two made the last units of a launch too long
+        // (the plain rows' gate/up 484 -> 531 us at 512 columns)
+        const int tpu = !pair && tiles % 2 == 0 && k <= 4 * S_STEP_BLOCKS * QK ? 2 : 1;
         // an upper bound of the units; the grid is at most two workgroups a
         // CU, a multiple of the XCDs, each taking its units in turn
-        const int64_t units = (std::min<int64_t>(R, n_local_expert) + R / S_CHUNK) * tiles;
+        const int64_t units = (std::min<int64_t>(R, n_local_expert) + R / S_CHUNK) * (tiles / tpu);
         if (units > 0xffffffffLL) return MOEQ8_EUNSUPPORTED;
         const int cus = compute_units();
         if (cus < 1) return MOEQ8_EHIP;
         const int64_t cap = (int64_t)S_WG_PER_CU * cus;
         const int64_t grid = (std::min<int64_t>(units, cap) + XCDS - 1) / XCDS * XCDS;
-        p.tiles = (int32_t)tiles;
+        p.tiles = (int32_t)(tiles / tpu);
+        const dim3 sg((uint32_t)grid), sb(S_THREADS);
         if (g8 && pair)
-            hipLaunchKernelGGL((k_grouped_gemm_staged<true, true>), dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+            hipLaunchKernelGGL((k_grouped_gemm_staged<true, true>), sg, sb, 0, hs, p);
+        else if (g8 && tpu == 2)
+            hipLaunchKernelGGL((k_grouped_gemm_staged<false, true, 2>), sg, sb, 0, hs, p);
         else if (g8)
-            hipLaunchKernelGGL((k_grouped_gemm_staged<false, true>), dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+            hipLaunchKernelGGL((k_grouped_gemm_staged<false, true>), sg, sb, 0, hs, p);
         else if (pair)
-            hipLaunchKernelGGL(k_grouped_gemm_staged<true>, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+            hipLaunchKernelGGL(k_grouped_gemm_staged<true>, sg, sb, 0, hs, p);
+        else if (tpu == 2)
+            hipLaunchKernelGGL((k_grouped_gemm_staged<false, false, 2>), sg, sb, 0, hs, p);
         else
-            hipLaunchKernelGGL(k_grouped_gemm_staged<false>, dim3((uint32_t)grid), dim3(S_THREADS), 0, hs, p);
+            hipLaunchKernelGGL(k_grouped_gemm_staged<false>, sg, sb, 0, hs, p);
         return check_launch();
     }
     if (g8) return MOEQ8_EUNSUPPORTED;                 // the GEMM layout is read by the staged form only

@@ -1034,6 +1034,8 @@ def _gemm_case(c, n_exp, local, topk, hidden, inter, seed):
     (3, 16, 16, 8, 128, 64),         # K = 128 and 64: fewer block pairs than a step holds
     (1, 4, 4, 4, 64, 64),
     (24, 8, 8, 8, 256, 2048),        # down K = 2048: the down staged in LDS too
+    (33, 16, 16, 8, 512, 1024),      # down K = 1024, 8 row tiles: units of two tiles
+    (20, 8, 8, 8, 320, 1024),        # down K = 1024, 5 row tiles: units of one
 ])
 def test_grouped_gemm_vs_oracle(c, n_exp, local, topk, hidden, inter):
     """moe_grouped_gemm gate/up (h) and down (y) against the oracle route by
@@ -1159,9 +1161,10 @@ def test_staged_gemm_work_counters_return_to_zero():
     counters (256 call slots, handed out in turn); a call leaves its counters
     at zero.  300 calls in a row (every slot reused) with units of one, two
     and four K steps (the next unit drawn at the last step, or two steps
-    before it) and a down of 8 steps, on the plain rows and the GEMM layout in
-    turn: every call gives the bits of the register-fed form (a counter left
-    off zero would skip units, leaving NaN rows)."""
+    before it) and downs of 8 steps and of 4 (units of two row tiles), on the
+    plain rows and the GEMM layout in turn: every call gives the bits of the
+    register-fed form (a counter left off zero would skip units, leaving NaN
+    rows)."""
     say("staged gemm work counters, 300 calls")
     c, n_exp, local, topk, inter = 40, 8, 8, 8, 64
     cases = []
@@ -1172,24 +1175,27 @@ def test_staged_gemm_work_counters_return_to_zero():
         moeq8.moe_grouped_gemm(moeq8.GATE_UP_SWIGLU, _off_alignment(wgd), _off_alignment(wud), xd, g, n=inter,
                                k=hidden, n_local_expert=local, ncols=c, topk=topk, out=ref)
         cases.append((hidden, wgd, wud, xd, g, ref))
-    (_, _, _), (_, _, wdd), _, _, _, gd = _gemm_case(c, n_exp, local, topk, 256, 2048, 11)
-    hq = moeq8.q8_1_quantize_rows(to_dev(workloads.normal_f32(12, (c * topk, 2048), 1.0)))
-    yref = torch.full((c, topk, 256), float("nan"), device=DEV)
-    moeq8.moe_grouped_gemm(moeq8.DOWN, _off_alignment(wdd), None, hq, gd, n=256, k=2048, n_local_expert=local,
-                           ncols=c, topk=topk, out=yref)
+    downs = []
+    for kd in (2048, 1024):                            # 8 steps a unit; 4, two row tiles a unit
+        (_, _, _), (_, _, wdd), _, _, _, gd = _gemm_case(c, n_exp, local, topk, 256, kd, 11 + kd)
+        hq = moeq8.q8_1_quantize_rows(to_dev(workloads.normal_f32(12 + kd, (c * topk, kd), 1.0)))
+        yref = torch.full((c, topk, 256), float("nan"), device=DEV)
+        moeq8.moe_grouped_gemm(moeq8.DOWN, _off_alignment(wdd), None, hq, gd, n=256, k=kd, n_local_expert=local,
+                               ncols=c, topk=topk, out=yref)
+        downs.append((kd, wdd, moeq8.q8_0_pack_gemm_rows(wdd, local * 256, kd), gd, hq, yref))
     # the GEMM layout's kernels draw from the same counters
     packed = {hidden: (moeq8.q8_0_pack_gemm_rows(wgd, local * inter, hidden),
                        moeq8.q8_0_pack_gemm_rows(wud, local * inter, hidden)) for hidden, wgd, wud, _, _, _ in cases}
-    pdd = moeq8.q8_0_pack_gemm_rows(wdd, local * 256, 2048)
     h = torch.empty((c, topk, inter), device=DEV)
     y = torch.empty((c, topk, 256), device=DEV)
     for i in range(300):
         g8 = (i // 4) % 2 == 1
         if i % 4 == 3:
+            kd, wdd, pdd, gd, hq, yref = downs[(i // 8) % 2]
             y.fill_(float("nan"))
             moeq8.moe_grouped_gemm(moeq8.DOWN_G8 if g8 else moeq8.DOWN, pdd if g8 else wdd, None, hq, gd, n=256,
-                                   k=2048, n_local_expert=local, ncols=c, topk=topk, out=y)
-            assert bits_equal(y, yref), i
+                                   k=kd, n_local_expert=local, ncols=c, topk=topk, out=y)
+            assert bits_equal(y, yref), (i, kd)
         else:
             hidden, wgd, wud, xd, g, ref = cases[i % 4]
             a, b = packed[hidden] if g8 else (wgd, wud)
