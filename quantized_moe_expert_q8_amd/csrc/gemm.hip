@@ -450,12 +450,14 @@ __global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(nt
 //   gate/up: wave w runs rows 16 (w & 1) + [0, 16) of both matrices against
 //            route tile w >> 1;  down: rows 16 (w & 3) + [0, 16) against route
 //            tiles 2 (w >> 2) and 2 (w >> 2) + 1.
-// The grid is two workgroups a CU; each takes every S-th unit of its XCD's
-// range (S = workgroups an XCD), and the steps of its units form one
-// pipeline: the next step's loads, the next unit's first step included, are
-// in flight while a step is computed, and the next unit's lookup and route
-// entries are read while its first step loads, so a unit costs its steps and
-// not a fresh fill (the down has only a few steps a unit).
+// The grid is two workgroups a CU; the workgroups of an XCD take that XCD's
+// units from a work counter in the order they ask (below), and the steps of a
+// workgroup's units form one pipeline: the next step's loads, the next unit's
+// first step included, are in flight while a step is computed, and the next
+// unit's lookup and route entries are read while the last step's data
+// arrives, so a unit costs its steps and not a fresh fill.  Units of at most
+// four steps a row tile (the down at k = 1024) take two row tiles of their
+// routes (TPU = 2): the second follows with no lookup.
 //   LDS per step: weights 64 rows x 272 bytes (a row's 8 blocks, as stored),
 //   activations 64 routes x 288 bytes; per wave, fp32 activation scales of
 //   its route slots.  A wave issues up to six loads a step (the stage's 17
@@ -465,8 +467,10 @@ __global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(nt
 //   three aligned dwords.
 // Arithmetic and order are those of the form above: acc = fma(float(sumi),
 // d_w * d_x, acc), blocks ascending from +0, so both forms give the same bits.
-// The form is bound by that per-block scaling (three VALU operations per
-// output, row and block) and its LDS reads more than by its loads.
+// Timing copies put the form's time in its loads and its instruction issue
+// together (on the GEMM layout at 1024 columns: loads alone about 85% of the
+// whole, the arithmetic alone about 25%, the per-block scaling two or three
+// VALU operations for every output, row and block).
 constexpr int S_THREADS = 512;
 constexpr int S_WG_PER_CU = 2;                   // the LDS below holds two
 constexpr int S_CHUNK = 64;                      // routes per unit
