@@ -288,7 +288,7 @@ def wide_products_for(ncols: int, topk: int, n_local_expert: int) -> str:
     """The faster grouped products for a batch: the matrix-core GEMM once the
     mean expert serves about four routes or more, else the MMVQ passes
     (measured on 256 experts, top-8: 32 columns, one route per expert, MMVQ
-    284 vs GEMM 350 us a layer; 128 columns, four routes, GEMM 577 vs 640)."""
+    282 vs GEMM 315 us a layer; 128 columns, four routes, GEMM 512 vs 636)."""
     return "gemm" if ncols * topk >= 4 * n_local_expert else "mmvq"
 
 
