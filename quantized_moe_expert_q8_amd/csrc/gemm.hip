@@ -483,7 +483,8 @@ constexpr int S_STAGE = S_W + S_A;               // 35840
 constexpr int S_DX = 2 * S_STAGE;                // per wave: fp32 [8 blocks][32 slots]
 constexpr int S_DX_WAVE = S_STEP_BLOCKS * 32 * 4;    // 1024
 constexpr int S_ZERO = S_DX + 8 * S_DX_WAVE;     // 256 zero bytes (the GEMM layout's scale operands)
-constexpr int S_LDS = S_ZERO + 256;              // 80128
+constexpr int S_ROUTES = S_ZERO + 256;           // the next unit's 64 route entries (the GEMM layout's gate/up)
+constexpr int S_LDS = S_ROUTES + 256;            // 80384
 constexpr int S_W_LOADS = S_W / 1024;            // 17 wave-loads of 1 KB
 constexpr int S_A_LOADS = S_A / 1024;            // 18
 constexpr int S_SLOTS = (S_A_LOADS + 7) / 8;     // 3 wave-loads of each kind per wave
@@ -522,6 +523,16 @@ __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) alone
+
+// One wave-wide direct load of 4 bytes a lane into LDS (lane i writes bytes
+// [lds + 4 i, lds + 4 i + 4)); as load_lds16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds4(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* b, int off) {
     return *reinterpret_cast<const uint32_t*>(b + off);
@@ -598,26 +609,92 @@ __device__ __forceinline__ void stage_geometry(const GemmParams& p, int wave, in
 // The activation sources of a unit: byte offsets into the activations of
 // this lane's pieces (a piece past the unit's staged route slots reads the
 // unit's first activation piece, one cached line for all such lanes).
-__device__ __forceinline__ void stage_act(const GemmParams& p, const StageGeometry& G, int rbegin, int nr,
-                                          int (&a_off)[S_SLOTS]) {
+// (in two parts: the route entries, read at indices inside the unit; the
+// offsets from them)
+__device__ __forceinline__ void stage_routes(const GemmParams& p, const StageGeometry& G, int rbegin, int nr,
+                                             int& r_first, int (&rts)[S_SLOTS]) {
     const int Rk = p.ncols * p.topk;
     const int32_t* route = p.grouping + 4 + 2 * (int64_t)Rk + 1;
+    r_first = route[rbegin];
+#pragma unroll
+    for (int j = 0; j < S_SLOTS; ++j) rts[j] = route[rbegin + min(max(G.a_slot[j], 0), nr - 1)];
+}
+
+__device__ __forceinline__ void stage_offsets(const GemmParams& p, const StageGeometry& G, int nr, int r_first,
+                                              const int (&rts)[S_SLOTS], int (&a_off)[S_SLOTS]) {
+    const int Rk = p.ncols * p.topk;
     const int nslot = (nr + 15) & ~15;                 // staged route slots: whole tiles
     auto row_off = [&](int rt) {
         const int rr = (rt >= 0 && rt < Rk) ? rt : 0;
         return (int)(((uint64_t)(uint32_t)rr * p.act_route_mul) >> 32) * (int)p.act_row_bytes;
     };
-    // every entry read at an index inside the unit, all before the first use
-    const int r_first = route[rbegin];
-    int rts[S_SLOTS];
-#pragma unroll
-    for (int j = 0; j < S_SLOTS; ++j) rts[j] = route[rbegin + min(max(G.a_slot[j], 0), nr - 1)];
     const int first = row_off(r_first);
 #pragma unroll
     for (int j = 0; j < S_SLOTS; ++j) {
         const int slot = G.a_slot[j];
         a_off[j] = (slot >= 0 && slot < nslot) ? row_off(rts[j]) + G.a_part[j] : first;
     }
+}
+
+__device__ __forceinline__ void stage_act(const GemmParams& p, const StageGeometry& G, int rbegin, int nr,
+                                          int (&a_off)[S_SLOTS]) {
+    int r_first, rts[S_SLOTS];
+    stage_routes(p, G, rbegin, nr, r_first, rts);
+    stage_offsets(p, G, nr, r_first, rts, a_off);
+}
+
+// The GEMM layout's kernels keep a copy of the grouping's group table in the
+// LDS the plain layout uses for its fp32 activation scales: entry a is
+// {expert, or -1 for an invalid entry; first route; end; units of groups
+// 0..a}, so a unit is looked up in LDS instead of by a scan over the table
+// in memory (a round trip a unit change).
+constexpr int S_TABLE_GROUPS = 8 * S_DX_WAVE / 16;   // 512
+
+// Wave-wide: the table of the n_active <= S_TABLE_GROUPS groups.
+__device__ void build_unit_table(const GemmParams& p, int l, int n_active, int4* tab) {
+    const int Rk = p.ncols * p.topk;
+    const int4* gt = reinterpret_cast<const int4*>(p.grouping + grouping_table_word(Rk));
+    const uint32_t tiles = (uint32_t)p.tiles;
+    uint32_t carry = 0;
+    for (int b0 = 0; b0 < n_active; b0 += 64) {
+        const int a = b0 + l;
+        const int4 g = a < n_active ? gt[a] : make_int4(-1, 0, 0, 0);
+        const bool ok = (a < n_active) & (g.x >= 0) & (g.x < p.n_local) & (g.y >= 0) & (g.z >= g.y) & (g.z <= Rk);
+        const uint32_t un = ok ? (uint32_t)((g.z - g.y + S_CHUNK - 1) / S_CHUNK) * tiles : 0u;
+        const uint32_t incl = wave_incl_scan(un, l) + carry;
+        if (a < n_active) tab[a] = make_int4(ok ? g.x : -1, g.y, g.z, (int)incl);
+        carry = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    }
+}
+
+// Unit u (below the total) from the LDS table, as unit_at.
+__device__ __forceinline__ bool unit_at_lds(const int4* tab, uint32_t tiles, int n_active, int l, uint32_t u,
+                                            int& e, int& rbegin, int& nr, uint32_t& t) {
+    int gbegin = 0, gend = 0;
+    uint32_t ubase = 0;
+    bool found = false;
+    for (int b0 = 0; b0 < n_active && !found; b0 += 64) {
+        const int a = b0 + l;
+        const int4 g = a < n_active ? tab[a] : make_int4(-1, 0, 0, 0);
+        const uint32_t un = g.x >= 0 ? (uint32_t)((g.z - g.y + S_CHUNK - 1) / S_CHUNK) * tiles : 0u;
+        const uint32_t incl = (uint32_t)g.w;
+        const uint64_t m = __ballot((un > 0) & (incl - un <= u) & (u < incl));
+        if (m) {
+            const int src = __builtin_ctzll(m);
+            e = __builtin_amdgcn_readlane(g.x, src);
+            gbegin = __builtin_amdgcn_readlane(g.y, src);
+            gend = __builtin_amdgcn_readlane(g.z, src);
+            ubase = (uint32_t)__builtin_amdgcn_readlane((int)(incl - un), src);
+            found = true;
+        }
+    }
+    if (!found || gend <= gbegin) return false;
+    const uint32_t nchunk = (uint32_t)(gend - gbegin + S_CHUNK - 1) / S_CHUNK;
+    const uint32_t rem = u - ubase;
+    t = rem / nchunk;
+    rbegin = gbegin + (int)(rem - t * nchunk) * S_CHUNK;
+    nr = min(gend - rbegin, S_CHUNK);
+    return true;
 }
 
 // G8: the weights (gate/up, or down) are in the layout of q8_0_pack_gemm_rows (per 8-block
@@ -667,6 +744,14 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
             while (draw() < cnt) {
             }
     };
+    // the GEMM layout's units are looked up in an LDS copy of the group table
+    int4* const tab = reinterpret_cast<int4*>(lds + S_DX);
+    const bool use_tab = G8 && n_active <= S_TABLE_GROUPS;
+    if (use_tab && wave == 0) build_unit_table(p, l, n_active, tab);
+    auto lookup = [&](uint32_t uu, int& ee, int& rb, int& rn, uint32_t& tt) -> bool {
+        return use_tab ? unit_at_lds(tab, (uint32_t)p.tiles, n_active, l, uu, ee, rb, rn, tt)
+                       : unit_at<S_CHUNK>(p, l, n_active, uu, ee, rb, rn, tt);
+    };
     if (threadIdx.x == 0) s_tick = draw();
     __syncthreads();
     uint32_t u = first + s_tick;
@@ -674,7 +759,7 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
     // the current unit: expert, route entries, row tile (wave-uniform)
     int e, rbegin, nr;
     uint32_t t;
-    if (!unit_at<S_CHUNK>(p, l, n_active, u, e, rbegin, nr, t)) {   // before any load
+    if (!lookup(u, e, rbegin, nr, t)) {                // before any load
         drain();
         return;
     }
@@ -870,12 +955,27 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
         // next row tile of the same routes follows, with no lookup
         const bool last_tile = ti + 1 == TPU;
         uint32_t t_pend = 0;
+        // the gate/up on the GEMM layout looks the next unit up in LDS a step
+        // before the last, and wave 0 fetches its 64 route entries into LDS
+        // then (the last step's wait covers the load, its barrier publishes
+        // the entries)
+        constexpr bool EARLY = G8 && PAIR;
+        bool x_done = false, x_has = false, x_more = false;
+        uint32_t x_un = 0, x_nt = 0;
+        int x_ne = 0, x_nrb = 0, x_nnr = 0;
         for (int s = 0; s + 1 < nsteps; ++s, ++g) {
             wait_vm0();
             if (last_tile && nsteps >= 3 && s == nsteps - 2 && threadIdx.x == 0) s_tick = t_pend;
             lds_barrier();
             load_step(e, t, a_off, s + 1, (g & 1) ^ 1);
             if (last_tile && nsteps >= 3 && s == nsteps - 3 && threadIdx.x == 0) t_pend = draw();
+            if (EARLY && use_tab && last_tile && nsteps >= 3 && s == nsteps - 2) {
+                x_un = first + s_tick;
+                x_more = x_un < end;
+                x_has = x_more && unit_at_lds(tab, (uint32_t)p.tiles, n_active, l, x_un, x_ne, x_nrb, x_nnr, x_nt);
+                if (x_has && wave == 0) load_lds4(route + x_nrb + min(l, x_nnr - 1), lds0 + S_ROUTES);
+                x_done = true;
+            }
             if (live[0]) compute(g & 1);
         }
         if (last_tile && nsteps < 3) {
@@ -889,15 +989,31 @@ __global__ __launch_bounds__(S_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)
         int ne = e, nrb = rbegin, nnr = nr;
         uint32_t nt = t + 1;
         bool more = true, has_next = true;
-        if (last_tile) {
+        if (last_tile && EARLY && x_done) {
+            un = x_un;
+            more = x_more;
+            has_next = x_has;
+            ne = x_ne;
+            nrb = x_nrb;
+            nnr = x_nnr;
+            nt = x_nt * (uint32_t)TPU;
+        } else if (last_tile) {
             un = first + s_tick;
             more = un < end;
-            has_next = more && unit_at<S_CHUNK>(p, l, n_active, un, ne, nrb, nnr, nt);
+            has_next = more && lookup(un, ne, nrb, nnr, nt);
             nt *= (uint32_t)TPU;
             if (has_next) stage_act(p, G, nrb, nnr, a_off);   // this unit's are no longer needed
         }
         wait_vm0();
         lds_barrier();
+        if (EARLY && x_done && has_next) {
+            // the activation sources of the next unit from its route entries in LDS
+            const int32_t* rr = reinterpret_cast<const int32_t*>(lds + S_ROUTES);
+            int rts[S_SLOTS];
+#pragma unroll
+            for (int j = 0; j < S_SLOTS; ++j) rts[j] = rr[min(max(G.a_slot[j], 0), nnr - 1)];
+            stage_offsets(p, G, nnr, rr[0], rts, a_off);
+        }
         if (has_next) load_step(ne, nt, a_off, 0, (g & 1) ^ 1);
         if (live[0]) compute(g & 1);
         ++g;
