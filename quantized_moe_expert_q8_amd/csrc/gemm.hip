@@ -457,7 +457,8 @@ __global__ __launch_bounds__(GEMM_THREADS) __attribute__((amdgpu_waves_per_eu(nt
 // unit's lookup and route entries are read while the last step's data
 // arrives, so a unit costs its steps and not a fresh fill.  Units of at most
 // four steps a row tile (the down at k = 1024) take two row tiles of their
-// routes (TPU = 2): the second follows with no lookup.
+// routes (TPU = 2): the second follows with no lookup.  On the GEMM layout
+// the lookup reads an LDS copy of the group table (below).
 //   LDS per step: weights 64 rows x 272 bytes (a row's 8 blocks, as stored),
 //   activations 64 routes x 288 bytes; per wave, fp32 activation scales of
 //   its route slots.  A wave issues up to six loads a step (the stage's 17
