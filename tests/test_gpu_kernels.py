@@ -1238,6 +1238,7 @@ def test_gemm_layout_bytes(rows, k):
     (96, 256, 256, 8, 1024, 1024),   # ~240 active experts; the down at k = 1024 (4 steps a unit)
     (20, 16, 16, 8, 2048, 2048),     # k = 2048 both ways: 8 steps a unit
     (48, 512, 512, 8, 1024, 256),    # 384 routes over 512 local experts
+    (128, 1024, 1024, 8, 256, 256),  # more active experts than the LDS unit table holds (global lookup)
 ])
 def test_gemm_layout_equals_plain(c, n_exp, local, topk, hidden, inter):
     """GATE_UP_SWIGLU_G8 and DOWN_G8 on weights repacked by q8_0_pack_gemm_rows
